@@ -1,0 +1,81 @@
+"""Seeded synthetic inputs shared by the CPU oracle and the HIP path.
+
+This module holds no arithmetic of the attention method: it only draws
+numbers and converts them to the storage format (bf16 bit patterns), so that
+the oracle and the GPU consume the very same input bits.
+
+Recipe (every tensor): ``numpy.random.Generator(PCG64(SeedSequence([cfg,
+tensor_id, layer])))`` draws float32 N(0,1) values, which are rounded to
+bfloat16 with round-to-nearest-even and kept as ``uint16`` bit patterns.
+RMSNorm weights are 1 + 0.1*N(0,1), gate logits N(0,1), gate bias absent.
+Position/page structure (decode contexts, random page permutation, chunked
+prefill lengths) is drawn from the same kind of generator with its own id.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# tensor ids for SeedSequence([cfg, tensor_id, layer])
+T_Q, T_K, T_V, T_GATE, T_QW, T_KW, T_POS, T_PERM, T_LEN, T_MISC = range(10)
+
+
+def rng(cfg: int, tensor_id: int, layer: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg, tensor_id, layer])))
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = u + 0x7FFF + ((u >> 16) & 1)
+    return (u >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 (exact)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def normal_bf16(shape, cfg: int, tensor_id: int, layer: int = 0, scale: float = 1.0,
+                offset: float = 0.0) -> np.ndarray:
+    g = rng(cfg, tensor_id, layer)
+    x = g.standard_normal(size=shape, dtype=np.float32) * np.float32(scale) + np.float32(offset)
+    return f32_to_bf16_bits(x)
+
+
+def attention_inputs(cfg: int, layer: int, n_tok: int, n_q: int = 48, n_kv: int = 8, d: int = 128):
+    """Q/K/V/gate-logit bf16 bits and the two RMSNorm weight vectors of one layer."""
+    return dict(
+        q=normal_bf16((n_tok, n_q, d), cfg, T_Q, layer),
+        k=normal_bf16((n_tok, n_kv, d), cfg, T_K, layer),
+        v=normal_bf16((n_tok, n_kv, d), cfg, T_V, layer),
+        gate=normal_bf16((n_tok, n_q, d), cfg, T_GATE, layer),
+        q_norm_w=normal_bf16((d,), cfg, T_QW, layer, scale=0.1, offset=1.0),
+        k_norm_w=normal_bf16((d,), cfg, T_KW, layer, scale=0.1, offset=1.0),
+    )
+
+
+def decode_positions(cfg: int, n_seqs: int, lo: int, hi: int) -> np.ndarray:
+    """Zero-based positions t of the new token, uniform integers in [lo, hi]."""
+    return rng(cfg, T_POS).integers(lo, hi + 1, size=n_seqs).astype(np.int32)
+
+
+def paged_block_table(cfg: int, ctx_lens, page_size: int = 16, extra_pages: int = 0):
+    """Deal a random permutation of physical pages to sequences in order.
+
+    Returns (block_table [n_seqs][max_pages] int32, n_pages). Unused entries are -1.
+    """
+    ctx_lens = np.asarray(ctx_lens, dtype=np.int64)
+    need = (ctx_lens + page_size - 1) // page_size
+    n_pages = int(need.sum()) + extra_pages
+    perm = rng(cfg, T_PERM).permutation(n_pages).astype(np.int32)
+    maxp = int(need.max()) if len(need) else 0
+    bt = np.full((len(ctx_lens), max(maxp, 1)), -1, dtype=np.int32)
+    off = 0
+    for i, n in enumerate(need):
+        bt[i, :n] = perm[off:off + n]
+        off += n
+    return bt, n_pages
+
+
+def chunked_lengths(cfg: int, n_seqs: int, lo: int, hi: int) -> np.ndarray:
+    return rng(cfg, T_LEN).integers(lo, hi + 1, size=n_seqs).astype(np.int64)
