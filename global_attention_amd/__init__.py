@@ -1,0 +1,281 @@
+"""Python binding of libbeam_attn.so (Beam 1.0 hybrid GQA attention, gfx950).
+
+Argument marshalling only: torch tensors are passed to the C ABI as device
+pointers together with torch's current HIP stream; every step of the
+computation runs in the library's HIP kernels. If the library is missing this
+module raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbeam_attn.so")
+
+LOCAL = 0
+GLOBAL = 1
+
+EXPORTED = [
+    "beam_kv_append", "beam_attn_prefill", "beam_attn_decode",
+    "beam_prefill_workspace_bytes", "beam_decode_workspace_bytes",
+    "beam_kv_bytes", "beam_kv_page_slot", "beam_debug_visibility",
+    "beam_status_str", "beam_last_error",
+]
+
+
+class BeamError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"beam status {status}: {message}")
+        self.status = status
+
+
+class CConfig(ctypes.Structure):
+    _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float),
+                ("ssmax_base", ctypes.c_float), ("ssmax_exp", ctypes.c_float)]
+
+
+class CCache(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("page_size", ctypes.c_int32), ("n_pages", ctypes.c_int32),
+                ("block_table", ctypes.c_void_p), ("max_pages_per_seq", ctypes.c_int32),
+                ("n_seqs", ctypes.c_int32)]
+
+
+@dataclass
+class Config:
+    n_q_heads: int = 48
+    n_kv_heads: int = 8
+    head_dim: int = 128
+    window: int = 512
+    rope_theta: float = 10000.0
+    rms_eps: float = 1e-6
+    ssmax_base: float = 2048.0
+    ssmax_exp: float = 0.1
+
+    def c(self) -> CConfig:
+        return CConfig(self.n_q_heads, self.n_kv_heads, self.head_dim, self.window,
+                       self.rope_theta, self.rms_eps, self.ssmax_base, self.ssmax_exp)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbeam_attn.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m global_attention_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.beam_kv_append.argtypes = [P, P, P, P, P, P, P, I32, P]
+    L.beam_attn_prefill.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, I32, I32, I32, P, P, SZ, P]
+    L.beam_attn_decode.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, P, P, SZ, P]
+    L.beam_prefill_workspace_bytes.argtypes = [P, I32, I32]
+    L.beam_prefill_workspace_bytes.restype = SZ
+    L.beam_decode_workspace_bytes.argtypes = [P, I32, I32, I32, I32]
+    L.beam_decode_workspace_bytes.restype = SZ
+    L.beam_kv_bytes.argtypes = [I64, I32, I32, I32, I32, I32, I32, I32, P, P]
+    L.beam_kv_page_slot.argtypes = [P, I32, I32, I32, I32, P, P]
+    L.beam_debug_visibility.argtypes = [I32, I32, I32, I32, I32, I32, P, P]
+    L.beam_status_str.argtypes = [I32]
+    L.beam_status_str.restype = ctypes.c_char_p
+    L.beam_last_error.restype = ctypes.c_char_p
+    for name in ("beam_kv_append", "beam_attn_prefill", "beam_attn_decode", "beam_kv_bytes",
+                 "beam_kv_page_slot", "beam_debug_visibility"):
+        getattr(L, name).restype = I32
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise BeamError(status, lib().beam_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, dtype, shape=None, name="tensor"):
+    import torch
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+@dataclass
+class KVCache:
+    """One layer's cache as torch device tensors (layouts in include/beam_attn.h)."""
+    kind: int
+    k: object
+    v: object
+    block_table: object = None  # int32 [n_seqs][max_pages] (global)
+    n_pages: int = 0
+    page_size: int = 16
+    _c: CCache = field(default=None, repr=False)
+
+    @staticmethod
+    def allocate_global(cfg: Config, n_pages: int, block_table, device="cuda", fill=None):
+        import torch
+        shape_k = (n_pages, cfg.n_kv_heads, 16, cfg.head_dim)
+        shape_v = (n_pages, cfg.n_kv_heads, cfg.head_dim, 16)
+        k = torch.empty(shape_k, dtype=torch.bfloat16, device=device)
+        v = torch.empty(shape_v, dtype=torch.bfloat16, device=device)
+        if fill is not None:
+            k.view(torch.int16).fill_(fill)
+            v.view(torch.int16).fill_(fill)
+        bt = block_table.to(device=device, dtype=torch.int32).contiguous()
+        return KVCache(GLOBAL, k, v, bt, n_pages)
+
+    @staticmethod
+    def allocate_local(cfg: Config, n_seqs: int, device="cuda", fill=None):
+        import torch
+        k = torch.empty((n_seqs, cfg.n_kv_heads, cfg.window, cfg.head_dim), dtype=torch.bfloat16, device=device)
+        v = torch.empty((n_seqs, cfg.n_kv_heads, cfg.head_dim, cfg.window), dtype=torch.bfloat16, device=device)
+        if fill is not None:
+            k.view(torch.int16).fill_(fill)
+            v.view(torch.int16).fill_(fill)
+        return KVCache(LOCAL, k, v, None, 0)
+
+    def c(self) -> CCache:
+        if self.kind == GLOBAL:
+            bt = self.block_table
+            return CCache(GLOBAL, self.k.data_ptr(), self.v.data_ptr(), self.page_size, self.n_pages,
+                          bt.data_ptr(), bt.shape[1], bt.shape[0])
+        return CCache(LOCAL, self.k.data_ptr(), self.v.data_ptr(), 0, 0, None, 0, self.k.shape[0])
+
+
+def prefill_workspace_bytes(cfg: Config, n_tok: int, n_seqs: int) -> int:
+    c = cfg.c()
+    return int(lib().beam_prefill_workspace_bytes(ctypes.byref(c), n_tok, n_seqs))
+
+
+def decode_workspace_bytes(cfg: Config, kind: int, n_seqs: int, max_pos: int, split_keys: int = 0) -> int:
+    c = cfg.c()
+    return int(lib().beam_decode_workspace_bytes(ctypes.byref(c), kind, n_seqs, max_pos, split_keys))
+
+
+def _workspace(nbytes, device, workspace):
+    import torch
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    if workspace.data_ptr() % 256:
+        raise ValueError("workspace must be 256-byte aligned")
+    if workspace.numel() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes")
+    return workspace
+
+
+def kv_append(cfg: Config, cache: KVCache, k_raw, v_raw, k_norm_w, seq_idx, pos, stream=None):
+    import torch
+    n = k_raw.shape[0]
+    for t, nm in ((k_raw, "k_raw"), (v_raw, "v_raw"), (k_norm_w, "k_norm_w")):
+        _need(t, torch.bfloat16, name=nm)
+    _need(seq_idx, torch.int32, (n,), "seq_idx")
+    _need(pos, torch.int32, (n,), "pos")
+    c, kc = cfg.c(), cache.c()
+    _check(lib().beam_kv_append(ctypes.byref(c), ctypes.byref(kc), _ptr(k_raw), _ptr(v_raw), _ptr(k_norm_w),
+                                _ptr(seq_idx), _ptr(pos), n, _stream(stream)))
+
+
+def prefill(cfg: Config, cache: KVCache, q_raw, k_raw, v_raw, q_norm_w, k_norm_w, gate, cu_seqlens, seq_idx,
+            start_pos, max_chunk_len: int, gate_bias=None, out=None, workspace=None, stream=None):
+    """Chunked varlen prefill of one layer; returns out [n_tok][H][d] (bf16)."""
+    import torch
+    n_tok = q_raw.shape[0]
+    n_seqs = cu_seqlens.shape[0] - 1
+    H, G, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    _need(q_raw, torch.bfloat16, (n_tok, H, d), "q_raw")
+    _need(k_raw, torch.bfloat16, (n_tok, G, d), "k_raw")
+    _need(v_raw, torch.bfloat16, (n_tok, G, d), "v_raw")
+    _need(gate, torch.bfloat16, (n_tok, H, d), "gate")
+    _need(q_norm_w, torch.bfloat16, (d,), "q_norm_w")
+    _need(k_norm_w, torch.bfloat16, (d,), "k_norm_w")
+    _need(cu_seqlens, torch.int32, (n_seqs + 1,), "cu_seqlens")
+    _need(seq_idx, torch.int32, (n_seqs,), "seq_idx")
+    _need(start_pos, torch.int32, (n_seqs,), "start_pos")
+    if gate_bias is not None:
+        _need(gate_bias, torch.float32, (H,), "gate_bias")
+    if out is None:
+        out = torch.empty((n_tok, H, d), dtype=torch.bfloat16, device=q_raw.device)
+    _need(out, torch.bfloat16, (n_tok, H, d), "out")
+    nbytes = prefill_workspace_bytes(cfg, n_tok, n_seqs)
+    workspace = _workspace(nbytes, q_raw.device, workspace)
+    c, kc = cfg.c(), cache.c()
+    _check(lib().beam_attn_prefill(
+        ctypes.byref(c), ctypes.byref(kc), _ptr(q_raw), _ptr(k_raw), _ptr(v_raw), _ptr(q_norm_w),
+        _ptr(k_norm_w), _ptr(gate), _ptr(gate_bias), _ptr(cu_seqlens), _ptr(seq_idx), _ptr(start_pos),
+        n_seqs, n_tok, max_chunk_len, _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def decode(cfg: Config, cache: KVCache, q_raw, q_norm_w, gate, seq_idx, pos, max_pos: int, gate_bias=None,
+           split_keys: int = 0, out=None, workspace=None, stream=None):
+    """One-token decode of one layer; returns out [n_seqs][H][d] (bf16)."""
+    import torch
+    n = q_raw.shape[0]
+    H, d = cfg.n_q_heads, cfg.head_dim
+    _need(q_raw, torch.bfloat16, (n, H, d), "q_raw")
+    _need(gate, torch.bfloat16, (n, H, d), "gate")
+    _need(q_norm_w, torch.bfloat16, (d,), "q_norm_w")
+    _need(seq_idx, torch.int32, (n,), "seq_idx")
+    _need(pos, torch.int32, (n,), "pos")
+    if gate_bias is not None:
+        _need(gate_bias, torch.float32, (H,), "gate_bias")
+    if out is None:
+        out = torch.empty((n, H, d), dtype=torch.bfloat16, device=q_raw.device)
+    _need(out, torch.bfloat16, (n, H, d), "out")
+    nbytes = decode_workspace_bytes(cfg, cache.kind, n, max_pos, split_keys)
+    if nbytes == 0:
+        raise BeamError(3, "invalid decode sizes (max_pos / split_keys)")
+    workspace = _workspace(nbytes, q_raw.device, workspace)
+    c, kc = cfg.c(), cache.c()
+    _check(lib().beam_attn_decode(
+        ctypes.byref(c), ctypes.byref(kc), _ptr(q_raw), _ptr(q_norm_w), _ptr(gate), _ptr(gate_bias),
+        _ptr(seq_idx), _ptr(pos), n, max_pos, split_keys, _ptr(out), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
+    return out
+
+
+def kv_bytes(n_tokens: int, bytes_per_scalar: int = 2, n_global: int = 9, n_local: int = 43, n_kv: int = 8,
+             d: int = 128, window: int = 512, page_size: int = 16):
+    """(logical, paged) KV payload bytes; host-only, no GPU needed."""
+    lg, pg = ctypes.c_uint64(), ctypes.c_uint64()
+    _check(lib().beam_kv_bytes(n_tokens, bytes_per_scalar, n_global, n_local, n_kv, d, window, page_size,
+                               ctypes.byref(lg), ctypes.byref(pg)))
+    return lg.value, pg.value
+
+
+def kv_page_slot(block_table_host, page_size: int, seq: int, t: int):
+    """(physical page, slot) of position t of sequence seq; host-only."""
+    import numpy as np
+    bt = np.ascontiguousarray(block_table_host, dtype=np.int32)
+    pg, sl = ctypes.c_int64(), ctypes.c_int32()
+    _check(lib().beam_kv_page_slot(bt.ctypes.data_as(ctypes.c_void_p), bt.shape[1], page_size, seq, t,
+                                   ctypes.byref(pg), ctypes.byref(sl)))
+    return pg.value, sl.value
+
+
+def debug_visibility(kind: int, window: int, t0: int, n_q: int, s0: int, n_k: int, device="cuda", stream=None):
+    import torch
+    mask = torch.empty((n_q, n_k), dtype=torch.uint8, device=device)
+    _check(lib().beam_debug_visibility(kind, window, t0, n_q, s0, n_k, _ptr(mask), _stream(stream)))
+    return mask

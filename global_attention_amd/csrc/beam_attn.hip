@@ -1,0 +1,389 @@
+// Host side of the C ABI declared in include/beam_attn.h: argument checks,
+// workspace carving and kernel launches. Nothing here allocates, frees or
+// synchronises; every call only enqueues work on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <string>
+
+#include "beam_attn.h"
+#include "beam_device.h"
+#include "beam_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+beam_status fail(beam_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+beam_status ok() {
+  g_last_error.clear();
+  return BEAM_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+beam_status check_cfg(const beam_attn_config* c) {
+  if (!c) return fail(BEAM_E_NULL, "cfg is NULL");
+  if (c->head_dim != beam::D) return fail(BEAM_E_UNSUPPORTED, "head_dim must be 128");
+  if (c->n_q_heads <= 0 || c->n_kv_heads <= 0) return fail(BEAM_E_SHAPE, "head counts must be positive");
+  if (c->n_q_heads % c->n_kv_heads != 0)
+    return fail(BEAM_E_SHAPE, "n_q_heads must be a multiple of n_kv_heads");
+  if (c->n_q_heads / c->n_kv_heads > 16)
+    return fail(BEAM_E_UNSUPPORTED, "at most 16 query heads per KV head");
+  if (c->window <= 0 || c->window % 64 != 0)
+    return fail(BEAM_E_UNSUPPORTED, "window must be a positive multiple of 64");
+  if (!(c->rms_eps >= 0.f) || !(c->ssmax_base > 0.f) || !(c->rope_theta > 0.f))
+    return fail(BEAM_E_RANGE, "rms_eps >= 0, ssmax_base > 0 and rope_theta > 0 required");
+  return BEAM_OK;
+}
+
+beam_status check_cache(const beam_kv_cache* kv) {
+  if (!kv) return fail(BEAM_E_NULL, "cache is NULL");
+  if (kv->kind != BEAM_LOCAL && kv->kind != BEAM_GLOBAL) return fail(BEAM_E_RANGE, "cache kind must be 0 or 1");
+  if (!kv->k || !kv->v) return fail(BEAM_E_NULL, "cache k/v is NULL");
+  if (kv->n_seqs <= 0) return fail(BEAM_E_RANGE, "cache n_seqs must be positive");
+  if (kv->kind == BEAM_GLOBAL) {
+    if (kv->page_size != 16) return fail(BEAM_E_UNSUPPORTED, "page_size must be 16");
+    if (!kv->block_table) return fail(BEAM_E_NULL, "block_table is NULL");
+    if (kv->max_pages_per_seq <= 0 || kv->n_pages <= 0)
+      return fail(BEAM_E_RANGE, "max_pages_per_seq and n_pages must be positive");
+  }
+  return BEAM_OK;
+}
+
+int default_split_keys(int kind) { return kind == BEAM_LOCAL ? 512 : 2048; }
+
+int decode_keys_max(const beam_attn_config* c, int kind, int max_pos) {
+  return kind == BEAM_LOCAL ? (max_pos + 1 < c->window ? max_pos + 1 : c->window) : max_pos + 1;
+}
+
+struct DecodeWs {
+  size_t qp, ml, acc, total;
+  int n_splits, split_keys;
+};
+
+bool decode_ws_layout(const beam_attn_config* c, int kind, int n_seqs, int max_pos, int split_keys,
+                      DecodeWs* ws) {
+  if (split_keys == 0) split_keys = default_split_keys(kind);
+  if (split_keys < 128 || split_keys % 128 != 0 || split_keys > 65536) return false;
+  if (n_seqs <= 0 || max_pos < 0) return false;
+  const int nk = decode_keys_max(c, kind, max_pos);
+  ws->split_keys = split_keys;
+  ws->n_splits = (nk + split_keys - 1) / split_keys;
+  const size_t rows = (size_t)n_seqs * c->n_q_heads * ws->n_splits;
+  ws->qp = 0;
+  ws->ml = align256((size_t)n_seqs * c->n_q_heads * beam::D * 2);
+  ws->acc = ws->ml + align256(rows * 2 * sizeof(float));
+  ws->total = ws->acc + align256(rows * beam::D * sizeof(float));
+  return true;
+}
+
+struct PrefillWs {
+  size_t qp, kw, vw, total;
+  int64_t P;
+};
+
+PrefillWs prefill_ws_layout(const beam_attn_config* c, int n_tok, int n_seqs) {
+  PrefillWs ws;
+  ws.P = beam::ws_positions(n_tok, n_seqs);
+  ws.qp = 0;
+  ws.kw = align256((size_t)n_tok * c->n_q_heads * beam::D * 2);
+  ws.vw = ws.kw + align256((size_t)c->n_kv_heads * ws.P * beam::D * 2);
+  ws.total = ws.vw + align256((size_t)c->n_kv_heads * beam::D * ws.P * 2);
+  return ws;
+}
+
+beam_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(BEAM_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return BEAM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* beam_status_str(beam_status s) {
+  switch (s) {
+    case BEAM_OK: return "ok";
+    case BEAM_E_NULL: return "null pointer";
+    case BEAM_E_SHAPE: return "inconsistent shape";
+    case BEAM_E_RANGE: return "value out of range";
+    case BEAM_E_UNSUPPORTED: return "unsupported configuration";
+    case BEAM_E_WORKSPACE: return "workspace too small";
+    case BEAM_E_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* beam_last_error(void) { return g_last_error.c_str(); }
+
+beam_status beam_kv_bytes(int64_t n_tokens, int32_t bytes_per_scalar, int32_t n_global, int32_t n_local,
+                          int32_t n_kv, int32_t d, int32_t window, int32_t page_size, uint64_t* logical,
+                          uint64_t* paged) {
+  if (!logical || !paged) return fail(BEAM_E_NULL, "output pointer is NULL");
+  if (n_tokens < 0 || bytes_per_scalar <= 0 || n_global < 0 || n_local < 0 || n_kv <= 0 || d <= 0 ||
+      window <= 0 || page_size <= 0)
+    return fail(BEAM_E_RANGE, "sizes must be positive (n_tokens, n_global, n_local >= 0)");
+  const uint64_t per_tok = 2ull * (uint64_t)bytes_per_scalar * (uint64_t)n_kv * (uint64_t)d;
+  const uint64_t n = (uint64_t)n_tokens;
+  const uint64_t slots = n < (uint64_t)window ? n : (uint64_t)window;
+  const uint64_t pages = (n + (uint64_t)page_size - 1) / (uint64_t)page_size;
+  *logical = per_tok * ((uint64_t)n_global * n + (uint64_t)n_local * slots);
+  *paged = per_tok * ((uint64_t)n_global * pages * (uint64_t)page_size + (uint64_t)n_local * slots);
+  return ok();
+}
+
+beam_status beam_kv_page_slot(const int32_t* block_table_host, int32_t max_pages_per_seq, int32_t page_size,
+                              int32_t seq, int32_t t, int64_t* phys_page, int32_t* slot) {
+  if (!block_table_host || !phys_page || !slot) return fail(BEAM_E_NULL, "NULL argument");
+  if (page_size <= 0 || max_pages_per_seq <= 0 || seq < 0 || t < 0)
+    return fail(BEAM_E_RANGE, "negative or zero size/index");
+  if (t / page_size >= max_pages_per_seq) return fail(BEAM_E_RANGE, "position beyond block-table row");
+  *phys_page = block_table_host[(int64_t)seq * max_pages_per_seq + t / page_size];
+  *slot = t % page_size;
+  return ok();
+}
+
+size_t beam_prefill_workspace_bytes(const beam_attn_config* cfg, int32_t n_tok, int32_t n_seqs) {
+  if (check_cfg(cfg) != BEAM_OK || n_tok < 0 || n_seqs <= 0) return 0;
+  return prefill_ws_layout(cfg, n_tok, n_seqs).total;
+}
+
+size_t beam_decode_workspace_bytes(const beam_attn_config* cfg, int32_t kind, int32_t n_seqs, int32_t max_pos,
+                                   int32_t split_keys) {
+  if (check_cfg(cfg) != BEAM_OK || (kind != BEAM_LOCAL && kind != BEAM_GLOBAL)) return 0;
+  DecodeWs ws;
+  if (!decode_ws_layout(cfg, kind, n_seqs, max_pos, split_keys, &ws)) return 0;
+  return ws.total;
+}
+
+beam_status beam_kv_append(const beam_attn_config* cfg, const beam_kv_cache* cache, const beam_bf16* k_raw,
+                           const beam_bf16* v_raw, const beam_bf16* k_norm_w, const int32_t* seq_idx,
+                           const int32_t* pos, int32_t n_tok, void* stream) {
+  beam_status st;
+  if ((st = check_cfg(cfg)) != BEAM_OK) return st;
+  if ((st = check_cache(cache)) != BEAM_OK) return st;
+  if (n_tok < 0) return fail(BEAM_E_RANGE, "n_tok must be >= 0");
+  if (n_tok == 0) return ok();
+  if (!k_raw || !v_raw || !k_norm_w || !seq_idx || !pos) return fail(BEAM_E_NULL, "NULL input pointer");
+  beam::AppendParams p{};
+  p.k_raw = k_raw;
+  p.v_raw = v_raw;
+  p.k_norm_w = k_norm_w;
+  p.seq_idx = seq_idx;
+  p.pos = pos;
+  p.cu = nullptr;
+  p.start_pos = nullptr;
+  p.n_seqs = 0;
+  p.ck = static_cast<uint16_t*>(cache->k);
+  p.cv = static_cast<uint16_t*>(cache->v);
+  p.bt = cache->block_table;
+  p.max_pages = cache->max_pages_per_seq;
+  p.n_cache_seqs = cache->n_seqs;
+  p.kind = cache->kind;
+  p.G = cfg->n_kv_heads;
+  p.window = cfg->window;
+  p.n_tok = n_tok;
+  p.rope_theta = cfg->rope_theta;
+  p.rms_eps = cfg->rms_eps;
+  if ((st = hip_status(beam::launch_kv_append(p, (hipStream_t)stream), "kv_append launch")) != BEAM_OK) return st;
+  return ok();
+}
+
+beam_status beam_attn_prefill(const beam_attn_config* cfg, const beam_kv_cache* cache, const beam_bf16* q_raw,
+                              const beam_bf16* k_raw, const beam_bf16* v_raw, const beam_bf16* q_norm_w,
+                              const beam_bf16* k_norm_w, const beam_bf16* gate_logits, const float* gate_bias,
+                              const int32_t* cu_seqlens, const int32_t* seq_idx, const int32_t* start_pos,
+                              int32_t n_seqs, int32_t n_tok, int32_t max_chunk_len, beam_bf16* out,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  beam_status st;
+  if ((st = check_cfg(cfg)) != BEAM_OK) return st;
+  if ((st = check_cache(cache)) != BEAM_OK) return st;
+  if (n_seqs <= 0) return fail(BEAM_E_RANGE, "n_seqs must be positive");
+  if (n_tok < 0 || max_chunk_len < 0) return fail(BEAM_E_RANGE, "n_tok and max_chunk_len must be >= 0");
+  if (n_tok == 0) return ok();
+  if (max_chunk_len == 0 || max_chunk_len > n_tok)
+    return fail(BEAM_E_RANGE, "max_chunk_len must be in [1, n_tok]");
+  if (!q_raw || !k_raw || !v_raw || !q_norm_w || !k_norm_w || !gate_logits || !cu_seqlens || !seq_idx ||
+      !start_pos || !out)
+    return fail(BEAM_E_NULL, "NULL input/output pointer");
+  if (!workspace) return fail(BEAM_E_NULL, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(BEAM_E_RANGE, "workspace must be 256-byte aligned");
+  const PrefillWs ws = prefill_ws_layout(cfg, n_tok, n_seqs);
+  if (ws_bytes < ws.total)
+    return fail(BEAM_E_WORKSPACE, "prefill workspace needs " + std::to_string(ws.total) + " bytes");
+  if (ws.P > 0x7fffffff) return fail(BEAM_E_RANGE, "too many tokens");
+  hipStream_t s = (hipStream_t)stream;
+  char* wsb = static_cast<char*>(workspace);
+  uint16_t* qp = reinterpret_cast<uint16_t*>(wsb + ws.qp);
+  uint16_t* kw = reinterpret_cast<uint16_t*>(wsb + ws.kw);
+  uint16_t* vw = reinterpret_cast<uint16_t*>(wsb + ws.vw);
+
+  beam::PrologueParams pp{};
+  pp.q_raw = q_raw;
+  pp.k_raw = k_raw;
+  pp.v_raw = v_raw;
+  pp.q_norm_w = q_norm_w;
+  pp.k_norm_w = k_norm_w;
+  pp.cu = cu_seqlens;
+  pp.start_pos = start_pos;
+  pp.qp = qp;
+  pp.kw = kw;
+  pp.vw = vw;
+  pp.kind = cache->kind;
+  pp.H = cfg->n_q_heads;
+  pp.G = cfg->n_kv_heads;
+  pp.P = (int)ws.P;
+  pp.rope_theta = cfg->rope_theta;
+  pp.rms_eps = cfg->rms_eps;
+  pp.ssmax_base = cfg->ssmax_base;
+  pp.ssmax_exp = cfg->ssmax_exp;
+  const int n_tiles = (max_chunk_len + 63) / 64 + 1;
+  if ((st = hip_status(beam::launch_prefill_prologue(pp, n_seqs, n_tiles, s), "prologue launch")) != BEAM_OK)
+    return st;
+
+  beam::PrefillParams ap{};
+  ap.qp = qp;
+  ap.kw = kw;
+  ap.vw = vw;
+  ap.gate = gate_logits;
+  ap.gate_bias = gate_bias;
+  ap.out = out;
+  ap.cu = cu_seqlens;
+  ap.seq_idx = seq_idx;
+  ap.start_pos = start_pos;
+  ap.ck = static_cast<const uint16_t*>(cache->k);
+  ap.cv = static_cast<const uint16_t*>(cache->v);
+  ap.bt = cache->block_table;
+  ap.max_pages = cache->max_pages_per_seq;
+  ap.n_cache_seqs = cache->n_seqs;
+  ap.kind = cache->kind;
+  ap.window = cfg->window;
+  ap.H = cfg->n_q_heads;
+  ap.G = cfg->n_kv_heads;
+  ap.n_seqs = n_seqs;
+  ap.n_qtiles = (max_chunk_len + 127) / 128;
+  ap.P = (int)ws.P;
+  if ((st = hip_status(beam::launch_prefill_attn(ap, s), "prefill attention launch")) != BEAM_OK) return st;
+
+  beam::AppendParams xp{};
+  xp.k_raw = k_raw;
+  xp.v_raw = v_raw;
+  xp.k_norm_w = k_norm_w;
+  xp.seq_idx = seq_idx;
+  xp.pos = nullptr;
+  xp.cu = cu_seqlens;
+  xp.start_pos = start_pos;
+  xp.n_seqs = n_seqs;
+  xp.ck = static_cast<uint16_t*>(cache->k);
+  xp.cv = static_cast<uint16_t*>(cache->v);
+  xp.bt = cache->block_table;
+  xp.max_pages = cache->max_pages_per_seq;
+  xp.n_cache_seqs = cache->n_seqs;
+  xp.kind = cache->kind;
+  xp.G = cfg->n_kv_heads;
+  xp.window = cfg->window;
+  xp.n_tok = n_tok;
+  xp.rope_theta = cfg->rope_theta;
+  xp.rms_eps = cfg->rms_eps;
+  if ((st = hip_status(beam::launch_kv_append(xp, s), "prefill append launch")) != BEAM_OK) return st;
+  return ok();
+}
+
+beam_status beam_attn_decode(const beam_attn_config* cfg, const beam_kv_cache* cache, const beam_bf16* q_raw,
+                             const beam_bf16* q_norm_w, const beam_bf16* gate_logits, const float* gate_bias,
+                             const int32_t* seq_idx, const int32_t* pos, int32_t n_seqs, int32_t max_pos,
+                             int32_t split_keys, beam_bf16* out, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  beam_status st;
+  if ((st = check_cfg(cfg)) != BEAM_OK) return st;
+  if ((st = check_cache(cache)) != BEAM_OK) return st;
+  if (n_seqs < 0) return fail(BEAM_E_RANGE, "n_seqs must be >= 0");
+  if (n_seqs == 0) return ok();
+  if (max_pos < 0) return fail(BEAM_E_RANGE, "max_pos must be >= 0");
+  if (cache->kind == BEAM_GLOBAL && (int64_t)max_pos + 1 > (int64_t)cache->max_pages_per_seq * cache->page_size)
+    return fail(BEAM_E_RANGE, "max_pos beyond block-table capacity");
+  if (!q_raw || !q_norm_w || !gate_logits || !seq_idx || !pos || !out)
+    return fail(BEAM_E_NULL, "NULL input/output pointer");
+  if (!workspace) return fail(BEAM_E_NULL, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(BEAM_E_RANGE, "workspace must be 256-byte aligned");
+  DecodeWs ws;
+  if (!decode_ws_layout(cfg, cache->kind, n_seqs, max_pos, split_keys, &ws))
+    return fail(BEAM_E_RANGE, "split_keys must be 0 or a multiple of 128 in [128, 65536]");
+  if (ws_bytes < ws.total)
+    return fail(BEAM_E_WORKSPACE, "decode workspace needs " + std::to_string(ws.total) + " bytes");
+  if ((int64_t)n_seqs * cfg->n_kv_heads * ws.n_splits > 0x7fffffffLL) return fail(BEAM_E_RANGE, "grid too large");
+  hipStream_t s = (hipStream_t)stream;
+  char* wsb = static_cast<char*>(workspace);
+  uint16_t* qp = reinterpret_cast<uint16_t*>(wsb + ws.qp);
+  float* ml = reinterpret_cast<float*>(wsb + ws.ml);
+  float* acc = reinterpret_cast<float*>(wsb + ws.acc);
+
+  beam::DecodeQParams qp_{};
+  qp_.q_raw = q_raw;
+  qp_.q_norm_w = q_norm_w;
+  qp_.pos = pos;
+  qp_.qp = qp;
+  qp_.kind = cache->kind;
+  qp_.H = cfg->n_q_heads;
+  qp_.n_seqs = n_seqs;
+  qp_.rope_theta = cfg->rope_theta;
+  qp_.rms_eps = cfg->rms_eps;
+  qp_.ssmax_base = cfg->ssmax_base;
+  qp_.ssmax_exp = cfg->ssmax_exp;
+  if ((st = hip_status(beam::launch_decode_q_prologue(qp_, s), "decode prologue launch")) != BEAM_OK) return st;
+
+  beam::DecodeParams dp{};
+  dp.qp = qp;
+  dp.ck = static_cast<const uint16_t*>(cache->k);
+  dp.cv = static_cast<const uint16_t*>(cache->v);
+  dp.bt = cache->block_table;
+  dp.max_pages = cache->max_pages_per_seq;
+  dp.seq_idx = seq_idx;
+  dp.pos = pos;
+  dp.part_ml = ml;
+  dp.part_acc = acc;
+  dp.n_cache_seqs = cache->n_seqs;
+  dp.max_pos = max_pos;
+  dp.kind = cache->kind;
+  dp.window = cfg->window;
+  dp.H = cfg->n_q_heads;
+  dp.G = cfg->n_kv_heads;
+  dp.n_splits = ws.n_splits;
+  dp.kpw = ws.split_keys / 4;
+  if ((st = hip_status(beam::launch_decode_split(dp, n_seqs, s), "decode split launch")) != BEAM_OK) return st;
+
+  beam::CombineParams cp{};
+  cp.part_ml = ml;
+  cp.part_acc = acc;
+  cp.pos = pos;
+  cp.gate = gate_logits;
+  cp.gate_bias = gate_bias;
+  cp.out = out;
+  cp.max_pos = max_pos;
+  cp.kind = cache->kind;
+  cp.window = cfg->window;
+  cp.H = cfg->n_q_heads;
+  cp.n_splits = ws.n_splits;
+  cp.split_keys = ws.split_keys;
+  if ((st = hip_status(beam::launch_decode_combine(cp, n_seqs, s), "decode combine launch")) != BEAM_OK) return st;
+  return ok();
+}
+
+beam_status beam_debug_visibility(int32_t kind, int32_t window, int32_t t0, int32_t n_q, int32_t s0, int32_t n_k,
+                                  uint8_t* mask, void* stream) {
+  if (kind != BEAM_LOCAL && kind != BEAM_GLOBAL) return fail(BEAM_E_RANGE, "kind must be 0 or 1");
+  if (!mask) return fail(BEAM_E_NULL, "mask is NULL");
+  if (window <= 0 || n_q < 0 || n_k < 0) return fail(BEAM_E_RANGE, "window > 0, n_q >= 0, n_k >= 0 required");
+  if ((int64_t)n_q * n_k == 0) return ok();
+  beam_status st = hip_status(beam::launch_visibility(kind, window, t0, n_q, s0, n_k, mask, (hipStream_t)stream),
+                              "visibility launch");
+  if (st != BEAM_OK) return st;
+  return ok();
+}
+
+}  // extern "C"

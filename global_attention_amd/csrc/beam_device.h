@@ -1,0 +1,136 @@
+// Device-side helpers shared by the Beam attention kernels (gfx950 / CDNA4).
+//
+// Types for the bf16 MFMA operands, bf16 packing, the visibility predicate,
+// the RMSNorm + RoPE/SSMax prologue math and the workspace indexing scheme.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace beam {
+
+constexpr int D = 128;  // head dimension (the only one supported)
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round two floats to bf16 (nearest-even) and pack (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Visibility of key position s to query position t: causal, plus the window on
+// local layers (window counts the current token, so window-1 earlier ones).
+__device__ __forceinline__ bool visible(int kind, int window, int t, int s) {
+  int dlt = t - s;
+  return dlt >= 0 && (kind == 1 || dlt <= window - 1);
+}
+
+// SSMax query scale a(p) = (1 + p/base)^exponent at one-based p = t + 1.
+__device__ __forceinline__ float ssmax_scale(int t, float base, float expo) {
+  return (float)pow(1.0 + (double)(t + 1) / (double)base, (double)expo);
+}
+
+// cos/sin of t * theta^(-2i/128), angle formed and range-reduced in float64.
+__device__ __forceinline__ void rope_cs(int t, int i, float theta, float* c, float* s) {
+  double w = pow((double)theta, -2.0 * (double)i / (double)D);
+  double ang = (double)t * w;
+  const double two_pi = 6.283185307179586476925;
+  double r = ang - two_pi * rint(ang / two_pi);
+  double sd, cd;
+  sincos(r, &sd, &cd);
+  *c = (float)cd;
+  *s = (float)sd;
+}
+
+// Sum over the 16 lanes of an aligned 16-lane group.
+__device__ __forceinline__ float sum16(float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 8);
+  return v;
+}
+
+// One head vector (128 bf16) is handled by a 16-lane group: lane j holds the
+// coordinates lo = [4j, 4j+4) and hi = [64+4j, 64+4j+4), so every rotate-half
+// RoPE pair (i, i+64) sits in one lane. Computes
+//   y = w * x / sqrt(mean(x^2) + eps)       (fp32)
+//   optional RoPE at position t with per-lane cos/sin of pairs 4j..4j+3
+//   y *= post_scale
+// and returns the bf16-packed results (2 words for lo, 2 for hi).
+struct HeadFrag {
+  uint32_t lo[2];
+  uint32_t hi[2];
+};
+
+__device__ __forceinline__ HeadFrag norm_rope_head(u32x2 xlo, u32x2 xhi, u32x2 wlo, u32x2 whi,
+                                                   float eps, bool do_rope, const float* cs,
+                                                   const float* sn, float post_scale) {
+  float a[4] = {bf16lo(xlo[0]), bf16hi(xlo[0]), bf16lo(xlo[1]), bf16hi(xlo[1])};
+  float b[4] = {bf16lo(xhi[0]), bf16hi(xhi[0]), bf16lo(xhi[1]), bf16hi(xhi[1])};
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ss += a[e] * a[e] + b[e] * b[e];
+  ss = sum16(ss);
+  float r = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+  float wa[4] = {bf16lo(wlo[0]), bf16hi(wlo[0]), bf16lo(wlo[1]), bf16hi(wlo[1])};
+  float wb[4] = {bf16lo(whi[0]), bf16hi(whi[0]), bf16lo(whi[1]), bf16hi(whi[1])};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    a[e] = wa[e] * (a[e] * r);
+    b[e] = wb[e] * (b[e] * r);
+  }
+  if (do_rope) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float x1 = a[e], x2 = b[e];
+      a[e] = x1 * cs[e] - x2 * sn[e];
+      b[e] = x2 * cs[e] + x1 * sn[e];
+    }
+  }
+  HeadFrag f;
+  f.lo[0] = pack_bf16x2(a[0] * post_scale, a[1] * post_scale);
+  f.lo[1] = pack_bf16x2(a[2] * post_scale, a[3] * post_scale);
+  f.hi[0] = pack_bf16x2(b[0] * post_scale, b[1] * post_scale);
+  f.hi[1] = pack_bf16x2(b[2] * post_scale, b[3] * post_scale);
+  return f;
+}
+
+// Prefill workspace indexing. K_hat and V^T of the chunk tokens live in
+// position-aligned per-sequence regions so that key tiles of 64 absolute
+// positions never straddle a region boundary and 8-key groups stay 16-byte
+// aligned: sequence i's region starts at 64*(cu[i]/64 + 2*i) and absolute
+// position s maps to region_base + s - (start & ~63).
+__device__ __forceinline__ int ws_region_base(int cu_i, int i) { return 64 * (cu_i / 64 + 2 * i); }
+__host__ __device__ inline int64_t ws_positions(int n_tok, int n_seqs) {
+  return 64 * ((int64_t)n_tok / 64 + 2 * (int64_t)n_seqs + 2);
+}
+
+// Index of the sequence whose token range [cu[i], cu[i+1]) holds token `tok`.
+__device__ __forceinline__ int find_seq(const int32_t* cu, int n_seqs, int tok) {
+  int lo = 0, hi = n_seqs - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= tok) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace beam

@@ -1,0 +1,106 @@
+// Kernel parameter blocks and kernel declarations (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace beam {
+
+struct PrologueParams {
+  const uint16_t* q_raw;
+  const uint16_t* k_raw;
+  const uint16_t* v_raw;
+  const uint16_t* q_norm_w;
+  const uint16_t* k_norm_w;
+  const int32_t* cu;
+  const int32_t* start_pos;
+  uint16_t* qp;  // Q' [n_tok][H][D]
+  uint16_t* kw;  // K_hat [G][P][D]
+  uint16_t* vw;  // V^T [G][D][P]
+  int kind, H, G, P;
+  float rope_theta, rms_eps, ssmax_base, ssmax_exp;
+};
+
+struct AppendParams {
+  const uint16_t* k_raw;
+  const uint16_t* v_raw;
+  const uint16_t* k_norm_w;
+  const int32_t* seq_idx;  // per token (public append) or per sequence (prefill)
+  const int32_t* pos;      // per token (public append), else null
+  const int32_t* cu;       // prefill chunk description, else null
+  const int32_t* start_pos;
+  int n_seqs;
+  uint16_t* ck;
+  uint16_t* cv;
+  const int32_t* bt;
+  int max_pages;
+  int n_cache_seqs;  // rows of the block table (global) or rings (local)
+  int kind, G, window, n_tok;
+  float rope_theta, rms_eps;
+};
+
+struct DecodeQParams {
+  const uint16_t* q_raw;
+  const uint16_t* q_norm_w;
+  const int32_t* pos;
+  uint16_t* qp;  // Q' [n_seqs][H][D]
+  int kind, H, n_seqs;
+  float rope_theta, rms_eps, ssmax_base, ssmax_exp;
+};
+
+struct PrefillParams {
+  const uint16_t* qp;  // Q' [n_tok][H][D]
+  const uint16_t* kw;  // K_hat workspace [G][P][D]
+  const uint16_t* vw;  // V^T workspace [G][D][P]
+  const uint16_t* gate;
+  const float* gate_bias;
+  uint16_t* out;
+  const int32_t* cu;
+  const int32_t* seq_idx;
+  const int32_t* start_pos;
+  const uint16_t* ck;
+  const uint16_t* cv;
+  const int32_t* bt;
+  int max_pages;
+  int n_cache_seqs;
+  int kind, window, H, G, n_seqs, n_qtiles, P;
+};
+
+struct DecodeParams {
+  const uint16_t* qp;  // Q' [n_seqs][H][D]
+  const uint16_t* ck;
+  const uint16_t* cv;
+  const int32_t* bt;
+  int max_pages;
+  const int32_t* seq_idx;
+  const int32_t* pos;
+  float* part_ml;   // [n_seqs][H][S][2] (max, sum) in base-2 logits
+  float* part_acc;  // [n_seqs][H][S][D]
+  int n_cache_seqs;
+  int max_pos;
+  int kind, window, H, G, n_splits, kpw;
+};
+
+struct CombineParams {
+  const float* part_ml;
+  const float* part_acc;
+  const int32_t* pos;
+  const uint16_t* gate;
+  const float* gate_bias;
+  uint16_t* out;
+  int max_pos;
+  int kind, window, H, n_splits, split_keys;
+};
+
+// Host-side launchers (each defined next to its kernel). They return the
+// launch status of the HIP runtime.
+hipError_t launch_prefill_prologue(const PrologueParams& p, int n_seqs, int n_tiles, hipStream_t s);
+hipError_t launch_kv_append(const AppendParams& p, hipStream_t s);
+hipError_t launch_decode_q_prologue(const DecodeQParams& p, hipStream_t s);
+hipError_t launch_visibility(int kind, int window, int t0, int n_q, int s0, int n_k, uint8_t* mask,
+                             hipStream_t s);
+hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s);
+hipError_t launch_decode_split(const DecodeParams& p, int n_seqs, hipStream_t s);
+hipError_t launch_decode_combine(const CombineParams& p, int n_seqs, hipStream_t s);
+
+}  // namespace beam

@@ -1,0 +1,273 @@
+// Split-K paged decode attention with bf16 MFMA (gfx950).
+//
+// One new query token per sequence attends over its cache: all t+1 positions
+// on a global layer (paged), the last min(t+1, window) on a local layer (ring);
+// "Beam 1.0: Local RoPE, Global NoPE and Scalable Softmax", sections "Two
+// attention paths in one decoder" and "KV memory: nine growing caches, not 52"
+// (every cached token is read once per layer and query).
+//
+// Each block handles one (sequence, KV head, split of 4*kpw keys); its four
+// wavefronts stream kpw keys each, 32 keys (two 16-token pages) per step. The
+// 6 query heads that share the KV head form the N side of
+// v_mfma_f32_16x16x32_bf16 (padded to 16), so every K/V byte is read from HBM
+// once for all of them. K pages are token-major, V pages are stored
+// transposed (d-major), so both MFMA operands are plain vector loads straight
+// from HBM into registers; nothing is staged in LDS on the hot path. The four
+// waves merge their (max, sum, acc) triples through LDS; a second kernel merges
+// the splits by log-sum-exp and applies the output gate.
+#include "beam_device.h"
+#include "beam_kernels.h"
+
+namespace beam {
+
+constexpr float kDecRescale = 8.0f;
+
+struct DecodeStep {
+  u32x4 k[2][4];  // [page][d-block of 32]
+  u32x2 v[2][8];  // [page][d-block of 16]
+};
+
+__global__ void __launch_bounds__(256, 2) decode_split_kernel(DecodeParams p) {
+  const int hpg = p.H / p.G;
+  int b = blockIdx.x;
+  const int g = b % p.G;
+  b /= p.G;
+  const int sp = b % p.n_splits;
+  const int seq = b / p.n_splits;
+
+  const int t = p.pos[seq];
+  const int cseq = p.seq_idx[seq];
+  // Positions beyond max_pos or bad cache rows are not read (the combine
+  // kernel writes NaN for such sequences).
+  if (t < 0 || t > p.max_pos || cseq < 0 || cseq >= p.n_cache_seqs) return;
+  const bool local = (p.kind == 0);
+  const int n_keys = local ? min(t + 1, p.window) : t + 1;
+  const int split0 = sp * 4 * p.kpw;
+  if (split0 >= n_keys) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int nn = lane & 15;  // head column (valid if < hpg); also the key row of K loads
+  const int q = lane >> 4;   // lane group 0..3
+
+  const int k0 = split0 + w * p.kpw;
+  const int k1 = min(k0 + p.kpw, n_keys);
+
+  // Q' fragments (B operand of S^T = K Q'^T): head nn, coords 32kk + 8q + 0..7.
+  u32x4 qf[4];
+  {
+    const bool hv = nn < hpg;
+    const uint16_t* qrow = p.qp + ((size_t)seq * p.H + g * hpg + (hv ? nn : 0)) * D + 8 * q;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qf[kk] = hv ? *reinterpret_cast<const u32x4*>(qrow + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  const int32_t* bt_row = p.bt + (size_t)cseq * p.max_pages;
+  const size_t ring = (size_t)cseq * p.G + g;
+
+  // Base pointers of the 16-key group starting at logical key kg.
+  auto kbase = [&](int kg) -> const uint16_t* {
+    if (local) return p.ck + (ring * p.window + kg) * D;
+    int page = bt_row[kg >> 4];
+    return p.ck + ((size_t)page * p.G + g) * 16 * D;
+  };
+  auto vbase = [&](int kg, int* dstride) -> const uint16_t* {
+    if (local) {
+      *dstride = p.window;
+      return p.cv + ring * D * p.window + kg;
+    }
+    *dstride = 16;
+    int page = bt_row[kg >> 4];
+    return p.cv + ((size_t)page * p.G + g) * D * 16;
+  };
+  auto load_step = [&](int kb, DecodeStep& st) {
+#pragma unroll
+    for (int X = 0; X < 2; ++X) {
+      const int kg = kb + 16 * X;
+      if (kg < k1) {
+        const uint16_t* kp = kbase(kg) + nn * D + 8 * q;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) st.k[X][kk] = *reinterpret_cast<const u32x4*>(kp + 32 * kk);
+        int ds;
+        const uint16_t* vp = vbase(kg, &ds) + 4 * q;
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+          st.v[X][db] = *reinterpret_cast<const u32x2*>(vp + (size_t)(16 * db + nn) * ds);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) st.k[X][kk] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int db = 0; db < 8; ++db) st.v[X][db] = u32x2{0u, 0u};
+      }
+    }
+  };
+
+  f32x4 o[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf;
+  float l_run = 0.f;
+
+  DecodeStep cur, nxt;
+  if (k0 < k1) load_step(k0, cur);
+  for (int kb = k0; kb < k1; kb += 32) {
+    const bool has_next = kb + 32 < k1;
+    if (has_next) load_step(kb + 32, nxt);
+
+    const bool partial = kb + 32 > k1;
+    if (partial) {
+      // Zero V of keys past the end (their pages may hold stale or unwritten data).
+#pragma unroll
+      for (int X = 0; X < 2; ++X)
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const int key0 = kb + 16 * X + 4 * q;
+          u32x2 v = cur.v[X][db];
+          uint32_t m0 = (key0 + 0 < k1 ? 0xffffu : 0u) | (key0 + 1 < k1 ? 0xffff0000u : 0u);
+          uint32_t m1 = (key0 + 2 < k1 ? 0xffffu : 0u) | (key0 + 3 < k1 ? 0xffff0000u : 0u);
+          cur.v[X][db] = u32x2{v[0] & m0, v[1] & m1};
+        }
+    }
+
+    f32x4 s[2];
+#pragma unroll
+    for (int X = 0; X < 2; ++X) {
+      s[X] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        s[X] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.k[X][kk]), as_bf16x8(qf[kk]), s[X], 0, 0, 0);
+    }
+    // lane holds head nn, keys kb + 16X + 4q + i
+    if (partial) {
+#pragma unroll
+      for (int X = 0; X < 2; ++X)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (kb + 16 * X + 4 * q + i >= k1) s[X][i] = kNegInf;
+    }
+    float mt = kNegInf;
+#pragma unroll
+    for (int X = 0; X < 2; ++X)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[X][i]);
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    if (__any(m_new > m_run + kDecRescale)) {
+      const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[db][i] *= alpha;
+    }
+    const float mu = (m_run == kNegInf) ? 0.f : m_run;
+    float e[8];
+#pragma unroll
+    for (int X = 0; X < 2; ++X)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        e[4 * X + i] = __builtin_amdgcn_exp2f(s[X][i] - mu);
+        l_run += e[4 * X + i];
+      }
+    // P^T operand: k-slot 8q + j <-> key 16(j>>2) + 4q + (j&3)
+    const u32x4 pf = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
+                           pack_bf16x2(e[6], e[7])};
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const u32x4 a = u32x4{cur.v[0][db][0], cur.v[0][db][1], cur.v[1][db][0], cur.v[1][db][1]};
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(pf), o[db], 0, 0, 0);
+    }
+    if (has_next) cur = nxt;
+  }
+
+  // Sum of the lane partials of each head (lanes nn, nn+16, nn+32, nn+48).
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+
+  // Merge the four waves through LDS. o[db][i] is head nn, coordinate 16db + 4q + i.
+  __shared__ float s_m[4][16];
+  __shared__ float s_l[4][16];
+  __shared__ float s_o[4][16][D + 4];
+  if (lane < 16) {
+    s_m[w][lane] = m_run;
+    s_l[w][lane] = l_run;
+  }
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_o[w][nn][16 * db + 4 * q + i] = o[db][i];
+  __syncthreads();
+
+  for (int e2 = tid; e2 < hpg * D; e2 += 256) {
+    const int hn = e2 / D, d = e2 - hn * D;
+    float M = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, s_m[ww][hn]);
+    float L = 0.f, A = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        const float sc = __builtin_amdgcn_exp2f(s_m[ww][hn] - M);
+        L += sc * s_l[ww][hn];
+        A += sc * s_o[ww][hn][d];
+      }
+    }
+    const size_t row = ((size_t)seq * p.H + g * hpg + hn) * p.n_splits + sp;
+    p.part_acc[row * D + d] = A;
+    if (d == 0) {
+      p.part_ml[2 * row] = M;
+      p.part_ml[2 * row + 1] = L;
+    }
+  }
+}
+
+// Log-sum-exp merge of the splits of one (sequence, query head), then the
+// per-coordinate sigmoid gate. One block of 128 threads (one per coordinate).
+__global__ void __launch_bounds__(128) decode_combine_kernel(CombineParams p) {
+  const int seq = blockIdx.x / p.H;
+  const int h = blockIdx.x - seq * p.H;
+  const int d = threadIdx.x;
+  const int t = p.pos[seq];
+  const size_t idx = ((size_t)seq * p.H + h) * D + d;
+  if (t < 0 || t > p.max_pos) {
+    p.out[idx] = 0x7fc0;  // NaN: the position was outside the decode grid
+    return;
+  }
+  const int n_keys = p.kind == 0 ? min(t + 1, p.window) : t + 1;
+  const int ns = (n_keys + p.split_keys - 1) / p.split_keys;
+  const size_t row0 = ((size_t)seq * p.H + h) * p.n_splits;
+  float M = kNegInf;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, p.part_ml[2 * (row0 + s)]);
+  float L = 0.f, A = 0.f;
+  if (M != kNegInf) {
+    for (int s = 0; s < ns; ++s) {
+      const float sc = __builtin_amdgcn_exp2f(p.part_ml[2 * (row0 + s)] - M);
+      L += sc * p.part_ml[2 * (row0 + s) + 1];
+      A += sc * p.part_acc[(row0 + s) * D + d];
+    }
+  }
+  const float o = L > 0.f ? A / L : 0.f;
+  const float bias = p.gate_bias ? p.gate_bias[h] : 0.f;
+  const float gz = bf16f(p.gate[idx]) + bias;
+  const float y = o / (1.f + __expf(-gz));
+  bf16x2 r;
+  r[0] = (__bf16)y;
+  p.out[idx] = __builtin_bit_cast(uint16_t, r[0]);
+}
+
+hipError_t launch_decode_split(const DecodeParams& p, int n_seqs, hipStream_t s) {
+  const long long blocks = (long long)n_seqs * p.G * p.n_splits;
+  hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_combine(const CombineParams& p, int n_seqs, hipStream_t s) {
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(n_seqs * p.H)), dim3(128), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace beam

@@ -1,0 +1,254 @@
+// Prologue and KV-append kernels for Beam attention (gfx950).
+//
+// Per-head RMSNorm of Q and K (eps inside the square root, learned 128-vector),
+// then RoPE on local layers or the SSMax scale a(t+1) on global layers, as on
+// "Beam 1.0: Local RoPE, Global NoPE and Scalable Softmax", section "Follow the
+// tensors, not the parameter label". Q leaves the prologue already multiplied
+// by log2(e)/sqrt(d) (and a(t+1) on global layers) so the attention kernels
+// work in base-2 logits; this is one bf16 rounding of Q, the same count as
+// rounding the normalised Q itself.
+#include "beam_device.h"
+#include "beam_kernels.h"
+
+namespace beam {
+
+// ----------------------------------------------------------------------------
+// Prefill prologue. One block per (sequence, 64-position tile). The tile covers
+// absolute positions [64*T, 64*T + 64) with T = (start >> 6) + blockIdx.y.
+// Real chunk tokens get Q' (into [n_tok][H][D]), K_hat and V^T (into the
+// position-aligned workspace); every other position of the tile gets zero K_hat
+// and V^T so that attention tiles can read whole 64-key tiles.
+// ----------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p) {
+  const int seq = blockIdx.x;
+  const int start = p.start_pos[seq];
+  const int cu0 = p.cu[seq];
+  const int len = p.cu[seq + 1] - cu0;
+  const int tile_pos0 = ((start >> 6) + (int)blockIdx.y) * 64;
+  if (tile_pos0 >= start + len) return;
+  const int region = ws_region_base(cu0, seq);
+  const int ws0 = region + tile_pos0 - (start & ~63);  // workspace index of tile_pos0
+
+  __shared__ float s_cos[64][64];
+  __shared__ float s_sin[64][64];
+  __shared__ uint16_t s_v[64][D + 2];
+
+  const int tid = threadIdx.x;
+  const bool local = (p.kind == 0);
+  if (local) {
+    for (int e = tid; e < 64 * 64; e += 256) {
+      int r = e >> 6, i = e & 63;
+      float c, s;
+      rope_cs(tile_pos0 + r, i, p.rope_theta, &c, &s);
+      s_cos[r][i] = c;
+      s_sin[r][i] = s;
+    }
+    __syncthreads();
+  }
+
+  const int grp = tid >> 4;  // 16 groups of 16 lanes
+  const int j = tid & 15;    // lane within group: coords [4j,4j+4) and [64+4j, 64+4j+4)
+  const u32x2* qw = reinterpret_cast<const u32x2*>(p.q_norm_w);
+  const u32x2* kwgt = reinterpret_cast<const u32x2*>(p.k_norm_w);
+  const u32x2 wq_lo = qw[j], wq_hi = qw[16 + j];
+  const u32x2 wk_lo = kwgt[j], wk_hi = kwgt[16 + j];
+  const float qbase = kLog2e / sqrtf((float)D);
+
+  // Q: 64 positions x H heads, one (position, head) pair per 16-lane group.
+  for (int pr = grp; pr < 64 * p.H; pr += 16) {
+    int r = pr / p.H, h = pr - r * p.H;
+    int t = tile_pos0 + r;
+    if (t < start || t >= start + len) continue;
+    size_t tok = (size_t)(cu0 + t - start);
+    const u32x2* src = reinterpret_cast<const u32x2*>(p.q_raw + (tok * p.H + h) * D);
+    float scale = local ? qbase : qbase * ssmax_scale(t, p.ssmax_base, p.ssmax_exp);
+    HeadFrag f = norm_rope_head(src[j], src[16 + j], wq_lo, wq_hi, p.rms_eps, local,
+                                local ? &s_cos[r][4 * j] : nullptr,
+                                local ? &s_sin[r][4 * j] : nullptr, scale);
+    u32x2* dst = reinterpret_cast<u32x2*>(p.qp + (tok * p.H + h) * D);
+    dst[j] = u32x2{f.lo[0], f.lo[1]};
+    dst[16 + j] = u32x2{f.hi[0], f.hi[1]};
+  }
+
+  // K: 64 positions x G heads into K_hat workspace [G][P][D].
+  for (int pr = grp; pr < 64 * p.G; pr += 16) {
+    int r = pr / p.G, g = pr - r * p.G;
+    int t = tile_pos0 + r;
+    u32x2* dst = reinterpret_cast<u32x2*>(p.kw + ((size_t)g * p.P + ws0 + r) * D);
+    if (t < start || t >= start + len) {
+      dst[j] = u32x2{0u, 0u};
+      dst[16 + j] = u32x2{0u, 0u};
+      continue;
+    }
+    size_t tok = (size_t)(cu0 + t - start);
+    const u32x2* src = reinterpret_cast<const u32x2*>(p.k_raw + (tok * p.G + g) * D);
+    HeadFrag f = norm_rope_head(src[j], src[16 + j], wk_lo, wk_hi, p.rms_eps, local,
+                                local ? &s_cos[r][4 * j] : nullptr,
+                                local ? &s_sin[r][4 * j] : nullptr, 1.0f);
+    dst[j] = u32x2{f.lo[0], f.lo[1]};
+    dst[16 + j] = u32x2{f.hi[0], f.hi[1]};
+  }
+
+  // V: transpose 64 positions x 128 coords per KV head through LDS into
+  // V^T workspace [G][D][P].
+  for (int g = 0; g < p.G; ++g) {
+    __syncthreads();
+    for (int e = tid; e < 64 * 16; e += 256) {  // 16-byte pieces: row r, coords 8c..8c+7
+      int r = e >> 4, c = e & 15;
+      int t = tile_pos0 + r;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (t >= start && t < start + len) {
+        size_t tok = (size_t)(cu0 + t - start);
+        v = *reinterpret_cast<const u32x4*>(p.v_raw + (tok * p.G + g) * D + 8 * c);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        s_v[r][8 * c + 2 * q] = (uint16_t)(v[q] & 0xffffu);
+        s_v[r][8 * c + 2 * q + 1] = (uint16_t)(v[q] >> 16);
+      }
+    }
+    __syncthreads();
+    for (int e = tid; e < D * 8; e += 256) {  // row d of V^T, keys 8c..8c+7
+      int d = e >> 3, c = e & 7;
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] = (uint32_t)s_v[8 * c + 2 * q][d] | ((uint32_t)s_v[8 * c + 2 * q + 1][d] << 16);
+      *reinterpret_cast<u32x4*>(p.vw + ((size_t)g * D + d) * p.P + ws0 + 8 * c) = o;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// KV append: one 16-lane group per token; the group loops over the KV heads.
+// Token -> (cache sequence, position) comes either from explicit arrays (public
+// append) or from the prefill chunk description (cu/start/seq_idx).
+// ----------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) kv_append_kernel(AppendParams p) {
+  const int tid = threadIdx.x;
+  const int tok = blockIdx.x * 16 + (tid >> 4);
+  const int j = tid & 15;
+  if (tok >= p.n_tok) return;
+  int cseq, t;
+  if (p.cu != nullptr) {
+    int s = find_seq(p.cu, p.n_seqs, tok);
+    int start = p.start_pos[s];
+    int len = p.cu[s + 1] - p.cu[s];
+    t = start + tok - p.cu[s];
+    cseq = p.seq_idx[s];
+    // Local ring: only the last `window` positions of the chunk survive; the
+    // earlier ones would be overwritten within this same call.
+    if (p.kind == 0 && t < start + len - p.window) return;
+  } else {
+    cseq = p.seq_idx[tok];
+    t = p.pos[tok];
+  }
+  // Out-of-range device indices are dropped rather than written out of bounds.
+  if (t < 0 || cseq < 0 || cseq >= p.n_cache_seqs) return;
+  if (p.kind == 1 && (t >> 4) >= p.max_pages) return;
+  const bool local = (p.kind == 0);
+  float cs[4], sn[4];
+  if (local) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rope_cs(t, 4 * j + e, p.rope_theta, &cs[e], &sn[e]);
+  }
+  const u32x2* kwgt = reinterpret_cast<const u32x2*>(p.k_norm_w);
+  const u32x2 w_lo = kwgt[j], w_hi = kwgt[16 + j];
+
+  for (int g = 0; g < p.G; ++g) {
+    const u32x2* src = reinterpret_cast<const u32x2*>(p.k_raw + ((size_t)tok * p.G + g) * D);
+    HeadFrag f = norm_rope_head(src[j], src[16 + j], w_lo, w_hi, p.rms_eps, local, cs, sn, 1.0f);
+    uint16_t* krow;
+    uint16_t* vcol;  // V^T element [0][slot]; coordinate d is at vcol[d * vstride]
+    int vstride;
+    if (local) {
+      int slot = t % p.window;
+      size_t base = (size_t)cseq * p.G + g;
+      krow = p.ck + (base * p.window + slot) * D;
+      vcol = p.cv + base * D * p.window + slot;
+      vstride = p.window;
+    } else {
+      int page = p.bt[(size_t)cseq * p.max_pages + (t >> 4)];
+      size_t base = (size_t)page * p.G + g;
+      krow = p.ck + (base * 16 + (t & 15)) * D;
+      vcol = p.cv + base * D * 16 + (t & 15);
+      vstride = 16;
+    }
+    reinterpret_cast<u32x2*>(krow)[j] = u32x2{f.lo[0], f.lo[1]};
+    reinterpret_cast<u32x2*>(krow)[16 + j] = u32x2{f.hi[0], f.hi[1]};
+    const uint16_t* vsrc = p.v_raw + ((size_t)tok * p.G + g) * D;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vcol[(size_t)(4 * j + e) * vstride] = vsrc[4 * j + e];
+      vcol[(size_t)(64 + 4 * j + e) * vstride] = vsrc[64 + 4 * j + e];
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Decode prologue: Q' for one new token per sequence, one 16-lane group per
+// (sequence, head).
+// ----------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) decode_q_prologue_kernel(DecodeQParams p) {
+  const int tid = threadIdx.x;
+  const int pr = blockIdx.x * 16 + (tid >> 4);
+  const int j = tid & 15;
+  if (pr >= p.n_seqs * p.H) return;
+  const int seq = pr / p.H;
+  const int h = pr - seq * p.H;
+  const int t = p.pos[seq];
+  const bool local = (p.kind == 0);
+  float cs[4], sn[4];
+  if (local) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rope_cs(t, 4 * j + e, p.rope_theta, &cs[e], &sn[e]);
+  }
+  const u32x2* qw = reinterpret_cast<const u32x2*>(p.q_norm_w);
+  const float qbase = kLog2e / sqrtf((float)D);
+  float scale = local ? qbase : qbase * ssmax_scale(t, p.ssmax_base, p.ssmax_exp);
+  const u32x2* src = reinterpret_cast<const u32x2*>(p.q_raw + ((size_t)seq * p.H + h) * D);
+  HeadFrag f = norm_rope_head(src[j], src[16 + j], qw[j], qw[16 + j], p.rms_eps, local, cs, sn, scale);
+  u32x2* dst = reinterpret_cast<u32x2*>(p.qp + ((size_t)seq * p.H + h) * D);
+  dst[j] = u32x2{f.lo[0], f.lo[1]};
+  dst[16 + j] = u32x2{f.hi[0], f.hi[1]};
+}
+
+// ----------------------------------------------------------------------------
+// Visibility mask with the kernels' own predicate (debug entry point).
+// ----------------------------------------------------------------------------
+__global__ void visibility_kernel(int kind, int window, int t0, int n_q, int s0, int n_k,
+                                  uint8_t* mask) {
+  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)n_q * n_k) return;
+  int r = (int)(i / n_k), c = (int)(i - (long long)r * n_k);
+  mask[i] = visible(kind, window, t0 + r, s0 + c) ? 1 : 0;
+}
+
+}  // namespace beam
+
+namespace beam {
+
+hipError_t launch_prefill_prologue(const PrologueParams& p, int n_seqs, int n_tiles, hipStream_t s) {
+  hipLaunchKernelGGL(prefill_prologue_kernel, dim3(n_seqs, n_tiles), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append(const AppendParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(kv_append_kernel, dim3((p.n_tok + 15) / 16), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_q_prologue(const DecodeQParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(decode_q_prologue_kernel, dim3((p.n_seqs * p.H + 15) / 16), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_visibility(int kind, int window, int t0, int n_q, int s0, int n_k, uint8_t* mask,
+                             hipStream_t s) {
+  long long n = (long long)n_q * n_k;
+  hipLaunchKernelGGL(visibility_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, kind,
+                     window, t0, n_q, s0, n_k, mask);
+  return hipGetLastError();
+}
+
+}  // namespace beam

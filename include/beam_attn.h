@@ -1,0 +1,175 @@
+/*
+ * beam_attn.h — C ABI of the Beam 1.0 hybrid GQA attention library (gfx950 only).
+ *
+ * The operation is the attention sublayer of Beam 1.0 as described on
+ *   "Beam 1.0: Local RoPE, Global NoPE and Scalable Softmax" (flozi.net, English),
+ *   sections "Two attention paths in one decoder", "Follow the tensors, not the
+ *   parameter label" and "KV memory: nine growing caches, not 52", with the SSMax
+ *   formula as given on techfi24.com ("Architecture et mécanismes d'inférence"):
+ *
+ *   Q_hat = RMSNorm(Q) * w_q, K_hat = RMSNorm(K) * w_k   (per head, 128 coords, eps)
+ *   local  layer: q' = RoPE(Q_hat, t), k' = RoPE(K_hat, s), visible iff 0 <= t-s <= window-1
+ *   global layer: q' = a(t+1) * Q_hat, k' = K_hat,          visible iff s <= t
+ *                 a(p) = (1 + p/ssmax_base)^ssmax_exp, p one-based absolute position
+ *   S = q'.k'/sqrt(d), P = softmax over visible keys, O = P V (V not normalised)
+ *   Y = O * sigmoid(gate_logits + gate_bias[h])           (per coordinate)
+ *   Query head h reads KV head h / (n_q_heads / n_kv_heads).
+ *
+ * Conventions
+ *   - Every pointer is a DEVICE pointer unless marked "host". The caller owns
+ *     all memory; the library never allocates, frees or synchronises.
+ *   - bf16 values are raw bfloat16 bit patterns (uint16_t).
+ *   - `stream` is a hipStream_t (NULL = the null stream). All work of a call is
+ *     enqueued on it in order; faults surface at the caller's next sync.
+ *   - Arguments are checked on the host before anything is enqueued. On error a
+ *     call returns a non-zero beam_status, launches nothing, and sets a
+ *     thread-local message readable with beam_last_error().
+ *   - Device-resident indices (block-table entries, seq_idx, positions,
+ *     cu_seqlens) are not read by the host; out-of-range values in them are
+ *     undefined behaviour.
+ *   - Only head_dim == 128 and bf16 storage are supported (BEAM_E_UNSUPPORTED).
+ *   - Calls hold no global mutable state and may be made from several threads.
+ *
+ * KV cache layouts (beam_kv_cache.k / .v)
+ *   GLOBAL (paged, page_size 16):
+ *     k: bf16 [n_pages][n_kv_heads][page_size][head_dim]   token-major rows
+ *     v: bf16 [n_pages][n_kv_heads][head_dim][page_size]   transposed within the page
+ *     position t of cache sequence c lives in page block_table[c][t / page_size],
+ *     slot t % page_size.
+ *   LOCAL (window-sized ring, one per cache sequence):
+ *     k: bf16 [n_seqs][n_kv_heads][window][head_dim]
+ *     v: bf16 [n_seqs][n_kv_heads][head_dim][window]
+ *     position t lives in slot t % window.
+ *   The cache stores K_hat (normalised; rotated on local layers) and raw V.
+ */
+#ifndef BEAM_ATTN_H
+#define BEAM_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t beam_bf16; /* raw bfloat16 bits */
+
+typedef enum { BEAM_LOCAL = 0, BEAM_GLOBAL = 1 } beam_layer_kind;
+
+typedef enum {
+  BEAM_OK = 0,
+  BEAM_E_NULL = 1,        /* a required pointer is NULL */
+  BEAM_E_SHAPE = 2,       /* inconsistent sizes (e.g. n_q_heads % n_kv_heads != 0) */
+  BEAM_E_RANGE = 3,       /* a size or position is out of its valid range */
+  BEAM_E_UNSUPPORTED = 4, /* head_dim != 128, page_size != 16, ... */
+  BEAM_E_WORKSPACE = 5,   /* workspace too small */
+  BEAM_E_HIP = 6          /* the HIP runtime refused a launch */
+} beam_status;
+
+/* Layer geometry. Defaults for Beam 1.0: 48, 8, 128, 512, 1e4, 1e-6, 2048, 0.1. */
+typedef struct {
+  int32_t n_q_heads;  /* 48 */
+  int32_t n_kv_heads; /* 8; must divide n_q_heads, n_q_heads/n_kv_heads <= 16 */
+  int32_t head_dim;   /* 128 (only value supported) */
+  int32_t window;     /* local window incl. the current token; 512 */
+  float rope_theta;   /* 10000 */
+  float rms_eps;      /* 1e-6 */
+  float ssmax_base;   /* 2048 */
+  float ssmax_exp;    /* 0.1 */
+} beam_attn_config;
+
+/* One layer's KV cache (layouts above). */
+typedef struct {
+  int32_t kind;               /* beam_layer_kind */
+  void *k;                    /* device, bf16 */
+  void *v;                    /* device, bf16 */
+  int32_t page_size;          /* GLOBAL: 16. LOCAL: ignored */
+  int32_t n_pages;            /* GLOBAL: physical pages. LOCAL: ignored */
+  const int32_t *block_table; /* GLOBAL: device [n_seqs][max_pages_per_seq]. LOCAL: ignored */
+  int32_t max_pages_per_seq;  /* GLOBAL: row length of block_table */
+  int32_t n_seqs;             /* GLOBAL: rows of block_table. LOCAL: rings allocated */
+} beam_kv_cache;
+
+/* Append new tokens to a layer's cache.
+ * k_raw, v_raw: bf16 [n_tok][n_kv_heads][head_dim] raw projections.
+ * k_norm_w:     bf16 [head_dim] RMSNorm weight of K for this layer.
+ * seq_idx:      int32 [n_tok] cache sequence (block-table row / ring) of each token.
+ * pos:          int32 [n_tok] zero-based absolute position t of each token.
+ * Writes K_hat (RMSNorm, then RoPE at t on LOCAL) and raw V at the token's slot.
+ * Two tokens of one call that map to the same slot race (the ring keeps one). */
+beam_status beam_kv_append(const beam_attn_config *cfg, const beam_kv_cache *cache,
+                           const beam_bf16 *k_raw, const beam_bf16 *v_raw,
+                           const beam_bf16 *k_norm_w, const int32_t *seq_idx,
+                           const int32_t *pos, int32_t n_tok, void *stream);
+
+/* Causal (chunked, varlen) prefill of one layer.
+ * The chunk of sequence i is tokens [cu_seqlens[i], cu_seqlens[i+1]) of the packed
+ * inputs, at absolute positions start_pos[i] + 0, 1, ...; positions < start_pos[i]
+ * must already be in the cache (cache sequence seq_idx[i]).
+ * q_raw, gate_logits, out: bf16 [n_tok][n_q_heads][head_dim].
+ * k_raw, v_raw:            bf16 [n_tok][n_kv_heads][head_dim].
+ * q_norm_w, k_norm_w:      bf16 [head_dim].  gate_bias: float [n_q_heads] or NULL.
+ * cu_seqlens: int32 [n_seqs+1] (cu_seqlens[0] == 0, cu_seqlens[n_seqs] == n_tok),
+ * seq_idx, start_pos: int32 [n_seqs]. max_chunk_len >= every chunk length.
+ * In stream order: prologue (norm, RoPE/SSMax) into the workspace, attention over
+ * cached prefix + chunk with the gate applied, then the chunk's K_hat/V are appended
+ * to the cache (last, so a local ring is never overwritten while it is read).
+ * workspace: device, >= beam_prefill_workspace_bytes(cfg, n_tok, n_seqs) bytes,
+ * 256-byte aligned. */
+beam_status beam_attn_prefill(const beam_attn_config *cfg, const beam_kv_cache *cache,
+                              const beam_bf16 *q_raw, const beam_bf16 *k_raw,
+                              const beam_bf16 *v_raw, const beam_bf16 *q_norm_w,
+                              const beam_bf16 *k_norm_w, const beam_bf16 *gate_logits,
+                              const float *gate_bias, const int32_t *cu_seqlens,
+                              const int32_t *seq_idx, const int32_t *start_pos,
+                              int32_t n_seqs, int32_t n_tok, int32_t max_chunk_len,
+                              beam_bf16 *out, void *workspace, size_t ws_bytes,
+                              void *stream);
+
+/* One-token decode of one layer for n_seqs sequences (split-K over the cache).
+ * The new token (position pos[i], cache sequence seq_idx[i]) must already have
+ * been appended with beam_kv_append.
+ * q_raw, gate_logits, out: bf16 [n_seqs][n_q_heads][head_dim].
+ * max_pos >= every pos[i] (sizes the split grid).
+ * split_keys: keys per split (multiple of 128, <= 65536), or 0 for the default.
+ * workspace: >= beam_decode_workspace_bytes(cfg, kind, n_seqs, max_pos, split_keys). */
+beam_status beam_attn_decode(const beam_attn_config *cfg, const beam_kv_cache *cache,
+                             const beam_bf16 *q_raw, const beam_bf16 *q_norm_w,
+                             const beam_bf16 *gate_logits, const float *gate_bias,
+                             const int32_t *seq_idx, const int32_t *pos, int32_t n_seqs,
+                             int32_t max_pos, int32_t split_keys, beam_bf16 *out,
+                             void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace sizes in bytes (host-only, no GPU needed). 0 on invalid arguments. */
+size_t beam_prefill_workspace_bytes(const beam_attn_config *cfg, int32_t n_tok, int32_t n_seqs);
+size_t beam_decode_workspace_bytes(const beam_attn_config *cfg, int32_t kind, int32_t n_seqs,
+                                   int32_t max_pos, int32_t split_keys);
+
+/* KV payload of n_global growing caches plus n_local window-sized caches, per
+ * sequence ("KV memory: nine growing caches, not 52"): logical =
+ * 2*b*n_kv*d*(n_global*N + n_local*min(N, window)); paged rounds N up to pages
+ * in the global term. Host-only; logical/paged are host pointers. */
+beam_status beam_kv_bytes(int64_t n_tokens, int32_t bytes_per_scalar, int32_t n_global,
+                          int32_t n_local, int32_t n_kv, int32_t d, int32_t window,
+                          int32_t page_size, uint64_t *logical, uint64_t *paged);
+
+/* Physical page and slot of position t of sequence seq. Host-only; block_table_host
+ * is a host copy [.. ][max_pages_per_seq]. */
+beam_status beam_kv_page_slot(const int32_t *block_table_host, int32_t max_pages_per_seq,
+                              int32_t page_size, int32_t seq, int32_t t, int64_t *phys_page,
+                              int32_t *slot);
+
+/* mask[i][j] = 1 iff key position s0+j is visible to query position t0+i for the
+ * layer kind, computed on the GPU by the same predicate the kernels use.
+ * mask: device uint8 [n_q][n_k]. */
+beam_status beam_debug_visibility(int32_t kind, int32_t window, int32_t t0, int32_t n_q,
+                                  int32_t s0, int32_t n_k, uint8_t *mask, void *stream);
+
+const char *beam_status_str(beam_status s);
+/* Message of the last failed call on this thread ("" if none). */
+const char *beam_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BEAM_ATTN_H */
