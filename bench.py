@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Benchmark of the Beam 1.0 hybrid-attention hot path on one MI355X.
+
+Step (the timed unit): causal prefill of T = 32,768 tokens (B = 1) through one
+local layer (RoPE, window 512) and one global layer (SSMax), 48 query / 8 KV
+heads, head_dim 128: for each layer the prologue (QK RMSNorm + RoPE/SSMax),
+attention with the fused sigmoid gate, and the append of the chunk into the
+layer's cache. `value` is the algorithmic attention TFLOP/s of the whole step
+(4*d*H flops per visible (query, key) pair, both layers).
+
+Also measured in the same run (reported under "decode"): batched decode of 64
+sequences at positions uniform in [65536, 131071] over a paged bf16 cache
+(16-token pages, random page permutation), global and local layer; value in
+GB/s of KV read (4,096 B per cached key per layer).
+
+Prints ONE JSON line on stdout. Everything else goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill attn TFLOP/s @32K; decode KV GB/s @128K ctx (% of MI355X peak)"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 bf16 flop/clk x 2.4 GHz (AMD: 2.5 PFLOP/s dense)
+PEAK_HBM_GBS = 8000.0       # HBM3E, 8 TB/s
+H, G, D, W = 48, 8, 128, 512
+FLOP_PER_PAIR = 4 * D * H   # QK^T and PV over all query heads of one (query, key) pair
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def pairs_global(T: int) -> int:
+    return T * (T + 1) // 2
+
+
+def pairs_local(T: int, w: int = W) -> int:
+    if T <= w:
+        return T * (T + 1) // 2
+    return w * (w + 1) // 2 + (T - w) * w
+
+
+def _dev(bits):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _i32(x):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
+
+
+# --------------------------------------------------------------------------- prefill
+
+def setup_prefill(T: int):
+    import torch
+    import global_attention_amd as ga
+    import synth
+    cfg = ga.Config()
+    layers = []
+    for kind in (ga.LOCAL, ga.GLOBAL):
+        log(f"[bench] generating prefill inputs kind={kind} T={T}")
+        inp = synth.attention_inputs(cfg=2, layer=kind, n_tok=T)
+        d = {k: _dev(v) for k, v in inp.items()}
+        if kind == ga.GLOBAL:
+            bt, n_pages = synth.paged_block_table(2, [T])
+            cache = ga.KVCache.allocate_global(cfg, n_pages, torch.from_numpy(bt))
+        else:
+            cache = ga.KVCache.allocate_local(cfg, 1)
+        out = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(ga.prefill_workspace_bytes(cfg, T, 1), dtype=torch.uint8, device="cuda")
+        layers.append(dict(kind=kind, inp=inp, d=d, cache=cache, out=out, ws=ws))
+    meta = dict(cu=_i32([0, T]), seq=_i32([0]), start=_i32([0]))
+    return cfg, layers, meta
+
+
+def prefill_step(cfg, layers, meta, T, events=None):
+    import global_attention_amd as ga
+    for i, L in enumerate(layers):
+        d = L["d"]
+        args = (cfg, L["cache"], d["q"], d["k"], d["v"], d["q_norm_w"], d["k_norm_w"], d["gate"], meta["cu"],
+                meta["seq"], meta["start"], T)
+        ga.prefill(*args, out=L["out"], workspace=L["ws"], stages=ga.STAGE_PROLOGUE)
+        if events is not None:
+            events[i][0].record()
+        ga.prefill(*args, out=L["out"], workspace=L["ws"], stages=ga.STAGE_ATTENTION)
+        if events is not None:
+            events[i][1].record()
+        ga.prefill(*args, out=L["out"], workspace=L["ws"], stages=ga.STAGE_APPEND)
+
+
+def bench_prefill(T, steps, warmup):
+    import torch
+    cfg, layers, meta = setup_prefill(T)
+    for _ in range(warmup):
+        prefill_step(cfg, layers, meta, T)
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in layers] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        prefill_step(cfg, layers, meta, T, evs[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    attn_ms = [sum(evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(steps)) / steps
+               for i in range(len(layers))]
+    return dict(cfg=cfg, layers=layers, ms_per_step=elapsed * 1e3 / steps, attn_ms=attn_ms)
+
+
+# --------------------------------------------------------------------------- decode
+
+def setup_decode(n_seqs=64, lo=65536, hi=131071, seed=3):
+    import numpy as np
+    import torch
+    import global_attention_amd as ga
+    import synth
+    cfg = ga.Config()
+    ts = synth.decode_positions(seed, n_seqs, lo, hi)
+    ctx = ts.astype(np.int64) + 1
+    bt, n_pages = synth.paged_block_table(seed, ctx)
+    log(f"[bench] decode cache: {n_seqs} seqs, {n_pages} pages ({n_pages * 65536 / 1e9:.1f} GB K+V)")
+    gcache = ga.KVCache.allocate_global(cfg, n_pages, torch.from_numpy(bt))
+    lcache = ga.KVCache.allocate_local(cfg, n_seqs)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    step = 8192
+    for t in (gcache.k, gcache.v):
+        for p0 in range(0, n_pages, step):
+            t[p0:p0 + step].normal_(generator=gen)
+    for t in (lcache.k, lcache.v):
+        t.normal_(generator=gen)
+    inp = synth.attention_inputs(cfg=seed, layer=7, n_tok=n_seqs)
+    d = {k: _dev(v) for k, v in inp.items()}
+    torch.cuda.synchronize()
+    return cfg, ts, gcache, lcache, d
+
+
+def bench_decode(steps, warmup):
+    import torch
+    import global_attention_amd as ga
+    cfg, ts, gcache, lcache, d = setup_decode()
+    n = len(ts)
+    seq = _i32(list(range(n)))
+    pos = _i32(ts)
+    max_pos = int(ts.max())
+    res = {}
+    for name, cache in (("global", gcache), ("local", lcache)):
+        out = torch.empty((n, H, D), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(ga.decode_workspace_bytes(cfg, cache.kind, n, max_pos), dtype=torch.uint8, device="cuda")
+        args = (cfg, cache, d["q"], d["q_norm_w"], d["gate"], seq, pos, max_pos)
+
+        def one(ev=None):
+            ga.decode(*args, out=out, workspace=ws, stages=ga.STAGE_PROLOGUE)
+            if ev is not None:
+                ev[0].record()
+            ga.decode(*args, out=out, workspace=ws, stages=ga.STAGE_ATTENTION)
+            if ev is not None:
+                ev[1].record()
+            ga.decode(*args, out=out, workspace=ws, stages=ga.STAGE_COMBINE)
+
+        for _ in range(warmup):
+            one()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for s in range(steps):
+            one(evs[s])
+        torch.cuda.synchronize()
+        el = (time.perf_counter() - t0) / steps
+        split_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+        keys = [int(t) + 1 if name == "global" else min(int(t) + 1, W) for t in ts]
+        nbytes = sum(keys) * G * D * 2 * 2
+        res[name] = dict(bytes=nbytes, ms_per_call=el * 1e3, split_ms=split_ms,
+                         gbs_call=nbytes / el / 1e9, gbs_split=nbytes / (split_ms / 1e3) / 1e9)
+        log(f"[bench] decode {name}: {nbytes / 1e9:.2f} GB, call {el * 1e3:.3f} ms, split kernel {split_ms:.3f} ms")
+    return res
+
+
+# --------------------------------------------------------------------------- CPU oracle
+
+def cpu_baseline(layers, T, rows):
+    """Time the float64 oracle on the last `rows` query rows of both layers."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    t0 = time.perf_counter()
+    flops = 0
+    for L in layers:
+        inp = L["inp"]
+        qs = np.arange(T - rows, T)
+        O.attention_layer(L["kind"], inp["q"][qs], inp["k"], inp["v"], inp["q_norm_w"], inp["k_norm_w"],
+                          inp["gate"][qs], qs, np.arange(T))
+        vis = (qs + 1) if L["kind"] == O.GLOBAL else np.minimum(qs + 1, W)
+        flops += FLOP_PER_PAIR * int(vis.sum())
+    el = time.perf_counter() - t0
+    return dict(value=flops / el / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
+                sample=f"float64 NumPy oracle on the last {rows} query rows (all 48 heads) of the T=32768 "
+                       f"local and global layers, full key history, incl. K normalisation; "
+                       f"{flops / 1e9:.1f} GFLOP in {el:.1f} s")
+
+
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """A plain device copy of known size, for scaling FETCH_SIZE/WRITE_SIZE counters."""
+    import torch
+    a = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {reps} copies of {nbytes} bytes")
+
+
+# --------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--seq-len", type=int, default=32768)
+    ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--skip-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=384)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the attention path shards by "
+              f"KV head or sequence with no exchange, but no multi-GPU run is part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+    import global_attention_amd as ga
+    ga.lib()
+    T = args.seq_len
+
+    rec = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"causal prefill T={T} B=1, one local (RoPE, window 512) + one global "
+                                  f"(SSMax) layer, 48 Q / 8 KV heads, d=128, bf16 N(0,1) inputs",
+                      "seq_len": T, "global_batch": 1, "parallelism": "none (1 GPU)"}}
+    layers = None
+    if not args.skip_prefill:
+        r = bench_prefill(T, args.steps, args.warmup)
+        layers = r["layers"]
+        flops_step = FLOP_PER_PAIR * (pairs_global(T) + pairs_local(T))
+        rec["ms_per_step"] = round(r["ms_per_step"], 4)
+        rec["value"] = round(flops_step / (r["ms_per_step"] / 1e3) / 1e12, 2)
+        g_ms = r["attn_ms"][1]
+        l_ms = r["attn_ms"][0]
+        g_flops = FLOP_PER_PAIR * pairs_global(T)
+        achieved = g_flops / (g_ms / 1e3) / 1e12
+        rec["roofline"] = {"kernel": "prefill_attn_kernel<1> (global layer)", "bound": "mfma",
+                           "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                           "avg_launch_ms": round(g_ms, 4), "flop_per_launch": g_flops}
+        l_flops = FLOP_PER_PAIR * pairs_local(T)
+        rec["prefill_layers"] = {
+            "global_attn_ms": round(g_ms, 4), "global_attn_tflops": round(achieved, 2),
+            "local_attn_ms": round(l_ms, 4), "local_attn_tflops": round(l_flops / (l_ms / 1e3) / 1e12, 2)}
+        log(f"[bench] prefill step {r['ms_per_step']:.3f} ms -> {rec['value']} TFLOP/s; "
+            f"global attn {g_ms:.3f} ms ({achieved:.1f} TFLOP/s), local attn {l_ms:.3f} ms")
+    if not args.skip_decode:
+        dres = bench_decode(args.decode_steps, 3)
+        g = dres["global"]
+        rec["decode"] = {
+            "workload": "64 seqs, 1 new token each at positions U[65536,131071], global layer over a paged "
+                        "bf16 cache (16-token pages, random permutation); local layer over its 512-slot ring",
+            "value": round(g["gbs_call"], 1), "unit": "GB/s",
+            "frac_of_hbm_peak": round(g["gbs_call"] / PEAK_HBM_GBS, 4),
+            "global_bytes": g["bytes"], "global_ms_per_call": round(g["ms_per_call"], 4),
+            "roofline": {"kernel": "decode_split_kernel<1>", "bound": "hbm", "achieved": round(g["gbs_split"], 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(g["gbs_split"] / PEAK_HBM_GBS, 4),
+                         "traffic": None, "avg_launch_ms": round(g["split_ms"], 4)},
+            "local": {"bytes": dres["local"]["bytes"], "ms_per_call": round(dres["local"]["ms_per_call"], 4),
+                      "gbs_call": round(dres["local"]["gbs_call"], 1),
+                      "note": "134 MB of rings can stay resident in the 256 MB MALL between calls"},
+        }
+    if not args.no_cpu_baseline and layers is not None:
+        log(f"[bench] timing the CPU oracle on {args.cpu_rows} rows per layer")
+        rec["cpu_baseline"] = cpu_baseline(layers, T, args.cpu_rows)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -17,8 +17,15 @@ LIB_PATH = os.path.join(_PKG, "libbeam_attn.so")
 LOCAL = 0
 GLOBAL = 1
 
+STAGE_PROLOGUE = 1
+STAGE_ATTENTION = 2
+STAGE_APPEND = 4
+STAGE_COMBINE = 4
+STAGE_ALL = 7
+
 EXPORTED = [
     "beam_kv_append", "beam_attn_prefill", "beam_attn_decode",
+    "beam_attn_prefill_stages", "beam_attn_decode_stages",
     "beam_prefill_workspace_bytes", "beam_decode_workspace_bytes",
     "beam_kv_bytes", "beam_kv_page_slot", "beam_debug_visibility",
     "beam_status_str", "beam_last_error",
@@ -76,6 +83,9 @@ def lib() -> ctypes.CDLL:
     L.beam_kv_append.argtypes = [P, P, P, P, P, P, P, I32, P]
     L.beam_attn_prefill.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, I32, I32, I32, P, P, SZ, P]
     L.beam_attn_decode.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, P, P, SZ, P]
+    U32 = ctypes.c_uint32
+    L.beam_attn_prefill_stages.argtypes = [U32] + L.beam_attn_prefill.argtypes
+    L.beam_attn_decode_stages.argtypes = [U32] + L.beam_attn_decode.argtypes
     L.beam_prefill_workspace_bytes.argtypes = [P, I32, I32]
     L.beam_prefill_workspace_bytes.restype = SZ
     L.beam_decode_workspace_bytes.argtypes = [P, I32, I32, I32, I32]
@@ -86,7 +96,8 @@ def lib() -> ctypes.CDLL:
     L.beam_status_str.argtypes = [I32]
     L.beam_status_str.restype = ctypes.c_char_p
     L.beam_last_error.restype = ctypes.c_char_p
-    for name in ("beam_kv_append", "beam_attn_prefill", "beam_attn_decode", "beam_kv_bytes",
+    for name in ("beam_kv_append", "beam_attn_prefill", "beam_attn_decode", "beam_attn_prefill_stages",
+                 "beam_attn_decode_stages", "beam_kv_bytes",
                  "beam_kv_page_slot", "beam_debug_visibility"):
         getattr(L, name).restype = I32
     _lib = L
@@ -197,8 +208,10 @@ def kv_append(cfg: Config, cache: KVCache, k_raw, v_raw, k_norm_w, seq_idx, pos,
 
 
 def prefill(cfg: Config, cache: KVCache, q_raw, k_raw, v_raw, q_norm_w, k_norm_w, gate, cu_seqlens, seq_idx,
-            start_pos, max_chunk_len: int, gate_bias=None, out=None, workspace=None, stream=None):
-    """Chunked varlen prefill of one layer; returns out [n_tok][H][d] (bf16)."""
+            start_pos, max_chunk_len: int, gate_bias=None, out=None, workspace=None, stream=None,
+            stages: int = STAGE_ALL):
+    """Chunked varlen prefill of one layer; returns out [n_tok][H][d] (bf16).
+    `stages` selects prologue / attention / append (beam_attn_prefill_stages)."""
     import torch
     n_tok = q_raw.shape[0]
     n_seqs = cu_seqlens.shape[0] - 1
@@ -220,16 +233,17 @@ def prefill(cfg: Config, cache: KVCache, q_raw, k_raw, v_raw, q_norm_w, k_norm_w
     nbytes = prefill_workspace_bytes(cfg, n_tok, n_seqs)
     workspace = _workspace(nbytes, q_raw.device, workspace)
     c, kc = cfg.c(), cache.c()
-    _check(lib().beam_attn_prefill(
-        ctypes.byref(c), ctypes.byref(kc), _ptr(q_raw), _ptr(k_raw), _ptr(v_raw), _ptr(q_norm_w),
+    _check(lib().beam_attn_prefill_stages(
+        stages, ctypes.byref(c), ctypes.byref(kc), _ptr(q_raw), _ptr(k_raw), _ptr(v_raw), _ptr(q_norm_w),
         _ptr(k_norm_w), _ptr(gate), _ptr(gate_bias), _ptr(cu_seqlens), _ptr(seq_idx), _ptr(start_pos),
         n_seqs, n_tok, max_chunk_len, _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
 
 
 def decode(cfg: Config, cache: KVCache, q_raw, q_norm_w, gate, seq_idx, pos, max_pos: int, gate_bias=None,
-           split_keys: int = 0, out=None, workspace=None, stream=None):
-    """One-token decode of one layer; returns out [n_seqs][H][d] (bf16)."""
+           split_keys: int = 0, out=None, workspace=None, stream=None, stages: int = STAGE_ALL):
+    """One-token decode of one layer; returns out [n_seqs][H][d] (bf16).
+    `stages` selects prologue / split attention / combine (beam_attn_decode_stages)."""
     import torch
     n = q_raw.shape[0]
     H, d = cfg.n_q_heads, cfg.head_dim
@@ -248,8 +262,8 @@ def decode(cfg: Config, cache: KVCache, q_raw, q_norm_w, gate, seq_idx, pos, max
         raise BeamError(3, "invalid decode sizes (max_pos / split_keys)")
     workspace = _workspace(nbytes, q_raw.device, workspace)
     c, kc = cfg.c(), cache.c()
-    _check(lib().beam_attn_decode(
-        ctypes.byref(c), ctypes.byref(kc), _ptr(q_raw), _ptr(q_norm_w), _ptr(gate), _ptr(gate_bias),
+    _check(lib().beam_attn_decode_stages(
+        stages, ctypes.byref(c), ctypes.byref(kc), _ptr(q_raw), _ptr(q_norm_w), _ptr(gate), _ptr(gate_bias),
         _ptr(seq_idx), _ptr(pos), n, max_pos, split_keys, _ptr(out), _ptr(workspace), workspace.numel(),
         _stream(stream)))
     return out

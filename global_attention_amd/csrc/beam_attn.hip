@@ -194,13 +194,15 @@ beam_status beam_kv_append(const beam_attn_config* cfg, const beam_kv_cache* cac
   return ok();
 }
 
-beam_status beam_attn_prefill(const beam_attn_config* cfg, const beam_kv_cache* cache, const beam_bf16* q_raw,
-                              const beam_bf16* k_raw, const beam_bf16* v_raw, const beam_bf16* q_norm_w,
-                              const beam_bf16* k_norm_w, const beam_bf16* gate_logits, const float* gate_bias,
-                              const int32_t* cu_seqlens, const int32_t* seq_idx, const int32_t* start_pos,
-                              int32_t n_seqs, int32_t n_tok, int32_t max_chunk_len, beam_bf16* out,
-                              void* workspace, size_t ws_bytes, void* stream) {
+beam_status beam_attn_prefill_stages(uint32_t stages, const beam_attn_config* cfg, const beam_kv_cache* cache,
+                                     const beam_bf16* q_raw, const beam_bf16* k_raw, const beam_bf16* v_raw,
+                                     const beam_bf16* q_norm_w, const beam_bf16* k_norm_w,
+                                     const beam_bf16* gate_logits, const float* gate_bias, const int32_t* cu_seqlens,
+                                     const int32_t* seq_idx, const int32_t* start_pos, int32_t n_seqs, int32_t n_tok,
+                                     int32_t max_chunk_len, beam_bf16* out, void* workspace, size_t ws_bytes,
+                                     void* stream) {
   beam_status st;
+  if (stages & ~7u) return fail(BEAM_E_RANGE, "unknown stage bits");
   if ((st = check_cfg(cfg)) != BEAM_OK) return st;
   if ((st = check_cache(cache)) != BEAM_OK) return st;
   if (n_seqs <= 0) return fail(BEAM_E_RANGE, "n_seqs must be positive");
@@ -243,7 +245,8 @@ beam_status beam_attn_prefill(const beam_attn_config* cfg, const beam_kv_cache* 
   pp.ssmax_base = cfg->ssmax_base;
   pp.ssmax_exp = cfg->ssmax_exp;
   const int n_tiles = (max_chunk_len + 63) / 64 + 1;
-  if ((st = hip_status(beam::launch_prefill_prologue(pp, n_seqs, n_tiles, s), "prologue launch")) != BEAM_OK)
+  if ((stages & BEAM_STAGE_PROLOGUE) &&
+      (st = hip_status(beam::launch_prefill_prologue(pp, n_seqs, n_tiles, s), "prologue launch")) != BEAM_OK)
     return st;
 
   beam::PrefillParams ap{};
@@ -268,7 +271,9 @@ beam_status beam_attn_prefill(const beam_attn_config* cfg, const beam_kv_cache* 
   ap.n_seqs = n_seqs;
   ap.n_qtiles = (max_chunk_len + 127) / 128;
   ap.P = (int)ws.P;
-  if ((st = hip_status(beam::launch_prefill_attn(ap, s), "prefill attention launch")) != BEAM_OK) return st;
+  if ((stages & BEAM_STAGE_ATTENTION) &&
+      (st = hip_status(beam::launch_prefill_attn(ap, s), "prefill attention launch")) != BEAM_OK)
+    return st;
 
   beam::AppendParams xp{};
   xp.k_raw = k_raw;
@@ -290,16 +295,30 @@ beam_status beam_attn_prefill(const beam_attn_config* cfg, const beam_kv_cache* 
   xp.n_tok = n_tok;
   xp.rope_theta = cfg->rope_theta;
   xp.rms_eps = cfg->rms_eps;
-  if ((st = hip_status(beam::launch_kv_append(xp, s), "prefill append launch")) != BEAM_OK) return st;
+  if ((stages & BEAM_STAGE_APPEND) &&
+      (st = hip_status(beam::launch_kv_append(xp, s), "prefill append launch")) != BEAM_OK)
+    return st;
   return ok();
 }
 
-beam_status beam_attn_decode(const beam_attn_config* cfg, const beam_kv_cache* cache, const beam_bf16* q_raw,
-                             const beam_bf16* q_norm_w, const beam_bf16* gate_logits, const float* gate_bias,
-                             const int32_t* seq_idx, const int32_t* pos, int32_t n_seqs, int32_t max_pos,
-                             int32_t split_keys, beam_bf16* out, void* workspace, size_t ws_bytes,
-                             void* stream) {
+beam_status beam_attn_prefill(const beam_attn_config* cfg, const beam_kv_cache* cache, const beam_bf16* q_raw,
+                              const beam_bf16* k_raw, const beam_bf16* v_raw, const beam_bf16* q_norm_w,
+                              const beam_bf16* k_norm_w, const beam_bf16* gate_logits, const float* gate_bias,
+                              const int32_t* cu_seqlens, const int32_t* seq_idx, const int32_t* start_pos,
+                              int32_t n_seqs, int32_t n_tok, int32_t max_chunk_len, beam_bf16* out,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  return beam_attn_prefill_stages(BEAM_STAGE_ALL, cfg, cache, q_raw, k_raw, v_raw, q_norm_w, k_norm_w, gate_logits,
+                                  gate_bias, cu_seqlens, seq_idx, start_pos, n_seqs, n_tok, max_chunk_len, out,
+                                  workspace, ws_bytes, stream);
+}
+
+beam_status beam_attn_decode_stages(uint32_t stages, const beam_attn_config* cfg, const beam_kv_cache* cache,
+                                    const beam_bf16* q_raw, const beam_bf16* q_norm_w, const beam_bf16* gate_logits,
+                                    const float* gate_bias, const int32_t* seq_idx, const int32_t* pos,
+                                    int32_t n_seqs, int32_t max_pos, int32_t split_keys, beam_bf16* out,
+                                    void* workspace, size_t ws_bytes, void* stream) {
   beam_status st;
+  if (stages & ~7u) return fail(BEAM_E_RANGE, "unknown stage bits");
   if ((st = check_cfg(cfg)) != BEAM_OK) return st;
   if ((st = check_cache(cache)) != BEAM_OK) return st;
   if (n_seqs < 0) return fail(BEAM_E_RANGE, "n_seqs must be >= 0");
@@ -335,7 +354,9 @@ beam_status beam_attn_decode(const beam_attn_config* cfg, const beam_kv_cache* c
   qp_.rms_eps = cfg->rms_eps;
   qp_.ssmax_base = cfg->ssmax_base;
   qp_.ssmax_exp = cfg->ssmax_exp;
-  if ((st = hip_status(beam::launch_decode_q_prologue(qp_, s), "decode prologue launch")) != BEAM_OK) return st;
+  if ((stages & BEAM_STAGE_PROLOGUE) &&
+      (st = hip_status(beam::launch_decode_q_prologue(qp_, s), "decode prologue launch")) != BEAM_OK)
+    return st;
 
   beam::DecodeParams dp{};
   dp.qp = qp;
@@ -355,7 +376,9 @@ beam_status beam_attn_decode(const beam_attn_config* cfg, const beam_kv_cache* c
   dp.G = cfg->n_kv_heads;
   dp.n_splits = ws.n_splits;
   dp.kpw = ws.split_keys / 4;
-  if ((st = hip_status(beam::launch_decode_split(dp, n_seqs, s), "decode split launch")) != BEAM_OK) return st;
+  if ((stages & BEAM_STAGE_ATTENTION) &&
+      (st = hip_status(beam::launch_decode_split(dp, n_seqs, s), "decode split launch")) != BEAM_OK)
+    return st;
 
   beam::CombineParams cp{};
   cp.part_ml = ml;
@@ -370,8 +393,19 @@ beam_status beam_attn_decode(const beam_attn_config* cfg, const beam_kv_cache* c
   cp.H = cfg->n_q_heads;
   cp.n_splits = ws.n_splits;
   cp.split_keys = ws.split_keys;
-  if ((st = hip_status(beam::launch_decode_combine(cp, n_seqs, s), "decode combine launch")) != BEAM_OK) return st;
+  if ((stages & BEAM_STAGE_COMBINE) &&
+      (st = hip_status(beam::launch_decode_combine(cp, n_seqs, s), "decode combine launch")) != BEAM_OK)
+    return st;
   return ok();
+}
+
+beam_status beam_attn_decode(const beam_attn_config* cfg, const beam_kv_cache* cache, const beam_bf16* q_raw,
+                             const beam_bf16* q_norm_w, const beam_bf16* gate_logits, const float* gate_bias,
+                             const int32_t* seq_idx, const int32_t* pos, int32_t n_seqs, int32_t max_pos,
+                             int32_t split_keys, beam_bf16* out, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  return beam_attn_decode_stages(BEAM_STAGE_ALL, cfg, cache, q_raw, q_norm_w, gate_logits, gate_bias, seq_idx, pos,
+                                 n_seqs, max_pos, split_keys, out, workspace, ws_bytes, stream);
 }
 
 beam_status beam_debug_visibility(int32_t kind, int32_t window, int32_t t0, int32_t n_q, int32_t s0, int32_t n_k,

@@ -27,6 +27,7 @@ struct DecodeStep {
   u32x2 v[2][8];  // [page][d-block of 16]
 };
 
+template <int KIND>
 __global__ void __launch_bounds__(256, 2) decode_split_kernel(DecodeParams p) {
   const int hpg = p.H / p.G;
   int b = blockIdx.x;
@@ -40,7 +41,7 @@ __global__ void __launch_bounds__(256, 2) decode_split_kernel(DecodeParams p) {
   // Positions beyond max_pos or bad cache rows are not read (the combine
   // kernel writes NaN for such sequences).
   if (t < 0 || t > p.max_pos || cseq < 0 || cseq >= p.n_cache_seqs) return;
-  const bool local = (p.kind == 0);
+  constexpr bool local = (KIND == 0);
   const int n_keys = local ? min(t + 1, p.window) : t + 1;
   const int split0 = sp * 4 * p.kpw;
   if (split0 >= n_keys) return;
@@ -261,7 +262,10 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(CombineParams p) {
 
 hipError_t launch_decode_split(const DecodeParams& p, int n_seqs, hipStream_t s) {
   const long long blocks = (long long)n_seqs * p.G * p.n_splits;
-  hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  if (p.kind == 0)
+    hipLaunchKernelGGL(decode_split_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(decode_split_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

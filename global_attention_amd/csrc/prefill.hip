@@ -117,6 +117,7 @@ __device__ __forceinline__ void store_tile(uint16_t* sK, uint16_t* sV, int tid, 
   }
 }
 
+template <int KIND>
 __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (K_TILE + V_TILE)];
 
@@ -136,7 +137,7 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillParams p) {
   const int start = p.start_pos[seq];
   const int cseq = p.seq_idx[seq];
   const int W = p.window;
-  const bool local = (p.kind == 0);
+  constexpr bool local = (KIND == 0);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -157,15 +158,15 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillParams p) {
   ks.vw = p.vw;
   ks.ck = p.ck;
   ks.cv = p.cv;
-  ks.bt_row = p.kind == 1 ? p.bt + (size_t)cseq * p.max_pages : nullptr;
+  ks.bt_row = KIND == 1 ? p.bt + (size_t)cseq * p.max_pages : nullptr;
   ks.start = start;
   // The cached prefix must fit the cache sequence's block-table row (global).
-  ks.cache_ok = cseq >= 0 && cseq < p.n_cache_seqs && (p.kind == 0 || ((start + 15) >> 4) <= p.max_pages);
+  ks.cache_ok = cseq >= 0 && cseq < p.n_cache_seqs && (KIND == 0 || ((start + 15) >> 4) <= p.max_pages);
   ks.ws_off = ws_region_base(cu0, seq) - (start & ~63);
   ks.g = g;
   ks.G = p.G;
   ks.P = p.P;
-  ks.kind = p.kind;
+  ks.kind = KIND;
   ks.window = W;
   ks.ring_base = (size_t)cseq * p.G + g;
 
@@ -227,7 +228,7 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillParams p) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             int sk = ks0 + 32 * mb + 8 * (i >> 2) + 4 * half + (i & 3);
-            if (!visible(p.kind, W, t, sk)) s[mb][i] = kNegInf;
+            if (!visible(KIND, W, t, sk)) s[mb][i] = kNegInf;
           }
       }
       float mt = kNegInf;
@@ -305,7 +306,10 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillParams p) {
 
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {
   const long long blocks = (long long)p.G * (p.H / p.G) * p.n_seqs * p.n_qtiles;
-  hipLaunchKernelGGL(prefill_attn_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  if (p.kind == 0)
+    hipLaunchKernelGGL(prefill_attn_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(prefill_attn_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -140,6 +140,38 @@ beam_status beam_attn_decode(const beam_attn_config *cfg, const beam_kv_cache *c
                              int32_t max_pos, int32_t split_keys, beam_bf16 *out,
                              void *workspace, size_t ws_bytes, void *stream);
 
+/* Stage selection for the *_stages variants. Running the stages of one call
+ * separately, in this order, on one stream, with the same arguments and
+ * workspace, is identical to the single call (the workspace carries the state
+ * between stages). Lets a caller bracket one stage with events, or overlap the
+ * cache append with other work.
+ *   prefill: PROLOGUE = norm + RoPE/SSMax into the workspace, ATTENTION =
+ *            attention + gate into `out`, APPEND = chunk K_hat/V into the cache.
+ *   decode:  PROLOGUE = query norm + RoPE/SSMax, ATTENTION = split-K partials,
+ *            COMBINE = merge of the splits + gate into `out`. */
+#define BEAM_STAGE_PROLOGUE 1u
+#define BEAM_STAGE_ATTENTION 2u
+#define BEAM_STAGE_APPEND 4u
+#define BEAM_STAGE_COMBINE 4u
+#define BEAM_STAGE_ALL 7u
+
+beam_status beam_attn_prefill_stages(uint32_t stages, const beam_attn_config *cfg,
+                                     const beam_kv_cache *cache, const beam_bf16 *q_raw,
+                                     const beam_bf16 *k_raw, const beam_bf16 *v_raw,
+                                     const beam_bf16 *q_norm_w, const beam_bf16 *k_norm_w,
+                                     const beam_bf16 *gate_logits, const float *gate_bias,
+                                     const int32_t *cu_seqlens, const int32_t *seq_idx,
+                                     const int32_t *start_pos, int32_t n_seqs, int32_t n_tok,
+                                     int32_t max_chunk_len, beam_bf16 *out, void *workspace,
+                                     size_t ws_bytes, void *stream);
+beam_status beam_attn_decode_stages(uint32_t stages, const beam_attn_config *cfg,
+                                    const beam_kv_cache *cache, const beam_bf16 *q_raw,
+                                    const beam_bf16 *q_norm_w, const beam_bf16 *gate_logits,
+                                    const float *gate_bias, const int32_t *seq_idx,
+                                    const int32_t *pos, int32_t n_seqs, int32_t max_pos,
+                                    int32_t split_keys, beam_bf16 *out, void *workspace,
+                                    size_t ws_bytes, void *stream);
+
 /* Workspace sizes in bytes (host-only, no GPU needed). 0 on invalid arguments. */
 size_t beam_prefill_workspace_bytes(const beam_attn_config *cfg, int32_t n_tok, int32_t n_seqs);
 size_t beam_decode_workspace_bytes(const beam_attn_config *cfg, int32_t kind, int32_t n_seqs,

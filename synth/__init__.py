@@ -4,16 +4,24 @@ This module holds no arithmetic of the attention method: it only draws
 numbers and converts them to the storage format (bf16 bit patterns), so that
 the oracle and the GPU consume the very same input bits.
 
-Recipe (every tensor): ``numpy.random.Generator(PCG64(SeedSequence([cfg,
-tensor_id, layer])))`` draws float32 N(0,1) values, which are rounded to
-bfloat16 with round-to-nearest-even and kept as ``uint16`` bit patterns.
+Recipe (every tensor): the tensor is cut into blocks of 1024 rows along its
+first (token) axis; block b is drawn by ``numpy.random.Generator(PCG64(
+SeedSequence([cfg, tensor_id, layer, b])))`` as float32 N(0,1) values (blocks
+are drawn in parallel threads), which are rounded to bfloat16 with
+round-to-nearest-even and kept as ``uint16`` bit patterns.
 RMSNorm weights are 1 + 0.1*N(0,1), gate logits N(0,1), gate bias absent.
 Position/page structure (decode contexts, random page permutation, chunked
 prefill lengths) is drawn from the same kind of generator with its own id.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
+
+BLOCK_ROWS = 1024
+_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 # tensor ids for SeedSequence([cfg, tensor_id, layer])
 T_Q, T_K, T_V, T_GATE, T_QW, T_KW, T_POS, T_PERM, T_LEN, T_MISC = range(10)
@@ -38,9 +46,28 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 def normal_bf16(shape, cfg: int, tensor_id: int, layer: int = 0, scale: float = 1.0,
                 offset: float = 0.0) -> np.ndarray:
-    g = rng(cfg, tensor_id, layer)
-    x = g.standard_normal(size=shape, dtype=np.float32) * np.float32(scale) + np.float32(offset)
-    return f32_to_bf16_bits(x)
+    """bf16 bits of scale*N(0,1)+offset, drawn in seeded blocks of 1024 rows."""
+    shape = tuple(shape)
+    out = np.empty(shape, dtype=np.uint16)
+    rows = shape[0] if shape else 1
+    n_blocks = max(1, -(-rows // BLOCK_ROWS))
+
+    def block(b):
+        lo, hi = b * BLOCK_ROWS, min(rows, (b + 1) * BLOCK_ROWS)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg, tensor_id, layer, b])))
+        x = g.standard_normal(size=(hi - lo,) + shape[1:], dtype=np.float32)
+        if scale != 1.0:
+            x *= np.float32(scale)
+        if offset != 0.0:
+            x += np.float32(offset)
+        out[lo:hi] = f32_to_bf16_bits(x)
+
+    if n_blocks == 1:
+        block(0)
+    else:
+        with ThreadPoolExecutor(min(_THREADS, n_blocks)) as ex:
+            list(ex.map(block, range(n_blocks)))
+    return out
 
 
 def attention_inputs(cfg: int, layer: int, n_tok: int, n_q: int = 48, n_kv: int = 8, d: int = 128):
