@@ -48,6 +48,18 @@ struct DecodeQParams {
   float rope_theta, rms_eps, ssmax_base, ssmax_exp;
 };
 
+// Prefill attention tiling: queries per wavefront (a multiple of 32) and
+// wavefronts per block.
+#ifndef BEAM_PREFILL_QW
+#define BEAM_PREFILL_QW 32
+#endif
+#ifndef BEAM_PREFILL_WAVES
+#define BEAM_PREFILL_WAVES 8
+#endif
+constexpr int kPrefillWaveQueries = BEAM_PREFILL_QW;
+constexpr int kPrefillWaves = BEAM_PREFILL_WAVES;
+constexpr int kPrefillBlockQueries = BEAM_PREFILL_QW * BEAM_PREFILL_WAVES;
+
 struct PrefillParams {
   const uint16_t* qp;  // Q' [n_tok][H][D]
   const uint16_t* kw;  // K_hat workspace [G][P][D]

@@ -8,28 +8,62 @@
 // the parameter label"). The score matrix is never materialised (section "KV
 // memory: nine growing caches, not 52" notes flash-style kernels avoid it).
 //
-// Block = 4 wavefronts = 128 queries of one query head; KV tiles of 64 keys are
-// staged through LDS (double-buffered). Each wave owns 32 queries and computes
-// S^T = K Q'^T with v_mfma_f32_32x32x16_bf16 (keys on M, queries on N), so each
-// lane holds one query column and a row max needs a single cross-half swap.
-// P^T is fed straight from the S accumulators into O^T += V^T P^T; V^T is kept
-// in LDS with the key order permuted inside each 16-key group to match the
-// accumulator layout. Softmax runs in base 2 (Q' carries log2 e / sqrt d and,
-// on global layers, a(t+1)); the running max is only moved when it grows by
-// more than 8 (exact: the final normalisation uses the same reference).
-// Local layers visit only the key tiles that intersect the window.
+// Tiling. A block is NWAVES wavefronts x QW queries of one query head. KV tiles
+// of 64 keys are double-buffered in LDS. Each wave computes
+// S^T = K Q'^T with v_mfma_f32_32x32x16_bf16 (keys on M, its queries on N), so
+// a lane holds one query column and the row max is an in-lane max plus one
+// v_permlane32_swap. The S accumulators are packed to bf16 and fed directly as
+// the B operand of O^T += V^T P^T.
+//
+// LDS layout. Tiles that lie inside the chunk are copied from the workspace
+// straight into LDS with global_load_lds_dwordx4 (no staging registers).
+//   K:   64 rows x 256 B. LDS row m holds key kappa(m) = m with bits 2 and 3
+//        swapped; the MFMA output row order then becomes natural key order,
+//        which is the order the PV operand needs.
+//   V^T: 128 rows (coordinates) x 128 B (64 keys, natural order).
+// Both XOR-swizzle their 16-byte chunks with the low 3 bits of the row, which
+// keeps the b128 operand reads free of bank conflicts without padding.
+// Tiles that reach into the cached prefix are gathered through registers.
+//
+// Softmax runs in base 2 (Q' carries log2 e / sqrt d and, on global layers,
+// a(t+1)); the running max only moves when it grows by more than 8 (exact:
+// the final normalisation uses the same reference). Local layers visit only
+// the key tiles that intersect the window.
 #include "beam_device.h"
 #include "beam_kernels.h"
 
 namespace beam {
 
-constexpr int BM = 128;       // queries per block
-constexpr int BN = 64;        // keys per tile
-constexpr int KROW = D + 8;   // LDS row of K (bf16): 272 B, conflict-free b128 reads
-constexpr int VROW = BN + 8;  // LDS row of V^T (bf16): 144 B
-constexpr int K_TILE = BN * KROW;
-constexpr int V_TILE = D * VROW;
+constexpr int QW = kPrefillWaveQueries;  // queries per wave (N-blocks of 32)
+constexpr int NWAVES = kPrefillWaves;
+constexpr int NTHREADS = 64 * NWAVES;
+constexpr int BM = NWAVES * QW;          // queries per block
+constexpr int NB = QW / 32;
+constexpr int BN = 64;                   // keys per tile
+constexpr int K_TILE = BN * D;           // bf16 elements
+constexpr int V_TILE = D * BN;
+constexpr int LPT = 1024 / NTHREADS;     // 16-byte K (and V) pieces per thread per tile (register path)
+constexpr int DMA_PER_WAVE = 16 / NWAVES;  // 1 KiB DMA instructions per wave per tile, for K and for V
 constexpr float kRescaleThreshold = 8.0f;
+static_assert(BM == kPrefillBlockQueries, "block size");
+static_assert(16 % NWAVES == 0 && 1024 % NTHREADS == 0, "tile split");
+
+// Key held by LDS row m of a K tile (bits 2 and 3 swapped; an involution).
+__device__ __forceinline__ int krow_key(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+// Element offsets of 16-byte chunk c of K row m and of V^T row d.
+__device__ __forceinline__ int k_off(int m, int c) { return m * D + ((c ^ (m & 7)) << 3); }
+__device__ __forceinline__ int v_off(int d, int c) { return d * BN + ((c ^ (d & 7)) << 3); }
+
+// Combine a value held by lanes l and l^32 (the two key halves of a query)
+// with v_permlane32_swap, without an LDS round trip.
+__device__ __forceinline__ float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 struct KeySource {
   const uint16_t* kw;
@@ -44,7 +78,8 @@ struct KeySource {
   size_t ring_base;       // (cseq*G + g) for the local ring
 };
 
-// 16 bytes of K row s, coordinates [8c, 8c+8).
+// ---------------------------------------------------------------- register path
+// 16 bytes of K row s, coordinates [8c, 8c+8), from wherever key s lives.
 __device__ __forceinline__ u32x4 load_k_piece(const KeySource& ks, int s, int c) {
   const uint16_t* src;
   if (s >= ks.start) {
@@ -93,33 +128,71 @@ __device__ __forceinline__ u32x4 load_v_piece(const KeySource& ks, int d, int s8
   return r;
 }
 
-__device__ __forceinline__ void load_tile(const KeySource& ks, int key0, int tid, u32x4 (&kr)[4],
-                                          u32x4 (&vr)[4]) {
+// Gather a tile through registers (tiles touching the cached prefix).
+__device__ __forceinline__ void gather_tile(const KeySource& ks, int key0, int tid, u32x4 (&kr)[LPT],
+                                            u32x4 (&vr)[LPT]) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    int id = tid + 256 * r;
-    kr[r] = load_k_piece(ks, key0 + (id >> 4), id & 15);
-    vr[r] = load_v_piece(ks, id >> 3, key0 + 8 * (id & 7));
+  for (int r = 0; r < LPT; ++r) {
+    const int id = tid + NTHREADS * r;
+    kr[r] = load_k_piece(ks, key0 + (id >> 4), id & 15);   // key row (id>>4), chunk (id&15)
+    vr[r] = load_v_piece(ks, id >> 3, key0 + 8 * (id & 7));  // V^T row (id>>3), chunk (id&7)
   }
 }
 
-__device__ __forceinline__ void store_tile(uint16_t* sK, uint16_t* sV, int tid, const u32x4 (&kr)[4],
-                                           const u32x4 (&vr)[4]) {
+__device__ __forceinline__ void scatter_tile(uint16_t* sK, uint16_t* sV, int tid, const u32x4 (&kr)[LPT],
+                                             const u32x4 (&vr)[LPT]) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    int id = tid + 256 * r;
-    *reinterpret_cast<u32x4*>(sK + (id >> 4) * KROW + 8 * (id & 15)) = kr[r];
-    // keys 8c+0..3 -> positions 16(c>>1) + 4(c&1) + 0..3, keys 8c+4..7 -> +8
-    int d = id >> 3, c = id & 7;
-    uint16_t* dst = sV + d * VROW + 16 * (c >> 1) + 4 * (c & 1);
-    *reinterpret_cast<u32x2*>(dst) = u32x2{vr[r][0], vr[r][1]};
-    *reinterpret_cast<u32x2*>(dst + 8) = u32x2{vr[r][2], vr[r][3]};
+  for (int r = 0; r < LPT; ++r) {
+    const int id = tid + NTHREADS * r;
+    *reinterpret_cast<u32x4*>(sK + k_off(krow_key(id >> 4), id & 15)) = kr[r];
+    *reinterpret_cast<u32x4*>(sV + v_off(id >> 3, id & 7)) = vr[r];
   }
 }
 
+// ---------------------------------------------------------------- DMA path
+// Element offsets (relative to the tile's first key in the workspace) of the
+// chunks this lane moves with each of its DMA instructions, and the LDS
+// offset of each instruction's 1 KiB.
+struct DmaPlan {
+  uint32_t k_src[DMA_PER_WAVE];
+  uint32_t v_src[DMA_PER_WAVE];
+  int k_lds[DMA_PER_WAVE];
+  int v_lds[DMA_PER_WAVE];
+};
+
+__device__ __forceinline__ DmaPlan make_dma_plan(int w, int lane, int P) {
+  DmaPlan pl;
+#pragma unroll
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    const int kI = w * DMA_PER_WAVE + i;  // K rows 4kI .. 4kI+3
+    const int m = 4 * kI + (lane >> 4);
+    const int c = (lane & 15) ^ (m & 7);
+    pl.k_src[i] = (uint32_t)(krow_key(m) * D + 8 * c);
+    pl.k_lds[i] = kI * 512;
+    const int vI = w * DMA_PER_WAVE + i;  // V^T rows 8vI .. 8vI+7
+    const int d = 8 * vI + (lane >> 3);
+    const int cv = (lane & 7) ^ (d & 7);
+    pl.v_src[i] = (uint32_t)(d * P + 8 * cv);
+    pl.v_lds[i] = vI * 512;
+  }
+  return pl;
+}
+
+__device__ __forceinline__ void dma_tile(const KeySource& ks, const DmaPlan& pl, int key0, uint16_t* sK,
+                                         uint16_t* sV) {
+  const uint16_t* kb = ks.kw + ((size_t)ks.g * ks.P + (key0 + ks.ws_off)) * D;
+  const uint16_t* vb = ks.vw + (size_t)ks.g * D * ks.P + (key0 + ks.ws_off);
+#pragma unroll
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    __builtin_amdgcn_global_load_lds(kb + pl.k_src[i], sK + pl.k_lds[i], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vb + pl.v_src[i], sV + pl.v_lds[i], 16, 0, 0);
+  }
+}
+
+// ---------------------------------------------------------------- kernel
 template <int KIND>
-__global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (K_TILE + V_TILE)];
+__global__ void __launch_bounds__(NTHREADS, (QW == 32 ? 8 / NWAVES : 1)) prefill_attn_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * (K_TILE + V_TILE)];
 
   const int hpg = p.H / p.G;
   int b = blockIdx.x;
@@ -141,17 +214,15 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (DMA bases go to M0)
   const int n = lane & 31;
   const int half = lane >> 5;
 
   const int q0 = start + qt * BM;                   // first query position of the block
   const int qlast = min(q0 + BM, start + len) - 1;  // last valid query position
-  const int wq_lo = q0 + 32 * w;
-  const int wq_hi = min(wq_lo + 31, qlast);
+  const int wq_lo = q0 + QW * w;
+  const int wq_hi = min(wq_lo + QW - 1, qlast);
   const bool wave_active = wq_lo <= qlast;
-  const int t = wq_lo + n;  // this lane's query position
-  const bool row_valid = t <= qlast;
 
   KeySource ks;
   ks.kw = p.kw;
@@ -169,137 +240,207 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillParams p) {
   ks.kind = KIND;
   ks.window = W;
   ks.ring_base = (size_t)cseq * p.G + g;
+  const DmaPlan plan = make_dma_plan(w, lane, p.P);
 
-  // Q' fragments (B operand of S^T = K Q'^T): lane holds query n, coords 16kk + 8*half + 0..7.
-  u32x4 qf[8];
-  {
+  // Q' fragments (B operand of S^T = K Q'^T): lane holds query n of N-block nb,
+  // coordinates 16kk + 8*half + 0..7.
+  u32x4 qf[NB][8];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int t = wq_lo + 32 * nb + n;
+    const bool valid = t <= qlast;
     const size_t tok = (size_t)(cu0 + (t - start));
     const uint16_t* qrow = p.qp + (tok * p.H + h) * D + 8 * half;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
-      qf[kk] = row_valid ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk) : u32x4{0u, 0u, 0u, 0u};
+      qf[nb][kk] = valid ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk) : u32x4{0u, 0u, 0u, 0u};
   }
 
   const int kmin = local ? max(0, q0 - (W - 1)) : 0;
   const int j_lo = kmin >> 6;
   const int j_hi = qlast >> 6;
+  const int j_ws = (start + BN - 1) >> 6;  // first tile whose keys all come from the workspace
 
-  f32x16 o[4];
+  f32x16 o[NB][4];
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-  float m_run = kNegInf;
-  float l_run = 0.f;
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[nb][db][i] = 0.f;
+  float m_run[NB], l_run[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    m_run[nb] = kNegInf;
+    l_run[nb] = 0.f;
+  }
 
-  u32x4 kr[4], vr[4];
-  load_tile(ks, j_lo * BN, tid, kr, vr);
-  store_tile(smem, smem + 2 * K_TILE, tid, kr, vr);
-  __syncthreads();
-
-  for (int jt = j_lo; jt <= j_hi; ++jt) {
-    const int buf = (jt - j_lo) & 1;
-    const uint16_t* sK = smem + buf * K_TILE;
-    const uint16_t* sV = smem + 2 * K_TILE + buf * V_TILE;
-    const bool has_next = jt < j_hi;
-    if (has_next) load_tile(ks, (jt + 1) * BN, tid, kr, vr);
-
+  // One KV tile of attention for this wave's queries (LDS buffer `buf`).
+  auto compute_tile = [&](int jt, int buf) {
+    const uint16_t* sK = smem + buf * (K_TILE + V_TILE);
+    const uint16_t* sV = sK + K_TILE;
     const int ks0 = jt * BN;
     const bool skip = !wave_active || ks0 > wq_hi || (local && ks0 + BN - 1 < wq_lo - (W - 1));
-    if (!skip) {
-      // S^T tile: keys 32mb + (lane&31) on M, queries on N.
-      f32x16 s[2];
+    if (skip) return;
+    const bool need_mask = (ks0 + BN - 1 > wq_lo) || (local && ks0 < wq_hi - (W - 1));
+    // S^T: LDS rows 32mb + (lane&31) on M, queries 32nb + n on N.
+    f32x16 s[NB][2];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[mb][i] = 0.f;
+        for (int i = 0; i < 16; ++i) s[nb][mb][i] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
+    for (int kk = 0; kk < 8; ++kk) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          u32x4 a = *reinterpret_cast<const u32x4*>(sK + (32 * mb + n) * KROW + 16 * kk + 8 * half);
-          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qf[kk]), s[mb], 0, 0, 0);
-        }
+      for (int mb = 0; mb < 2; ++mb) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sK + k_off(32 * mb + n, 2 * kk + half));
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          s[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qf[nb][kk]), s[nb][mb], 0, 0, 0);
       }
-      const bool need_mask = (ks0 + BN - 1 > wq_lo) || (local && ks0 < wq_hi - (W - 1));
-      if (need_mask) {
+    }
+    // Element i of block mb holds key ks0 + 32mb + 16(i>>3) + 8*half + (i&7).
+    if (need_mask) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int t = wq_lo + 32 * nb + n;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            int sk = ks0 + 32 * mb + 8 * (i >> 2) + 4 * half + (i & 3);
-            if (!visible(KIND, W, t, sk)) s[mb][i] = kNegInf;
+            const int sk = ks0 + 32 * mb + 16 * (i >> 3) + 8 * half + (i & 7);
+            if (!visible(KIND, W, t, sk)) s[nb][mb][i] = kNegInf;
           }
       }
+    }
+    float m_new[NB];
+    bool grow = false;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
       float mt = kNegInf;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[mb][i]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(m_run, mt);
-      if (__any(m_new > m_run + kRescaleThreshold)) {
-        const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[nb][mb][i]);
+      mt = max_halves(mt);
+      m_new[nb] = fmaxf(m_run[nb], mt);
+      grow = grow || (m_new[nb] > m_run[nb] + kRescaleThreshold);
+    }
+    if (__any(grow)) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const float alpha = (m_new[nb] == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run[nb] - m_new[nb]);
+        m_run[nb] = m_new[nb];
+        l_run[nb] *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+          for (int i = 0; i < 16; ++i) o[nb][db][i] *= alpha;
       }
-      const float mu = (m_run == kNegInf) ? 0.f : m_run;
-      u32x4 pf[4];
+    }
+    // P^T operand of key block kb: elements 8(kb&1)..+7 of S block kb>>1, i.e.
+    // keys 16kb + 8*half + 0..7 in order.
+    u32x4 pf[NB][4];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float mu = (m_run[nb] == kNegInf) ? 0.f : m_run[nb];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         float e[8];
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-          e[jj] = __builtin_amdgcn_exp2f(s[kb >> 1][8 * (kb & 1) + jj] - mu);
-          l_run += e[jj];
+          e[jj] = __builtin_amdgcn_exp2f(s[nb][kb >> 1][8 * (kb & 1) + jj] - mu);
+          l_run[nb] += e[jj];
         }
-        pf[kb] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
-                       pack_bf16x2(e[6], e[7])};
-      }
-      // O^T += V^T P^T over the 4 key blocks of 16.
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          u32x4 a = *reinterpret_cast<const u32x4*>(sV + (32 * db + n) * VROW + 16 * kb + 8 * half);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pf[kb]), o[db], 0, 0, 0);
-        }
+        pf[nb][kb] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
+                           pack_bf16x2(e[6], e[7])};
       }
     }
+    // O^T += V^T P^T: A operand = coordinates 32db + n, keys 16kb + 8*half + 0..7.
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sV + v_off(32 * db + n, 2 * kb + half));
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          o[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pf[nb][kb]), o[nb][db], 0, 0, 0);
+      }
+    }
+  };
 
-    if (has_next) {
-      store_tile(smem + (buf ^ 1) * K_TILE, smem + 2 * K_TILE + (buf ^ 1) * V_TILE, tid, kr, vr);
+  // First tile.
+  {
+    uint16_t* sK = smem;
+    if (j_lo >= j_ws) {
+      dma_tile(ks, plan, j_lo * BN, sK, sK + K_TILE);
+    } else {
+      u32x4 kr[LPT], vr[LPT];
+      gather_tile(ks, j_lo * BN, tid, kr, vr);
+      scatter_tile(sK, sK + K_TILE, tid, kr, vr);
     }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
-  // Epilogue: normalise, gate, write bf16. Lane holds query n and coordinates
-  // d = 32db + 8a + 4*half + 0..3.
-  if (!row_valid) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  int jt = j_lo;
+  // Phase 1: tiles that reach into the cached prefix (chunked prefill only).
+  for (; jt <= j_hi && jt < j_ws; ++jt) {
+    const int buf = (jt - j_lo) & 1;
+    uint16_t* nK = smem + (buf ^ 1) * (K_TILE + V_TILE);
+    const bool has_next = jt < j_hi;
+    const bool next_dma = jt + 1 >= j_ws;
+    u32x4 kr[LPT], vr[LPT];
+    if (has_next) {
+      if (next_dma) dma_tile(ks, plan, (jt + 1) * BN, nK, nK + K_TILE);
+      else gather_tile(ks, (jt + 1) * BN, tid, kr, vr);
+    }
+    compute_tile(jt, buf);
+    if (has_next && !next_dma) scatter_tile(nK, nK + K_TILE, tid, kr, vr);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  // Phase 2: tiles entirely inside the chunk (the hot loop).
+  for (; jt <= j_hi; ++jt) {
+    const int buf = (jt - j_lo) & 1;
+    if (jt < j_hi) {
+      uint16_t* nK = smem + (buf ^ 1) * (K_TILE + V_TILE);
+      dma_tile(ks, plan, (jt + 1) * BN, nK, nK + K_TILE);
+    }
+    compute_tile(jt, buf);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  // Epilogue: normalise, gate, write bf16. Lane holds query n of each N-block
+  // and coordinates d = 32db + 8a + 4*half + 0..3.
   const float bias = p.gate_bias ? p.gate_bias[h] : 0.f;
-  const size_t tok = (size_t)(cu0 + (t - start));
-  const uint16_t* grow = p.gate + (tok * p.H + h) * D;
-  uint16_t* orow = p.out + (tok * p.H + h) * D;
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
+  for (int nb = 0; nb < NB; ++nb) {
+    const int t = wq_lo + 32 * nb + n;
+    const float l_tot = sum_halves(l_run[nb]);
+    if (t > qlast) continue;
+    const float inv = l_tot > 0.f ? __frcp_rn(l_tot) : 0.f;
+    const size_t tok = (size_t)(cu0 + (t - start));
+    const uint16_t* grow_ = p.gate + (tok * p.H + h) * D;
+    uint16_t* orow = p.out + (tok * p.H + h) * D;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int d0 = 32 * db + 8 * a + 4 * half;
-      u32x2 gv = *reinterpret_cast<const u32x2*>(grow + d0);
-      float gz[4] = {bf16lo(gv[0]), bf16hi(gv[0]), bf16lo(gv[1]), bf16hi(gv[1])};
-      float y[4];
+    for (int db = 0; db < 4; ++db) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float sg = 1.f / (1.f + __expf(-(gz[e] + bias)));
-        y[e] = o[db][4 * a + e] * inv * sg;
+      for (int a = 0; a < 4; ++a) {
+        const int d0 = 32 * db + 8 * a + 4 * half;
+        const u32x2 gv = *reinterpret_cast<const u32x2*>(grow_ + d0);
+        const float gz[4] = {bf16lo(gv[0]), bf16hi(gv[0]), bf16lo(gv[1]), bf16hi(gv[1])};
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float sg = __frcp_rn(1.f + __expf(-(gz[e] + bias)));
+          y[e] = o[nb][db][4 * a + e] * inv * sg;
+        }
+        *reinterpret_cast<u32x2*>(orow + d0) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
       }
-      *reinterpret_cast<u32x2*>(orow + d0) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
     }
   }
 }
@@ -307,9 +448,9 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillParams p) {
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {
   const long long blocks = (long long)p.G * (p.H / p.G) * p.n_seqs * p.n_qtiles;
   if (p.kind == 0)
-    hipLaunchKernelGGL(prefill_attn_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(prefill_attn_kernel<0>, dim3((unsigned)blocks), dim3(NTHREADS), 0, s, p);
   else
-    hipLaunchKernelGGL(prefill_attn_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(prefill_attn_kernel<1>, dim3((unsigned)blocks), dim3(NTHREADS), 0, s, p);
   return hipGetLastError();
 }
 
