@@ -271,7 +271,7 @@ def main():
         l_ms = r["attn_ms"][0]
         g_flops = FLOP_PER_PAIR * pairs_global(T)
         achieved = g_flops / (g_ms / 1e3) / 1e12
-        rec["roofline"] = {"kernel": "prefill_attn_kernel<1> (global layer)", "bound": "mfma",
+        rec["roofline"] = {"kernel": "prefill_attn_kernel<1, 8> (global layer)", "bound": "mfma",
                            "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
                            "avg_launch_ms": round(g_ms, 4), "flop_per_launch": g_flops}

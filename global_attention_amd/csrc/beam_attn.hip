@@ -269,7 +269,7 @@ beam_status beam_attn_prefill_stages(uint32_t stages, const beam_attn_config* cf
   ap.H = cfg->n_q_heads;
   ap.G = cfg->n_kv_heads;
   ap.n_seqs = n_seqs;
-  ap.n_qtiles = (max_chunk_len + beam::kPrefillBlockQueries - 1) / beam::kPrefillBlockQueries;
+  ap.n_qtiles = (max_chunk_len + beam::prefill_block_queries(cache->kind) - 1) / beam::prefill_block_queries(cache->kind);
   ap.P = (int)ws.P;
   if ((stages & BEAM_STAGE_ATTENTION) &&
       (st = hip_status(beam::launch_prefill_attn(ap, s), "prefill attention launch")) != BEAM_OK)

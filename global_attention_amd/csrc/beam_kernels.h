@@ -48,17 +48,12 @@ struct DecodeQParams {
   float rope_theta, rms_eps, ssmax_base, ssmax_exp;
 };
 
-// Prefill attention tiling: queries per wavefront (a multiple of 32) and
-// wavefronts per block.
-#ifndef BEAM_PREFILL_QW
-#define BEAM_PREFILL_QW 32
-#endif
-#ifndef BEAM_PREFILL_WAVES
-#define BEAM_PREFILL_WAVES 8
-#endif
-constexpr int kPrefillWaveQueries = BEAM_PREFILL_QW;
-constexpr int kPrefillWaves = BEAM_PREFILL_WAVES;
-constexpr int kPrefillBlockQueries = BEAM_PREFILL_QW * BEAM_PREFILL_WAVES;
+// Prefill attention tiling: 32 queries per wavefront; 8 wavefronts per block
+// on global layers (one block per CU), 4 on local layers (two blocks per CU:
+// a window-limited tile range favours smaller, independent blocks).
+constexpr int kPrefillWavesGlobal = 8;
+constexpr int kPrefillWavesLocal = 4;
+constexpr int prefill_block_queries(int kind) { return 32 * (kind == 0 ? kPrefillWavesLocal : kPrefillWavesGlobal); }
 
 struct PrefillParams {
   const uint16_t* qp;  // Q' [n_tok][H][D]

@@ -34,19 +34,16 @@
 
 namespace beam {
 
-constexpr int QW = kPrefillWaveQueries;  // queries per wave (N-blocks of 32)
-constexpr int NWAVES = kPrefillWaves;
-constexpr int NTHREADS = 64 * NWAVES;
-constexpr int BM = NWAVES * QW;          // queries per block
+constexpr int QW = 32;                   // queries per wave (one 32-wide MFMA N-block)
 constexpr int NB = QW / 32;
 constexpr int BN = 64;                   // keys per tile
 constexpr int K_TILE = BN * D;           // bf16 elements
 constexpr int V_TILE = D * BN;
-constexpr int LPT = 1024 / NTHREADS;     // 16-byte K (and V) pieces per thread per tile (register path)
-constexpr int DMA_PER_WAVE = 16 / NWAVES;  // 1 KiB DMA instructions per wave per tile, for K and for V
+#ifndef BEAM_PREFILL_NBUF
+#define BEAM_PREFILL_NBUF 2
+#endif
+constexpr int NBUF = BEAM_PREFILL_NBUF;  // LDS tile buffers; tile j+NBUF-1 is fetched while tile j is computed
 constexpr float kRescaleThreshold = 8.0f;
-static_assert(BM == kPrefillBlockQueries, "block size");
-static_assert(16 % NWAVES == 0 && 1024 % NTHREADS == 0, "tile split");
 
 // Key held by LDS row m of a K tile (bits 2 and 3 swapped; an involution).
 __device__ __forceinline__ int krow_key(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
@@ -128,22 +125,25 @@ __device__ __forceinline__ u32x4 load_v_piece(const KeySource& ks, int d, int s8
   return r;
 }
 
-// Gather a tile through registers (tiles touching the cached prefix).
-__device__ __forceinline__ void gather_tile(const KeySource& ks, int key0, int tid, u32x4 (&kr)[LPT],
-                                            u32x4 (&vr)[LPT]) {
+// Gather a tile through registers (tiles touching the cached prefix); NW
+// wavefronts share the 1024 16-byte pieces of K and of V^T.
+template <int NW>
+__device__ __forceinline__ void gather_tile(const KeySource& ks, int key0, int tid, u32x4 (&kr)[16 / NW],
+                                            u32x4 (&vr)[16 / NW]) {
 #pragma unroll
-  for (int r = 0; r < LPT; ++r) {
-    const int id = tid + NTHREADS * r;
+  for (int r = 0; r < 16 / NW; ++r) {
+    const int id = tid + 64 * NW * r;
     kr[r] = load_k_piece(ks, key0 + (id >> 4), id & 15);   // key row (id>>4), chunk (id&15)
     vr[r] = load_v_piece(ks, id >> 3, key0 + 8 * (id & 7));  // V^T row (id>>3), chunk (id&7)
   }
 }
 
-__device__ __forceinline__ void scatter_tile(uint16_t* sK, uint16_t* sV, int tid, const u32x4 (&kr)[LPT],
-                                             const u32x4 (&vr)[LPT]) {
+template <int NW>
+__device__ __forceinline__ void scatter_tile(uint16_t* sK, uint16_t* sV, int tid, const u32x4 (&kr)[16 / NW],
+                                             const u32x4 (&vr)[16 / NW]) {
 #pragma unroll
-  for (int r = 0; r < LPT; ++r) {
-    const int id = tid + NTHREADS * r;
+  for (int r = 0; r < 16 / NW; ++r) {
+    const int id = tid + 64 * NW * r;
     *reinterpret_cast<u32x4*>(sK + k_off(krow_key(id >> 4), id & 15)) = kr[r];
     *reinterpret_cast<u32x4*>(sV + v_off(id >> 3, id & 7)) = vr[r];
   }
@@ -153,23 +153,26 @@ __device__ __forceinline__ void scatter_tile(uint16_t* sK, uint16_t* sV, int tid
 // Element offsets (relative to the tile's first key in the workspace) of the
 // chunks this lane moves with each of its DMA instructions, and the LDS
 // offset of each instruction's 1 KiB.
+template <int NW>
 struct DmaPlan {
-  uint32_t k_src[DMA_PER_WAVE];
-  uint32_t v_src[DMA_PER_WAVE];
-  int k_lds[DMA_PER_WAVE];
-  int v_lds[DMA_PER_WAVE];
+  static constexpr int N = 16 / NW;  // 1 KiB instructions per wave per tile, for K and for V
+  uint32_t k_src[N];
+  uint32_t v_src[N];
+  int k_lds[N];
+  int v_lds[N];
 };
 
-__device__ __forceinline__ DmaPlan make_dma_plan(int w, int lane, int P) {
-  DmaPlan pl;
+template <int NW>
+__device__ __forceinline__ DmaPlan<NW> make_dma_plan(int w, int lane, int P) {
+  DmaPlan<NW> pl;
 #pragma unroll
-  for (int i = 0; i < DMA_PER_WAVE; ++i) {
-    const int kI = w * DMA_PER_WAVE + i;  // K rows 4kI .. 4kI+3
+  for (int i = 0; i < DmaPlan<NW>::N; ++i) {
+    const int kI = w * DmaPlan<NW>::N + i;  // K rows 4kI .. 4kI+3
     const int m = 4 * kI + (lane >> 4);
     const int c = (lane & 15) ^ (m & 7);
     pl.k_src[i] = (uint32_t)(krow_key(m) * D + 8 * c);
     pl.k_lds[i] = kI * 512;
-    const int vI = w * DMA_PER_WAVE + i;  // V^T rows 8vI .. 8vI+7
+    const int vI = w * DmaPlan<NW>::N + i;  // V^T rows 8vI .. 8vI+7
     const int d = 8 * vI + (lane >> 3);
     const int cv = (lane & 7) ^ (d & 7);
     pl.v_src[i] = (uint32_t)(d * P + 8 * cv);
@@ -178,21 +181,25 @@ __device__ __forceinline__ DmaPlan make_dma_plan(int w, int lane, int P) {
   return pl;
 }
 
-__device__ __forceinline__ void dma_tile(const KeySource& ks, const DmaPlan& pl, int key0, uint16_t* sK,
+template <int NW>
+__device__ __forceinline__ void dma_tile(const KeySource& ks, const DmaPlan<NW>& pl, int key0, uint16_t* sK,
                                          uint16_t* sV) {
   const uint16_t* kb = ks.kw + ((size_t)ks.g * ks.P + (key0 + ks.ws_off)) * D;
   const uint16_t* vb = ks.vw + (size_t)ks.g * D * ks.P + (key0 + ks.ws_off);
 #pragma unroll
-  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+  for (int i = 0; i < DmaPlan<NW>::N; ++i) {
     __builtin_amdgcn_global_load_lds(kb + pl.k_src[i], sK + pl.k_lds[i], 16, 0, 0);
     __builtin_amdgcn_global_load_lds(vb + pl.v_src[i], sV + pl.v_lds[i], 16, 0, 0);
   }
 }
 
 // ---------------------------------------------------------------- kernel
-template <int KIND>
-__global__ void __launch_bounds__(NTHREADS, (QW == 32 ? 8 / NWAVES : 1)) prefill_attn_kernel(PrefillParams p) {
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * (K_TILE + V_TILE)];
+template <int KIND, int NWAVES>
+__global__ void __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
+prefill_attn_kernel(PrefillParams p) {
+  constexpr int BM = NWAVES * QW;  // queries per block
+  static_assert(16 % NWAVES == 0, "tile split");
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[NBUF * (K_TILE + V_TILE)];
 
   const int hpg = p.H / p.G;
   int b = blockIdx.x;
@@ -240,7 +247,7 @@ __global__ void __launch_bounds__(NTHREADS, (QW == 32 ? 8 / NWAVES : 1)) prefill
   ks.kind = KIND;
   ks.window = W;
   ks.ring_base = (size_t)cseq * p.G + g;
-  const DmaPlan plan = make_dma_plan(w, lane, p.P);
+  const DmaPlan<NWAVES> plan = make_dma_plan<NWAVES>(w, lane, p.P);
 
   // Q' fragments (B operand of S^T = K Q'^T): lane holds query n of N-block nb,
   // coordinates 16kk + 8*half + 0..7.
@@ -275,16 +282,19 @@ __global__ void __launch_bounds__(NTHREADS, (QW == 32 ? 8 / NWAVES : 1)) prefill
     l_run[nb] = 0.f;
   }
 
-  // One KV tile of attention for this wave's queries (LDS buffer `buf`).
-  auto compute_tile = [&](int jt, int buf) {
-    const uint16_t* sK = smem + buf * (K_TILE + V_TILE);
-    const uint16_t* sV = sK + K_TILE;
-    const int ks0 = jt * BN;
-    const bool skip = !wave_active || ks0 > wq_hi || (local && ks0 + BN - 1 < wq_lo - (W - 1));
-    if (skip) return;
-    const bool need_mask = (ks0 + BN - 1 > wq_lo) || (local && ks0 < wq_hi - (W - 1));
-    // S^T: LDS rows 32mb + (lane&31) on M, queries 32nb + n on N.
-    f32x16 s[NB][2];
+  // ---- pieces of one 64-key tile of attention for this wave's queries ----
+  auto buf_k = [&](int j) -> const uint16_t* { return smem + ((j - j_lo) % NBUF) * (K_TILE + V_TILE); };
+  auto active = [&](int j) {
+    const int k0 = j * BN;
+    return wave_active && k0 <= wq_hi && !(local && k0 + BN - 1 < wq_lo - (W - 1));
+  };
+  auto needs_mask = [&](int j) {
+    const int k0 = j * BN;
+    return (k0 + BN - 1 > wq_lo) || (local && k0 < wq_hi - (W - 1));
+  };
+  // S^T = K Q'^T: LDS rows 32mb + (lane&31) on M, queries 32nb + n on N.
+  auto qk = [&](int j, f32x16 (&s)[NB][2]) {
+    const uint16_t* sK = buf_k(j);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -301,21 +311,22 @@ __global__ void __launch_bounds__(NTHREADS, (QW == 32 ? 8 / NWAVES : 1)) prefill
           s[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qf[nb][kk]), s[nb][mb], 0, 0, 0);
       }
     }
-    // Element i of block mb holds key ks0 + 32mb + 16(i>>3) + 8*half + (i&7).
-    if (need_mask) {
+  };
+  // Element i of block mb holds key 64j + 32mb + 16(i>>3) + 8*half + (i&7).
+  auto apply_mask = [&](int j, f32x16 (&s)[NB][2]) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int t = wq_lo + 32 * nb + n;
+    for (int nb = 0; nb < NB; ++nb) {
+      const int t = wq_lo + 32 * nb + n;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int sk = ks0 + 32 * mb + 16 * (i >> 3) + 8 * half + (i & 7);
-            if (!visible(KIND, W, t, sk)) s[nb][mb][i] = kNegInf;
-          }
-      }
+        for (int i = 0; i < 16; ++i) {
+          const int sk = j * BN + 32 * mb + 16 * (i >> 3) + 8 * half + (i & 7);
+          if (!visible(KIND, W, t, sk)) s[nb][mb][i] = kNegInf;
+        }
     }
-    float m_new[NB];
+  };
+  auto row_max = [&](const f32x16 (&s)[NB][2], float (&m_new)[NB]) {
     bool grow = false;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -328,21 +339,23 @@ __global__ void __launch_bounds__(NTHREADS, (QW == 32 ? 8 / NWAVES : 1)) prefill
       m_new[nb] = fmaxf(m_run[nb], mt);
       grow = grow || (m_new[nb] > m_run[nb] + kRescaleThreshold);
     }
-    if (__any(grow)) {
+    return grow;
+  };
+  auto rescale = [&](const float (&m_new)[NB]) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const float alpha = (m_new[nb] == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run[nb] - m_new[nb]);
-        m_run[nb] = m_new[nb];
-        l_run[nb] *= alpha;
+    for (int nb = 0; nb < NB; ++nb) {
+      const float alpha = (m_new[nb] == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run[nb] - m_new[nb]);
+      m_run[nb] = m_new[nb];
+      l_run[nb] *= alpha;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) o[nb][db][i] *= alpha;
-      }
+        for (int i = 0; i < 16; ++i) o[nb][db][i] *= alpha;
     }
-    // P^T operand of key block kb: elements 8(kb&1)..+7 of S block kb>>1, i.e.
-    // keys 16kb + 8*half + 0..7 in order.
-    u32x4 pf[NB][4];
+  };
+  // P^T operand of key block kb: elements 8(kb&1)..+7 of S block kb>>1, i.e.
+  // keys 16kb + 8*half + 0..7 in order.
+  auto softmax = [&](const f32x16 (&s)[NB][2], u32x4 (&pf)[NB][4]) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const float mu = (m_run[nb] == kNegInf) ? 0.f : m_run[nb];
@@ -358,7 +371,10 @@ __global__ void __launch_bounds__(NTHREADS, (QW == 32 ? 8 / NWAVES : 1)) prefill
                            pack_bf16x2(e[6], e[7])};
       }
     }
-    // O^T += V^T P^T: A operand = coordinates 32db + n, keys 16kb + 8*half + 0..7.
+  };
+  // O^T += V^T P^T: A operand = coordinates 32db + n, keys 16kb + 8*half + 0..7.
+  auto pv = [&](int j, const u32x4 (&pf)[NB][4]) {
+    const uint16_t* sV = buf_k(j) + K_TILE;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
@@ -370,46 +386,41 @@ __global__ void __launch_bounds__(NTHREADS, (QW == 32 ? 8 / NWAVES : 1)) prefill
       }
     }
   };
-
-  // First tile.
-  {
-    uint16_t* sK = smem;
-    if (j_lo >= j_ws) {
-      dma_tile(ks, plan, j_lo * BN, sK, sK + K_TILE);
+  // Fetch tile j into its buffer: DMA from the workspace, or a register gather
+  // for tiles that reach into the cached prefix (stored before returning).
+  auto fetch = [&](int j) {
+    uint16_t* sK = smem + ((j - j_lo) % NBUF) * (K_TILE + V_TILE);
+    if (j >= j_ws) {
+      dma_tile(ks, plan, j * BN, sK, sK + K_TILE);
     } else {
-      u32x4 kr[LPT], vr[LPT];
-      gather_tile(ks, j_lo * BN, tid, kr, vr);
-      scatter_tile(sK, sK + K_TILE, tid, kr, vr);
+      u32x4 kr[16 / NWAVES], vr[16 / NWAVES];
+      gather_tile<NWAVES>(ks, j * BN, tid, kr, vr);
+      scatter_tile<NWAVES>(sK, sK + K_TILE, tid, kr, vr);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
+  };
 
-  int jt = j_lo;
-  // Phase 1: tiles that reach into the cached prefix (chunked prefill only).
-  for (; jt <= j_hi && jt < j_ws; ++jt) {
-    const int buf = (jt - j_lo) & 1;
-    uint16_t* nK = smem + (buf ^ 1) * (K_TILE + V_TILE);
-    const bool has_next = jt < j_hi;
-    const bool next_dma = jt + 1 >= j_ws;
-    u32x4 kr[LPT], vr[LPT];
-    if (has_next) {
-      if (next_dma) dma_tile(ks, plan, (jt + 1) * BN, nK, nK + K_TILE);
-      else gather_tile(ks, (jt + 1) * BN, tid, kr, vr);
-    }
-    compute_tile(jt, buf);
-    if (has_next && !next_dma) scatter_tile(nK, nK + K_TILE, tid, kr, vr);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-  // Phase 2: tiles entirely inside the chunk (the hot loop).
-  for (; jt <= j_hi; ++jt) {
-    const int buf = (jt - j_lo) & 1;
-    if (jt < j_hi) {
-      uint16_t* nK = smem + (buf ^ 1) * (K_TILE + V_TILE);
-      dma_tile(ks, plan, (jt + 1) * BN, nK, nK + K_TILE);
-    }
-    compute_tile(jt, buf);
+  // One 64-key tile of attention for this wave's queries.
+  auto compute_tile = [&](int j) {
+    if (!active(j)) return;
+    f32x16 st[NB][2];
+    qk(j, st);
+    if (needs_mask(j)) apply_mask(j, st);
+    float m_new[NB];
+    if (__any(row_max(st, m_new))) rescale(m_new);
+    u32x4 pf[NB][4];
+    softmax(st, pf);
+    pv(j, pf);
+  };
+
+  // ---- tile loop: tile j+NBUF-1 streams in while tile j is computed ----
+#pragma unroll
+  for (int f = 0; f < NBUF - 1; ++f)
+    if (j_lo + f <= j_hi) fetch(j_lo + f);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int jt = j_lo; jt <= j_hi; ++jt) {
+    if (jt + NBUF - 1 <= j_hi) fetch(jt + NBUF - 1);
+    compute_tile(jt);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
@@ -448,9 +459,11 @@ __global__ void __launch_bounds__(NTHREADS, (QW == 32 ? 8 / NWAVES : 1)) prefill
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {
   const long long blocks = (long long)p.G * (p.H / p.G) * p.n_seqs * p.n_qtiles;
   if (p.kind == 0)
-    hipLaunchKernelGGL(prefill_attn_kernel<0>, dim3((unsigned)blocks), dim3(NTHREADS), 0, s, p);
+    hipLaunchKernelGGL((prefill_attn_kernel<0, kPrefillWavesLocal>), dim3((unsigned)blocks), dim3(64 * kPrefillWavesLocal),
+                       0, s, p);
   else
-    hipLaunchKernelGGL(prefill_attn_kernel<1>, dim3((unsigned)blocks), dim3(NTHREADS), 0, s, p);
+    hipLaunchKernelGGL((prefill_attn_kernel<1, kPrefillWavesGlobal>), dim3((unsigned)blocks),
+                       dim3(64 * kPrefillWavesGlobal), 0, s, p);
   return hipGetLastError();
 }
 

@@ -13,19 +13,25 @@
 namespace beam {
 
 // ----------------------------------------------------------------------------
-// Prefill prologue. One block per (sequence, 64-position tile). The tile covers
+// Prefill prologue. Grid (sequence, 64-position tile, part). The tile covers
 // absolute positions [64*T, 64*T + 64) with T = (start >> 6) + blockIdx.y.
-// Real chunk tokens get Q' (into [n_tok][H][D]), K_hat and V^T (into the
-// position-aligned workspace); every other position of the tile gets zero K_hat
-// and V^T so that attention tiles can read whole 64-key tiles.
+// Part 0 writes K_hat and V^T of the tile into the position-aligned workspace
+// (zeros for positions outside the chunk, so attention can read whole 64-key
+// tiles); part z >= 1 writes Q' for query heads [8(z-1), 8z) of the chunk's
+// tokens into [n_tok][H][D].
 // ----------------------------------------------------------------------------
+constexpr int kQHeadsPerBlock = 8;
+
 __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p) {
   const int seq = blockIdx.x;
+  const int part = blockIdx.z;
   const int start = p.start_pos[seq];
   const int cu0 = p.cu[seq];
   const int len = p.cu[seq + 1] - cu0;
   const int tile_pos0 = ((start >> 6) + (int)blockIdx.y) * 64;
   if (tile_pos0 >= start + len) return;
+  const int h_lo = (part - 1) * kQHeadsPerBlock;
+  if (part > 0 && h_lo >= p.H) return;
   const int region = ws_region_base(cu0, seq);
   const int ws0 = region + tile_pos0 - (start & ~63);  // workspace index of tile_pos0
 
@@ -38,53 +44,55 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
   if (local) {
     for (int e = tid; e < 64 * 64; e += 256) {
       int r = e >> 6, i = e & 63;
-      float c, s;
-      rope_cs(tile_pos0 + r, i, p.rope_theta, &c, &s);
+      float c, sn;
+      rope_cs(tile_pos0 + r, i, p.rope_theta, &c, &sn);
       s_cos[r][i] = c;
-      s_sin[r][i] = s;
+      s_sin[r][i] = sn;
     }
     __syncthreads();
   }
 
   const int grp = tid >> 4;  // 16 groups of 16 lanes
   const int j = tid & 15;    // lane within group: coords [4j,4j+4) and [64+4j, 64+4j+4)
-  const u32x2* qw = reinterpret_cast<const u32x2*>(p.q_norm_w);
-  const u32x2* kwgt = reinterpret_cast<const u32x2*>(p.k_norm_w);
-  const u32x2 wq_lo = qw[j], wq_hi = qw[16 + j];
-  const u32x2 wk_lo = kwgt[j], wk_hi = kwgt[16 + j];
-  const float qbase = kLog2e / sqrtf((float)D);
 
-  // Q: 64 positions x H heads, one (position, head) pair per 16-lane group.
-  for (int pr = grp; pr < 64 * p.H; pr += 16) {
-    int r = pr / p.H, h = pr - r * p.H;
-    int t = tile_pos0 + r;
-    if (t < start || t >= start + len) continue;
-    size_t tok = (size_t)(cu0 + t - start);
-    const u32x2* src = reinterpret_cast<const u32x2*>(p.q_raw + (tok * p.H + h) * D);
-    float scale = local ? qbase : qbase * ssmax_scale(t, p.ssmax_base, p.ssmax_exp);
-    HeadFrag f = norm_rope_head(src[j], src[16 + j], wq_lo, wq_hi, p.rms_eps, local,
-                                local ? &s_cos[r][4 * j] : nullptr,
-                                local ? &s_sin[r][4 * j] : nullptr, scale);
-    u32x2* dst = reinterpret_cast<u32x2*>(p.qp + (tok * p.H + h) * D);
-    dst[j] = u32x2{f.lo[0], f.lo[1]};
-    dst[16 + j] = u32x2{f.hi[0], f.hi[1]};
+  if (part > 0) {
+    // Q: 64 positions x 8 heads, one (position, head) pair per 16-lane group.
+    const u32x2* qw = reinterpret_cast<const u32x2*>(p.q_norm_w);
+    const u32x2 wq_lo = qw[j], wq_hi = qw[16 + j];
+    const float qbase = kLog2e / sqrtf((float)D);
+    const int nh = min(kQHeadsPerBlock, p.H - h_lo);
+    for (int pr = grp; pr < 64 * nh; pr += 16) {
+      const int r = pr / nh, h = h_lo + (pr - r * nh);
+      const int t = tile_pos0 + r;
+      if (t < start || t >= start + len) continue;
+      const size_t tok = (size_t)(cu0 + t - start);
+      const u32x2* src = reinterpret_cast<const u32x2*>(p.q_raw + (tok * p.H + h) * D);
+      const float scale = local ? qbase : qbase * ssmax_scale(t, p.ssmax_base, p.ssmax_exp);
+      HeadFrag f = norm_rope_head(src[j], src[16 + j], wq_lo, wq_hi, p.rms_eps, local,
+                                  local ? &s_cos[r][4 * j] : nullptr, local ? &s_sin[r][4 * j] : nullptr, scale);
+      u32x2* dst = reinterpret_cast<u32x2*>(p.qp + (tok * p.H + h) * D);
+      dst[j] = u32x2{f.lo[0], f.lo[1]};
+      dst[16 + j] = u32x2{f.hi[0], f.hi[1]};
+    }
+    return;
   }
 
   // K: 64 positions x G heads into K_hat workspace [G][P][D].
+  const u32x2* kwgt = reinterpret_cast<const u32x2*>(p.k_norm_w);
+  const u32x2 wk_lo = kwgt[j], wk_hi = kwgt[16 + j];
   for (int pr = grp; pr < 64 * p.G; pr += 16) {
-    int r = pr / p.G, g = pr - r * p.G;
-    int t = tile_pos0 + r;
+    const int r = pr / p.G, g = pr - r * p.G;
+    const int t = tile_pos0 + r;
     u32x2* dst = reinterpret_cast<u32x2*>(p.kw + ((size_t)g * p.P + ws0 + r) * D);
     if (t < start || t >= start + len) {
       dst[j] = u32x2{0u, 0u};
       dst[16 + j] = u32x2{0u, 0u};
       continue;
     }
-    size_t tok = (size_t)(cu0 + t - start);
+    const size_t tok = (size_t)(cu0 + t - start);
     const u32x2* src = reinterpret_cast<const u32x2*>(p.k_raw + (tok * p.G + g) * D);
     HeadFrag f = norm_rope_head(src[j], src[16 + j], wk_lo, wk_hi, p.rms_eps, local,
-                                local ? &s_cos[r][4 * j] : nullptr,
-                                local ? &s_sin[r][4 * j] : nullptr, 1.0f);
+                                local ? &s_cos[r][4 * j] : nullptr, local ? &s_sin[r][4 * j] : nullptr, 1.0f);
     dst[j] = u32x2{f.lo[0], f.lo[1]};
     dst[16 + j] = u32x2{f.hi[0], f.hi[1]};
   }
@@ -94,11 +102,11 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
   for (int g = 0; g < p.G; ++g) {
     __syncthreads();
     for (int e = tid; e < 64 * 16; e += 256) {  // 16-byte pieces: row r, coords 8c..8c+7
-      int r = e >> 4, c = e & 15;
-      int t = tile_pos0 + r;
+      const int r = e >> 4, c = e & 15;
+      const int t = tile_pos0 + r;
       u32x4 v = {0u, 0u, 0u, 0u};
       if (t >= start && t < start + len) {
-        size_t tok = (size_t)(cu0 + t - start);
+        const size_t tok = (size_t)(cu0 + t - start);
         v = *reinterpret_cast<const u32x4*>(p.v_raw + (tok * p.G + g) * D + 8 * c);
       }
 #pragma unroll
@@ -109,7 +117,7 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
     }
     __syncthreads();
     for (int e = tid; e < D * 8; e += 256) {  // row d of V^T, keys 8c..8c+7
-      int d = e >> 3, c = e & 7;
+      const int d = e >> 3, c = e & 7;
       u32x4 o;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
@@ -229,7 +237,8 @@ __global__ void visibility_kernel(int kind, int window, int t0, int n_q, int s0,
 namespace beam {
 
 hipError_t launch_prefill_prologue(const PrologueParams& p, int n_seqs, int n_tiles, hipStream_t s) {
-  hipLaunchKernelGGL(prefill_prologue_kernel, dim3(n_seqs, n_tiles), dim3(256), 0, s, p);
+  const int parts = 1 + (p.H + kQHeadsPerBlock - 1) / kQHeadsPerBlock;
+  hipLaunchKernelGGL(prefill_prologue_kernel, dim3(n_seqs, n_tiles, parts), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
