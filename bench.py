@@ -38,6 +38,40 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+_CSRC = os.path.join(ROOT, "global_attention_amd", "csrc")
+_KERNEL_SOURCES = {
+    "prefill_attn_kernel<1, 8>": "prefill.hip",
+    "prefill_attn_kernel<0, 4>": "prefill.hip",
+    "decode_split_kernel<1>": "decode.hip",
+    "decode_split_kernel<0>": "decode.hip",
+    "prefill_prologue_kernel": "prologue.hip",
+}
+
+
+def source_digest(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in (_KERNEL_SOURCES[kernel], "beam_device.h", "beam_kernels.h"):
+        with open(os.path.join(_CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE summary,
+    or None when the kernel's sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_pmc.md")
+    if not os.path.exists(path):
+        return None
+    digest = source_digest(kernel)
+    with open(path) as fh:
+        for line in fh:
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            if len(cells) == 6 and cells[0] == kernel and cells[1] == digest:
+                return int(cells[4])
+    return None
+
+
 def pairs_global(T: int) -> int:
     return T * (T + 1) // 2
 
@@ -273,7 +307,8 @@ def main():
         achieved = g_flops / (g_ms / 1e3) / 1e12
         rec["roofline"] = {"kernel": "prefill_attn_kernel<1, 8> (global layer)", "bound": "mfma",
                            "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                           "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                           "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                           "traffic": recorded_traffic("prefill_attn_kernel<1, 8>"),
                            "avg_launch_ms": round(g_ms, 4), "flop_per_launch": g_flops}
         l_flops = FLOP_PER_PAIR * pairs_local(T)
         rec["prefill_layers"] = {
@@ -292,7 +327,8 @@ def main():
             "global_bytes": g["bytes"], "global_ms_per_call": round(g["ms_per_call"], 4),
             "roofline": {"kernel": "decode_split_kernel<1>", "bound": "hbm", "achieved": round(g["gbs_split"], 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(g["gbs_split"] / PEAK_HBM_GBS, 4),
-                         "traffic": None, "avg_launch_ms": round(g["split_ms"], 4)},
+                         "traffic": recorded_traffic("decode_split_kernel<1>"),
+                         "avg_launch_ms": round(g["split_ms"], 4), "bytes_per_launch": g["bytes"]},
             "local": {"bytes": dres["local"]["bytes"], "ms_per_call": round(dres["local"]["ms_per_call"], 4),
                       "gbs_call": round(dres["local"]["gbs_call"], 1),
                       "note": "134 MB of rings can stay resident in the 256 MB MALL between calls"},
