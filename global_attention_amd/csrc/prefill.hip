@@ -23,7 +23,9 @@
 //   V^T: 128 rows (coordinates) x 128 B (64 keys, natural order).
 // Both XOR-swizzle their 16-byte chunks with the low 3 bits of the row, which
 // keeps the b128 operand reads free of bank conflicts without padding.
-// Tiles that reach into the cached prefix are gathered through registers.
+// Tiles that reach into the cached prefix are also copied by DMA, with each
+// lane addressing its chunk in the paged cache or ring; only a tile in which an
+// 8-key V^T chunk straddles the chunk start is gathered through registers.
 //
 // Softmax runs in base 2 (Q' carries log2 e / sqrt d and, on global layers,
 // a(t+1)); the running max only moves when it grows by more than 8 (exact:
@@ -190,6 +192,47 @@ __device__ __forceinline__ void dma_tile(const KeySource& ks, const DmaPlan<NW>&
   for (int i = 0; i < DmaPlan<NW>::N; ++i) {
     __builtin_amdgcn_global_load_lds(kb + pl.k_src[i], sK + pl.k_lds[i], 16, 0, 0);
     __builtin_amdgcn_global_load_lds(vb + pl.v_src[i], sV + pl.v_lds[i], 16, 0, 0);
+  }
+}
+
+// DMA of a tile that lies (partly) in the cached prefix: every lane computes
+// the address of its 16-byte chunk from the key's location (cache page / ring
+// slot below `start`, workspace from `start` on). Requires that no 8-key V^T
+// chunk straddles `start` and that the cache row is valid.
+template <int NW>
+__device__ __forceinline__ void dma_tile_prefix(const KeySource& ks, int w, int lane, int key0, uint16_t* sK,
+                                                uint16_t* sV) {
+#pragma unroll
+  for (int i = 0; i < DmaPlan<NW>::N; ++i) {
+    const int kI = w * DmaPlan<NW>::N + i;
+    const int m = 4 * kI + (lane >> 4);
+    const int c = (lane & 15) ^ (m & 7);
+    const int s = key0 + krow_key(m);
+    const uint16_t* ksrc;
+    if (s >= ks.start) {
+      ksrc = ks.kw + ((size_t)ks.g * ks.P + (s + ks.ws_off)) * D;
+    } else if (ks.kind == 1) {
+      const int page = ks.bt_row[s >> 4];
+      ksrc = ks.ck + (((size_t)page * ks.G + ks.g) * 16 + (s & 15)) * D;
+    } else {
+      ksrc = ks.ck + (ks.ring_base * ks.window + (s % ks.window)) * D;
+    }
+    __builtin_amdgcn_global_load_lds(ksrc + 8 * c, sK + kI * 512, 16, 0, 0);
+
+    const int vI = w * DmaPlan<NW>::N + i;
+    const int d = 8 * vI + (lane >> 3);
+    const int cv = (lane & 7) ^ (d & 7);
+    const int s8 = key0 + 8 * cv;
+    const uint16_t* vsrc;
+    if (s8 >= ks.start) {
+      vsrc = ks.vw + ((size_t)ks.g * D + d) * ks.P + (s8 + ks.ws_off);
+    } else if (ks.kind == 1) {
+      const int page = ks.bt_row[s8 >> 4];
+      vsrc = ks.cv + (((size_t)page * ks.G + ks.g) * D + d) * 16 + (s8 & 15);
+    } else {
+      vsrc = ks.cv + (ks.ring_base * D + d) * ks.window + (s8 % ks.window);
+    }
+    __builtin_amdgcn_global_load_lds(vsrc, sV + vI * 512, 16, 0, 0);
   }
 }
 
@@ -392,6 +435,8 @@ prefill_attn_kernel(PrefillParams p) {
     uint16_t* sK = smem + ((j - j_lo) % NBUF) * (K_TILE + V_TILE);
     if (j >= j_ws) {
       dma_tile(ks, plan, j * BN, sK, sK + K_TILE);
+    } else if (ks.cache_ok && ((start & 7) == 0 || j * BN + BN <= start)) {
+      dma_tile_prefix<NWAVES>(ks, w, lane, j * BN, sK, sK + K_TILE);
     } else {
       u32x4 kr[16 / NWAVES], vr[16 / NWAVES];
       gather_tile<NWAVES>(ks, j * BN, tid, kr, vr);
