@@ -218,7 +218,7 @@ beam_status beam_attn_prefill_stages(uint32_t stages, const beam_attn_config* cf
   const PrefillWs ws = prefill_ws_layout(cfg, n_tok, n_seqs);
   if (ws_bytes < ws.total)
     return fail(BEAM_E_WORKSPACE, "prefill workspace needs " + std::to_string(ws.total) + " bytes");
-  if (ws.P > 0x7fffffff) return fail(BEAM_E_RANGE, "too many tokens");
+  if (ws.P * beam::D > 0x7fffffff) return fail(BEAM_E_RANGE, "too many tokens in one call (workspace positions x 128 must stay below 2^31)");
   hipStream_t s = (hipStream_t)stream;
   char* wsb = static_cast<char*>(workspace);
   uint16_t* qp = reinterpret_cast<uint16_t*>(wsb + ws.qp);

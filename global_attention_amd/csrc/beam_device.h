@@ -35,6 +35,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// acc + lo + hi of a packed bf16 pair (v_dot2c_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float sum_bf16x2(uint32_t pair, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), __builtin_bit_cast(bf16x2, 0x3f803f80u), acc,
+                                         false);
+}
+
 // Visibility of key position s to query position t: causal, plus the window on
 // local layers (window counts the current token, so window-1 earlier ones).
 __device__ __forceinline__ bool visible(int kind, int window, int t, int s) {

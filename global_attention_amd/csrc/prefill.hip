@@ -28,9 +28,14 @@
 // 8-key V^T chunk straddles the chunk start is gathered through registers.
 //
 // Softmax runs in base 2 (Q' carries log2 e / sqrt d and, on global layers,
-// a(t+1)); the running max only moves when it grows by more than 8 (exact:
-// the final normalisation uses the same reference). Local layers visit only
-// the key tiles that intersect the window.
+// a(t+1)). Each query keeps a reference m (its running max, moved only when
+// the max grows by more than 8; exact, since the final normalisation uses the
+// same reference). The S MFMA chain starts from -m instead of 0, so the scores
+// arrive already shifted and feed exp2 directly; the row sum adds the bf16 P
+// values that the PV product uses, two at a time (v_dot2c_f32_bf16 against
+// ones). Local layers visit only the key tiles that intersect the window.
+#include <type_traits>
+
 #include "beam_device.h"
 #include "beam_kernels.h"
 
@@ -41,10 +46,7 @@ constexpr int NB = QW / 32;
 constexpr int BN = 64;                   // keys per tile
 constexpr int K_TILE = BN * D;           // bf16 elements
 constexpr int V_TILE = D * BN;
-#ifndef BEAM_PREFILL_NBUF
-#define BEAM_PREFILL_NBUF 2
-#endif
-constexpr int NBUF = BEAM_PREFILL_NBUF;  // LDS tile buffers; tile j+NBUF-1 is fetched while tile j is computed
+constexpr int NBUF = 2;                  // LDS tile buffers; tile j+1 is fetched while tile j is computed
 constexpr float kRescaleThreshold = 8.0f;
 
 // Key held by LDS row m of a K tile (bits 2 and 3 swapped; an involution).
@@ -64,61 +66,52 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Where the keys of one (sequence, KV head) live. All pointers are
+// wave-uniform; per-lane offsets from them fit in 32 bits (the host keeps
+// P * D below 2^31), except the page term of the paged cache.
 struct KeySource {
-  const uint16_t* kw;
-  const uint16_t* vw;
-  const uint16_t* ck;
-  const uint16_t* cv;
+  const uint16_t* kw;     // workspace K rows of head g: row s + ws_off
+  const uint16_t* vw;     // workspace V^T of head g: [d][s + ws_off], row stride P
+  const uint16_t* ck;     // cache K: global page p at ck + p * page_stride; local ring rows
+  const uint16_t* cv;     // cache V^T: global as ck; local ring [d][slot]
   const int32_t* bt_row;  // block-table row of the cache sequence (global)
+  size_t page_stride;     // elements per page of the paged cache (all KV heads)
   int start;              // first chunk position; keys below it come from the cache
   int cache_ok;           // the cache sequence index is in range
   int ws_off;             // workspace index = s + ws_off
-  int g, G, P, kind, window;
-  size_t ring_base;       // (cseq*G + g) for the local ring
+  int P, kind, window;
 };
 
 // ---------------------------------------------------------------- register path
 // 16 bytes of K row s, coordinates [8c, 8c+8), from wherever key s lives.
+// Address of K row s (any position below the chunk end; cache rows need
+// cache_ok) and of V^T element (d, s).
+__device__ __forceinline__ const uint16_t* k_row_src(const KeySource& ks, int s) {
+  if (s >= ks.start) return ks.kw + (uint32_t)((s + ks.ws_off) * D);
+  if (ks.kind == 1) return ks.ck + ks.bt_row[s >> 4] * ks.page_stride + (uint32_t)((s & 15) * D);
+  return ks.ck + (uint32_t)((s % ks.window) * D);
+}
+__device__ __forceinline__ const uint16_t* v_elem_src(const KeySource& ks, int d, int s) {
+  if (s >= ks.start) return ks.vw + (uint32_t)(d * ks.P + s + ks.ws_off);
+  if (ks.kind == 1) return ks.cv + ks.bt_row[s >> 4] * ks.page_stride + (uint32_t)(d * 16 + (s & 15));
+  return ks.cv + (uint32_t)(d * ks.window + s % ks.window);
+}
+
 __device__ __forceinline__ u32x4 load_k_piece(const KeySource& ks, int s, int c) {
-  const uint16_t* src;
-  if (s >= ks.start) {
-    src = ks.kw + ((size_t)ks.g * ks.P + (s + ks.ws_off)) * D;
-  } else if (!ks.cache_ok) {
-    return u32x4{0u, 0u, 0u, 0u};
-  } else if (ks.kind == 1) {
-    int page = ks.bt_row[s >> 4];
-    src = ks.ck + (((size_t)page * ks.G + ks.g) * 16 + (s & 15)) * D;
-  } else {
-    src = ks.ck + (ks.ring_base * ks.window + (s % ks.window)) * D;
-  }
-  return *reinterpret_cast<const u32x4*>(src + 8 * c);
+  if (s < ks.start && !ks.cache_ok) return u32x4{0u, 0u, 0u, 0u};
+  return *reinterpret_cast<const u32x4*>(k_row_src(ks, s) + 8 * c);
 }
 
 __device__ __forceinline__ uint16_t load_v_elem(const KeySource& ks, int d, int s) {
-  if (s >= ks.start) return ks.vw[((size_t)ks.g * D + d) * ks.P + (s + ks.ws_off)];
-  if (!ks.cache_ok) return 0;
-  if (ks.kind == 1) {
-    int page = ks.bt_row[s >> 4];
-    return ks.cv[(((size_t)page * ks.G + ks.g) * D + d) * 16 + (s & 15)];
-  }
-  return ks.cv[(ks.ring_base * D + d) * ks.window + (s % ks.window)];
+  if (s < ks.start && !ks.cache_ok) return 0;
+  return *v_elem_src(ks, d, s);
 }
 
 // 8 consecutive V^T values: row d, keys [s8, s8+8) (s8 a multiple of 8).
 __device__ __forceinline__ u32x4 load_v_piece(const KeySource& ks, int d, int s8) {
-  if (s8 >= ks.start) {
-    return *reinterpret_cast<const u32x4*>(ks.vw + ((size_t)ks.g * D + d) * ks.P + (s8 + ks.ws_off));
-  }
-  if (s8 + 8 <= ks.start) {
-    if (!ks.cache_ok) return u32x4{0u, 0u, 0u, 0u};
-    const uint16_t* src;
-    if (ks.kind == 1) {
-      int page = ks.bt_row[s8 >> 4];
-      src = ks.cv + (((size_t)page * ks.G + ks.g) * D + d) * 16 + (s8 & 15);
-    } else {
-      src = ks.cv + (ks.ring_base * D + d) * ks.window + (s8 % ks.window);
-    }
-    return *reinterpret_cast<const u32x4*>(src);
+  if (s8 >= ks.start || s8 + 8 <= ks.start) {
+    if (s8 < ks.start && !ks.cache_ok) return u32x4{0u, 0u, 0u, 0u};
+    return *reinterpret_cast<const u32x4*>(v_elem_src(ks, d, s8));
   }
   u32x4 r;
 #pragma unroll
@@ -186,8 +179,8 @@ __device__ __forceinline__ DmaPlan<NW> make_dma_plan(int w, int lane, int P) {
 template <int NW>
 __device__ __forceinline__ void dma_tile(const KeySource& ks, const DmaPlan<NW>& pl, int key0, uint16_t* sK,
                                          uint16_t* sV) {
-  const uint16_t* kb = ks.kw + ((size_t)ks.g * ks.P + (key0 + ks.ws_off)) * D;
-  const uint16_t* vb = ks.vw + (size_t)ks.g * D * ks.P + (key0 + ks.ws_off);
+  const uint16_t* kb = ks.kw + (uint32_t)((key0 + ks.ws_off) * D);
+  const uint16_t* vb = ks.vw + (uint32_t)(key0 + ks.ws_off);
 #pragma unroll
   for (int i = 0; i < DmaPlan<NW>::N; ++i) {
     __builtin_amdgcn_global_load_lds(kb + pl.k_src[i], sK + pl.k_lds[i], 16, 0, 0);
@@ -207,32 +200,12 @@ __device__ __forceinline__ void dma_tile_prefix(const KeySource& ks, int w, int 
     const int kI = w * DmaPlan<NW>::N + i;
     const int m = 4 * kI + (lane >> 4);
     const int c = (lane & 15) ^ (m & 7);
-    const int s = key0 + krow_key(m);
-    const uint16_t* ksrc;
-    if (s >= ks.start) {
-      ksrc = ks.kw + ((size_t)ks.g * ks.P + (s + ks.ws_off)) * D;
-    } else if (ks.kind == 1) {
-      const int page = ks.bt_row[s >> 4];
-      ksrc = ks.ck + (((size_t)page * ks.G + ks.g) * 16 + (s & 15)) * D;
-    } else {
-      ksrc = ks.ck + (ks.ring_base * ks.window + (s % ks.window)) * D;
-    }
-    __builtin_amdgcn_global_load_lds(ksrc + 8 * c, sK + kI * 512, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(k_row_src(ks, key0 + krow_key(m)) + 8 * c, sK + kI * 512, 16, 0, 0);
 
     const int vI = w * DmaPlan<NW>::N + i;
     const int d = 8 * vI + (lane >> 3);
     const int cv = (lane & 7) ^ (d & 7);
-    const int s8 = key0 + 8 * cv;
-    const uint16_t* vsrc;
-    if (s8 >= ks.start) {
-      vsrc = ks.vw + ((size_t)ks.g * D + d) * ks.P + (s8 + ks.ws_off);
-    } else if (ks.kind == 1) {
-      const int page = ks.bt_row[s8 >> 4];
-      vsrc = ks.cv + (((size_t)page * ks.G + ks.g) * D + d) * 16 + (s8 & 15);
-    } else {
-      vsrc = ks.cv + (ks.ring_base * D + d) * ks.window + (s8 % ks.window);
-    }
-    __builtin_amdgcn_global_load_lds(vsrc, sV + vI * 512, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(v_elem_src(ks, d, key0 + 8 * cv), sV + vI * 512, 16, 0, 0);
   }
 }
 
@@ -275,21 +248,26 @@ prefill_attn_kernel(PrefillParams p) {
   const bool wave_active = wq_lo <= qlast;
 
   KeySource ks;
-  ks.kw = p.kw;
-  ks.vw = p.vw;
-  ks.ck = p.ck;
-  ks.cv = p.cv;
+  ks.kw = p.kw + (size_t)g * p.P * D;
+  ks.vw = p.vw + (size_t)g * D * p.P;
+  if (KIND == 1) {
+    ks.ck = p.ck + (size_t)g * 16 * D;
+    ks.cv = p.cv + (size_t)g * D * 16;
+    ks.page_stride = (size_t)p.G * 16 * D;
+  } else {
+    const size_t ring = (size_t)cseq * p.G + g;  // (cache sequence, head) ring
+    ks.ck = p.ck + ring * W * D;
+    ks.cv = p.cv + ring * D * W;
+    ks.page_stride = 0;
+  }
   ks.bt_row = KIND == 1 ? p.bt + (size_t)cseq * p.max_pages : nullptr;
   ks.start = start;
   // The cached prefix must fit the cache sequence's block-table row (global).
   ks.cache_ok = cseq >= 0 && cseq < p.n_cache_seqs && (KIND == 0 || ((start + 15) >> 4) <= p.max_pages);
   ks.ws_off = ws_region_base(cu0, seq) - (start & ~63);
-  ks.g = g;
-  ks.G = p.G;
   ks.P = p.P;
   ks.kind = KIND;
   ks.window = W;
-  ks.ring_base = (size_t)cseq * p.G + g;
   const DmaPlan<NWAVES> plan = make_dma_plan<NWAVES>(w, lane, p.P);
 
   // Q' fragments (B operand of S^T = K Q'^T): lane holds query n of N-block nb,
@@ -318,15 +296,32 @@ prefill_attn_kernel(PrefillParams p) {
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[nb][db][i] = 0.f;
+  // m_run: reference of the query (kNegInf until a key is visible); sref holds
+  // -m_run (0 while m_run is kNegInf) splatted, the accumulator input of S.
   float m_run[NB], l_run[NB];
+  f32x16 sref[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     m_run[nb] = kNegInf;
     l_run[nb] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sref[nb][i] = 0.f;
+  }
+  // Loop-invariant LDS element offsets of this lane's operand chunks: K row n,
+  // chunk (2q + half) ^ (n & 7) for q = 0..3 (chunks 8..15 add 64 elements and
+  // M-block 1 adds 32 rows); V^T row n, chunk (2kb + half) ^ (n & 7) (row
+  // block db adds 32 rows).
+  int koff[4], voff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    koff[q] = k_off(n, 2 * q + half);
+    voff[q] = v_off(n, 2 * q + half);
   }
 
   // ---- pieces of one 64-key tile of attention for this wave's queries ----
-  auto buf_k = [&](int j) -> const uint16_t* { return smem + ((j - j_lo) % NBUF) * (K_TILE + V_TILE); };
+  // Tile jt uses LDS buffer (jt - j_lo) & 1; the loop is unrolled by two so
+  // that the buffer offset is a compile-time constant of every LDS read.
+  auto buf = [&](auto B) -> uint16_t* { return smem + decltype(B)::value * (K_TILE + V_TILE); };
   auto active = [&](int j) {
     const int k0 = j * BN;
     return wave_active && k0 <= wq_hi && !(local && k0 + BN - 1 < wq_lo - (W - 1));
@@ -335,23 +330,19 @@ prefill_attn_kernel(PrefillParams p) {
     const int k0 = j * BN;
     return (k0 + BN - 1 > wq_lo) || (local && k0 < wq_hi - (W - 1));
   };
-  // S^T = K Q'^T: LDS rows 32mb + (lane&31) on M, queries 32nb + n on N.
-  auto qk = [&](int j, f32x16 (&s)[NB][2]) {
-    const uint16_t* sK = buf_k(j);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[nb][mb][i] = 0.f;
+  // S^T - m = K Q'^T - m: LDS rows 32mb + (lane&31) on M, queries 32nb + n on
+  // N; the chain starts from sref = -m.
+  auto qk = [&](auto B, f32x16 (&s)[NB][2]) {
+    const uint16_t* sK = buf(B);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(sK + k_off(32 * mb + n, 2 * kk + half));
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sK + koff[kk & 3] + 64 * (kk >> 2) + 32 * D * mb);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          s[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qf[nb][kk]), s[nb][mb], 0, 0, 0);
+          s[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qf[nb][kk]),
+                                                             kk == 0 ? sref[nb] : s[nb][mb], 0, 0, 0);
       }
     }
   };
@@ -369,7 +360,10 @@ prefill_attn_kernel(PrefillParams p) {
         }
     }
   };
-  auto row_max = [&](const f32x16 (&s)[NB][2], float (&m_new)[NB]) {
+  // Shift of the reference this tile needs, per query: the tile max of the
+  // shifted scores when it exceeds the threshold (or is the first finite
+  // score of the query), else 0.
+  auto row_shift = [&](const f32x16 (&s)[NB][2], float (&delta)[NB], bool (&need)[NB]) {
     bool grow = false;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -379,21 +373,32 @@ prefill_attn_kernel(PrefillParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[nb][mb][i]);
       mt = max_halves(mt);
-      m_new[nb] = fmaxf(m_run[nb], mt);
-      grow = grow || (m_new[nb] > m_run[nb] + kRescaleThreshold);
+      need[nb] = (m_run[nb] == kNegInf) ? (mt != kNegInf) : (mt > kRescaleThreshold);
+      delta[nb] = need[nb] ? mt : 0.f;
+      grow = grow || need[nb];
     }
     return grow;
   };
-  auto rescale = [&](const float (&m_new)[NB]) {
+  // Move the reference up by delta: rescale O and l by 2^-delta (nothing to
+  // rescale while no key was visible) and shift this tile's scores.
+  auto rescale = [&](const float (&delta)[NB], const bool (&need)[NB], f32x16 (&s)[NB][2]) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const float alpha = (m_new[nb] == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run[nb] - m_new[nb]);
-      m_run[nb] = m_new[nb];
+      const bool first = m_run[nb] == kNegInf;
+      const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(-delta[nb]);
+      if (need[nb]) m_run[nb] = (first ? 0.f : m_run[nb]) + delta[nb];
+      const float r = m_run[nb] == kNegInf ? 0.f : -m_run[nb];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sref[nb][i] = r;
       l_run[nb] *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[nb][db][i] *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[nb][mb][i] -= delta[nb];
     }
   };
   // P^T operand of key block kb: elements 8(kb&1)..+7 of S block kb>>1, i.e.
@@ -401,28 +406,27 @@ prefill_attn_kernel(PrefillParams p) {
   auto softmax = [&](const f32x16 (&s)[NB][2], u32x4 (&pf)[NB][4]) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const float mu = (m_run[nb] == kNegInf) ? 0.f : m_run[nb];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         float e[8];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          e[jj] = __builtin_amdgcn_exp2f(s[nb][kb >> 1][8 * (kb & 1) + jj] - mu);
-          l_run[nb] += e[jj];
+        for (int jj = 0; jj < 8; ++jj) e[jj] = __builtin_amdgcn_exp2f(s[nb][kb >> 1][8 * (kb & 1) + jj]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          pf[nb][kb][c] = pack_bf16x2(e[2 * c], e[2 * c + 1]);
+          l_run[nb] = sum_bf16x2(pf[nb][kb][c], l_run[nb]);
         }
-        pf[nb][kb] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
-                           pack_bf16x2(e[6], e[7])};
       }
     }
   };
   // O^T += V^T P^T: A operand = coordinates 32db + n, keys 16kb + 8*half + 0..7.
-  auto pv = [&](int j, const u32x4 (&pf)[NB][4]) {
-    const uint16_t* sV = buf_k(j) + K_TILE;
+  auto pv = [&](auto B, const u32x4 (&pf)[NB][4]) {
+    const uint16_t* sV = buf(B) + K_TILE;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(sV + v_off(32 * db + n, 2 * kb + half));
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sV + voff[kb] + 32 * BN * db);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
           o[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pf[nb][kb]), o[nb][db], 0, 0, 0);
@@ -431,8 +435,8 @@ prefill_attn_kernel(PrefillParams p) {
   };
   // Fetch tile j into its buffer: DMA from the workspace, or a register gather
   // for tiles that reach into the cached prefix (stored before returning).
-  auto fetch = [&](int j) {
-    uint16_t* sK = smem + ((j - j_lo) % NBUF) * (K_TILE + V_TILE);
+  auto fetch = [&](int j, auto B) {
+    uint16_t* sK = buf(B);
     if (j >= j_ws) {
       dma_tile(ks, plan, j * BN, sK, sK + K_TILE);
     } else if (ks.cache_ok && ((start & 7) == 0 || j * BN + BN <= start)) {
@@ -445,29 +449,34 @@ prefill_attn_kernel(PrefillParams p) {
   };
 
   // One 64-key tile of attention for this wave's queries.
-  auto compute_tile = [&](int j) {
+  auto compute_tile = [&](int j, auto B) {
     if (!active(j)) return;
     f32x16 st[NB][2];
-    qk(j, st);
+    qk(B, st);
     if (needs_mask(j)) apply_mask(j, st);
-    float m_new[NB];
-    if (__any(row_max(st, m_new))) rescale(m_new);
+    float delta[NB];
+    bool need[NB];
+    if (__any(row_shift(st, delta, need))) rescale(delta, need, st);
     u32x4 pf[NB][4];
     softmax(st, pf);
-    pv(j, pf);
+    pv(B, pf);
   };
-
-  // ---- tile loop: tile j+NBUF-1 streams in while tile j is computed ----
-#pragma unroll
-  for (int f = 0; f < NBUF - 1; ++f)
-    if (j_lo + f <= j_hi) fetch(j_lo + f);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int jt = j_lo; jt <= j_hi; ++jt) {
-    if (jt + NBUF - 1 <= j_hi) fetch(jt + NBUF - 1);
-    compute_tile(jt);
+  // Tile jt (in buffer B) is computed while tile jt+1 streams into the other.
+  auto step = [&](int jt, auto B) {
+    if (jt + 1 <= j_hi) fetch(jt + 1, std::integral_constant<int, 1 - decltype(B)::value>{});
+    compute_tile(jt, B);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+
+  // ---- tile loop ----
+  if (j_lo <= j_hi) fetch(j_lo, std::integral_constant<int, 0>{});
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int jt = j_lo; jt <= j_hi; jt += 2) {
+    step(jt, std::integral_constant<int, 0>{});
+    if (jt + 1 > j_hi) break;
+    step(jt + 1, std::integral_constant<int, 1>{});
   }
 
   // Epilogue: normalise, gate, write bf16. Lane holds query n of each N-block
