@@ -46,7 +46,22 @@ constexpr int NB = QW / 32;
 constexpr int BN = 64;                   // keys per tile
 constexpr int K_TILE = BN * D;           // bf16 elements
 constexpr int V_TILE = D * BN;
-constexpr int NBUF = 2;                  // LDS tile buffers; tile j+1 is fetched while tile j is computed
+// Tiles are staged in LDS TPS at a time (one barrier per stage); two stages
+// are resident, so stage s+1 streams in while stage s is computed. Global
+// layers run one 8-wave block per CU and stage two tiles (128 KiB of LDS);
+// local layers run two 4-wave blocks per CU and stage one (64 KiB each).
+template <int KIND>
+constexpr int tiles_per_stage() { return KIND == 1 ? 2 : 1; }
+
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), in order.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 constexpr float kRescaleThreshold = 8.0f;
 
 // Key held by LDS row m of a K tile (bits 2 and 3 swapped; an involution).
@@ -215,7 +230,9 @@ __global__ void __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_e
 prefill_attn_kernel(PrefillParams p) {
   constexpr int BM = NWAVES * QW;  // queries per block
   static_assert(16 % NWAVES == 0, "tile split");
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[NBUF * (K_TILE + V_TILE)];
+  constexpr int TPS = tiles_per_stage<KIND>();
+  constexpr int SLOTS = 2 * TPS;  // tile slots: two stages
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[SLOTS * (K_TILE + V_TILE)];
 
   const int hpg = p.H / p.G;
   int b = blockIdx.x;
@@ -319,14 +336,14 @@ prefill_attn_kernel(PrefillParams p) {
   }
 
   // ---- pieces of one 64-key tile of attention for this wave's queries ----
-  // Tile jt uses LDS buffer (jt - j_lo) & 1; the loop is unrolled by two so
-  // that the buffer offset is a compile-time constant of every LDS read.
+  // Tile jt uses LDS slot (jt - j_lo) % SLOTS; the loop is unrolled by SLOTS
+  // so that the slot offset is a compile-time constant of every LDS read.
   auto buf = [&](auto B) -> uint16_t* { return smem + decltype(B)::value * (K_TILE + V_TILE); };
-  auto active = [&](int j) {
+  auto active = [&](int j) __attribute__((always_inline)) {
     const int k0 = j * BN;
     return wave_active && k0 <= wq_hi && !(local && k0 + BN - 1 < wq_lo - (W - 1));
   };
-  auto needs_mask = [&](int j) {
+  auto needs_mask = [&](int j) __attribute__((always_inline)) {
     const int k0 = j * BN;
     return (k0 + BN - 1 > wq_lo) || (local && k0 < wq_hi - (W - 1));
   };
@@ -435,7 +452,7 @@ prefill_attn_kernel(PrefillParams p) {
   };
   // Fetch tile j into its buffer: DMA from the workspace, or a register gather
   // for tiles that reach into the cached prefix (stored before returning).
-  auto fetch = [&](int j, auto B) {
+  auto fetch = [&](int j, auto B) __attribute__((always_inline)) {
     uint16_t* sK = buf(B);
     if (j >= j_ws) {
       dma_tile(ks, plan, j * BN, sK, sK + K_TILE);
@@ -449,7 +466,7 @@ prefill_attn_kernel(PrefillParams p) {
   };
 
   // One 64-key tile of attention for this wave's queries.
-  auto compute_tile = [&](int j, auto B) {
+  auto compute_tile = [&](int j, auto B) __attribute__((always_inline)) {
     if (!active(j)) return;
     f32x16 st[NB][2];
     qk(B, st);
@@ -461,22 +478,30 @@ prefill_attn_kernel(PrefillParams p) {
     softmax(st, pf);
     pv(B, pf);
   };
-  // Tile jt (in buffer B) is computed while tile jt+1 streams into the other.
-  auto step = [&](int jt, auto B) {
-    if (jt + 1 <= j_hi) fetch(jt + 1, std::integral_constant<int, 1 - decltype(B)::value>{});
-    compute_tile(jt, B);
+  // Stage of tiles j0 .. j0+TPS-1 in slots S0 .. S0+TPS-1: before tile j0+u
+  // is computed, tile j0+TPS+u is sent to the other stage's slot (freed by the
+  // previous barrier); the barrier then publishes the next stage.
+  auto stage = [&](int j0, auto S0) __attribute__((always_inline)) {
+    static_for<TPS>([&](auto U) __attribute__((always_inline)) {
+      constexpr int u = decltype(U)::value;
+      constexpr int s0 = decltype(S0)::value;
+      if (j0 + TPS + u <= j_hi) fetch(j0 + TPS + u, std::integral_constant<int, (s0 + TPS + u) % SLOTS>{});
+      if (j0 + u <= j_hi) compute_tile(j0 + u, std::integral_constant<int, s0 + u>{});
+    });
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
 
   // ---- tile loop ----
-  if (j_lo <= j_hi) fetch(j_lo, std::integral_constant<int, 0>{});
+  static_for<TPS>([&](auto U) __attribute__((always_inline)) {
+    if (j_lo + decltype(U)::value <= j_hi) fetch(j_lo + decltype(U)::value, U);
+  });
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int jt = j_lo; jt <= j_hi; jt += 2) {
-    step(jt, std::integral_constant<int, 0>{});
-    if (jt + 1 > j_hi) break;
-    step(jt + 1, std::integral_constant<int, 1>{});
+  for (int jt = j_lo; jt <= j_hi; jt += SLOTS) {
+    stage(jt, std::integral_constant<int, 0>{});
+    if (jt + TPS > j_hi) break;
+    stage(jt + TPS, std::integral_constant<int, TPS>{});
   }
 
   // Epilogue: normalise, gate, write bf16. Lane holds query n of each N-block
