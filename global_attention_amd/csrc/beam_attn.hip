@@ -236,6 +236,13 @@ beam_status beam_attn_prefill_stages(uint32_t stages, const beam_attn_config* cf
   pp.qp = qp;
   pp.kw = kw;
   pp.vw = vw;
+  pp.ck = static_cast<const uint16_t*>(cache->k);
+  pp.cv = static_cast<const uint16_t*>(cache->v);
+  pp.bt = cache->block_table;
+  pp.seq_idx = seq_idx;
+  pp.max_pages = cache->max_pages_per_seq;
+  pp.n_cache_seqs = cache->n_seqs;
+  pp.window = cfg->window;
   pp.kind = cache->kind;
   pp.H = cfg->n_q_heads;
   pp.G = cfg->n_kv_heads;

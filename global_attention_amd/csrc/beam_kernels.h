@@ -17,6 +17,13 @@ struct PrologueParams {
   uint16_t* qp;  // Q' [n_tok][H][D]
   uint16_t* kw;  // K_hat [G][P][D]
   uint16_t* vw;  // V^T [G][D][P]
+  // Cache of the layer: the cached keys of a chunk's first 64-key tile (from
+  // start & ~63 up to start) are copied into the workspace.
+  const uint16_t* ck;
+  const uint16_t* cv;
+  const int32_t* bt;
+  const int32_t* seq_idx;
+  int max_pages, n_cache_seqs, window;
   int kind, H, G, P;
   float rope_theta, rms_eps, ssmax_base, ssmax_exp;
 };

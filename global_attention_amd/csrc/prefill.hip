@@ -23,9 +23,9 @@
 //   V^T: 128 rows (coordinates) x 128 B (64 keys, natural order).
 // Both XOR-swizzle their 16-byte chunks with the low 3 bits of the row, which
 // keeps the b128 operand reads free of bank conflicts without padding.
-// Tiles that reach into the cached prefix are also copied by DMA, with each
-// lane addressing its chunk in the paged cache or ring; only a tile in which an
-// 8-key V^T chunk straddles the chunk start is gathered through registers.
+// Tiles of the cached prefix are also copied by DMA, each lane addressing its
+// chunk in the paged cache or ring; the prologue has already copied the cached
+// keys of the chunk's first tile into the workspace, so no tile mixes the two.
 //
 // Softmax runs in base 2 (Q' carries log2 e / sqrt d and, on global layers,
 // a(t+1)). Each query keeps a reference m (its running max, moved only when
@@ -81,9 +81,10 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Where the keys of one (sequence, KV head) live. All pointers are
-// wave-uniform; per-lane offsets from them fit in 32 bits (the host keeps
-// P * D below 2^31), except the page term of the paged cache.
+// Where the keys of one (sequence, KV head) live: keys from start & ~63 on
+// in the workspace, earlier ones in the cache. All pointers are wave-uniform;
+// per-lane offsets from them fit in 32 bits (the host keeps P * D below
+// 2^31), except the page term of the paged cache.
 struct KeySource {
   const uint16_t* kw;     // workspace K rows of head g: row s + ws_off
   const uint16_t* vw;     // workspace V^T of head g: [d][s + ws_off], row stride P
@@ -91,73 +92,9 @@ struct KeySource {
   const uint16_t* cv;     // cache V^T: global as ck; local ring [d][slot]
   const int32_t* bt_row;  // block-table row of the cache sequence (global)
   size_t page_stride;     // elements per page of the paged cache (all KV heads)
-  int start;              // first chunk position; keys below it come from the cache
-  int cache_ok;           // the cache sequence index is in range
   int ws_off;             // workspace index = s + ws_off
   int P, kind, window;
 };
-
-// ---------------------------------------------------------------- register path
-// 16 bytes of K row s, coordinates [8c, 8c+8), from wherever key s lives.
-// Address of K row s (any position below the chunk end; cache rows need
-// cache_ok) and of V^T element (d, s).
-__device__ __forceinline__ const uint16_t* k_row_src(const KeySource& ks, int s) {
-  if (s >= ks.start) return ks.kw + (uint32_t)((s + ks.ws_off) * D);
-  if (ks.kind == 1) return ks.ck + ks.bt_row[s >> 4] * ks.page_stride + (uint32_t)((s & 15) * D);
-  return ks.ck + (uint32_t)((s % ks.window) * D);
-}
-__device__ __forceinline__ const uint16_t* v_elem_src(const KeySource& ks, int d, int s) {
-  if (s >= ks.start) return ks.vw + (uint32_t)(d * ks.P + s + ks.ws_off);
-  if (ks.kind == 1) return ks.cv + ks.bt_row[s >> 4] * ks.page_stride + (uint32_t)(d * 16 + (s & 15));
-  return ks.cv + (uint32_t)(d * ks.window + s % ks.window);
-}
-
-__device__ __forceinline__ u32x4 load_k_piece(const KeySource& ks, int s, int c) {
-  if (s < ks.start && !ks.cache_ok) return u32x4{0u, 0u, 0u, 0u};
-  return *reinterpret_cast<const u32x4*>(k_row_src(ks, s) + 8 * c);
-}
-
-__device__ __forceinline__ uint16_t load_v_elem(const KeySource& ks, int d, int s) {
-  if (s < ks.start && !ks.cache_ok) return 0;
-  return *v_elem_src(ks, d, s);
-}
-
-// 8 consecutive V^T values: row d, keys [s8, s8+8) (s8 a multiple of 8).
-__device__ __forceinline__ u32x4 load_v_piece(const KeySource& ks, int d, int s8) {
-  if (s8 >= ks.start || s8 + 8 <= ks.start) {
-    if (s8 < ks.start && !ks.cache_ok) return u32x4{0u, 0u, 0u, 0u};
-    return *reinterpret_cast<const u32x4*>(v_elem_src(ks, d, s8));
-  }
-  u32x4 r;
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    r[q] = (uint32_t)load_v_elem(ks, d, s8 + 2 * q) | ((uint32_t)load_v_elem(ks, d, s8 + 2 * q + 1) << 16);
-  return r;
-}
-
-// Gather a tile through registers (tiles touching the cached prefix); NW
-// wavefronts share the 1024 16-byte pieces of K and of V^T.
-template <int NW>
-__device__ __forceinline__ void gather_tile(const KeySource& ks, int key0, int tid, u32x4 (&kr)[16 / NW],
-                                            u32x4 (&vr)[16 / NW]) {
-#pragma unroll
-  for (int r = 0; r < 16 / NW; ++r) {
-    const int id = tid + 64 * NW * r;
-    kr[r] = load_k_piece(ks, key0 + (id >> 4), id & 15);   // key row (id>>4), chunk (id&15)
-    vr[r] = load_v_piece(ks, id >> 3, key0 + 8 * (id & 7));  // V^T row (id>>3), chunk (id&7)
-  }
-}
-
-template <int NW>
-__device__ __forceinline__ void scatter_tile(uint16_t* sK, uint16_t* sV, int tid, const u32x4 (&kr)[16 / NW],
-                                             const u32x4 (&vr)[16 / NW]) {
-#pragma unroll
-  for (int r = 0; r < 16 / NW; ++r) {
-    const int id = tid + 64 * NW * r;
-    *reinterpret_cast<u32x4*>(sK + k_off(krow_key(id >> 4), id & 15)) = kr[r];
-    *reinterpret_cast<u32x4*>(sV + v_off(id >> 3, id & 7)) = vr[r];
-  }
-}
 
 // ---------------------------------------------------------------- DMA path
 // Element offsets (relative to the tile's first key in the workspace) of the
@@ -203,10 +140,19 @@ __device__ __forceinline__ void dma_tile(const KeySource& ks, const DmaPlan<NW>&
   }
 }
 
-// DMA of a tile that lies (partly) in the cached prefix: every lane computes
-// the address of its 16-byte chunk from the key's location (cache page / ring
-// slot below `start`, workspace from `start` on). Requires that no 8-key V^T
-// chunk straddles `start` and that the cache row is valid.
+// Address of cached K row s and of cached V^T element (d, s) (s < start).
+__device__ __forceinline__ const uint16_t* k_row_src(const KeySource& ks, int s) {
+  if (ks.kind == 1) return ks.ck + ks.bt_row[s >> 4] * ks.page_stride + (uint32_t)((s & 15) * D);
+  return ks.ck + (uint32_t)((s % ks.window) * D);
+}
+__device__ __forceinline__ const uint16_t* v_elem_src(const KeySource& ks, int d, int s) {
+  if (ks.kind == 1) return ks.cv + ks.bt_row[s >> 4] * ks.page_stride + (uint32_t)(d * 16 + (s & 15));
+  return ks.cv + (uint32_t)(d * ks.window + s % ks.window);
+}
+
+// DMA of a tile of the cached prefix (all keys below start & ~63): every lane
+// computes the address of its 16-byte chunk from the key's page or ring slot.
+// Requires a valid cache row.
 template <int NW>
 __device__ __forceinline__ void dma_tile_prefix(const KeySource& ks, int w, int lane, int key0, uint16_t* sK,
                                                 uint16_t* sV) {
@@ -278,9 +224,10 @@ prefill_attn_kernel(PrefillParams p) {
     ks.page_stride = 0;
   }
   ks.bt_row = KIND == 1 ? p.bt + (size_t)cseq * p.max_pages : nullptr;
-  ks.start = start;
-  // The cached prefix must fit the cache sequence's block-table row (global).
-  ks.cache_ok = cseq >= 0 && cseq < p.n_cache_seqs && (KIND == 0 || ((start + 15) >> 4) <= p.max_pages);
+  // The cached prefix must fit the cache sequence's block-table row (global);
+  // an out-of-range row leaves the prefix out (the prologue zeroed its part
+  // of the first tile).
+  const bool cache_ok = cseq >= 0 && cseq < p.n_cache_seqs && (KIND == 0 || ((start + 15) >> 4) <= p.max_pages);
   ks.ws_off = ws_region_base(cu0, seq) - (start & ~63);
   ks.P = p.P;
   ks.kind = KIND;
@@ -301,10 +248,10 @@ prefill_attn_kernel(PrefillParams p) {
       qf[nb][kk] = valid ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk) : u32x4{0u, 0u, 0u, 0u};
   }
 
+  const int j_ws = start >> 6;  // first tile in the workspace; earlier tiles are wholly cached
   const int kmin = local ? max(0, q0 - (W - 1)) : 0;
-  const int j_lo = kmin >> 6;
+  const int j_lo = cache_ok ? kmin >> 6 : max(kmin >> 6, j_ws);
   const int j_hi = qlast >> 6;
-  const int j_ws = (start + BN - 1) >> 6;  // first tile whose keys all come from the workspace
 
   f32x16 o[NB][4];
 #pragma unroll
@@ -450,19 +397,13 @@ prefill_attn_kernel(PrefillParams p) {
       }
     }
   };
-  // Fetch tile j into its buffer: DMA from the workspace, or a register gather
-  // for tiles that reach into the cached prefix (stored before returning).
+  // Fetch tile j into its slot by DMA, from the workspace or the cache.
   auto fetch = [&](int j, auto B) __attribute__((always_inline)) {
     uint16_t* sK = buf(B);
-    if (j >= j_ws) {
+    if (j >= j_ws)
       dma_tile(ks, plan, j * BN, sK, sK + K_TILE);
-    } else if (ks.cache_ok && ((start & 7) == 0 || j * BN + BN <= start)) {
+    else
       dma_tile_prefix<NWAVES>(ks, w, lane, j * BN, sK, sK + K_TILE);
-    } else {
-      u32x4 kr[16 / NWAVES], vr[16 / NWAVES];
-      gather_tile<NWAVES>(ks, j * BN, tid, kr, vr);
-      scatter_tile<NWAVES>(sK, sK + K_TILE, tid, kr, vr);
-    }
   };
 
   // One 64-key tile of attention for this wave's queries.

@@ -15,12 +15,34 @@ namespace beam {
 // ----------------------------------------------------------------------------
 // Prefill prologue. Grid (sequence, 64-position tile, part). The tile covers
 // absolute positions [64*T, 64*T + 64) with T = (start >> 6) + blockIdx.y.
-// Part 0 writes K_hat and V^T of the tile into the position-aligned workspace
-// (zeros for positions outside the chunk, so attention can read whole 64-key
-// tiles); part z >= 1 writes Q' for query heads [8(z-1), 8z) of the chunk's
-// tokens into [n_tok][H][D].
+// Part 0 writes K_hat and V^T of the tile into the position-aligned workspace:
+// the chunk's own positions from the projections, the cached positions
+// [start & ~63, start) of its first tile copied from the cache (zeros when the
+// cache row is out of range), zeros after the chunk end. Attention then reads
+// every tile either wholly from the workspace or wholly from the cache. Part
+// z >= 1 writes Q' for query heads [8(z-1), 8z) of the chunk's tokens into
+// [n_tok][H][D].
 // ----------------------------------------------------------------------------
 constexpr int kQHeadsPerBlock = 8;
+
+// Cached K_hat row of position t (paged: block-table page; local: ring slot).
+__device__ __forceinline__ const uint16_t* cache_k_row(const PrologueParams& p, int cseq, int g, int t) {
+  if (p.kind == 1) {
+    const int page = p.bt[(size_t)cseq * p.max_pages + (t >> 4)];
+    return p.ck + (((size_t)page * p.G + g) * 16 + (t & 15)) * D;
+  }
+  return p.ck + (((size_t)cseq * p.G + g) * p.window + t % p.window) * D;
+}
+// Cached V^T element (0, t); coordinate d is at [d * stride].
+__device__ __forceinline__ const uint16_t* cache_v_col(const PrologueParams& p, int cseq, int g, int t, int* stride) {
+  if (p.kind == 1) {
+    const int page = p.bt[(size_t)cseq * p.max_pages + (t >> 4)];
+    *stride = 16;
+    return p.cv + ((size_t)page * p.G + g) * D * 16 + (t & 15);
+  }
+  *stride = p.window;
+  return p.cv + ((size_t)cseq * p.G + g) * D * p.window + t % p.window;
+}
 
 __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p) {
   const int seq = blockIdx.x;
@@ -34,6 +56,9 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
   if (part > 0 && h_lo >= p.H) return;
   const int region = ws_region_base(cu0, seq);
   const int ws0 = region + tile_pos0 - (start & ~63);  // workspace index of tile_pos0
+  // Cache row of the sequence, for the cached positions of the first tile.
+  const int cseq = p.seq_idx[seq];
+  const bool cache_ok = cseq >= 0 && cseq < p.n_cache_seqs && (p.kind == 0 || ((start + 15) >> 4) <= p.max_pages);
 
   __shared__ float s_cos[64][64];
   __shared__ float s_sin[64][64];
@@ -84,6 +109,12 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
     const int r = pr / p.G, g = pr - r * p.G;
     const int t = tile_pos0 + r;
     u32x2* dst = reinterpret_cast<u32x2*>(p.kw + ((size_t)g * p.P + ws0 + r) * D);
+    if (t < start && cache_ok) {  // cached K_hat row, already normalised (and rotated)
+      const u32x2* src = reinterpret_cast<const u32x2*>(cache_k_row(p, cseq, g, t));
+      dst[j] = src[j];
+      dst[16 + j] = src[16 + j];
+      continue;
+    }
     if (t < start || t >= start + len) {
       dst[j] = u32x2{0u, 0u};
       dst[16 + j] = u32x2{0u, 0u};
@@ -108,6 +139,12 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
       if (t >= start && t < start + len) {
         const size_t tok = (size_t)(cu0 + t - start);
         v = *reinterpret_cast<const u32x4*>(p.v_raw + (tok * p.G + g) * D + 8 * c);
+      } else if (t < start && cache_ok) {  // cached V^T column of position t
+        int stride;
+        const uint16_t* col = cache_v_col(p, cseq, g, t, &stride);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          v[q] = (uint32_t)col[(size_t)(8 * c + 2 * q) * stride] | ((uint32_t)col[(size_t)(8 * c + 2 * q + 1) * stride] << 16);
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
