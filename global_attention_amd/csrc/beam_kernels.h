@@ -16,7 +16,7 @@ struct PrologueParams {
   const int32_t* start_pos;
   uint16_t* qp;  // Q' [n_tok][H][D]
   uint16_t* kw;  // K_hat [G][P][D]
-  uint16_t* vw;  // V^T [G][D][P]
+  uint16_t* vw;  // V^T [G][P/64][D][64] (64-position tiles)
   // Cache of the layer: the cached keys of a chunk's first 64-key tile (from
   // start & ~63 up to start) are copied into the workspace.
   const uint16_t* ck;
@@ -65,7 +65,7 @@ constexpr int prefill_block_queries(int kind) { return 32 * (kind == 0 ? kPrefil
 struct PrefillParams {
   const uint16_t* qp;  // Q' [n_tok][H][D]
   const uint16_t* kw;  // K_hat workspace [G][P][D]
-  const uint16_t* vw;  // V^T workspace [G][D][P]
+  const uint16_t* vw;  // V^T workspace [G][P/64][D][64]
   const uint16_t* gate;
   const float* gate_bias;
   uint16_t* out;

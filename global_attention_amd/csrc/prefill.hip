@@ -87,7 +87,7 @@ __device__ __forceinline__ float sum_halves(float x) {
 // 2^31), except the page term of the paged cache.
 struct KeySource {
   const uint16_t* kw;     // workspace K rows of head g: row s + ws_off
-  const uint16_t* vw;     // workspace V^T of head g: [d][s + ws_off], row stride P
+  const uint16_t* vw;     // workspace V^T of head g: 64-key tiles [(s + ws_off) / 64][d][64]
   const uint16_t* ck;     // cache K: global page p at ck + p * page_stride; local ring rows
   const uint16_t* cv;     // cache V^T: global as ck; local ring [d][slot]
   const int32_t* bt_row;  // block-table row of the cache sequence (global)
@@ -110,7 +110,7 @@ struct DmaPlan {
 };
 
 template <int NW>
-__device__ __forceinline__ DmaPlan<NW> make_dma_plan(int w, int lane, int P) {
+__device__ __forceinline__ DmaPlan<NW> make_dma_plan(int w, int lane) {
   DmaPlan<NW> pl;
 #pragma unroll
   for (int i = 0; i < DmaPlan<NW>::N; ++i) {
@@ -122,7 +122,7 @@ __device__ __forceinline__ DmaPlan<NW> make_dma_plan(int w, int lane, int P) {
     const int vI = w * DmaPlan<NW>::N + i;  // V^T rows 8vI .. 8vI+7
     const int d = 8 * vI + (lane >> 3);
     const int cv = (lane & 7) ^ (d & 7);
-    pl.v_src[i] = (uint32_t)(d * P + 8 * cv);
+    pl.v_src[i] = (uint32_t)(d * BN + 8 * cv);
     pl.v_lds[i] = vI * 512;
   }
   return pl;
@@ -132,7 +132,7 @@ template <int NW>
 __device__ __forceinline__ void dma_tile(const KeySource& ks, const DmaPlan<NW>& pl, int key0, uint16_t* sK,
                                          uint16_t* sV) {
   const uint16_t* kb = ks.kw + (uint32_t)((key0 + ks.ws_off) * D);
-  const uint16_t* vb = ks.vw + (uint32_t)(key0 + ks.ws_off);
+  const uint16_t* vb = ks.vw + (uint32_t)((key0 + ks.ws_off) * D);
 #pragma unroll
   for (int i = 0; i < DmaPlan<NW>::N; ++i) {
     __builtin_amdgcn_global_load_lds(kb + pl.k_src[i], sK + pl.k_lds[i], 16, 0, 0);
@@ -232,7 +232,7 @@ prefill_attn_kernel(PrefillParams p) {
   ks.P = p.P;
   ks.kind = KIND;
   ks.window = W;
-  const DmaPlan<NWAVES> plan = make_dma_plan<NWAVES>(w, lane, p.P);
+  const DmaPlan<NWAVES> plan = make_dma_plan<NWAVES>(w, lane);
 
   // Q' fragments (B operand of S^T = K Q'^T): lane holds query n of N-block nb,
   // coordinates 16kk + 8*half + 0..7.

@@ -129,7 +129,7 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
   }
 
   // V: transpose 64 positions x 128 coords per KV head through LDS into
-  // V^T workspace [G][D][P].
+  // V^T workspace [G][P/64][D][64] (each 64-position tile contiguous).
   for (int g = 0; g < p.G; ++g) {
     __syncthreads();
     for (int e = tid; e < 64 * 16; e += 256) {  // 16-byte pieces: row r, coords 8c..8c+7
@@ -159,7 +159,7 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         o[q] = (uint32_t)s_v[8 * c + 2 * q][d] | ((uint32_t)s_v[8 * c + 2 * q + 1][d] << 16);
-      *reinterpret_cast<u32x4*>(p.vw + ((size_t)g * D + d) * p.P + ws0 + 8 * c) = o;
+      *reinterpret_cast<u32x4*>(p.vw + (size_t)g * D * p.P + ((size_t)(ws0 >> 6) * D + d) * 64 + 8 * c) = o;
     }
   }
 }
