@@ -48,21 +48,28 @@ __device__ __forceinline__ bool visible(int kind, int window, int t, int s) {
   return dlt >= 0 && (kind == 1 || dlt <= window - 1);
 }
 
-// SSMax query scale a(p) = (1 + p/base)^exponent at one-based p = t + 1.
+// SSMax query scale a(p) = (1 + p/base)^exponent at one-based p = t + 1, as
+// 2^(exponent * log2(1 + p/base)) in float32 (relative error ~2e-7, far below
+// the bf16 rounding of the scaled query).
 __device__ __forceinline__ float ssmax_scale(int t, float base, float expo) {
-  return (float)pow(1.0 + (double)(t + 1) / (double)base, (double)expo);
+  return exp2f(expo * log2f(1.0f + (float)(t + 1) / base));
 }
 
-// cos/sin of t * theta^(-2i/128), angle formed and range-reduced in float64.
-__device__ __forceinline__ void rope_cs(int t, int i, float theta, float* c, float* s) {
-  double w = pow((double)theta, -2.0 * (double)i / (double)D);
-  double ang = (double)t * w;
+// RoPE inverse frequency theta^(-2i/128) of pair i (float64).
+__device__ __forceinline__ double rope_inv_freq(int i, float theta) {
+  return pow((double)theta, -2.0 * (double)i / (double)D);
+}
+// cos/sin of t * w: the angle is formed and reduced to [-pi, pi] in float64,
+// then its cosine and sine are taken in float32 (error ~1e-7, far below the
+// bf16 rounding of the rotated vectors).
+__device__ __forceinline__ void rope_cs_w(int t, double w, float* c, float* s) {
+  const double ang = (double)t * w;
   const double two_pi = 6.283185307179586476925;
-  double r = ang - two_pi * rint(ang / two_pi);
-  double sd, cd;
-  sincos(r, &sd, &cd);
-  *c = (float)cd;
-  *s = (float)sd;
+  const float r = (float)(ang - two_pi * rint(ang / two_pi));
+  sincosf(r, s, c);
+}
+__device__ __forceinline__ void rope_cs(int t, int i, float theta, float* c, float* s) {
+  rope_cs_w(t, rope_inv_freq(i, theta), c, s);
 }
 
 // Sum over the 16 lanes of an aligned 16-lane group.

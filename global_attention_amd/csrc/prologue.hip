@@ -15,27 +15,37 @@ namespace beam {
 // ----------------------------------------------------------------------------
 // Prefill prologue. Grid (sequence, 64-position tile, part). The tile covers
 // absolute positions [64*T, 64*T + 64) with T = (start >> 6) + blockIdx.y.
-// Part 0 writes K_hat and V^T of the tile into the position-aligned workspace:
-// the chunk's own positions from the projections, the cached positions
-// [start & ~63, start) of its first tile copied from the cache (zeros when the
-// cache row is out of range), zeros after the chunk end. Attention then reads
-// every tile either wholly from the workspace or wholly from the cache. Part
-// z >= 1 writes Q' for query heads [8(z-1), 8z) of the chunk's tokens into
-// [n_tok][H][D].
+// Part 0 writes K_hat of the tile and parts 1..2 write V^T (KV heads
+// [4(z-1), 4z)) into the position-aligned workspace: the chunk's own positions
+// from the projections, the cached positions [start & ~63, start) of its first
+// tile copied from the cache (zeros when the cache row is out of range), zeros
+// after the chunk end. Attention then reads every tile either wholly from the
+// workspace or wholly from the cache. Part z >= 3 writes Q' for query heads
+// [8(z-3), 8(z-2)) of the chunk's tokens into [n_tok][H][D].
+//
+// A 16-lane group owns one position at a time (positions grp, grp+16, ...) and
+// handles all of its heads: the position's RoPE cos/sin (local) or SSMax scale
+// (global) is formed once, and the group's loads for every head are issued
+// before any is used.
 // ----------------------------------------------------------------------------
 constexpr int kQHeadsPerBlock = 8;
+constexpr int kVHeadsPerBlock = 4;
+constexpr int kPrologueFixedParts = 3;  // K, V (two halves)
+constexpr int kMaxHeadsPerGroup = 8;
 
 // Cached K_hat row of position t (paged: block-table page; local: ring slot).
+template <int KIND>
 __device__ __forceinline__ const uint16_t* cache_k_row(const PrologueParams& p, int cseq, int g, int t) {
-  if (p.kind == 1) {
+  if (KIND == 1) {
     const int page = p.bt[(size_t)cseq * p.max_pages + (t >> 4)];
     return p.ck + (((size_t)page * p.G + g) * 16 + (t & 15)) * D;
   }
   return p.ck + (((size_t)cseq * p.G + g) * p.window + t % p.window) * D;
 }
 // Cached V^T element (0, t); coordinate d is at [d * stride].
+template <int KIND>
 __device__ __forceinline__ const uint16_t* cache_v_col(const PrologueParams& p, int cseq, int g, int t, int* stride) {
-  if (p.kind == 1) {
+  if (KIND == 1) {
     const int page = p.bt[(size_t)cseq * p.max_pages + (t >> 4)];
     *stride = 16;
     return p.cv + ((size_t)page * p.G + g) * D * 16 + (t & 15);
@@ -44,7 +54,9 @@ __device__ __forceinline__ const uint16_t* cache_v_col(const PrologueParams& p, 
   return p.cv + ((size_t)cseq * p.G + g) * D * p.window + t % p.window;
 }
 
+template <int KIND>
 __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p) {
+  constexpr bool local = (KIND == 0);
   const int seq = blockIdx.x;
   const int part = blockIdx.z;
   const int start = p.start_pos[seq];
@@ -52,114 +64,165 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
   const int len = p.cu[seq + 1] - cu0;
   const int tile_pos0 = ((start >> 6) + (int)blockIdx.y) * 64;
   if (tile_pos0 >= start + len) return;
-  const int h_lo = (part - 1) * kQHeadsPerBlock;
-  if (part > 0 && h_lo >= p.H) return;
   const int region = ws_region_base(cu0, seq);
-  const int ws0 = region + tile_pos0 - (start & ~63);  // workspace index of tile_pos0
-  // Cache row of the sequence, for the cached positions of the first tile.
-  const int cseq = p.seq_idx[seq];
-  const bool cache_ok = cseq >= 0 && cseq < p.n_cache_seqs && (p.kind == 0 || ((start + 15) >> 4) <= p.max_pages);
-
-  __shared__ float s_cos[64][64];
-  __shared__ float s_sin[64][64];
-  __shared__ uint16_t s_v[64][D + 2];
+  const int ws0 = region + tile_pos0 - (start & ~63);  // workspace index of tile_pos0 (multiple of 64)
 
   const int tid = threadIdx.x;
-  const bool local = (p.kind == 0);
-  if (local) {
-    for (int e = tid; e < 64 * 64; e += 256) {
-      int r = e >> 6, i = e & 63;
-      float c, sn;
-      rope_cs(tile_pos0 + r, i, p.rope_theta, &c, &sn);
-      s_cos[r][i] = c;
-      s_sin[r][i] = sn;
-    }
-    __syncthreads();
-  }
-
   const int grp = tid >> 4;  // 16 groups of 16 lanes
   const int j = tid & 15;    // lane within group: coords [4j,4j+4) and [64+4j, 64+4j+4)
 
-  if (part > 0) {
-    // Q: 64 positions x 8 heads, one (position, head) pair per 16-lane group.
+  // Inverse RoPE frequencies of this lane's pairs 4j..4j+3.
+  double inv_freq[4];
+  if (local && part != 1 && part != 2) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) inv_freq[e] = rope_inv_freq(4 * j + e, p.rope_theta);
+  }
+
+  if (part >= kPrologueFixedParts) {
+    // Q': 64 positions x up to 8 heads.
+    const int h_lo = (part - kPrologueFixedParts) * kQHeadsPerBlock;
+    if (h_lo >= p.H) return;
+    const int nh = min(kQHeadsPerBlock, p.H - h_lo);
     const u32x2* qw = reinterpret_cast<const u32x2*>(p.q_norm_w);
     const u32x2 wq_lo = qw[j], wq_hi = qw[16 + j];
     const float qbase = kLog2e / sqrtf((float)D);
-    const int nh = min(kQHeadsPerBlock, p.H - h_lo);
-    for (int pr = grp; pr < 64 * nh; pr += 16) {
-      const int r = pr / nh, h = h_lo + (pr - r * nh);
+    for (int r = grp; r < 64; r += 16) {
       const int t = tile_pos0 + r;
       if (t < start || t >= start + len) continue;
       const size_t tok = (size_t)(cu0 + t - start);
-      const u32x2* src = reinterpret_cast<const u32x2*>(p.q_raw + (tok * p.H + h) * D);
+      const u32x2* src = reinterpret_cast<const u32x2*>(p.q_raw + (tok * p.H + h_lo) * D);
+      u32x2 xlo[kMaxHeadsPerGroup], xhi[kMaxHeadsPerGroup];
+#pragma unroll
+      for (int hh = 0; hh < kMaxHeadsPerGroup; ++hh)
+        if (hh < nh) {
+          xlo[hh] = src[hh * (D / 4) + j];
+          xhi[hh] = src[hh * (D / 4) + 16 + j];
+        }
+      float cs[4], sn[4];
+      if (local) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rope_cs_w(t, inv_freq[e], &cs[e], &sn[e]);
+      }
       const float scale = local ? qbase : qbase * ssmax_scale(t, p.ssmax_base, p.ssmax_exp);
-      HeadFrag f = norm_rope_head(src[j], src[16 + j], wq_lo, wq_hi, p.rms_eps, local,
-                                  local ? &s_cos[r][4 * j] : nullptr, local ? &s_sin[r][4 * j] : nullptr, scale);
-      u32x2* dst = reinterpret_cast<u32x2*>(p.qp + (tok * p.H + h) * D);
-      dst[j] = u32x2{f.lo[0], f.lo[1]};
-      dst[16 + j] = u32x2{f.hi[0], f.hi[1]};
+      u32x2* dst = reinterpret_cast<u32x2*>(p.qp + (tok * p.H + h_lo) * D);
+#pragma unroll
+      for (int hh = 0; hh < kMaxHeadsPerGroup; ++hh)
+        if (hh < nh) {
+          HeadFrag f = norm_rope_head(xlo[hh], xhi[hh], wq_lo, wq_hi, p.rms_eps, local, cs, sn, scale);
+          dst[hh * (D / 4) + j] = u32x2{f.lo[0], f.lo[1]};
+          dst[hh * (D / 4) + 16 + j] = u32x2{f.hi[0], f.hi[1]};
+        }
     }
     return;
   }
 
-  // K: 64 positions x G heads into K_hat workspace [G][P][D].
-  const u32x2* kwgt = reinterpret_cast<const u32x2*>(p.k_norm_w);
-  const u32x2 wk_lo = kwgt[j], wk_hi = kwgt[16 + j];
-  for (int pr = grp; pr < 64 * p.G; pr += 16) {
-    const int r = pr / p.G, g = pr - r * p.G;
-    const int t = tile_pos0 + r;
-    u32x2* dst = reinterpret_cast<u32x2*>(p.kw + ((size_t)g * p.P + ws0 + r) * D);
-    if (t < start && cache_ok) {  // cached K_hat row, already normalised (and rotated)
-      const u32x2* src = reinterpret_cast<const u32x2*>(cache_k_row(p, cseq, g, t));
-      dst[j] = src[j];
-      dst[16 + j] = src[16 + j];
-      continue;
+  // Cache row of the sequence, for the cached positions of the first tile.
+  const int cseq = p.seq_idx[seq];
+  const bool cache_ok = cseq >= 0 && cseq < p.n_cache_seqs && (local || ((start + 15) >> 4) <= p.max_pages);
+
+  if (part == 0) {
+    // K_hat: 64 positions x G heads into the workspace [G][P][D].
+    if (p.G > kMaxHeadsPerGroup) return;  // rejected by the host
+    const u32x2* kwgt = reinterpret_cast<const u32x2*>(p.k_norm_w);
+    const u32x2 wk_lo = kwgt[j], wk_hi = kwgt[16 + j];
+    for (int r = grp; r < 64; r += 16) {
+      const int t = tile_pos0 + r;
+      u32x2* dst0 = reinterpret_cast<u32x2*>(p.kw + ((size_t)ws0 + r) * D);
+      const size_t hstride = (size_t)p.P * (D / 4);  // u32x2 units between heads
+      if (t < start && cache_ok) {  // cached K_hat rows, already normalised (and rotated)
+        u32x2 clo[kMaxHeadsPerGroup], chi[kMaxHeadsPerGroup];
+#pragma unroll
+        for (int g = 0; g < kMaxHeadsPerGroup; ++g)
+          if (g < p.G) {
+            const u32x2* src = reinterpret_cast<const u32x2*>(cache_k_row<KIND>(p, cseq, g, t));
+            clo[g] = src[j];
+            chi[g] = src[16 + j];
+          }
+#pragma unroll
+        for (int g = 0; g < kMaxHeadsPerGroup; ++g)
+          if (g < p.G) {
+            dst0[g * hstride + j] = clo[g];
+            dst0[g * hstride + 16 + j] = chi[g];
+          }
+        continue;
+      }
+      if (t < start || t >= start + len) {
+        for (int g = 0; g < p.G; ++g) {
+          dst0[g * hstride + j] = u32x2{0u, 0u};
+          dst0[g * hstride + 16 + j] = u32x2{0u, 0u};
+        }
+        continue;
+      }
+      const size_t tok = (size_t)(cu0 + t - start);
+      const u32x2* src = reinterpret_cast<const u32x2*>(p.k_raw + tok * p.G * D);
+      u32x2 xlo[kMaxHeadsPerGroup], xhi[kMaxHeadsPerGroup];
+#pragma unroll
+      for (int g = 0; g < kMaxHeadsPerGroup; ++g)
+        if (g < p.G) {
+          xlo[g] = src[g * (D / 4) + j];
+          xhi[g] = src[g * (D / 4) + 16 + j];
+        }
+      float cs[4], sn[4];
+      if (local) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rope_cs_w(t, inv_freq[e], &cs[e], &sn[e]);
+      }
+#pragma unroll
+      for (int g = 0; g < kMaxHeadsPerGroup; ++g)
+        if (g < p.G) {
+          HeadFrag f = norm_rope_head(xlo[g], xhi[g], wk_lo, wk_hi, p.rms_eps, local, cs, sn, 1.0f);
+          dst0[g * hstride + j] = u32x2{f.lo[0], f.lo[1]};
+          dst0[g * hstride + 16 + j] = u32x2{f.hi[0], f.hi[1]};
+        }
     }
-    if (t < start || t >= start + len) {
-      dst[j] = u32x2{0u, 0u};
-      dst[16 + j] = u32x2{0u, 0u};
-      continue;
-    }
-    const size_t tok = (size_t)(cu0 + t - start);
-    const u32x2* src = reinterpret_cast<const u32x2*>(p.k_raw + (tok * p.G + g) * D);
-    HeadFrag f = norm_rope_head(src[j], src[16 + j], wk_lo, wk_hi, p.rms_eps, local,
-                                local ? &s_cos[r][4 * j] : nullptr, local ? &s_sin[r][4 * j] : nullptr, 1.0f);
-    dst[j] = u32x2{f.lo[0], f.lo[1]};
-    dst[16 + j] = u32x2{f.hi[0], f.hi[1]};
+    return;
   }
 
-  // V: transpose 64 positions x 128 coords per KV head through LDS into
-  // V^T workspace [G][P/64][D][64] (each 64-position tile contiguous).
-  for (int g = 0; g < p.G; ++g) {
-    __syncthreads();
-    for (int e = tid; e < 64 * 16; e += 256) {  // 16-byte pieces: row r, coords 8c..8c+7
+  // V^T: transpose 64 positions x 128 coords per KV head through LDS into the
+  // workspace [G][P/64][D][64] (each 64-position tile contiguous).
+  __shared__ uint16_t s_v[64][D + 2];
+  const int g_lo = (part - 1) * kVHeadsPerBlock;
+  for (int g = g_lo; g < min(g_lo + kVHeadsPerBlock, p.G); ++g) {
+    u32x4 v[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {  // 16-byte pieces: row r, coords 8c..8c+7
+      const int e = tid + 256 * q4;
       const int r = e >> 4, c = e & 15;
       const int t = tile_pos0 + r;
-      u32x4 v = {0u, 0u, 0u, 0u};
+      v[q4] = u32x4{0u, 0u, 0u, 0u};
       if (t >= start && t < start + len) {
         const size_t tok = (size_t)(cu0 + t - start);
-        v = *reinterpret_cast<const u32x4*>(p.v_raw + (tok * p.G + g) * D + 8 * c);
+        v[q4] = *reinterpret_cast<const u32x4*>(p.v_raw + (tok * p.G + g) * D + 8 * c);
       } else if (t < start && cache_ok) {  // cached V^T column of position t
         int stride;
-        const uint16_t* col = cache_v_col(p, cseq, g, t, &stride);
+        const uint16_t* col = cache_v_col<KIND>(p, cseq, g, t, &stride);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          v[q] = (uint32_t)col[(size_t)(8 * c + 2 * q) * stride] | ((uint32_t)col[(size_t)(8 * c + 2 * q + 1) * stride] << 16);
+          v[q4][q] = (uint32_t)col[(size_t)(8 * c + 2 * q) * stride] | ((uint32_t)col[(size_t)(8 * c + 2 * q + 1) * stride] << 16);
       }
+    }
+    __syncthreads();  // the previous head's transposed reads are done
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int e = tid + 256 * q4;
+      const int r = e >> 4, c = e & 15;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        s_v[r][8 * c + 2 * q] = (uint16_t)(v[q] & 0xffffu);
-        s_v[r][8 * c + 2 * q + 1] = (uint16_t)(v[q] >> 16);
+        s_v[r][8 * c + 2 * q] = (uint16_t)(v[q4][q] & 0xffffu);
+        s_v[r][8 * c + 2 * q + 1] = (uint16_t)(v[q4][q] >> 16);
       }
     }
     __syncthreads();
-    for (int e = tid; e < D * 8; e += 256) {  // row d of V^T, keys 8c..8c+7
+    uint16_t* vt = p.vw + (size_t)g * D * p.P + (size_t)(ws0 >> 6) * D * 64;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {  // row d of V^T, keys 8c..8c+7
+      const int e = tid + 256 * q4;
       const int d = e >> 3, c = e & 7;
       u32x4 o;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         o[q] = (uint32_t)s_v[8 * c + 2 * q][d] | ((uint32_t)s_v[8 * c + 2 * q + 1][d] << 16);
-      *reinterpret_cast<u32x4*>(p.vw + (size_t)g * D * p.P + ((size_t)(ws0 >> 6) * D + d) * 64 + 8 * c) = o;
+      *reinterpret_cast<u32x4*>(vt + d * 64 + 8 * c) = o;
     }
   }
 }
@@ -274,8 +337,12 @@ __global__ void visibility_kernel(int kind, int window, int t0, int n_q, int s0,
 namespace beam {
 
 hipError_t launch_prefill_prologue(const PrologueParams& p, int n_seqs, int n_tiles, hipStream_t s) {
-  const int parts = 1 + (p.H + kQHeadsPerBlock - 1) / kQHeadsPerBlock;
-  hipLaunchKernelGGL(prefill_prologue_kernel, dim3(n_seqs, n_tiles, parts), dim3(256), 0, s, p);
+  const int parts = kPrologueFixedParts + (p.H + kQHeadsPerBlock - 1) / kQHeadsPerBlock;
+  if (p.G > kMaxHeadsPerGroup || p.G > 2 * kVHeadsPerBlock) return hipErrorInvalidValue;
+  if (p.kind == 0)
+    hipLaunchKernelGGL(prefill_prologue_kernel<0>, dim3(n_seqs, n_tiles, parts), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(prefill_prologue_kernel<1>, dim3(n_seqs, n_tiles, parts), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -69,7 +69,7 @@ typedef enum {
 /* Layer geometry. Defaults for Beam 1.0: 48, 8, 128, 512, 1e4, 1e-6, 2048, 0.1. */
 typedef struct {
   int32_t n_q_heads;  /* 48 */
-  int32_t n_kv_heads; /* 8; must divide n_q_heads, n_q_heads/n_kv_heads <= 16 */
+  int32_t n_kv_heads; /* 8; at most 8, must divide n_q_heads, n_q_heads/n_kv_heads <= 16 */
   int32_t head_dim;   /* 128 (only value supported) */
   int32_t window;     /* local window incl. the current token; 512 */
   float rope_theta;   /* 10000 */

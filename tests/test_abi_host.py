@@ -90,6 +90,7 @@ def test_argument_checks_fail_before_launch():
     assert _call_prefill(ga.Config(head_dim=64), _cache()) == 4
     assert _call_prefill(ga.Config(n_q_heads=47), _cache()) == 2
     assert _call_prefill(ga.Config(n_q_heads=48, n_kv_heads=2), _cache()) == 4   # 24 heads per KV head
+    assert _call_prefill(ga.Config(n_q_heads=64, n_kv_heads=16), _cache()) == 4  # more than 8 KV heads
     assert _call_prefill(ga.Config(window=500), _cache()) == 4
     assert _call_prefill(ga.Config(), _cache(page_size=64)) == 4
     assert _call_prefill(ga.Config(), _cache(), ws_bytes=10) == 5
