@@ -44,7 +44,8 @@ _KERNEL_SOURCES = {
     "prefill_attn_kernel<0, 4>": "prefill.hip",
     "decode_split_kernel<1>": "decode.hip",
     "decode_split_kernel<0>": "decode.hip",
-    "prefill_prologue_kernel": "prologue.hip",
+    "prefill_prologue_kernel<0>": "prologue.hip",
+    "prefill_prologue_kernel<1>": "prologue.hip",
 }
 
 
