@@ -220,6 +220,11 @@ beam_status beam_attn_prefill_stages(uint32_t stages, const beam_attn_config* cf
   if (ws_bytes < ws.total)
     return fail(BEAM_E_WORKSPACE, "prefill workspace needs " + std::to_string(ws.total) + " bytes");
   if (ws.P * beam::D > 0x7fffffff) return fail(BEAM_E_RANGE, "too many tokens in one call (workspace positions x 128 must stay below 2^31)");
+  {
+    const int bq = beam::prefill_block_queries(cache->kind);
+    const int64_t blocks = (int64_t)cfg->n_q_heads * n_seqs * ((max_chunk_len + bq - 1) / bq);
+    if (blocks > 0x7fffffffLL) return fail(BEAM_E_RANGE, "prefill grid too large (n_seqs x max_chunk_len)");
+  }
   hipStream_t s = (hipStream_t)stream;
   char* wsb = static_cast<char*>(workspace);
   uint16_t* qp = reinterpret_cast<uint16_t*>(wsb + ws.qp);

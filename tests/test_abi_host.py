@@ -72,12 +72,12 @@ def test_workspace_sizes():
     assert ga.prefill_workspace_bytes(ga.Config(head_dim=64), 10, 1) == 0
 
 
-def _call_prefill(cfg, cache, ws_bytes=1 << 30, n_tok=4, max_chunk=4, ws=0x1000):
+def _call_prefill(cfg, cache, ws_bytes=1 << 30, n_tok=4, max_chunk=4, ws=0x1000, n_seqs=1):
     L = ga.lib()
     c = cfg.c()
     fake = ctypes.c_void_p(0x100000)  # never dereferenced: the checks fail first
     return L.beam_attn_prefill(ctypes.byref(c), ctypes.byref(cache), fake, fake, fake, fake, fake, fake,
-                               None, fake, fake, fake, 1, n_tok, max_chunk, fake,
+                               None, fake, fake, fake, n_seqs, n_tok, max_chunk, fake,
                                ctypes.c_void_p(ws), ws_bytes, None)
 
 
@@ -91,6 +91,10 @@ def test_argument_checks_fail_before_launch():
     assert _call_prefill(ga.Config(n_q_heads=47), _cache()) == 2
     assert _call_prefill(ga.Config(n_q_heads=48, n_kv_heads=2), _cache()) == 4   # 24 heads per KV head
     assert _call_prefill(ga.Config(n_q_heads=64, n_kv_heads=16), _cache()) == 4  # more than 8 KV heads
+    # 2^15 sequences with 2^22-token chunks: the workspace fits 32-bit offsets but the grid would not
+    assert _call_prefill(ga.Config(), _cache(), ws_bytes=1 << 40, n_tok=1 << 22, max_chunk=1 << 22, n_seqs=1 << 15) == 3
+    # workspace positions x 128 beyond 2^31
+    assert _call_prefill(ga.Config(), _cache(), ws_bytes=1 << 40, n_tok=1 << 24, max_chunk=64) == 3
     assert _call_prefill(ga.Config(window=500), _cache()) == 4
     assert _call_prefill(ga.Config(), _cache(page_size=64)) == 4
     assert _call_prefill(ga.Config(), _cache(), ws_bytes=10) == 5
