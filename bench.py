@@ -125,13 +125,18 @@ def prefill_step(cfg, layers, meta, T, events=None):
         d = L["d"]
         args = (cfg, L["cache"], d["q"], d["k"], d["v"], d["q_norm_w"], d["k_norm_w"], d["gate"], meta["cu"],
                 meta["seq"], meta["start"], T)
-        ga.prefill(*args, out=L["out"], workspace=L["ws"], stages=ga.STAGE_PROLOGUE)
+        # Global layers: the append is fused into the prologue (paged slots of
+        # new positions never alias the prefix). Local: append after attention.
+        fused = L["kind"] == ga.GLOBAL
+        first = ga.STAGE_PROLOGUE | (ga.STAGE_APPEND if fused else 0)
+        ga.prefill(*args, out=L["out"], workspace=L["ws"], stages=first)
         if events is not None:
             events[i][0].record()
         ga.prefill(*args, out=L["out"], workspace=L["ws"], stages=ga.STAGE_ATTENTION)
         if events is not None:
             events[i][1].record()
-        ga.prefill(*args, out=L["out"], workspace=L["ws"], stages=ga.STAGE_APPEND)
+        if not fused:
+            ga.prefill(*args, out=L["out"], workspace=L["ws"], stages=ga.STAGE_APPEND)
 
 
 def bench_prefill(T, steps, warmup):

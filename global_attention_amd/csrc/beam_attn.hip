@@ -242,8 +242,10 @@ beam_status beam_attn_prefill_stages(uint32_t stages, const beam_attn_config* cf
   pp.qp = qp;
   pp.kw = kw;
   pp.vw = vw;
-  pp.ck = static_cast<const uint16_t*>(cache->k);
-  pp.cv = static_cast<const uint16_t*>(cache->v);
+  pp.ck = static_cast<uint16_t*>(cache->k);
+  pp.cv = static_cast<uint16_t*>(cache->v);
+  // Global layers: the append rides along with the prologue when both run.
+  pp.append = cache->kind == BEAM_GLOBAL && (stages & BEAM_STAGE_PROLOGUE) && (stages & BEAM_STAGE_APPEND);
   pp.bt = cache->block_table;
   pp.seq_idx = seq_idx;
   pp.max_pages = cache->max_pages_per_seq;
@@ -308,7 +310,7 @@ beam_status beam_attn_prefill_stages(uint32_t stages, const beam_attn_config* cf
   xp.n_tok = n_tok;
   xp.rope_theta = cfg->rope_theta;
   xp.rms_eps = cfg->rms_eps;
-  if ((stages & BEAM_STAGE_APPEND) &&
+  if ((stages & BEAM_STAGE_APPEND) && !pp.append &&
       (st = hip_status(beam::launch_kv_append(xp, s), "prefill append launch")) != BEAM_OK)
     return st;
   return ok();

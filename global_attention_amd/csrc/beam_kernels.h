@@ -19,11 +19,15 @@ struct PrologueParams {
   uint16_t* vw;  // V^T [G][P/64][D][64] (64-position tiles)
   // Cache of the layer: the cached keys of a chunk's first 64-key tile (from
   // start & ~63 up to start) are copied into the workspace.
-  const uint16_t* ck;
-  const uint16_t* cv;
+  uint16_t* ck;
+  uint16_t* cv;
   const int32_t* bt;
   const int32_t* seq_idx;
   int max_pages, n_cache_seqs, window;
+  // Global layers: also write the chunk's K_hat and V into their cache slots
+  // (the append stage, fused; new positions never share a slot with the
+  // cached prefix that attention reads).
+  int append;
   int kind, H, G, P;
   float rope_theta, rms_eps, ssmax_base, ssmax_exp;
 };

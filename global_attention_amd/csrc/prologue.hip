@@ -35,7 +35,7 @@ constexpr int kMaxHeadsPerGroup = 8;
 
 // Cached K_hat row of position t (paged: block-table page; local: ring slot).
 template <int KIND>
-__device__ __forceinline__ const uint16_t* cache_k_row(const PrologueParams& p, int cseq, int g, int t) {
+__device__ __forceinline__ uint16_t* cache_k_row(const PrologueParams& p, int cseq, int g, int t) {
   if (KIND == 1) {
     const int page = p.bt[(size_t)cseq * p.max_pages + (t >> 4)];
     return p.ck + (((size_t)page * p.G + g) * 16 + (t & 15)) * D;
@@ -44,7 +44,7 @@ __device__ __forceinline__ const uint16_t* cache_k_row(const PrologueParams& p, 
 }
 // Cached V^T element (0, t); coordinate d is at [d * stride].
 template <int KIND>
-__device__ __forceinline__ const uint16_t* cache_v_col(const PrologueParams& p, int cseq, int g, int t, int* stride) {
+__device__ __forceinline__ uint16_t* cache_v_col(const PrologueParams& p, int cseq, int g, int t, int* stride) {
   if (KIND == 1) {
     const int page = p.bt[(size_t)cseq * p.max_pages + (t >> 4)];
     *stride = 16;
@@ -119,6 +119,9 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
   // Cache row of the sequence, for the cached positions of the first tile.
   const int cseq = p.seq_idx[seq];
   const bool cache_ok = cseq >= 0 && cseq < p.n_cache_seqs && (local || ((start + 15) >> 4) <= p.max_pages);
+  // Fused append (global layers): chunk positions whose page is in the row.
+  const bool append = KIND == 1 && p.append && cseq >= 0 && cseq < p.n_cache_seqs;
+  auto append_pos = [&](int t) { return append && t >= start && t < start + len && (t >> 4) < p.max_pages; };
 
   if (part == 0) {
     // K_hat: 64 positions x G heads into the workspace [G][P][D].
@@ -173,6 +176,11 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
           HeadFrag f = norm_rope_head(xlo[g], xhi[g], wk_lo, wk_hi, p.rms_eps, local, cs, sn, 1.0f);
           dst0[g * hstride + j] = u32x2{f.lo[0], f.lo[1]};
           dst0[g * hstride + 16 + j] = u32x2{f.hi[0], f.hi[1]};
+          if (append_pos(t)) {
+            u32x2* crow = reinterpret_cast<u32x2*>(cache_k_row<KIND>(p, cseq, g, t));
+            crow[j] = u32x2{f.lo[0], f.lo[1]};
+            crow[16 + j] = u32x2{f.hi[0], f.hi[1]};
+          }
         }
     }
     return;
@@ -223,6 +231,27 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
       for (int q = 0; q < 4; ++q)
         o[q] = (uint32_t)s_v[8 * c + 2 * q][d] | ((uint32_t)s_v[8 * c + 2 * q + 1][d] << 16);
       *reinterpret_cast<u32x4*>(vt + d * 64 + 8 * c) = o;
+    }
+    if (append) {
+      // V^T into the cache pages of the tile, [page][g][d][16]: 16-byte pieces
+      // of 8 positions; pieces at the chunk's edges go element by element.
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int e = tid + 256 * q4;  // (page q, row d, half hf)
+        const int q = e >> 8, d = (e >> 1) & 127, hf = e & 1;
+        const int r0 = 16 * q + 8 * hf, t0 = tile_pos0 + r0;
+        int stride;
+        if (append_pos(t0) && append_pos(t0 + 7)) {
+          u32x4 o;
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            o[k] = (uint32_t)s_v[r0 + 2 * k][d] | ((uint32_t)s_v[r0 + 2 * k + 1][d] << 16);
+          *reinterpret_cast<u32x4*>(cache_v_col<KIND>(p, cseq, g, t0, &stride) + (size_t)d * 16) = o;
+        } else {
+          for (int k = 0; k < 8; ++k)
+            if (append_pos(t0 + k)) cache_v_col<KIND>(p, cseq, g, t0 + k, &stride)[(size_t)d * 16] = s_v[r0 + k][d];
+        }
+      }
     }
   }
 }

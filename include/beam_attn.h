@@ -113,7 +113,9 @@ beam_status beam_kv_append(const beam_attn_config *cfg, const beam_kv_cache *cac
  * seq_idx, start_pos: int32 [n_seqs]. max_chunk_len >= every chunk length.
  * In stream order: prologue (norm, RoPE/SSMax) into the workspace, attention over
  * cached prefix + chunk with the gate applied, then the chunk's K_hat/V are appended
- * to the cache (last, so a local ring is never overwritten while it is read).
+ * to the cache (last, so a local ring is never overwritten while it is read). On a
+ * global (paged) cache the append is done by the prologue itself: the chunk's
+ * positions never share a slot with the prefix that attention reads.
  * workspace: device, >= beam_prefill_workspace_bytes(cfg, n_tok, n_seqs) bytes,
  * 256-byte aligned. */
 beam_status beam_attn_prefill(const beam_attn_config *cfg, const beam_kv_cache *cache,
@@ -147,6 +149,10 @@ beam_status beam_attn_decode(const beam_attn_config *cfg, const beam_kv_cache *c
  * cache append with other work.
  *   prefill: PROLOGUE = norm + RoPE/SSMax into the workspace, ATTENTION =
  *            attention + gate into `out`, APPEND = chunk K_hat/V into the cache.
+ *            On a global cache, PROLOGUE | APPEND in one call fuses the append
+ *            into the prologue; ATTENTION may follow it (the order of the two
+ *            does not matter there). On a local cache APPEND must come after
+ *            ATTENTION when the chunk has a cached prefix.
  *   decode:  PROLOGUE = query norm + RoPE/SSMax, ATTENTION = split-K partials,
  *            COMBINE = merge of the splits + gate into `out`. */
 #define BEAM_STAGE_PROLOGUE 1u

@@ -215,6 +215,38 @@ def test_chunked_prefill_with_cached_prefix(kind):
             pos_done[sq] += n
 
 
+@pytest.mark.parametrize("kind", [O.LOCAL, O.GLOBAL])
+def test_prefill_stage_orders_bit_identical(kind):
+    """The stage splits of a prefill call (including the global layers' fused
+    PROLOGUE|APPEND and the standalone append) give the same output and cache
+    bytes as the single call, for a chunk with an unaligned cached prefix."""
+    import torch
+    inp = _inputs(6, kind, 633)
+    c1 = {k: (v[:333] if v.ndim == 3 else v) for k, v in inp.items()}
+    c2 = {k: (v[333:] if v.ndim == 3 else v) for k, v in inp.items()}
+    orders = [[ga.STAGE_ALL], [ga.STAGE_PROLOGUE, ga.STAGE_ATTENTION, ga.STAGE_APPEND]]
+    if kind == O.GLOBAL:
+        orders.append([ga.STAGE_PROLOGUE | ga.STAGE_APPEND, ga.STAGE_ATTENTION])
+    results = []
+    for order in orders:
+        say(f"[case] stage order kind={kind} order={order}")
+        cache, _ = _cache_for(kind, 6, [633])
+        _run_prefill(kind, [c1], [0], cache, [0])
+        args = (CFG, cache, dev_bf16(c2["q"]), dev_bf16(c2["k"]), dev_bf16(c2["v"]), dev_bf16(c2["q_norm_w"]),
+                dev_bf16(c2["k_norm_w"]), dev_bf16(c2["gate"]), dev_i32([0, 300]), dev_i32([0]), dev_i32([333]), 300)
+        out = torch.empty((300, 48, 128), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(ga.prefill_workspace_bytes(CFG, 300, 1), dtype=torch.uint8, device="cuda")
+        for st in order:
+            ga.prefill(*args, out=out, workspace=ws, stages=st)
+        sync()
+        results.append((host_bits(out), host_bits(cache.k), host_bits(cache.v)))
+    for r in results[1:]:
+        for a_, b_ in zip(results[0], r):
+            assert np.array_equal(a_, b_)
+    ref = _oracle_layer(kind, inp, slice(333, 633), slice(0, 633), np.arange(333, 633), np.arange(633))
+    compare(results[0][0], ref, f"stage orders kind={kind}")
+
+
 # ----------------------------------------------------------------- decode
 
 def _decode_setup(kind, cfg_id, ts):
