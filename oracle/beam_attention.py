@@ -191,13 +191,16 @@ def output_gate(o: np.ndarray, gate_logits: np.ndarray, gate_bias=None) -> np.nd
 
 def attention_layer(kind: int, q_bits, k_bits, v_bits, q_norm_w_bits, k_norm_w_bits,
                     gate_bits, q_pos, k_pos, cfg: Config = Config(), gate_bias=None,
-                    return_pre_gate: bool = False):
+                    return_pre_gate: bool = False, fp8_cache=None):
     """One attention sublayer for the queries of one sequence.
 
     q_bits [nq, H, d]: raw query projections at positions q_pos.
     k_bits, v_bits [nk, G, d]: raw K/V projections of the sequence's history
     (the oracle's own cache model) at positions k_pos, including the queries'
     own tokens. Returns Y [nq, H, d] in float64 (and O if asked).
+    fp8_cache: None, or (k_scale, v_scale, cached_end): keys at positions below
+    cached_end come from an FP8 cache, so their K_hat (after the position op,
+    which is what the cache holds) and V pass through fp8_roundtrip.
     """
     q = bf16_to_f64(q_bits)
     k = bf16_to_f64(k_bits)
@@ -205,9 +208,66 @@ def attention_layer(kind: int, q_bits, k_bits, v_bits, q_norm_w_bits, k_norm_w_b
     qn = rms_norm(q, bf16_to_f64(q_norm_w_bits), cfg.rms_eps)
     kn = rms_norm(k, bf16_to_f64(k_norm_w_bits), cfg.rms_eps)
     qp, kp = position_op(kind, qn, kn, np.asarray(q_pos), np.asarray(k_pos), cfg)
+    if fp8_cache is not None:
+        k_scale, v_scale, cached_end = fp8_cache
+        m = np.asarray(k_pos) < cached_end
+        kp = kp.copy()
+        v = v.copy()
+        kp[m] = fp8_roundtrip(kp[m], k_scale)
+        v[m] = fp8_roundtrip(v[m], v_scale)
     o = attend(kind, qp, kp, v, q_pos, k_pos, cfg)
     y = output_gate(o, bf16_to_f64(gate_bits), gate_bias)
     return (y, o) if return_pre_gate else y
+
+
+# ---------------------------------------------------------------- FP8 KV cache
+# The pages' serving recipes keep the KV cache in FP8 E4M3 ([BEAM-EN] "KV
+# memory: nine growing caches, not 52": 18 KiB per token across the nine
+# global layers in FP8; the German serving article: FP8 E4M3 cache by default).
+# They state no scale convention. Reading used here: one scale per tensor (K
+# and V of a layer), code = nearest E4M3FN value of x / scale with ties to the
+# even code and saturation at +-448, value = decode(code) * scale.
+
+def _e4m3_finite_values() -> np.ndarray:
+    """Values of the non-negative finite E4M3FN codes 0x00..0x7E, in code order
+    (OCP 8-bit float E4M3: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+    bits, subnormals at exponent 0, no infinities, 0x7F is NaN)."""
+    vals = []
+    for c in range(0x7F):
+        e, m = c >> 3, c & 7
+        vals.append(m * 2.0 ** -9 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return np.array(vals)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Float value of E4M3FN codes (uint8); 0x7F and 0xFF decode to NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    mag = c & 0x7F
+    vals = np.append(_e4m3_finite_values(), np.nan)[mag]
+    return np.where(c & 0x80, -vals, vals)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Code of the E4M3FN value nearest to x (ties to the even code, |x| >= 448
+    saturates to +-448, NaN -> 0x7F), found by searching the table of
+    representable values."""
+    x = np.asarray(x, dtype=np.float64)
+    table = _e4m3_finite_values()
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(table, a, side="left"), 0, len(table) - 1)  # first value >= a
+    lo = np.clip(hi - 1, 0, len(table) - 1)
+    d_lo = a - table[lo]
+    d_hi = table[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a >= table[-1], 0x7E, code)
+    code = np.where(np.isnan(x), 0x7F, code).astype(np.uint8)
+    return np.where(np.signbit(x) & ~np.isnan(x), code | 0x80, code).astype(np.uint8)
+
+
+def fp8_roundtrip(x, scale: float) -> np.ndarray:
+    """What an FP8 cache returns for values x stored with `scale`."""
+    return e4m3_decode(e4m3_encode(np.asarray(x, dtype=np.float64) / scale)) * scale
 
 
 def cached_key(kind: int, k_bits, k_norm_w_bits, pos, cfg: Config = Config()) -> np.ndarray:

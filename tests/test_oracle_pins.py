@@ -435,3 +435,78 @@ def test_synth_bf16_rounding_matches_torch():
     ours = f32_to_bf16_bits(x)
     ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(ours, ref)
+
+
+# ---------------------------------------------------------------- FP8 E4M3 cache
+
+def test_e4m3_decode_closed_forms():
+    """Code values fixed by the E4M3FN layout (bias 7, 3 mantissa bits,
+    subnormals at exponent 0, no infinities, 0x7F NaN)."""
+    d = O.e4m3_decode
+    assert d(0x00) == 0.0 and np.signbit(d(0x80))
+    assert d(0x01) == 2.0 ** -9          # smallest subnormal
+    assert d(0x07) == 7 * 2.0 ** -9      # largest subnormal
+    assert d(0x08) == 2.0 ** -6          # smallest normal
+    assert d(0x38) == 1.0
+    assert d(0x39) == 1.125
+    assert d(0x7E) == 448.0 and d(0xFE) == -448.0
+    assert np.isnan(d(0x7F)) and np.isnan(d(0xFF))
+    codes = np.arange(0x7F, dtype=np.uint8)
+    vals = d(codes)
+    assert np.all(np.diff(vals) > 0)                  # code order is value order
+    assert np.array_equal(d(codes | 0x80), -vals)     # sign bit only flips the sign
+
+
+def test_e4m3_encode_matches_torch_within_range():
+    """Nearest-value, ties-to-even encoding, checked against torch's own
+    float8_e4m3fn conversion (an independent implementation) on random values
+    over the whole exponent range and on every midpoint between neighbouring
+    codes (the tie cases), where torch does not overflow (|x| < 464)."""
+    torch = pytest.importorskip("torch")
+    # float32 inputs: torch converts wider floats through float32 first, which
+    # would round a value just below a midpoint onto it.
+    rng = np.random.default_rng(7)
+    vals = O.e4m3_decode(np.arange(0x7F, dtype=np.uint8)).astype(np.float32)
+    mids = (vals[1:] + vals[:-1]) / 2                 # exact in float32
+    x = np.concatenate([
+        (rng.standard_normal(20000) * 10.0 ** rng.uniform(-4, 2.5, 20000)).astype(np.float32),
+        mids, -mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9)), vals, -vals])
+    x = x[np.abs(x) < 464]
+    ours = O.e4m3_encode(x.astype(np.float64))
+    theirs = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, theirs)
+
+
+def test_e4m3_saturation_and_roundtrip():
+    e = O.e4m3_encode
+    assert np.array_equal(e([448.0, 463.9, 464.0, 1e6, np.inf]), [0x7E] * 5)
+    assert np.array_equal(e([-448.0, -1e30, -np.inf]), [0xFE] * 3)
+    assert e(np.nan) == 0x7F
+    codes = np.concatenate([np.arange(0x7F), np.arange(0x80, 0xFF)]).astype(np.uint8)
+    assert np.array_equal(e(O.e4m3_decode(codes)), codes)   # every finite code maps back to itself
+    x = np.linspace(-500, 500, 100001)
+    assert np.all(np.diff(O.e4m3_decode(e(x))) >= 0)         # monotone
+
+
+def test_fp8_cache_attention_reduces_to_bf16_on_grid_values():
+    """With K_hat and V on the E4M3 grid (times the scale) the FP8 cache is
+    exact, so the layer equals the BF16-cache layer; with no cached position
+    the argument changes nothing; off-grid values do change the result."""
+    cfg = O.Config(n_q_heads=4, n_kv_heads=2, head_dim=8, window=4, rms_eps=0.0)
+    rng = np.random.default_rng(3)
+    n = 6
+    q = f32_to_bf16_bits(rng.standard_normal((n, 4, 8)).astype(np.float32))
+    # K rows of equal-magnitude entries: rms = |c|, so K_hat = w * sign(k).
+    k = f32_to_bf16_bits(np.sign(rng.standard_normal((n, 2, 8))).astype(np.float32) * 3.0)
+    v = f32_to_bf16_bits(rng.integers(-8, 9, (n, 2, 8)).astype(np.float32) * 0.25)
+    wq = f32_to_bf16_bits(np.ones(8, np.float32))
+    wk = f32_to_bf16_bits(np.array([1, 0.5, 2, 1.5, 1, 0.75, 1.25, 1], np.float32))
+    g = f32_to_bf16_bits(rng.standard_normal((n, 4, 8)).astype(np.float32))
+    pos = np.arange(n)
+    base = O.attention_layer(O.GLOBAL, q, k, v, wq, wk, g, pos, pos, cfg)
+    on_grid = O.attention_layer(O.GLOBAL, q, k, v, wq, wk, g, pos, pos, cfg, fp8_cache=(0.5, 0.25, n))
+    assert np.array_equal(base, on_grid)
+    none = O.attention_layer(O.GLOBAL, q, k, v, wq, wk, g, pos, pos, cfg, fp8_cache=(0.3, 0.3, 0))
+    assert np.array_equal(base, none)
+    off = O.attention_layer(O.GLOBAL, q, k, v, wq, wk, g, pos, pos, cfg, fp8_cache=(0.3, 0.3, n))
+    assert not np.array_equal(base, off) and np.max(np.abs(off - base)) < 0.2
