@@ -40,10 +40,10 @@ def log(*a):
 
 _CSRC = os.path.join(ROOT, "global_attention_amd", "csrc")
 _KERNEL_SOURCES = {
-    "prefill_attn_kernel<1, 8>": "prefill.hip",
-    "prefill_attn_kernel<0, 4>": "prefill.hip",
-    "decode_split_kernel<1>": "decode.hip",
-    "decode_split_kernel<0>": "decode.hip",
+    "prefill_attn_kernel<1, 8, 0>": "prefill.hip",
+    "prefill_attn_kernel<0, 4, 0>": "prefill.hip",
+    "decode_split_kernel<1, 0>": "decode.hip",
+    "decode_split_kernel<0, 0>": "decode.hip",
     "prefill_prologue_kernel<0>": "prologue.hip",
     "prefill_prologue_kernel<1>": "prologue.hip",
 }
@@ -311,10 +311,10 @@ def main():
         l_ms = r["attn_ms"][0]
         g_flops = FLOP_PER_PAIR * pairs_global(T)
         achieved = g_flops / (g_ms / 1e3) / 1e12
-        rec["roofline"] = {"kernel": "prefill_attn_kernel<1, 8> (global layer)", "bound": "mfma",
+        rec["roofline"] = {"kernel": "prefill_attn_kernel<1, 8, 0> (global layer)", "bound": "mfma",
                            "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                           "traffic": recorded_traffic("prefill_attn_kernel<1, 8>"),
+                           "traffic": recorded_traffic("prefill_attn_kernel<1, 8, 0>"),
                            "avg_launch_ms": round(g_ms, 4), "flop_per_launch": g_flops}
         l_flops = FLOP_PER_PAIR * pairs_local(T)
         rec["prefill_layers"] = {
@@ -331,9 +331,9 @@ def main():
             "value": round(g["gbs_call"], 1), "unit": "GB/s",
             "frac_of_hbm_peak": round(g["gbs_call"] / PEAK_HBM_GBS, 4),
             "global_bytes": g["bytes"], "global_ms_per_call": round(g["ms_per_call"], 4),
-            "roofline": {"kernel": "decode_split_kernel<1>", "bound": "hbm", "achieved": round(g["gbs_split"], 1),
+            "roofline": {"kernel": "decode_split_kernel<1, 0>", "bound": "hbm", "achieved": round(g["gbs_split"], 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(g["gbs_split"] / PEAK_HBM_GBS, 4),
-                         "traffic": recorded_traffic("decode_split_kernel<1>"),
+                         "traffic": recorded_traffic("decode_split_kernel<1, 0>"),
                          "avg_launch_ms": round(g["split_ms"], 4), "bytes_per_launch": g["bytes"]},
             "local": {"bytes": dres["local"]["bytes"], "ms_per_call": round(dres["local"]["ms_per_call"], 4),
                       "gbs_call": round(dres["local"]["gbs_call"], 1),

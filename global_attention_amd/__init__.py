@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(_PKG, "libbeam_attn.so")
 
 LOCAL = 0
 GLOBAL = 1
+KV_BF16 = 0
+KV_FP8_E4M3 = 1
 
 STAGE_PROLOGUE = 1
 STAGE_ATTENTION = 2
@@ -49,7 +51,8 @@ class CCache(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("page_size", ctypes.c_int32), ("n_pages", ctypes.c_int32),
                 ("block_table", ctypes.c_void_p), ("max_pages_per_seq", ctypes.c_int32),
-                ("n_seqs", ctypes.c_int32)]
+                ("n_seqs", ctypes.c_int32), ("dtype", ctypes.c_int32), ("k_scale", ctypes.c_float),
+                ("v_scale", ctypes.c_float)]
 
 
 @dataclass
@@ -134,44 +137,54 @@ def _need(t, dtype, shape=None, name="tensor"):
 
 @dataclass
 class KVCache:
-    """One layer's cache as torch device tensors (layouts in include/beam_attn.h)."""
+    """One layer's cache as torch device tensors (layouts in include/beam_attn.h).
+    dtype KV_BF16 holds bfloat16 tensors, KV_FP8_E4M3 uint8 codes with the
+    per-tensor scales k_scale / v_scale."""
     kind: int
     k: object
     v: object
     block_table: object = None  # int32 [n_seqs][max_pages] (global)
     n_pages: int = 0
     page_size: int = 16
+    dtype: int = KV_BF16
+    k_scale: float = 1.0
+    v_scale: float = 1.0
     _c: CCache = field(default=None, repr=False)
 
     @staticmethod
-    def allocate_global(cfg: Config, n_pages: int, block_table, device="cuda", fill=None):
+    def _alloc(shape_k, shape_v, dtype, device, fill):
         import torch
-        shape_k = (n_pages, cfg.n_kv_heads, 16, cfg.head_dim)
-        shape_v = (n_pages, cfg.n_kv_heads, cfg.head_dim, 16)
-        k = torch.empty(shape_k, dtype=torch.bfloat16, device=device)
-        v = torch.empty(shape_v, dtype=torch.bfloat16, device=device)
+        tdt = torch.bfloat16 if dtype == KV_BF16 else torch.uint8
+        k = torch.empty(shape_k, dtype=tdt, device=device)
+        v = torch.empty(shape_v, dtype=tdt, device=device)
         if fill is not None:
-            k.view(torch.int16).fill_(fill)
-            v.view(torch.int16).fill_(fill)
-        bt = block_table.to(device=device, dtype=torch.int32).contiguous()
-        return KVCache(GLOBAL, k, v, bt, n_pages)
+            view = torch.int16 if dtype == KV_BF16 else torch.uint8
+            k.view(view).fill_(fill)
+            v.view(view).fill_(fill)
+        return k, v
 
     @staticmethod
-    def allocate_local(cfg: Config, n_seqs: int, device="cuda", fill=None):
+    def allocate_global(cfg: Config, n_pages: int, block_table, device="cuda", fill=None, dtype=KV_BF16,
+                        k_scale=1.0, v_scale=1.0):
+        k, v = KVCache._alloc((n_pages, cfg.n_kv_heads, 16, cfg.head_dim), (n_pages, cfg.n_kv_heads, cfg.head_dim, 16),
+                              dtype, device, fill)
         import torch
-        k = torch.empty((n_seqs, cfg.n_kv_heads, cfg.window, cfg.head_dim), dtype=torch.bfloat16, device=device)
-        v = torch.empty((n_seqs, cfg.n_kv_heads, cfg.head_dim, cfg.window), dtype=torch.bfloat16, device=device)
-        if fill is not None:
-            k.view(torch.int16).fill_(fill)
-            v.view(torch.int16).fill_(fill)
-        return KVCache(LOCAL, k, v, None, 0)
+        bt = block_table.to(device=device, dtype=torch.int32).contiguous()
+        return KVCache(GLOBAL, k, v, bt, n_pages, 16, dtype, float(k_scale), float(v_scale))
+
+    @staticmethod
+    def allocate_local(cfg: Config, n_seqs: int, device="cuda", fill=None, dtype=KV_BF16, k_scale=1.0, v_scale=1.0):
+        k, v = KVCache._alloc((n_seqs, cfg.n_kv_heads, cfg.window, cfg.head_dim),
+                              (n_seqs, cfg.n_kv_heads, cfg.head_dim, cfg.window), dtype, device, fill)
+        return KVCache(LOCAL, k, v, None, 0, 16, dtype, float(k_scale), float(v_scale))
 
     def c(self) -> CCache:
         if self.kind == GLOBAL:
             bt = self.block_table
             return CCache(GLOBAL, self.k.data_ptr(), self.v.data_ptr(), self.page_size, self.n_pages,
-                          bt.data_ptr(), bt.shape[1], bt.shape[0])
-        return CCache(LOCAL, self.k.data_ptr(), self.v.data_ptr(), 0, 0, None, 0, self.k.shape[0])
+                          bt.data_ptr(), bt.shape[1], bt.shape[0], self.dtype, self.k_scale, self.v_scale)
+        return CCache(LOCAL, self.k.data_ptr(), self.v.data_ptr(), 0, 0, None, 0, self.k.shape[0], self.dtype,
+                      self.k_scale, self.v_scale)
 
 
 def prefill_workspace_bytes(cfg: Config, n_tok: int, n_seqs: int) -> int:

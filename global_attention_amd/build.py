@@ -50,8 +50,21 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    _check_kernel_stubs(tmp)
     os.replace(tmp, LIB)
     return LIB
+
+
+def _check_kernel_stubs(lib: str) -> None:
+    """Every kernel the host code launches must have its launch stub in the
+    library: the compiler's host pass can drop one without an error."""
+    try:
+        r = subprocess.run(["nm", "-D", "--undefined-only", lib], capture_output=True, text=True)
+    except FileNotFoundError:
+        return
+    missing = [l.split()[-1] for l in r.stdout.splitlines() if "__device_stub__" in l]
+    if missing:
+        raise RuntimeError(f"kernel launch stubs missing from {lib}: {missing}")
 
 
 if __name__ == "__main__":

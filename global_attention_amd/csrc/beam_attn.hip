@@ -45,6 +45,11 @@ beam_status check_cfg(const beam_attn_config* c) {
 beam_status check_cache(const beam_kv_cache* kv) {
   if (!kv) return fail(BEAM_E_NULL, "cache is NULL");
   if (kv->kind != BEAM_LOCAL && kv->kind != BEAM_GLOBAL) return fail(BEAM_E_RANGE, "cache kind must be 0 or 1");
+  if (kv->dtype != BEAM_KV_BF16 && kv->dtype != BEAM_KV_FP8_E4M3)
+    return fail(BEAM_E_UNSUPPORTED, "cache dtype must be BEAM_KV_BF16 or BEAM_KV_FP8_E4M3");
+  if (kv->dtype == BEAM_KV_FP8_E4M3 &&
+      !(kv->k_scale > 0.f && kv->v_scale > 0.f && kv->k_scale < 3.0e38f && kv->v_scale < 3.0e38f))
+    return fail(BEAM_E_RANGE, "FP8 cache scales must be finite and positive");
   if (!kv->k || !kv->v) return fail(BEAM_E_NULL, "cache k/v is NULL");
   if (kv->n_seqs <= 0) return fail(BEAM_E_RANGE, "cache n_seqs must be positive");
   if (kv->kind == BEAM_GLOBAL) {
@@ -191,6 +196,9 @@ beam_status beam_kv_append(const beam_attn_config* cfg, const beam_kv_cache* cac
   p.n_tok = n_tok;
   p.rope_theta = cfg->rope_theta;
   p.rms_eps = cfg->rms_eps;
+  p.kv_fp8 = cache->dtype == BEAM_KV_FP8_E4M3;
+  p.k_scale = cache->k_scale;
+  p.v_scale = cache->v_scale;
   if ((st = hip_status(beam::launch_kv_append(p, (hipStream_t)stream), "kv_append launch")) != BEAM_OK) return st;
   return ok();
 }
@@ -246,6 +254,9 @@ beam_status beam_attn_prefill_stages(uint32_t stages, const beam_attn_config* cf
   pp.cv = static_cast<uint16_t*>(cache->v);
   // Global layers: the append rides along with the prologue when both run.
   pp.append = cache->kind == BEAM_GLOBAL && (stages & BEAM_STAGE_PROLOGUE) && (stages & BEAM_STAGE_APPEND);
+  pp.kv_fp8 = cache->dtype == BEAM_KV_FP8_E4M3;
+  pp.k_scale = cache->k_scale;
+  pp.v_scale = cache->v_scale;
   pp.bt = cache->block_table;
   pp.seq_idx = seq_idx;
   pp.max_pages = cache->max_pages_per_seq;
@@ -286,6 +297,9 @@ beam_status beam_attn_prefill_stages(uint32_t stages, const beam_attn_config* cf
   ap.n_seqs = n_seqs;
   ap.n_qtiles = (max_chunk_len + beam::prefill_block_queries(cache->kind) - 1) / beam::prefill_block_queries(cache->kind);
   ap.P = (int)ws.P;
+  ap.kv_fp8 = cache->dtype == BEAM_KV_FP8_E4M3;
+  ap.k_scale = cache->k_scale;
+  ap.v_scale = cache->v_scale;
   if ((stages & BEAM_STAGE_ATTENTION) &&
       (st = hip_status(beam::launch_prefill_attn(ap, s), "prefill attention launch")) != BEAM_OK)
     return st;
@@ -310,6 +324,9 @@ beam_status beam_attn_prefill_stages(uint32_t stages, const beam_attn_config* cf
   xp.n_tok = n_tok;
   xp.rope_theta = cfg->rope_theta;
   xp.rms_eps = cfg->rms_eps;
+  xp.kv_fp8 = cache->dtype == BEAM_KV_FP8_E4M3;
+  xp.k_scale = cache->k_scale;
+  xp.v_scale = cache->v_scale;
   if ((stages & BEAM_STAGE_APPEND) && !pp.append &&
       (st = hip_status(beam::launch_kv_append(xp, s), "prefill append launch")) != BEAM_OK)
     return st;
@@ -369,6 +386,7 @@ beam_status beam_attn_decode_stages(uint32_t stages, const beam_attn_config* cfg
   qp_.rms_eps = cfg->rms_eps;
   qp_.ssmax_base = cfg->ssmax_base;
   qp_.ssmax_exp = cfg->ssmax_exp;
+  qp_.k_scale = cache->dtype == BEAM_KV_FP8_E4M3 ? cache->k_scale : 1.f;
   if ((stages & BEAM_STAGE_PROLOGUE) &&
       (st = hip_status(beam::launch_decode_q_prologue(qp_, s), "decode prologue launch")) != BEAM_OK)
     return st;
@@ -391,6 +409,7 @@ beam_status beam_attn_decode_stages(uint32_t stages, const beam_attn_config* cfg
   dp.G = cfg->n_kv_heads;
   dp.n_splits = ws.n_splits;
   dp.kpw = ws.split_keys / 4;
+  dp.kv_fp8 = cache->dtype == BEAM_KV_FP8_E4M3;
   if ((stages & BEAM_STAGE_ATTENTION) &&
       (st = hip_status(beam::launch_decode_split(dp, n_seqs, s), "decode split launch")) != BEAM_OK)
     return st;
@@ -408,6 +427,7 @@ beam_status beam_attn_decode_stages(uint32_t stages, const beam_attn_config* cfg
   cp.H = cfg->n_q_heads;
   cp.n_splits = ws.n_splits;
   cp.split_keys = ws.split_keys;
+  cp.v_scale = cache->dtype == BEAM_KV_FP8_E4M3 ? cache->v_scale : 1.f;
   if ((stages & BEAM_STAGE_COMBINE) &&
       (st = hip_status(beam::launch_decode_combine(cp, n_seqs, s), "decode combine launch")) != BEAM_OK)
     return st;

@@ -41,6 +41,48 @@ __device__ __forceinline__ float sum_bf16x2(uint32_t pair, float acc) {
                                          false);
 }
 
+// ---- FP8 E4M3 (OCP E4M3FN) cache codes ----
+// Code of the E4M3FN value nearest to x: ties to the even code, |x| >= 448
+// saturates to +-448, NaN -> 0x7F. Normal range: round the fp32 exponent and
+// top 3 mantissa bits to nearest even in one integer step (a carry moves into
+// the exponent), then rebias 127 -> 7. Below 2^-6 the grid is k * 2^-9.
+__device__ __forceinline__ uint32_t fp8_e4m3_encode(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (a != a) return 0x7Fu;
+  uint32_t code;
+  if (a >= 448.f) {
+    code = 0x7Eu;
+  } else if (a < 0.015625f) {
+    code = (uint32_t)__builtin_rintf(a * 512.f);  // 0..8; 8 is the smallest normal, 2^-6
+  } else {
+    const uint32_t ua = __float_as_uint(a);
+    code = ((ua + 0x7FFFFu + ((ua >> 20) & 1u)) >> 20) - (120u << 3);
+    if (code > 0x7Eu) code = 0x7Eu;
+  }
+  return code | sign;
+}
+// Four codes (bytes of w, low first) -> four bf16 (exact: every E4M3 value is a bf16 value).
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
+  const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+// Four floats -> four codes of x / scale, packed low byte first.
+__device__ __forceinline__ uint32_t fp8x4_encode(const float (&x)[4], float scale) {
+  return fp8_e4m3_encode(x[0] / scale) | (fp8_e4m3_encode(x[1] / scale) << 8) | (fp8_e4m3_encode(x[2] / scale) << 16) |
+         (fp8_e4m3_encode(x[3] / scale) << 24);
+}
+// Four codes -> four floats (exact).
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float (&f)[4]) {
+  const u32x2 b = fp8x4_to_bf16x4(w);
+  f[0] = bf16lo(b[0]);
+  f[1] = bf16hi(b[0]);
+  f[2] = bf16lo(b[1]);
+  f[3] = bf16hi(b[1]);
+}
+
 // Visibility of key position s to query position t: causal, plus the window on
 // local layers (window counts the current token, so window-1 earlier ones).
 __device__ __forceinline__ bool visible(int kind, int window, int t, int s) {
@@ -93,11 +135,18 @@ struct HeadFrag {
   uint32_t hi[2];
 };
 
-__device__ __forceinline__ HeadFrag norm_rope_head(u32x2 xlo, u32x2 xhi, u32x2 wlo, u32x2 whi,
-                                                   float eps, bool do_rope, const float* cs,
-                                                   const float* sn, float post_scale) {
-  float a[4] = {bf16lo(xlo[0]), bf16hi(xlo[0]), bf16lo(xlo[1]), bf16hi(xlo[1])};
-  float b[4] = {bf16lo(xhi[0]), bf16hi(xhi[0]), bf16lo(xhi[1]), bf16hi(xhi[1])};
+// The fp32 values before the final scale and rounding: a = lo coordinates,
+// b = hi coordinates.
+__device__ __forceinline__ void norm_rope_f32(u32x2 xlo, u32x2 xhi, u32x2 wlo, u32x2 whi, float eps, bool do_rope,
+                                              const float* cs, const float* sn, float (&a)[4], float (&b)[4]) {
+  a[0] = bf16lo(xlo[0]);
+  a[1] = bf16hi(xlo[0]);
+  a[2] = bf16lo(xlo[1]);
+  a[3] = bf16hi(xlo[1]);
+  b[0] = bf16lo(xhi[0]);
+  b[1] = bf16hi(xhi[0]);
+  b[2] = bf16lo(xhi[1]);
+  b[3] = bf16hi(xhi[1]);
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) ss += a[e] * a[e] + b[e] * b[e];
@@ -118,6 +167,13 @@ __device__ __forceinline__ HeadFrag norm_rope_head(u32x2 xlo, u32x2 xhi, u32x2 w
       b[e] = x2 * cs[e] + x1 * sn[e];
     }
   }
+}
+
+__device__ __forceinline__ HeadFrag norm_rope_head(u32x2 xlo, u32x2 xhi, u32x2 wlo, u32x2 whi,
+                                                   float eps, bool do_rope, const float* cs,
+                                                   const float* sn, float post_scale) {
+  float a[4], b[4];
+  norm_rope_f32(xlo, xhi, wlo, whi, eps, do_rope, cs, sn, a, b);
   HeadFrag f;
   f.lo[0] = pack_bf16x2(a[0] * post_scale, a[1] * post_scale);
   f.lo[1] = pack_bf16x2(a[2] * post_scale, a[3] * post_scale);

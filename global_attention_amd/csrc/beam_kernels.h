@@ -30,6 +30,9 @@ struct PrologueParams {
   int append;
   int kind, H, G, P;
   float rope_theta, rms_eps, ssmax_base, ssmax_exp;
+  // FP8 E4M3 cache: ck/cv hold one-byte codes at the same element offsets.
+  int kv_fp8;
+  float k_scale, v_scale;
 };
 
 struct AppendParams {
@@ -48,6 +51,9 @@ struct AppendParams {
   int n_cache_seqs;  // rows of the block table (global) or rings (local)
   int kind, G, window, n_tok;
   float rope_theta, rms_eps;
+  // FP8 E4M3 cache: ck/cv hold one-byte codes at the same element offsets.
+  int kv_fp8;
+  float k_scale, v_scale;
 };
 
 struct DecodeQParams {
@@ -57,6 +63,7 @@ struct DecodeQParams {
   uint16_t* qp;  // Q' [n_seqs][H][D]
   int kind, H, n_seqs;
   float rope_theta, rms_eps, ssmax_base, ssmax_exp;
+  float k_scale;  // FP8 cache: K scale folded into Q' (1 for bf16)
 };
 
 // Prefill attention tiling: 32 queries per wavefront; 8 wavefronts per block
@@ -82,6 +89,9 @@ struct PrefillParams {
   int max_pages;
   int n_cache_seqs;
   int kind, window, H, G, n_seqs, n_qtiles, P;
+  // FP8 E4M3 cache: a cached prefix is read as codes and dequantised to bf16.
+  int kv_fp8;
+  float k_scale, v_scale;
 };
 
 struct DecodeParams {
@@ -97,6 +107,7 @@ struct DecodeParams {
   int n_cache_seqs;
   int max_pos;
   int kind, window, H, G, n_splits, kpw;
+  int kv_fp8;  // the cache holds FP8 E4M3 codes (one byte per element)
 };
 
 struct CombineParams {
@@ -108,6 +119,7 @@ struct CombineParams {
   uint16_t* out;
   int max_pos;
   int kind, window, H, n_splits, split_keys;
+  float v_scale;  // FP8 cache: V scale applied to O (1 for bf16)
 };
 
 // Host-side launchers (each defined next to its kernel). They return the

@@ -12,7 +12,10 @@
 // v_mfma_f32_16x16x32_bf16 (padded to 16), so every K/V byte is read from HBM
 // once for all of them. K pages are token-major, V pages are stored
 // transposed (d-major), so both MFMA operands are plain vector loads straight
-// from HBM into registers; nothing is staged in LDS on the hot path. The four
+// from HBM into registers; nothing is staged in LDS on the hot path. An FP8
+// E4M3 cache is read the same way at one byte per element; its codes convert
+// exactly to bf16 in registers (the K scale rides on Q', the V scale on the
+// output). The four
 // waves merge their (max, sum, acc) triples through LDS; a second kernel merges
 // the splits by log-sum-exp and applies the output gate.
 #include "beam_device.h"
@@ -22,12 +25,33 @@ namespace beam {
 
 constexpr float kDecRescale = 8.0f;
 
-struct DecodeStep {
+// One step's operands as loaded: bf16 (8 K coordinates, 4 V keys per lane and
+// block) or FP8 E4M3 codes (the same elements at one byte each).
+template <int FP8>
+struct DecodeStep;
+template <>
+struct DecodeStep<0> {
   u32x4 k[2][4];  // [page][d-block of 32]
   u32x2 v[2][8];  // [page][d-block of 16]
 };
+template <>
+struct DecodeStep<1> {
+  u32x2 k[2][4];
+  uint32_t v[2][8];
+};
 
-template <int KIND>
+// bf16 MFMA operands of a step (FP8 codes convert exactly).
+__device__ __forceinline__ u32x4 k_operand(const DecodeStep<0>& st, int X, int kk) { return st.k[X][kk]; }
+__device__ __forceinline__ u32x4 k_operand(const DecodeStep<1>& st, int X, int kk) {
+  const u32x2 lo = fp8x4_to_bf16x4(st.k[X][kk][0]), hi = fp8x4_to_bf16x4(st.k[X][kk][1]);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+__device__ __forceinline__ u32x2 v_operand(const DecodeStep<0>& st, int X, int db) { return st.v[X][db]; }
+__device__ __forceinline__ u32x2 v_operand(const DecodeStep<1>& st, int X, int db) {
+  return fp8x4_to_bf16x4(st.v[X][db]);
+}
+
+template <int KIND, int FP8>
 __global__ void __launch_bounds__(256, 2) decode_split_kernel(DecodeParams p) {
   const int hpg = p.H / p.G;
   int b = blockIdx.x;
@@ -68,39 +92,52 @@ __global__ void __launch_bounds__(256, 2) decode_split_kernel(DecodeParams p) {
   const int32_t* bt_row = p.bt + (size_t)cseq * p.max_pages;
   const size_t ring = (size_t)cseq * p.G + g;
 
-  // Base pointers of the 16-key group starting at logical key kg.
-  auto kbase = [&](int kg) -> const uint16_t* {
-    if (local) return p.ck + (ring * p.window + kg) * D;
+  // Element offsets of the 16-key group starting at logical key kg (bytes
+  // for an FP8 cache, which keeps the same element layout).
+  auto kbase = [&](int kg) -> size_t {
+    if (local) return (ring * p.window + kg) * D;
     int page = bt_row[kg >> 4];
-    return p.ck + ((size_t)page * p.G + g) * 16 * D;
+    return ((size_t)page * p.G + g) * 16 * D;
   };
-  auto vbase = [&](int kg, int* dstride) -> const uint16_t* {
+  auto vbase = [&](int kg, int* dstride) -> size_t {
     if (local) {
       *dstride = p.window;
-      return p.cv + ring * D * p.window + kg;
+      return ring * D * p.window + kg;
     }
     *dstride = 16;
     int page = bt_row[kg >> 4];
-    return p.cv + ((size_t)page * p.G + g) * D * 16;
+    return ((size_t)page * p.G + g) * D * 16;
   };
-  auto load_step = [&](int kb, DecodeStep& st) {
+  auto load_step = [&](int kb, DecodeStep<FP8>& st) {
 #pragma unroll
     for (int X = 0; X < 2; ++X) {
       const int kg = kb + 16 * X;
       if (kg < k1) {
-        const uint16_t* kp = kbase(kg) + nn * D + 8 * q;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) st.k[X][kk] = *reinterpret_cast<const u32x4*>(kp + 32 * kk);
+        const size_t ke = kbase(kg) + nn * D + 8 * q;
         int ds;
-        const uint16_t* vp = vbase(kg, &ds) + 4 * q;
+        const size_t ve = vbase(kg, &ds) + 4 * q;
+        if constexpr (FP8) {
+          const uint8_t* kp = reinterpret_cast<const uint8_t*>(p.ck) + ke;
 #pragma unroll
-        for (int db = 0; db < 8; ++db)
-          st.v[X][db] = *reinterpret_cast<const u32x2*>(vp + (size_t)(16 * db + nn) * ds);
+          for (int kk = 0; kk < 4; ++kk) st.k[X][kk] = *reinterpret_cast<const u32x2*>(kp + 32 * kk);
+          const uint8_t* vp = reinterpret_cast<const uint8_t*>(p.cv) + ve;
+#pragma unroll
+          for (int db = 0; db < 8; ++db)
+            st.v[X][db] = *reinterpret_cast<const uint32_t*>(vp + (size_t)(16 * db + nn) * ds);
+        } else {
+          const uint16_t* kp = p.ck + ke;
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) st.k[X][kk] = *reinterpret_cast<const u32x4*>(kp + 32 * kk);
+          const uint16_t* vp = p.cv + ve;
+#pragma unroll
+          for (int db = 0; db < 8; ++db)
+            st.v[X][db] = *reinterpret_cast<const u32x2*>(vp + (size_t)(16 * db + nn) * ds);
+        }
       } else {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) st.k[X][kk] = u32x4{0u, 0u, 0u, 0u};
+        for (int kk = 0; kk < 4; ++kk) st.k[X][kk] = {};
 #pragma unroll
-        for (int db = 0; db < 8; ++db) st.v[X][db] = u32x2{0u, 0u};
+        for (int db = 0; db < 8; ++db) st.v[X][db] = {};
       }
     }
   };
@@ -111,12 +148,17 @@ __global__ void __launch_bounds__(256, 2) decode_split_kernel(DecodeParams p) {
   float m_run = kNegInf;
   float l_run = 0.f;
 
-  DecodeStep cur, nxt;
+  DecodeStep<FP8> cur, nxt;
   if (k0 < k1) load_step(k0, cur);
   for (int kb = k0; kb < k1; kb += 32) {
     const bool has_next = kb + 32 < k1;
     if (has_next) load_step(kb + 32, nxt);
 
+    u32x2 vop[2][8];
+#pragma unroll
+    for (int X = 0; X < 2; ++X)
+#pragma unroll
+      for (int db = 0; db < 8; ++db) vop[X][db] = v_operand(cur, X, db);
     const bool partial = kb + 32 > k1;
     if (partial) {
       // Zero V of keys past the end (their pages may hold stale or unwritten data).
@@ -125,10 +167,10 @@ __global__ void __launch_bounds__(256, 2) decode_split_kernel(DecodeParams p) {
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
           const int key0 = kb + 16 * X + 4 * q;
-          u32x2 v = cur.v[X][db];
+          u32x2 v = vop[X][db];
           uint32_t m0 = (key0 + 0 < k1 ? 0xffffu : 0u) | (key0 + 1 < k1 ? 0xffff0000u : 0u);
           uint32_t m1 = (key0 + 2 < k1 ? 0xffffu : 0u) | (key0 + 3 < k1 ? 0xffff0000u : 0u);
-          cur.v[X][db] = u32x2{v[0] & m0, v[1] & m1};
+          vop[X][db] = u32x2{v[0] & m0, v[1] & m1};
         }
     }
 
@@ -138,7 +180,8 @@ __global__ void __launch_bounds__(256, 2) decode_split_kernel(DecodeParams p) {
       s[X] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        s[X] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.k[X][kk]), as_bf16x8(qf[kk]), s[X], 0, 0, 0);
+        s[X] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k_operand(cur, X, kk)), as_bf16x8(qf[kk]), s[X], 0,
+                                                       0, 0);
     }
     // lane holds head nn, keys kb + 16X + 4q + i
     if (partial) {
@@ -179,7 +222,7 @@ __global__ void __launch_bounds__(256, 2) decode_split_kernel(DecodeParams p) {
                            pack_bf16x2(e[6], e[7])};
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const u32x4 a = u32x4{cur.v[0][db][0], cur.v[0][db][1], cur.v[1][db][0], cur.v[1][db][1]};
+      const u32x4 a = u32x4{vop[0][db][0], vop[0][db][1], vop[1][db][0], vop[1][db][1]};
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(pf), o[db], 0, 0, 0);
     }
     if (has_next) cur = nxt;
@@ -251,7 +294,7 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(CombineParams p) {
       A += sc * p.part_acc[(row0 + s) * D + d];
     }
   }
-  const float o = L > 0.f ? A / L : 0.f;
+  const float o = L > 0.f ? A / L * p.v_scale : 0.f;
   const float bias = p.gate_bias ? p.gate_bias[h] : 0.f;
   const float gz = bf16f(p.gate[idx]) + bias;
   const float y = o / (1.f + __expf(-gz));
@@ -262,10 +305,15 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(CombineParams p) {
 
 hipError_t launch_decode_split(const DecodeParams& p, int n_seqs, hipStream_t s) {
   const long long blocks = (long long)n_seqs * p.G * p.n_splits;
-  if (p.kind == 0)
-    hipLaunchKernelGGL(decode_split_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  const dim3 grid((unsigned)blocks), block(256);
+  if (p.kind == 0 && !p.kv_fp8)
+    hipLaunchKernelGGL((decode_split_kernel<0, 0>), grid, block, 0, s, p);
+  else if (p.kind == 0)
+    hipLaunchKernelGGL((decode_split_kernel<0, 1>), grid, block, 0, s, p);
+  else if (!p.kv_fp8)
+    hipLaunchKernelGGL((decode_split_kernel<1, 0>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL(decode_split_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((decode_split_kernel<1, 1>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 

@@ -97,6 +97,15 @@ struct KeySource {
 };
 
 // ---------------------------------------------------------------- DMA path
+// One 16-byte-per-lane global -> LDS DMA (global_load_lds_dwordx4): lane l's
+// 16 bytes land at dst + 16 l (dst must be wave-uniform). Kept a plain
+// function: the kernel templates reach it from lambdas, and clang's host pass
+// drops the stub of a second kernel instantiation when a function template on
+// that path names the target builtin itself.
+__device__ __forceinline__ void lds_dma16(const uint16_t* src, uint16_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
 // Element offsets (relative to the tile's first key in the workspace) of the
 // chunks this lane moves with each of its DMA instructions, and the LDS
 // offset of each instruction's 1 KiB.
@@ -107,6 +116,17 @@ struct DmaPlan {
   uint32_t v_src[N];
   int k_lds[N];
   int v_lds[N];
+  // DMA of the workspace tile whose first key is key0 (K rows kw, V^T tiles vw).
+  __device__ __forceinline__ void copy(const uint16_t* kw, const uint16_t* vw, int ws_off, int key0, uint16_t* sK,
+                                       uint16_t* sV) const {
+    const uint16_t* kb = kw + (uint32_t)((key0 + ws_off) * D);
+    const uint16_t* vb = vw + (uint32_t)((key0 + ws_off) * D);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      lds_dma16(kb + k_src[i], sK + k_lds[i]);
+      lds_dma16(vb + v_src[i], sV + v_lds[i]);
+    }
+  }
 };
 
 template <int NW>
@@ -128,17 +148,6 @@ __device__ __forceinline__ DmaPlan<NW> make_dma_plan(int w, int lane) {
   return pl;
 }
 
-template <int NW>
-__device__ __forceinline__ void dma_tile(const KeySource& ks, const DmaPlan<NW>& pl, int key0, uint16_t* sK,
-                                         uint16_t* sV) {
-  const uint16_t* kb = ks.kw + (uint32_t)((key0 + ks.ws_off) * D);
-  const uint16_t* vb = ks.vw + (uint32_t)((key0 + ks.ws_off) * D);
-#pragma unroll
-  for (int i = 0; i < DmaPlan<NW>::N; ++i) {
-    __builtin_amdgcn_global_load_lds(kb + pl.k_src[i], sK + pl.k_lds[i], 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vb + pl.v_src[i], sV + pl.v_lds[i], 16, 0, 0);
-  }
-}
 
 // Address of cached K row s and of cached V^T element (d, s) (s < start).
 __device__ __forceinline__ const uint16_t* k_row_src(const KeySource& ks, int s) {
@@ -161,17 +170,73 @@ __device__ __forceinline__ void dma_tile_prefix(const KeySource& ks, int w, int 
     const int kI = w * DmaPlan<NW>::N + i;
     const int m = 4 * kI + (lane >> 4);
     const int c = (lane & 15) ^ (m & 7);
-    __builtin_amdgcn_global_load_lds(k_row_src(ks, key0 + krow_key(m)) + 8 * c, sK + kI * 512, 16, 0, 0);
+    lds_dma16(k_row_src(ks, key0 + krow_key(m)) + 8 * c, sK + kI * 512);
 
     const int vI = w * DmaPlan<NW>::N + i;
     const int d = 8 * vI + (lane >> 3);
     const int cv = (lane & 7) ^ (d & 7);
-    __builtin_amdgcn_global_load_lds(v_elem_src(ks, d, key0 + 8 * cv), sV + vI * 512, 16, 0, 0);
+    lds_dma16(v_elem_src(ks, d, key0 + 8 * cv), sV + vI * 512);
+  }
+}
+
+// Prefix tile from an FP8 E4M3 cache: the DMA engine cannot convert, so each
+// thread loads 16 codes of a K row (or of a V^T row), dequantises them to bf16
+// (decode(code) * scale, one rounding) and stores the two 16-byte chunks at
+// their swizzled LDS positions. k8/v8 are the byte bases of the (sequence,
+// KV head) in the cache, at the element offsets the bf16 layout uses.
+struct Fp8Prefix {
+  const uint8_t* k8;
+  const uint8_t* v8;
+  const int32_t* bt_row;
+  size_t page_stride;  // bytes per page of the paged cache (all KV heads)
+  int kind, window;
+  float k_scale, v_scale;
+};
+
+__device__ __forceinline__ u32x4 fp8x8_dequant_bf16(uint32_t w0, uint32_t w1, float scale) {
+  float a[4], b[4];
+  fp8x4_to_f32(w0, a);
+  fp8x4_to_f32(w1, b);
+  return u32x4{pack_bf16x2(a[0] * scale, a[1] * scale), pack_bf16x2(a[2] * scale, a[3] * scale),
+               pack_bf16x2(b[0] * scale, b[1] * scale), pack_bf16x2(b[2] * scale, b[3] * scale)};
+}
+
+template <int NW>
+__device__ __forceinline__ void fetch_prefix_fp8(const Fp8Prefix& fp, int tid, int key0, uint16_t* sK, uint16_t* sV) {
+  constexpr int R = 8 / NW;  // 16-byte loads per thread, for K and for V
+  u32x4 kc[R], vc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int id = tid + 64 * NW * r;  // 0..511
+    {
+      const int m = id >> 3, c2 = id & 7;  // LDS row m, codes 16c2 .. 16c2+15
+      const int s = key0 + krow_key(m);
+      const uint8_t* src = fp.kind == 1 ? fp.k8 + fp.bt_row[s >> 4] * fp.page_stride + (size_t)((s & 15) * D)
+                                        : fp.k8 + (size_t)((s % fp.window) * D);
+      kc[r] = *reinterpret_cast<const u32x4*>(src + 16 * c2);
+    }
+    {
+      const int d = id >> 2, c2 = id & 3;  // V^T row d, keys 16c2 .. 16c2+15 (one page / no ring wrap)
+      const int s = key0 + 16 * c2;
+      const uint8_t* src = fp.kind == 1 ? fp.v8 + fp.bt_row[s >> 4] * fp.page_stride + (size_t)(d * 16)
+                                        : fp.v8 + (size_t)(d * fp.window + s % fp.window);
+      vc[r] = *reinterpret_cast<const u32x4*>(src);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int id = tid + 64 * NW * r;
+    const int m = id >> 3, ck = id & 7;
+    *reinterpret_cast<u32x4*>(sK + k_off(m, 2 * ck)) = fp8x8_dequant_bf16(kc[r][0], kc[r][1], fp.k_scale);
+    *reinterpret_cast<u32x4*>(sK + k_off(m, 2 * ck + 1)) = fp8x8_dequant_bf16(kc[r][2], kc[r][3], fp.k_scale);
+    const int d = id >> 2, cv = id & 3;
+    *reinterpret_cast<u32x4*>(sV + v_off(d, 2 * cv)) = fp8x8_dequant_bf16(vc[r][0], vc[r][1], fp.v_scale);
+    *reinterpret_cast<u32x4*>(sV + v_off(d, 2 * cv + 1)) = fp8x8_dequant_bf16(vc[r][2], vc[r][3], fp.v_scale);
   }
 }
 
 // ---------------------------------------------------------------- kernel
-template <int KIND, int NWAVES>
+template <int KIND, int NWAVES, int KV_FP8>
 __global__ void __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_attn_kernel(PrefillParams p) {
   constexpr int BM = NWAVES * QW;  // queries per block
@@ -233,6 +298,18 @@ prefill_attn_kernel(PrefillParams p) {
   ks.kind = KIND;
   ks.window = W;
   const DmaPlan<NWAVES> plan = make_dma_plan<NWAVES>(w, lane);
+  Fp8Prefix fp8;
+  if constexpr (KV_FP8) {
+    const size_t head = KIND == 1 ? (size_t)g * 16 * D : ((size_t)cseq * p.G + g) * W * D;
+    fp8.k8 = reinterpret_cast<const uint8_t*>(p.ck) + head;
+    fp8.v8 = reinterpret_cast<const uint8_t*>(p.cv) + head;
+    fp8.bt_row = ks.bt_row;
+    fp8.page_stride = (size_t)p.G * 16 * D;
+    fp8.kind = KIND;
+    fp8.window = W;
+    fp8.k_scale = p.k_scale;
+    fp8.v_scale = p.v_scale;
+  }
 
   // Q' fragments (B operand of S^T = K Q'^T): lane holds query n of N-block nb,
   // coordinates 16kk + 8*half + 0..7.
@@ -401,7 +478,9 @@ prefill_attn_kernel(PrefillParams p) {
   auto fetch = [&](int j, auto B) __attribute__((always_inline)) {
     uint16_t* sK = buf(B);
     if (j >= j_ws)
-      dma_tile(ks, plan, j * BN, sK, sK + K_TILE);
+      plan.copy(ks.kw, ks.vw, ks.ws_off, j * BN, sK, sK + K_TILE);
+    else if constexpr (KV_FP8)
+      fetch_prefix_fp8<NWAVES>(fp8, tid, j * BN, sK, sK + K_TILE);
     else
       dma_tile_prefix<NWAVES>(ks, w, lane, j * BN, sK, sK + K_TILE);
   };
@@ -478,12 +557,15 @@ prefill_attn_kernel(PrefillParams p) {
 
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {
   const long long blocks = (long long)p.G * (p.H / p.G) * p.n_seqs * p.n_qtiles;
-  if (p.kind == 0)
-    hipLaunchKernelGGL((prefill_attn_kernel<0, kPrefillWavesLocal>), dim3((unsigned)blocks), dim3(64 * kPrefillWavesLocal),
-                       0, s, p);
+  const dim3 grid((unsigned)blocks), local_block(64 * kPrefillWavesLocal), global_block(64 * kPrefillWavesGlobal);
+  if (p.kind == 0 && !p.kv_fp8)
+    hipLaunchKernelGGL((prefill_attn_kernel<0, kPrefillWavesLocal, 0>), grid, local_block, 0, s, p);
+  else if (p.kind == 0)
+    hipLaunchKernelGGL((prefill_attn_kernel<0, kPrefillWavesLocal, 1>), grid, local_block, 0, s, p);
+  else if (!p.kv_fp8)
+    hipLaunchKernelGGL((prefill_attn_kernel<1, kPrefillWavesGlobal, 0>), grid, global_block, 0, s, p);
   else
-    hipLaunchKernelGGL((prefill_attn_kernel<1, kPrefillWavesGlobal>), dim3((unsigned)blocks),
-                       dim3(64 * kPrefillWavesGlobal), 0, s, p);
+    hipLaunchKernelGGL((prefill_attn_kernel<1, kPrefillWavesGlobal, 1>), grid, global_block, 0, s, p);
   return hipGetLastError();
 }
 

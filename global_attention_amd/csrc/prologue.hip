@@ -33,25 +33,32 @@ constexpr int kVHeadsPerBlock = 4;
 constexpr int kPrologueFixedParts = 3;  // K, V (two halves)
 constexpr int kMaxHeadsPerGroup = 8;
 
-// Cached K_hat row of position t (paged: block-table page; local: ring slot).
+// Element offset of the cached K_hat row of position t (paged: block-table
+// page; local: ring slot). An FP8 cache uses the same offsets in bytes.
 template <int KIND>
-__device__ __forceinline__ uint16_t* cache_k_row(const PrologueParams& p, int cseq, int g, int t) {
+__device__ __forceinline__ size_t cache_k_off(const PrologueParams& p, int cseq, int g, int t) {
   if (KIND == 1) {
     const int page = p.bt[(size_t)cseq * p.max_pages + (t >> 4)];
-    return p.ck + (((size_t)page * p.G + g) * 16 + (t & 15)) * D;
+    return (((size_t)page * p.G + g) * 16 + (t & 15)) * D;
   }
-  return p.ck + (((size_t)cseq * p.G + g) * p.window + t % p.window) * D;
+  return (((size_t)cseq * p.G + g) * p.window + t % p.window) * D;
 }
-// Cached V^T element (0, t); coordinate d is at [d * stride].
+// Element offset of cached V^T element (0, t); coordinate d is d * stride further.
 template <int KIND>
-__device__ __forceinline__ uint16_t* cache_v_col(const PrologueParams& p, int cseq, int g, int t, int* stride) {
+__device__ __forceinline__ size_t cache_v_off(const PrologueParams& p, int cseq, int g, int t, int* stride) {
   if (KIND == 1) {
     const int page = p.bt[(size_t)cseq * p.max_pages + (t >> 4)];
     *stride = 16;
-    return p.cv + ((size_t)page * p.G + g) * D * 16 + (t & 15);
+    return ((size_t)page * p.G + g) * D * 16 + (t & 15);
   }
   *stride = p.window;
-  return p.cv + ((size_t)cseq * p.G + g) * D * p.window + t % p.window;
+  return ((size_t)cseq * p.G + g) * D * p.window + t % p.window;
+}
+// Four FP8 codes of x / scale -> bf16 of decode(code) * scale (one rounding).
+__device__ __forceinline__ u32x2 fp8x4_dequant_bf16(uint32_t w, float scale) {
+  float f[4];
+  fp8x4_to_f32(w, f);
+  return u32x2{pack_bf16x2(f[0] * scale, f[1] * scale), pack_bf16x2(f[2] * scale, f[3] * scale)};
 }
 
 template <int KIND>
@@ -137,9 +144,16 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
 #pragma unroll
         for (int g = 0; g < kMaxHeadsPerGroup; ++g)
           if (g < p.G) {
-            const u32x2* src = reinterpret_cast<const u32x2*>(cache_k_row<KIND>(p, cseq, g, t));
-            clo[g] = src[j];
-            chi[g] = src[16 + j];
+            const size_t off = cache_k_off<KIND>(p, cseq, g, t);
+            if (p.kv_fp8) {
+              const uint8_t* src = reinterpret_cast<const uint8_t*>(p.ck) + off;
+              clo[g] = fp8x4_dequant_bf16(*reinterpret_cast<const uint32_t*>(src + 4 * j), p.k_scale);
+              chi[g] = fp8x4_dequant_bf16(*reinterpret_cast<const uint32_t*>(src + 64 + 4 * j), p.k_scale);
+            } else {
+              const u32x2* src = reinterpret_cast<const u32x2*>(p.ck + off);
+              clo[g] = src[j];
+              chi[g] = src[16 + j];
+            }
           }
 #pragma unroll
         for (int g = 0; g < kMaxHeadsPerGroup; ++g)
@@ -173,13 +187,23 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
 #pragma unroll
       for (int g = 0; g < kMaxHeadsPerGroup; ++g)
         if (g < p.G) {
-          HeadFrag f = norm_rope_head(xlo[g], xhi[g], wk_lo, wk_hi, p.rms_eps, local, cs, sn, 1.0f);
-          dst0[g * hstride + j] = u32x2{f.lo[0], f.lo[1]};
-          dst0[g * hstride + 16 + j] = u32x2{f.hi[0], f.hi[1]};
+          float a[4], bq[4];
+          norm_rope_f32(xlo[g], xhi[g], wk_lo, wk_hi, p.rms_eps, local, cs, sn, a, bq);
+          const u32x2 flo = u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+          const u32x2 fhi = u32x2{pack_bf16x2(bq[0], bq[1]), pack_bf16x2(bq[2], bq[3])};
+          dst0[g * hstride + j] = flo;
+          dst0[g * hstride + 16 + j] = fhi;
           if (append_pos(t)) {
-            u32x2* crow = reinterpret_cast<u32x2*>(cache_k_row<KIND>(p, cseq, g, t));
-            crow[j] = u32x2{f.lo[0], f.lo[1]};
-            crow[16 + j] = u32x2{f.hi[0], f.hi[1]};
+            const size_t off = cache_k_off<KIND>(p, cseq, g, t);
+            if (p.kv_fp8) {
+              uint8_t* crow = reinterpret_cast<uint8_t*>(p.ck) + off;
+              *reinterpret_cast<uint32_t*>(crow + 4 * j) = fp8x4_encode(a, p.k_scale);
+              *reinterpret_cast<uint32_t*>(crow + 64 + 4 * j) = fp8x4_encode(bq, p.k_scale);
+            } else {
+              u32x2* crow = reinterpret_cast<u32x2*>(p.ck + off);
+              crow[j] = flo;
+              crow[16 + j] = fhi;
+            }
           }
         }
     }
@@ -203,10 +227,23 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
         v[q4] = *reinterpret_cast<const u32x4*>(p.v_raw + (tok * p.G + g) * D + 8 * c);
       } else if (t < start && cache_ok) {  // cached V^T column of position t
         int stride;
-        const uint16_t* col = cache_v_col<KIND>(p, cseq, g, t, &stride);
+        const size_t off = cache_v_off<KIND>(p, cseq, g, t, &stride);
+        if (p.kv_fp8) {
+          const uint8_t* col = reinterpret_cast<const uint8_t*>(p.cv) + off;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          v[q4][q] = (uint32_t)col[(size_t)(8 * c + 2 * q) * stride] | ((uint32_t)col[(size_t)(8 * c + 2 * q + 1) * stride] << 16);
+          for (int q = 0; q < 4; ++q) {
+            float f0[4], f1[4];
+            fp8x4_to_f32(col[(size_t)(8 * c + 2 * q) * stride], f0);
+            fp8x4_to_f32(col[(size_t)(8 * c + 2 * q + 1) * stride], f1);
+            v[q4][q] = pack_bf16x2(f0[0] * p.v_scale, f1[0] * p.v_scale);
+          }
+        } else {
+          const uint16_t* col = p.cv + off;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            v[q4][q] = (uint32_t)col[(size_t)(8 * c + 2 * q) * stride] |
+                       ((uint32_t)col[(size_t)(8 * c + 2 * q + 1) * stride] << 16);
+        }
       }
     }
     __syncthreads();  // the previous head's transposed reads are done
@@ -242,14 +279,29 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
         const int r0 = 16 * q + 8 * hf, t0 = tile_pos0 + r0;
         int stride;
         if (append_pos(t0) && append_pos(t0 + 7)) {
-          u32x4 o;
+          const size_t off = cache_v_off<KIND>(p, cseq, g, t0, &stride) + (size_t)d * 16;
+          if (p.kv_fp8) {
+            uint32_t w[2] = {0u, 0u};
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
-            o[k] = (uint32_t)s_v[r0 + 2 * k][d] | ((uint32_t)s_v[r0 + 2 * k + 1][d] << 16);
-          *reinterpret_cast<u32x4*>(cache_v_col<KIND>(p, cseq, g, t0, &stride) + (size_t)d * 16) = o;
+            for (int k = 0; k < 8; ++k)
+              w[k >> 2] |= fp8_e4m3_encode(bf16f(s_v[r0 + k][d]) / p.v_scale) << (8 * (k & 3));
+            *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(p.cv) + off) = u32x2{w[0], w[1]};
+          } else {
+            u32x4 o;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              o[k] = (uint32_t)s_v[r0 + 2 * k][d] | ((uint32_t)s_v[r0 + 2 * k + 1][d] << 16);
+            *reinterpret_cast<u32x4*>(p.cv + off) = o;
+          }
         } else {
           for (int k = 0; k < 8; ++k)
-            if (append_pos(t0 + k)) cache_v_col<KIND>(p, cseq, g, t0 + k, &stride)[(size_t)d * 16] = s_v[r0 + k][d];
+            if (append_pos(t0 + k)) {
+              const size_t off = cache_v_off<KIND>(p, cseq, g, t0 + k, &stride) + (size_t)d * 16;
+              if (p.kv_fp8)
+                reinterpret_cast<uint8_t*>(p.cv)[off] = (uint8_t)fp8_e4m3_encode(bf16f(s_v[r0 + k][d]) / p.v_scale);
+              else
+                p.cv[off] = s_v[r0 + k][d];
+            }
         }
       }
     }
@@ -294,30 +346,44 @@ __global__ void __launch_bounds__(256) kv_append_kernel(AppendParams p) {
 
   for (int g = 0; g < p.G; ++g) {
     const u32x2* src = reinterpret_cast<const u32x2*>(p.k_raw + ((size_t)tok * p.G + g) * D);
-    HeadFrag f = norm_rope_head(src[j], src[16 + j], w_lo, w_hi, p.rms_eps, local, cs, sn, 1.0f);
-    uint16_t* krow;
-    uint16_t* vcol;  // V^T element [0][slot]; coordinate d is at vcol[d * vstride]
+    size_t krow;  // element offset of the K_hat row
+    size_t vcol;  // element offset of V^T element [0][slot]; coordinate d is at vcol + d * vstride
     int vstride;
     if (local) {
       int slot = t % p.window;
       size_t base = (size_t)cseq * p.G + g;
-      krow = p.ck + (base * p.window + slot) * D;
-      vcol = p.cv + base * D * p.window + slot;
+      krow = (base * p.window + slot) * D;
+      vcol = base * D * p.window + slot;
       vstride = p.window;
     } else {
       int page = p.bt[(size_t)cseq * p.max_pages + (t >> 4)];
       size_t base = (size_t)page * p.G + g;
-      krow = p.ck + (base * 16 + (t & 15)) * D;
-      vcol = p.cv + base * D * 16 + (t & 15);
+      krow = (base * 16 + (t & 15)) * D;
+      vcol = base * D * 16 + (t & 15);
       vstride = 16;
     }
-    reinterpret_cast<u32x2*>(krow)[j] = u32x2{f.lo[0], f.lo[1]};
-    reinterpret_cast<u32x2*>(krow)[16 + j] = u32x2{f.hi[0], f.hi[1]};
     const uint16_t* vsrc = p.v_raw + ((size_t)tok * p.G + g) * D;
+    if (p.kv_fp8) {
+      float a[4], b[4];
+      norm_rope_f32(src[j], src[16 + j], w_lo, w_hi, p.rms_eps, local, cs, sn, a, b);
+      uint8_t* k8 = reinterpret_cast<uint8_t*>(p.ck) + krow;
+      *reinterpret_cast<uint32_t*>(k8 + 4 * j) = fp8x4_encode(a, p.k_scale);
+      *reinterpret_cast<uint32_t*>(k8 + 64 + 4 * j) = fp8x4_encode(b, p.k_scale);
+      uint8_t* v8 = reinterpret_cast<uint8_t*>(p.cv) + vcol;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v8[(size_t)(4 * j + e) * vstride] = (uint8_t)fp8_e4m3_encode(bf16f(vsrc[4 * j + e]) / p.v_scale);
+        v8[(size_t)(64 + 4 * j + e) * vstride] = (uint8_t)fp8_e4m3_encode(bf16f(vsrc[64 + 4 * j + e]) / p.v_scale);
+      }
+      continue;
+    }
+    HeadFrag f = norm_rope_head(src[j], src[16 + j], w_lo, w_hi, p.rms_eps, local, cs, sn, 1.0f);
+    reinterpret_cast<u32x2*>(p.ck + krow)[j] = u32x2{f.lo[0], f.lo[1]};
+    reinterpret_cast<u32x2*>(p.ck + krow)[16 + j] = u32x2{f.hi[0], f.hi[1]};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      vcol[(size_t)(4 * j + e) * vstride] = vsrc[4 * j + e];
-      vcol[(size_t)(64 + 4 * j + e) * vstride] = vsrc[64 + 4 * j + e];
+      p.cv[vcol + (size_t)(4 * j + e) * vstride] = vsrc[4 * j + e];
+      p.cv[vcol + (size_t)(64 + 4 * j + e) * vstride] = vsrc[64 + 4 * j + e];
     }
   }
 }
@@ -342,7 +408,7 @@ __global__ void __launch_bounds__(256) decode_q_prologue_kernel(DecodeQParams p)
   }
   const u32x2* qw = reinterpret_cast<const u32x2*>(p.q_norm_w);
   const float qbase = kLog2e / sqrtf((float)D);
-  float scale = local ? qbase : qbase * ssmax_scale(t, p.ssmax_base, p.ssmax_exp);
+  float scale = (local ? qbase : qbase * ssmax_scale(t, p.ssmax_base, p.ssmax_exp)) * p.k_scale;
   const u32x2* src = reinterpret_cast<const u32x2*>(p.q_raw + ((size_t)seq * p.H + h) * D);
   HeadFrag f = norm_rope_head(src[j], src[16 + j], qw[j], qw[16 + j], p.rms_eps, local, cs, sn, scale);
   u32x2* dst = reinterpret_cast<u32x2*>(p.qp + ((size_t)seq * p.H + h) * D);

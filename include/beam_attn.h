@@ -27,7 +27,8 @@
  *   - Device-resident indices (block-table entries, seq_idx, positions,
  *     cu_seqlens) are not read by the host; out-of-range values in them are
  *     undefined behaviour.
- *   - Only head_dim == 128 and bf16 storage are supported (BEAM_E_UNSUPPORTED).
+ *   - Only head_dim == 128 is supported (BEAM_E_UNSUPPORTED). Inputs and
+ *     outputs are bf16; the KV cache is bf16 or FP8 E4M3 (below).
  *   - Calls hold no global mutable state and may be made from several threads.
  *
  * KV cache layouts (beam_kv_cache.k / .v)
@@ -41,6 +42,17 @@
  *     v: bf16 [n_seqs][n_kv_heads][head_dim][window]
  *     position t lives in slot t % window.
  *   The cache stores K_hat (normalised; rotated on local layers) and raw V.
+ *
+ * FP8 KV cache (dtype BEAM_KV_FP8_E4M3; one byte per element, same layouts)
+ *   The pages' serving recipes keep the cache in FP8 E4M3 (18 KiB per token
+ *   across the nine global layers, "KV memory: nine growing caches, not 52";
+ *   the German serving article: FP8 E4M3 cache by default). They state no
+ *   scale convention; here each layer's cache has one scale for K and one for
+ *   V. A value x is stored as the OCP E4M3FN code nearest to x / scale (ties
+ *   to the even code, |x / scale| >= 448 saturates to +-448) and read back as
+ *   decode(code) * scale. Decode reads codes exactly (k_scale is folded into
+ *   the query, v_scale into the output); prefill dequantises a cached prefix
+ *   to bf16. The chunk being prefilled attends to its own keys unquantised.
  */
 #ifndef BEAM_ATTN_H
 #define BEAM_ATTN_H
@@ -55,6 +67,8 @@ extern "C" {
 typedef uint16_t beam_bf16; /* raw bfloat16 bits */
 
 typedef enum { BEAM_LOCAL = 0, BEAM_GLOBAL = 1 } beam_layer_kind;
+
+typedef enum { BEAM_KV_BF16 = 0, BEAM_KV_FP8_E4M3 = 1 } beam_kv_dtype;
 
 typedef enum {
   BEAM_OK = 0,
@@ -81,13 +95,16 @@ typedef struct {
 /* One layer's KV cache (layouts above). */
 typedef struct {
   int32_t kind;               /* beam_layer_kind */
-  void *k;                    /* device, bf16 */
-  void *v;                    /* device, bf16 */
+  void *k;                    /* device, bf16 or FP8 codes (dtype) */
+  void *v;                    /* device, bf16 or FP8 codes (dtype) */
   int32_t page_size;          /* GLOBAL: 16. LOCAL: ignored */
   int32_t n_pages;            /* GLOBAL: physical pages. LOCAL: ignored */
   const int32_t *block_table; /* GLOBAL: device [n_seqs][max_pages_per_seq]. LOCAL: ignored */
   int32_t max_pages_per_seq;  /* GLOBAL: row length of block_table */
   int32_t n_seqs;             /* GLOBAL: rows of block_table. LOCAL: rings allocated */
+  int32_t dtype;              /* beam_kv_dtype (0 = bf16) */
+  float k_scale;              /* FP8: K_hat = decode(code) * k_scale; finite, > 0. bf16: ignored */
+  float v_scale;              /* FP8: V = decode(code) * v_scale; finite, > 0. bf16: ignored */
 } beam_kv_cache;
 
 /* Append new tokens to a layer's cache.

@@ -91,6 +91,14 @@ def test_argument_checks_fail_before_launch():
     assert _call_prefill(ga.Config(n_q_heads=47), _cache()) == 2
     assert _call_prefill(ga.Config(n_q_heads=48, n_kv_heads=2), _cache()) == 4   # 24 heads per KV head
     assert _call_prefill(ga.Config(n_q_heads=64, n_kv_heads=16), _cache()) == 4  # more than 8 KV heads
+    # cache dtype and FP8 scales
+    c = _cache()
+    c.dtype = 2
+    assert _call_prefill(ga.Config(), c) == 4
+    for ks, vs in ((0.0, 1.0), (1.0, -1.0), (float("nan"), 1.0), (1.0, float("inf"))):
+        c = _cache()
+        c.dtype, c.k_scale, c.v_scale = ga.KV_FP8_E4M3, ks, vs
+        assert _call_prefill(ga.Config(), c) == 3
     # 2^15 sequences with 2^22-token chunks: the workspace fits 32-bit offsets but the grid would not
     assert _call_prefill(ga.Config(), _cache(), ws_bytes=1 << 40, n_tok=1 << 22, max_chunk=1 << 22, n_seqs=1 << 15) == 3
     # workspace positions x 128 beyond 2^31
