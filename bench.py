@@ -42,10 +42,11 @@ _CSRC = os.path.join(ROOT, "global_attention_amd", "csrc")
 _KERNEL_SOURCES = {
     "prefill_attn_kernel<1, 8, 0>": "prefill.hip",
     "prefill_attn_kernel<0, 4, 0>": "prefill.hip",
-    "decode_split_kernel<1, 0>": "decode.hip",
-    "decode_split_kernel<0, 0>": "decode.hip",
-    "prefill_prologue_kernel<0>": "prologue.hip",
-    "prefill_prologue_kernel<1>": "prologue.hip",
+    "decode_split_kernel<1>": "decode.hip",
+    "decode_split_kernel<0>": "decode.hip",
+    "decode_fp8_kernel<1>": "decode.hip",
+    "prefill_prologue_kernel<0, 0>": "prologue.hip",
+    "prefill_prologue_kernel<1, 0>": "prologue.hip",
 }
 
 
@@ -179,22 +180,29 @@ def setup_decode(n_seqs=64, lo=65536, hi=131071, seed=3):
             t[p0:p0 + step].normal_(generator=gen)
     for t in (lcache.k, lcache.v):
         t.normal_(generator=gen)
+    # The same global layer over an FP8 E4M3 cache (scales 1): N(0,1) values
+    # rounded to E4M3 by torch are its (input) contents.
+    fcache = ga.KVCache.allocate_global(cfg, n_pages, torch.from_numpy(bt), dtype=ga.KV_FP8_E4M3)
+    for t in (fcache.k, fcache.v):
+        for p0 in range(0, n_pages, step):
+            blk = t[p0:p0 + step]
+            blk.copy_(torch.randn(blk.shape, generator=gen, device="cuda").to(torch.float8_e4m3fn).view(torch.uint8))
     inp = synth.attention_inputs(cfg=seed, layer=7, n_tok=n_seqs)
     d = {k: _dev(v) for k, v in inp.items()}
     torch.cuda.synchronize()
-    return cfg, ts, gcache, lcache, d
+    return cfg, ts, gcache, lcache, fcache, d
 
 
 def bench_decode(steps, warmup):
     import torch
     import global_attention_amd as ga
-    cfg, ts, gcache, lcache, d = setup_decode()
+    cfg, ts, gcache, lcache, fcache, d = setup_decode()
     n = len(ts)
     seq = _i32(list(range(n)))
     pos = _i32(ts)
     max_pos = int(ts.max())
     res = {}
-    for name, cache in (("global", gcache), ("local", lcache)):
+    for name, cache in (("global", gcache), ("local", lcache), ("global_fp8", fcache)):
         out = torch.empty((n, H, D), dtype=torch.bfloat16, device="cuda")
         ws = torch.empty(ga.decode_workspace_bytes(cfg, cache.kind, n, max_pos), dtype=torch.uint8, device="cuda")
         args = (cfg, cache, d["q"], d["q_norm_w"], d["gate"], seq, pos, max_pos)
@@ -218,8 +226,8 @@ def bench_decode(steps, warmup):
         torch.cuda.synchronize()
         el = (time.perf_counter() - t0) / steps
         split_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
-        keys = [int(t) + 1 if name == "global" else min(int(t) + 1, W) for t in ts]
-        nbytes = sum(keys) * G * D * 2 * 2
+        keys = [min(int(t) + 1, W) if name == "local" else int(t) + 1 for t in ts]
+        nbytes = sum(keys) * G * D * 2 * (1 if cache.dtype == ga.KV_FP8_E4M3 else 2)
         res[name] = dict(bytes=nbytes, ms_per_call=el * 1e3, split_ms=split_ms,
                          gbs_call=nbytes / el / 1e9, gbs_split=nbytes / (split_ms / 1e3) / 1e9)
         log(f"[bench] decode {name}: {nbytes / 1e9:.2f} GB, call {el * 1e3:.3f} ms, split kernel {split_ms:.3f} ms")
@@ -331,13 +339,26 @@ def main():
             "value": round(g["gbs_call"], 1), "unit": "GB/s",
             "frac_of_hbm_peak": round(g["gbs_call"] / PEAK_HBM_GBS, 4),
             "global_bytes": g["bytes"], "global_ms_per_call": round(g["ms_per_call"], 4),
-            "roofline": {"kernel": "decode_split_kernel<1, 0>", "bound": "hbm", "achieved": round(g["gbs_split"], 1),
+            "roofline": {"kernel": "decode_split_kernel<1>", "bound": "hbm", "achieved": round(g["gbs_split"], 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(g["gbs_split"] / PEAK_HBM_GBS, 4),
-                         "traffic": recorded_traffic("decode_split_kernel<1, 0>"),
+                         "traffic": recorded_traffic("decode_split_kernel<1>"),
                          "avg_launch_ms": round(g["split_ms"], 4), "bytes_per_launch": g["bytes"]},
             "local": {"bytes": dres["local"]["bytes"], "ms_per_call": round(dres["local"]["ms_per_call"], 4),
                       "gbs_call": round(dres["local"]["gbs_call"], 1),
                       "note": "134 MB of rings can stay resident in the 256 MB MALL between calls"},
+        }
+        f = dres["global_fp8"]
+        rec["decode_fp8"] = {
+            "workload": "the same 64-sequence global-layer decode over an FP8 E4M3 cache (1 byte per element, "
+                        "per-tensor scales 1): half the bytes per token",
+            "value": round(f["gbs_call"], 1), "unit": "GB/s",
+            "frac_of_hbm_peak": round(f["gbs_call"] / PEAK_HBM_GBS, 4),
+            "global_bytes": f["bytes"], "global_ms_per_call": round(f["ms_per_call"], 4),
+            "speedup_vs_bf16_call": round(g["ms_per_call"] / f["ms_per_call"], 3),
+            "roofline": {"kernel": "decode_fp8_kernel<1>", "bound": "hbm", "achieved": round(f["gbs_split"], 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(f["gbs_split"] / PEAK_HBM_GBS, 4),
+                         "traffic": recorded_traffic("decode_fp8_kernel<1>"),
+                         "avg_launch_ms": round(f["split_ms"], 4), "bytes_per_launch": f["bytes"]},
         }
     if not args.no_cpu_baseline and layers is not None:
         log(f"[bench] timing the CPU oracle on {args.cpu_rows} rows per layer")

@@ -61,7 +61,7 @@ __device__ __forceinline__ u32x2 fp8x4_dequant_bf16(uint32_t w, float scale) {
   return u32x2{pack_bf16x2(f[0] * scale, f[1] * scale), pack_bf16x2(f[2] * scale, f[3] * scale)};
 }
 
-template <int KIND>
+template <int KIND, int KV_FP8>
 __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p) {
   constexpr bool local = (KIND == 0);
   const int seq = blockIdx.x;
@@ -145,7 +145,7 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
         for (int g = 0; g < kMaxHeadsPerGroup; ++g)
           if (g < p.G) {
             const size_t off = cache_k_off<KIND>(p, cseq, g, t);
-            if (p.kv_fp8) {
+            if constexpr (KV_FP8) {
               const uint8_t* src = reinterpret_cast<const uint8_t*>(p.ck) + off;
               clo[g] = fp8x4_dequant_bf16(*reinterpret_cast<const uint32_t*>(src + 4 * j), p.k_scale);
               chi[g] = fp8x4_dequant_bf16(*reinterpret_cast<const uint32_t*>(src + 64 + 4 * j), p.k_scale);
@@ -195,7 +195,7 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
           dst0[g * hstride + 16 + j] = fhi;
           if (append_pos(t)) {
             const size_t off = cache_k_off<KIND>(p, cseq, g, t);
-            if (p.kv_fp8) {
+            if constexpr (KV_FP8) {
               uint8_t* crow = reinterpret_cast<uint8_t*>(p.ck) + off;
               *reinterpret_cast<uint32_t*>(crow + 4 * j) = fp8x4_encode(a, p.k_scale);
               *reinterpret_cast<uint32_t*>(crow + 64 + 4 * j) = fp8x4_encode(bq, p.k_scale);
@@ -228,7 +228,7 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
       } else if (t < start && cache_ok) {  // cached V^T column of position t
         int stride;
         const size_t off = cache_v_off<KIND>(p, cseq, g, t, &stride);
-        if (p.kv_fp8) {
+        if constexpr (KV_FP8) {
           const uint8_t* col = reinterpret_cast<const uint8_t*>(p.cv) + off;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -280,7 +280,7 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
         int stride;
         if (append_pos(t0) && append_pos(t0 + 7)) {
           const size_t off = cache_v_off<KIND>(p, cseq, g, t0, &stride) + (size_t)d * 16;
-          if (p.kv_fp8) {
+          if constexpr (KV_FP8) {
             uint32_t w[2] = {0u, 0u};
 #pragma unroll
             for (int k = 0; k < 8; ++k)
@@ -297,7 +297,7 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
           for (int k = 0; k < 8; ++k)
             if (append_pos(t0 + k)) {
               const size_t off = cache_v_off<KIND>(p, cseq, g, t0 + k, &stride) + (size_t)d * 16;
-              if (p.kv_fp8)
+              if constexpr (KV_FP8)
                 reinterpret_cast<uint8_t*>(p.cv)[off] = (uint8_t)fp8_e4m3_encode(bf16f(s_v[r0 + k][d]) / p.v_scale);
               else
                 p.cv[off] = s_v[r0 + k][d];
@@ -434,10 +434,15 @@ namespace beam {
 hipError_t launch_prefill_prologue(const PrologueParams& p, int n_seqs, int n_tiles, hipStream_t s) {
   const int parts = kPrologueFixedParts + (p.H + kQHeadsPerBlock - 1) / kQHeadsPerBlock;
   if (p.G > kMaxHeadsPerGroup || p.G > 2 * kVHeadsPerBlock) return hipErrorInvalidValue;
-  if (p.kind == 0)
-    hipLaunchKernelGGL(prefill_prologue_kernel<0>, dim3(n_seqs, n_tiles, parts), dim3(256), 0, s, p);
+  const dim3 grid(n_seqs, n_tiles, parts), block(256);
+  if (p.kind == 0 && !p.kv_fp8)
+    hipLaunchKernelGGL((prefill_prologue_kernel<0, 0>), grid, block, 0, s, p);
+  else if (p.kind == 0)
+    hipLaunchKernelGGL((prefill_prologue_kernel<0, 1>), grid, block, 0, s, p);
+  else if (!p.kv_fp8)
+    hipLaunchKernelGGL((prefill_prologue_kernel<1, 0>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL(prefill_prologue_kernel<1>, dim3(n_seqs, n_tiles, parts), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((prefill_prologue_kernel<1, 1>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
