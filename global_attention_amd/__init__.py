@@ -24,11 +24,13 @@ STAGE_ATTENTION = 2
 STAGE_APPEND = 4
 STAGE_COMBINE = 4
 STAGE_ALL = 7
+STAGE_VERIFY_COMBINE = 8
+STAGE_VERIFY_ALL = 15
 
 EXPORTED = [
-    "beam_kv_append", "beam_attn_prefill", "beam_attn_decode",
-    "beam_attn_prefill_stages", "beam_attn_decode_stages",
-    "beam_prefill_workspace_bytes", "beam_decode_workspace_bytes",
+    "beam_kv_append", "beam_attn_prefill", "beam_attn_decode", "beam_attn_verify",
+    "beam_attn_prefill_stages", "beam_attn_decode_stages", "beam_attn_verify_stages",
+    "beam_prefill_workspace_bytes", "beam_decode_workspace_bytes", "beam_verify_workspace_bytes",
     "beam_kv_bytes", "beam_kv_page_slot", "beam_debug_visibility",
     "beam_status_str", "beam_last_error",
 ]
@@ -89,6 +91,10 @@ def lib() -> ctypes.CDLL:
     U32 = ctypes.c_uint32
     L.beam_attn_prefill_stages.argtypes = [U32] + L.beam_attn_prefill.argtypes
     L.beam_attn_decode_stages.argtypes = [U32] + L.beam_attn_decode.argtypes
+    L.beam_attn_verify.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, P, P, SZ, P]
+    L.beam_attn_verify_stages.argtypes = [U32] + L.beam_attn_verify.argtypes
+    L.beam_verify_workspace_bytes.argtypes = [P, I32, I32, I32, I32, I32, I32]
+    L.beam_verify_workspace_bytes.restype = SZ
     L.beam_prefill_workspace_bytes.argtypes = [P, I32, I32]
     L.beam_prefill_workspace_bytes.restype = SZ
     L.beam_decode_workspace_bytes.argtypes = [P, I32, I32, I32, I32]
@@ -100,7 +106,7 @@ def lib() -> ctypes.CDLL:
     L.beam_status_str.restype = ctypes.c_char_p
     L.beam_last_error.restype = ctypes.c_char_p
     for name in ("beam_kv_append", "beam_attn_prefill", "beam_attn_decode", "beam_attn_prefill_stages",
-                 "beam_attn_decode_stages", "beam_kv_bytes",
+                 "beam_attn_decode_stages", "beam_attn_verify", "beam_attn_verify_stages", "beam_kv_bytes",
                  "beam_kv_page_slot", "beam_debug_visibility"):
         getattr(L, name).restype = I32
     _lib = L
@@ -197,6 +203,13 @@ def decode_workspace_bytes(cfg: Config, kind: int, n_seqs: int, max_pos: int, sp
     return int(lib().beam_decode_workspace_bytes(ctypes.byref(c), kind, n_seqs, max_pos, split_keys))
 
 
+def verify_workspace_bytes(cfg: Config, kind: int, n_tok: int, n_seqs: int, max_chunk_len: int, max_pos: int,
+                           split_keys: int = 0) -> int:
+    c = cfg.c()
+    return int(lib().beam_verify_workspace_bytes(ctypes.byref(c), kind, n_tok, n_seqs, max_chunk_len, max_pos,
+                                                 split_keys))
+
+
 def _workspace(nbytes, device, workspace):
     import torch
     if workspace is None:
@@ -225,6 +238,41 @@ def prefill(cfg: Config, cache: KVCache, q_raw, k_raw, v_raw, q_norm_w, k_norm_w
             stages: int = STAGE_ALL):
     """Chunked varlen prefill of one layer; returns out [n_tok][H][d] (bf16).
     `stages` selects prologue / attention / append (beam_attn_prefill_stages)."""
+    n_tok, n_seqs, out = _chunk_args(cfg, q_raw, k_raw, v_raw, q_norm_w, k_norm_w, gate, cu_seqlens, seq_idx,
+                                     start_pos, gate_bias, out)
+    nbytes = prefill_workspace_bytes(cfg, n_tok, n_seqs)
+    workspace = _workspace(nbytes, q_raw.device, workspace)
+    c, kc = cfg.c(), cache.c()
+    _check(lib().beam_attn_prefill_stages(
+        stages, ctypes.byref(c), ctypes.byref(kc), _ptr(q_raw), _ptr(k_raw), _ptr(v_raw), _ptr(q_norm_w),
+        _ptr(k_norm_w), _ptr(gate), _ptr(gate_bias), _ptr(cu_seqlens), _ptr(seq_idx), _ptr(start_pos),
+        n_seqs, n_tok, max_chunk_len, _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def verify(cfg: Config, cache: KVCache, q_raw, k_raw, v_raw, q_norm_w, k_norm_w, gate, cu_seqlens, seq_idx,
+           start_pos, max_chunk_len: int, max_pos: int, gate_bias=None, split_keys: int = 0, out=None,
+           workspace=None, stream=None, stages: int = STAGE_VERIFY_ALL):
+    """Verify step (a short chunk per sequence over its cache); same semantics as
+    prefill, returns out [n_tok][H][d] (bf16). max_pos bounds start_pos + chunk
+    length - 1. `stages` selects prologue / split attention / combine / append
+    (beam_attn_verify_stages)."""
+    n_tok, n_seqs, out = _chunk_args(cfg, q_raw, k_raw, v_raw, q_norm_w, k_norm_w, gate, cu_seqlens, seq_idx,
+                                     start_pos, gate_bias, out)
+    nbytes = verify_workspace_bytes(cfg, cache.kind, n_tok, n_seqs, max_chunk_len, max_pos, split_keys)
+    if nbytes == 0:
+        raise BeamError(3, "invalid verify sizes (max_chunk_len / max_pos / split_keys)")
+    workspace = _workspace(nbytes, q_raw.device, workspace)
+    c, kc = cfg.c(), cache.c()
+    _check(lib().beam_attn_verify_stages(
+        stages, ctypes.byref(c), ctypes.byref(kc), _ptr(q_raw), _ptr(k_raw), _ptr(v_raw), _ptr(q_norm_w),
+        _ptr(k_norm_w), _ptr(gate), _ptr(gate_bias), _ptr(cu_seqlens), _ptr(seq_idx), _ptr(start_pos),
+        n_seqs, n_tok, max_chunk_len, max_pos, split_keys, _ptr(out), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
+    return out
+
+
+def _chunk_args(cfg, q_raw, k_raw, v_raw, q_norm_w, k_norm_w, gate, cu_seqlens, seq_idx, start_pos, gate_bias, out):
     import torch
     n_tok = q_raw.shape[0]
     n_seqs = cu_seqlens.shape[0] - 1
@@ -243,14 +291,7 @@ def prefill(cfg: Config, cache: KVCache, q_raw, k_raw, v_raw, q_norm_w, k_norm_w
     if out is None:
         out = torch.empty((n_tok, H, d), dtype=torch.bfloat16, device=q_raw.device)
     _need(out, torch.bfloat16, (n_tok, H, d), "out")
-    nbytes = prefill_workspace_bytes(cfg, n_tok, n_seqs)
-    workspace = _workspace(nbytes, q_raw.device, workspace)
-    c, kc = cfg.c(), cache.c()
-    _check(lib().beam_attn_prefill_stages(
-        stages, ctypes.byref(c), ctypes.byref(kc), _ptr(q_raw), _ptr(k_raw), _ptr(v_raw), _ptr(q_norm_w),
-        _ptr(k_norm_w), _ptr(gate), _ptr(gate_bias), _ptr(cu_seqlens), _ptr(seq_idx), _ptr(start_pos),
-        n_seqs, n_tok, max_chunk_len, _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
-    return out
+    return n_tok, n_seqs, out
 
 
 def decode(cfg: Config, cache: KVCache, q_raw, q_norm_w, gate, seq_idx, pos, max_pos: int, gate_bias=None,

@@ -103,6 +103,37 @@ PrefillWs prefill_ws_layout(const beam_attn_config* c, int n_tok, int n_seqs) {
   return ws;
 }
 
+int default_verify_split_keys(int kind) { return kind == BEAM_LOCAL ? 256 : 1024; }
+
+// Verify (short-chunk) calls: the prefill workspace, then the split partials
+// (reference max and sum, and the unnormalised accumulator) per (token, head,
+// split). A sequence's keys span at most n_tiles 64-key tiles.
+struct VerifyWs {
+  PrefillWs pre;
+  size_t ml, acc, total;
+  int n_splits, split_tiles;
+};
+
+bool verify_ws_layout(const beam_attn_config* c, int kind, int n_tok, int n_seqs, int max_chunk_len, int max_pos,
+                      int split_keys, VerifyWs* ws) {
+  if (split_keys == 0) split_keys = default_verify_split_keys(kind);
+  if (split_keys < 64 || split_keys % 64 != 0 || split_keys > 65536) return false;
+  if (n_seqs <= 0 || n_tok < 0 || max_chunk_len < 0 || max_pos < 0) return false;
+  int n_tiles = (max_pos >> 6) + 1;
+  if (kind == BEAM_LOCAL) {
+    const int span = ((c->window - 1 + (max_chunk_len > 0 ? max_chunk_len - 1 : 0)) >> 6) + 2;
+    if (span < n_tiles) n_tiles = span;
+  }
+  ws->split_tiles = split_keys / 64;
+  ws->n_splits = (n_tiles + ws->split_tiles - 1) / ws->split_tiles;
+  ws->pre = prefill_ws_layout(c, n_tok, n_seqs);
+  const size_t rows = (size_t)n_tok * c->n_q_heads * ws->n_splits;
+  ws->ml = ws->pre.total;
+  ws->acc = ws->ml + align256(rows * 2 * sizeof(float));
+  ws->total = ws->acc + align256(rows * beam::D * sizeof(float));
+  return true;
+}
+
 beam_status hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(BEAM_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
   return BEAM_OK;
@@ -159,6 +190,14 @@ size_t beam_prefill_workspace_bytes(const beam_attn_config* cfg, int32_t n_tok, 
   return prefill_ws_layout(cfg, n_tok, n_seqs).total;
 }
 
+size_t beam_verify_workspace_bytes(const beam_attn_config* cfg, int32_t kind, int32_t n_tok, int32_t n_seqs,
+                                   int32_t max_chunk_len, int32_t max_pos, int32_t split_keys) {
+  if (check_cfg(cfg) != BEAM_OK || (kind != BEAM_LOCAL && kind != BEAM_GLOBAL)) return 0;
+  VerifyWs ws;
+  if (!verify_ws_layout(cfg, kind, n_tok, n_seqs, max_chunk_len, max_pos, split_keys, &ws)) return 0;
+  return ws.total;
+}
+
 size_t beam_decode_workspace_bytes(const beam_attn_config* cfg, int32_t kind, int32_t n_seqs, int32_t max_pos,
                                    int32_t split_keys) {
   if (check_cfg(cfg) != BEAM_OK || (kind != BEAM_LOCAL && kind != BEAM_GLOBAL)) return 0;
@@ -203,15 +242,22 @@ beam_status beam_kv_append(const beam_attn_config* cfg, const beam_kv_cache* cac
   return ok();
 }
 
-beam_status beam_attn_prefill_stages(uint32_t stages, const beam_attn_config* cfg, const beam_kv_cache* cache,
-                                     const beam_bf16* q_raw, const beam_bf16* k_raw, const beam_bf16* v_raw,
-                                     const beam_bf16* q_norm_w, const beam_bf16* k_norm_w,
-                                     const beam_bf16* gate_logits, const float* gate_bias, const int32_t* cu_seqlens,
-                                     const int32_t* seq_idx, const int32_t* start_pos, int32_t n_seqs, int32_t n_tok,
-                                     int32_t max_chunk_len, beam_bf16* out, void* workspace, size_t ws_bytes,
-                                     void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Prefill and verify share the prologue, the workspace layout and the append;
+// verify (verify == true) runs the split-key attention and its combine instead
+// of the prefill attention kernel.
+beam_status chunk_call(bool verify, uint32_t stages, const beam_attn_config* cfg, const beam_kv_cache* cache,
+                       const beam_bf16* q_raw, const beam_bf16* k_raw, const beam_bf16* v_raw,
+                       const beam_bf16* q_norm_w, const beam_bf16* k_norm_w, const beam_bf16* gate_logits,
+                       const float* gate_bias, const int32_t* cu_seqlens, const int32_t* seq_idx,
+                       const int32_t* start_pos, int32_t n_seqs, int32_t n_tok, int32_t max_chunk_len,
+                       int32_t max_pos, int32_t split_keys, beam_bf16* out, void* workspace, size_t ws_bytes,
+                       void* stream) {
   beam_status st;
-  if (stages & ~7u) return fail(BEAM_E_RANGE, "unknown stage bits");
+  if (stages & ~(verify ? 15u : 7u)) return fail(BEAM_E_RANGE, "unknown stage bits");
   if ((st = check_cfg(cfg)) != BEAM_OK) return st;
   if ((st = check_cache(cache)) != BEAM_OK) return st;
   if (n_seqs <= 0) return fail(BEAM_E_RANGE, "n_seqs must be positive");
@@ -224,11 +270,25 @@ beam_status beam_attn_prefill_stages(uint32_t stages, const beam_attn_config* cf
     return fail(BEAM_E_NULL, "NULL input/output pointer");
   if (!workspace) return fail(BEAM_E_NULL, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(BEAM_E_RANGE, "workspace must be 256-byte aligned");
+  VerifyWs vws{};
+  if (verify) {
+    const int hpg = cfg->n_q_heads / cfg->n_kv_heads;
+    if ((int64_t)max_chunk_len * hpg > beam::kVerifyMaxRows)
+      return fail(BEAM_E_RANGE, "verify chunk too long: max_chunk_len x (n_q_heads / n_kv_heads) must be <= " +
+                                    std::to_string(beam::kVerifyMaxRows));
+    if (max_pos < max_chunk_len - 1) return fail(BEAM_E_RANGE, "max_pos must be >= max_chunk_len - 1");
+    if (!verify_ws_layout(cfg, cache->kind, n_tok, n_seqs, max_chunk_len, max_pos, split_keys, &vws))
+      return fail(BEAM_E_RANGE, "split_keys must be 0 or a multiple of 64 in [64, 65536]");
+    if (ws_bytes < vws.total)
+      return fail(BEAM_E_WORKSPACE, "verify workspace needs " + std::to_string(vws.total) + " bytes");
+    if ((int64_t)cfg->n_kv_heads * vws.n_splits * n_seqs > 0x7fffffffLL || (int64_t)n_tok * cfg->n_q_heads > 0x7fffffffLL)
+      return fail(BEAM_E_RANGE, "verify grid too large");
+  }
   const PrefillWs ws = prefill_ws_layout(cfg, n_tok, n_seqs);
-  if (ws_bytes < ws.total)
+  if (!verify && ws_bytes < ws.total)
     return fail(BEAM_E_WORKSPACE, "prefill workspace needs " + std::to_string(ws.total) + " bytes");
   if (ws.P * beam::D > 0x7fffffff) return fail(BEAM_E_RANGE, "too many tokens in one call (workspace positions x 128 must stay below 2^31)");
-  {
+  if (!verify) {
     const int bq = beam::prefill_block_queries(cache->kind);
     const int64_t blocks = (int64_t)cfg->n_q_heads * n_seqs * ((max_chunk_len + bq - 1) / bq);
     if (blocks > 0x7fffffffLL) return fail(BEAM_E_RANGE, "prefill grid too large (n_seqs x max_chunk_len)");
@@ -300,9 +360,41 @@ beam_status beam_attn_prefill_stages(uint32_t stages, const beam_attn_config* cf
   ap.kv_fp8 = cache->dtype == BEAM_KV_FP8_E4M3;
   ap.k_scale = cache->k_scale;
   ap.v_scale = cache->v_scale;
-  if ((stages & BEAM_STAGE_ATTENTION) &&
-      (st = hip_status(beam::launch_prefill_attn(ap, s), "prefill attention launch")) != BEAM_OK)
-    return st;
+  if (!verify) {
+    if ((stages & BEAM_STAGE_ATTENTION) &&
+        (st = hip_status(beam::launch_prefill_attn(ap, s), "prefill attention launch")) != BEAM_OK)
+      return st;
+  } else {
+    ap.part_ml = reinterpret_cast<float*>(wsb + vws.ml);
+    ap.part_acc = reinterpret_cast<float*>(wsb + vws.acc);
+    ap.split_tiles = vws.split_tiles;
+    ap.n_splits = vws.n_splits;
+    if ((stages & BEAM_STAGE_ATTENTION) &&
+        (st = hip_status(beam::launch_verify_attn(ap, s), "verify attention launch")) != BEAM_OK)
+      return st;
+    beam::VerifyCombineParams cp{};
+    cp.part_ml = ap.part_ml;
+    cp.part_acc = ap.part_acc;
+    cp.cu = cu_seqlens;
+    cp.start_pos = start_pos;
+    cp.seq_idx = seq_idx;
+    cp.gate = gate_logits;
+    cp.gate_bias = gate_bias;
+    cp.out = out;
+    cp.bt = cache->block_table;
+    cp.max_pages = cache->max_pages_per_seq;
+    cp.n_cache_seqs = cache->n_seqs;
+    cp.kind = cache->kind;
+    cp.window = cfg->window;
+    cp.H = cfg->n_q_heads;
+    cp.n_seqs = n_seqs;
+    cp.n_tok = n_tok;
+    cp.n_splits = vws.n_splits;
+    cp.split_tiles = vws.split_tiles;
+    if ((stages & BEAM_STAGE_VERIFY_COMBINE) &&
+        (st = hip_status(beam::launch_verify_combine(cp, s), "verify combine launch")) != BEAM_OK)
+      return st;
+  }
 
   beam::AppendParams xp{};
   xp.k_raw = k_raw;
@@ -331,6 +423,45 @@ beam_status beam_attn_prefill_stages(uint32_t stages, const beam_attn_config* cf
       (st = hip_status(beam::launch_kv_append(xp, s), "prefill append launch")) != BEAM_OK)
     return st;
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+beam_status beam_attn_prefill_stages(uint32_t stages, const beam_attn_config* cfg, const beam_kv_cache* cache,
+                                     const beam_bf16* q_raw, const beam_bf16* k_raw, const beam_bf16* v_raw,
+                                     const beam_bf16* q_norm_w, const beam_bf16* k_norm_w,
+                                     const beam_bf16* gate_logits, const float* gate_bias, const int32_t* cu_seqlens,
+                                     const int32_t* seq_idx, const int32_t* start_pos, int32_t n_seqs, int32_t n_tok,
+                                     int32_t max_chunk_len, beam_bf16* out, void* workspace, size_t ws_bytes,
+                                     void* stream) {
+  return chunk_call(false, stages, cfg, cache, q_raw, k_raw, v_raw, q_norm_w, k_norm_w, gate_logits, gate_bias,
+                    cu_seqlens, seq_idx, start_pos, n_seqs, n_tok, max_chunk_len, 0, 0, out, workspace, ws_bytes,
+                    stream);
+}
+
+beam_status beam_attn_verify_stages(uint32_t stages, const beam_attn_config* cfg, const beam_kv_cache* cache,
+                                    const beam_bf16* q_raw, const beam_bf16* k_raw, const beam_bf16* v_raw,
+                                    const beam_bf16* q_norm_w, const beam_bf16* k_norm_w,
+                                    const beam_bf16* gate_logits, const float* gate_bias, const int32_t* cu_seqlens,
+                                    const int32_t* seq_idx, const int32_t* start_pos, int32_t n_seqs, int32_t n_tok,
+                                    int32_t max_chunk_len, int32_t max_pos, int32_t split_keys, beam_bf16* out,
+                                    void* workspace, size_t ws_bytes, void* stream) {
+  return chunk_call(true, stages, cfg, cache, q_raw, k_raw, v_raw, q_norm_w, k_norm_w, gate_logits, gate_bias,
+                    cu_seqlens, seq_idx, start_pos, n_seqs, n_tok, max_chunk_len, max_pos, split_keys, out,
+                    workspace, ws_bytes, stream);
+}
+
+beam_status beam_attn_verify(const beam_attn_config* cfg, const beam_kv_cache* cache, const beam_bf16* q_raw,
+                             const beam_bf16* k_raw, const beam_bf16* v_raw, const beam_bf16* q_norm_w,
+                             const beam_bf16* k_norm_w, const beam_bf16* gate_logits, const float* gate_bias,
+                             const int32_t* cu_seqlens, const int32_t* seq_idx, const int32_t* start_pos,
+                             int32_t n_seqs, int32_t n_tok, int32_t max_chunk_len, int32_t max_pos, int32_t split_keys,
+                             beam_bf16* out, void* workspace, size_t ws_bytes, void* stream) {
+  return beam_attn_verify_stages(BEAM_STAGE_VERIFY_ALL, cfg, cache, q_raw, k_raw, v_raw, q_norm_w, k_norm_w,
+                                 gate_logits, gate_bias, cu_seqlens, seq_idx, start_pos, n_seqs, n_tok, max_chunk_len,
+                                 max_pos, split_keys, out, workspace, ws_bytes, stream);
 }
 
 beam_status beam_attn_prefill(const beam_attn_config* cfg, const beam_kv_cache* cache, const beam_bf16* q_raw,

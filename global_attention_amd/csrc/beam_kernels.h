@@ -92,6 +92,30 @@ struct PrefillParams {
   // FP8 E4M3 cache: a cached prefix is read as codes and dequantised to bf16.
   int kv_fp8;
   float k_scale, v_scale;
+  // Verify (short chunks; key range split over blocks): partials per (token,
+  // query head, split), and the split size in 64-key tiles.
+  float* part_ml;   // [n_tok][H][n_splits][2] (reference max, sum) in base-2 logits
+  float* part_acc;  // [n_tok][H][n_splits][D]
+  int split_tiles, n_splits;
+};
+
+// Verify attention: a block takes one (sequence, KV head, key split) and packs
+// the (token, query head) rows of the chunk, 32 per wavefront.
+constexpr int kVerifyWaves = 4;
+constexpr int kVerifyMaxRows = 32 * kVerifyWaves;
+
+struct VerifyCombineParams {
+  const float* part_ml;
+  const float* part_acc;
+  const int32_t* cu;
+  const int32_t* start_pos;
+  const int32_t* seq_idx;
+  const uint16_t* gate;
+  const float* gate_bias;
+  uint16_t* out;
+  const int32_t* bt;
+  int max_pages, n_cache_seqs;
+  int kind, window, H, n_seqs, n_tok, n_splits, split_tiles;
 };
 
 struct DecodeParams {
@@ -132,5 +156,7 @@ hipError_t launch_visibility(int kind, int window, int t0, int n_q, int s0, int 
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s);
 hipError_t launch_decode_split(const DecodeParams& p, int n_seqs, hipStream_t s);
 hipError_t launch_decode_combine(const CombineParams& p, int n_seqs, hipStream_t s);
+hipError_t launch_verify_attn(const PrefillParams& p, hipStream_t s);
+hipError_t launch_verify_combine(const VerifyCombineParams& p, hipStream_t s);
 
 }  // namespace beam

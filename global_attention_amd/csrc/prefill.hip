@@ -555,6 +555,297 @@ prefill_attn_kernel(PrefillParams p) {
   }
 }
 
+// ---------------------------------------------------------------- verify
+// Attention of a short chunk (the verify step of speculative decoding: a few
+// new tokens per sequence over a long cached history). The chunk's rows are
+// (token, query head) pairs of one KV head, 32 per wavefront (token r / hpg,
+// head r % hpg), so every K/V tile feeds all of them; a block takes one key
+// split of one (sequence, KV head) and writes its partial (reference max, sum,
+// accumulator) per row; verify_combine_kernel merges the splits and gates.
+// Keys come from the cache below the chunk start and from the workspace
+// (written by the prologue) for the chunk itself, as in prefill. Each lane's
+// row has its own query position, so masks are evaluated per lane.
+template <int KIND, int KV_FP8>
+__global__ void __launch_bounds__(64 * kVerifyWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+verify_attn_kernel(PrefillParams p) {
+  constexpr int NWAVES = kVerifyWaves;
+  constexpr bool local = (KIND == 0);
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * (K_TILE + V_TILE)];
+
+  const int hpg = p.H / p.G;
+  int b = blockIdx.x;
+  const int g = b % p.G;  // consecutive blocks -> consecutive XCDs
+  b /= p.G;
+  const int sp = b % p.n_splits;
+  const int seq = b / p.n_splits;
+  const int cu0 = p.cu[seq];
+  const int len = p.cu[seq + 1] - cu0;
+  if (len <= 0) return;
+  const int start = p.start_pos[seq];
+  const int cseq = p.seq_idx[seq];
+  const int W = p.window;
+  const int t_last = start + len - 1;
+
+  KeySource ks;
+  ks.kw = p.kw + (size_t)g * p.P * D;
+  ks.vw = p.vw + (size_t)g * D * p.P;
+  if (KIND == 1) {
+    ks.ck = p.ck + (size_t)g * 16 * D;
+    ks.cv = p.cv + (size_t)g * D * 16;
+    ks.page_stride = (size_t)p.G * 16 * D;
+  } else {
+    const size_t ring = (size_t)cseq * p.G + g;
+    ks.ck = p.ck + ring * W * D;
+    ks.cv = p.cv + ring * D * W;
+    ks.page_stride = 0;
+  }
+  ks.bt_row = KIND == 1 ? p.bt + (size_t)cseq * p.max_pages : nullptr;
+  const bool cache_ok = cseq >= 0 && cseq < p.n_cache_seqs && (KIND == 0 || ((start + 15) >> 4) <= p.max_pages);
+  ks.ws_off = ws_region_base(cu0, seq) - (start & ~63);
+  ks.P = p.P;
+  ks.kind = KIND;
+  ks.window = W;
+
+  // Key tiles of this split.
+  const int j_ws = start >> 6;
+  const int kmin = local ? max(0, start - (W - 1)) : 0;
+  const int j_first = cache_ok ? kmin >> 6 : max(kmin >> 6, j_ws);
+  const int j_last = t_last >> 6;
+  const int j_lo = j_first + sp * p.split_tiles;
+  if (j_lo > j_last) return;  // past this sequence's keys; the combine skips the split
+  const int j_hi = min(j_last, j_lo + p.split_tiles - 1);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31;
+  const int half = lane >> 5;
+  const DmaPlan<NWAVES> plan = make_dma_plan<NWAVES>(w, lane);
+  Fp8Prefix fp8;
+  if constexpr (KV_FP8) {
+    const size_t head = KIND == 1 ? (size_t)g * 16 * D : ((size_t)cseq * p.G + g) * W * D;
+    fp8.k8 = reinterpret_cast<const uint8_t*>(p.ck) + head;
+    fp8.v8 = reinterpret_cast<const uint8_t*>(p.cv) + head;
+    fp8.bt_row = ks.bt_row;
+    fp8.page_stride = (size_t)p.G * 16 * D;
+    fp8.kind = KIND;
+    fp8.window = W;
+    fp8.k_scale = p.k_scale;
+    fp8.v_scale = p.v_scale;
+  }
+
+  // This lane's row and the wave's range of query positions.
+  const int n_rows = len * hpg;
+  const int r = QW * w + n;
+  const bool row_valid = r < n_rows;
+  const int tok_j = row_valid ? r / hpg : 0;
+  const int h = g * hpg + (row_valid ? r - tok_j * hpg : 0);
+  const int t_row = start + tok_j;
+  const int r_lo = QW * w;
+  const bool wave_active = r_lo < n_rows;
+  const int wq_lo = start + r_lo / hpg;
+  const int wq_hi = start + (min(r_lo + QW, n_rows) - 1) / hpg;
+
+  u32x4 qf[8];
+  {
+    const uint16_t* qrow = p.qp + ((size_t)(cu0 + tok_j) * p.H + h) * D + 8 * half;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      qf[kk] = row_valid ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk) : u32x4{0u, 0u, 0u, 0u};
+  }
+  f32x16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+  float m_run = kNegInf, l_run = 0.f;
+  f32x16 sref;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sref[i] = 0.f;
+  int koff[4], voff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    koff[q] = k_off(n, 2 * q + half);
+    voff[q] = v_off(n, 2 * q + half);
+  }
+
+  auto buf = [&](auto B) -> uint16_t* { return smem + decltype(B)::value * (K_TILE + V_TILE); };
+  auto active = [&](int j) __attribute__((always_inline)) {
+    const int k0 = j * BN;
+    return wave_active && k0 <= wq_hi && !(local && k0 + BN - 1 < wq_lo - (W - 1));
+  };
+  auto needs_mask = [&](int j) __attribute__((always_inline)) {
+    const int k0 = j * BN;
+    return (k0 + BN - 1 > wq_lo) || (local && k0 < wq_hi - (W - 1));
+  };
+  auto tile = [&](int j, auto B) __attribute__((always_inline)) {
+    if (!active(j)) return;
+    const uint16_t* sK = buf(B);
+    f32x16 s[2];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sK + koff[kk & 3] + 64 * (kk >> 2) + 32 * D * mb);
+        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qf[kk]), kk == 0 ? sref : s[mb], 0,
+                                                        0, 0);
+      }
+    if (needs_mask(j)) {  // element i of block mb holds key 64j + 32mb + 16(i>>3) + 8*half + (i&7)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int sk = j * BN + 32 * mb + 16 * (i >> 3) + 8 * half + (i & 7);
+          if (!visible(KIND, W, t_row, sk)) s[mb][i] = kNegInf;
+        }
+    }
+    // Reference shift (the row max of the shifted scores when it exceeds the
+    // threshold, or the first finite score of the row).
+    float mt = kNegInf;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[mb][i]);
+    mt = max_halves(mt);
+    const bool need = (m_run == kNegInf) ? (mt != kNegInf) : (mt > kRescaleThreshold);
+    if (__any(need)) {
+      const float delta = need ? mt : 0.f;
+      const bool first = m_run == kNegInf;
+      const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(-delta);
+      if (need) m_run = (first ? 0.f : m_run) + delta;
+      const float rr = m_run == kNegInf ? 0.f : -m_run;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sref[i] = rr;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[mb][i] -= delta;
+    }
+    u32x4 pf[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      float e[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) e[jj] = __builtin_amdgcn_exp2f(s[kb >> 1][8 * (kb & 1) + jj]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        pf[kb][c] = pack_bf16x2(e[2 * c], e[2 * c + 1]);
+        l_run = sum_bf16x2(pf[kb][c], l_run);
+      }
+    }
+    const uint16_t* sV = buf(B) + K_TILE;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sV + voff[kb] + 32 * BN * db);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pf[kb]), o[db], 0, 0, 0);
+      }
+  };
+  auto fetch = [&](int j, auto B) __attribute__((always_inline)) {
+    uint16_t* sK = buf(B);
+    if (j >= j_ws)
+      plan.copy(ks.kw, ks.vw, ks.ws_off, j * BN, sK, sK + K_TILE);
+    else if constexpr (KV_FP8)
+      fetch_prefix_fp8<NWAVES>(fp8, tid, j * BN, sK, sK + K_TILE);
+    else
+      dma_tile_prefix<NWAVES>(ks, w, lane, j * BN, sK, sK + K_TILE);
+  };
+  auto step = [&](int jt, auto B) __attribute__((always_inline)) {
+    if (jt + 1 <= j_hi) fetch(jt + 1, std::integral_constant<int, 1 - decltype(B)::value>{});
+    tile(jt, B);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  fetch(j_lo, std::integral_constant<int, 0>{});
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int jt = j_lo; jt <= j_hi; jt += 2) {
+    step(jt, std::integral_constant<int, 0>{});
+    if (jt + 1 > j_hi) break;
+    step(jt + 1, std::integral_constant<int, 1>{});
+  }
+
+  // Partials of this split: lane holds row n's sum half and coordinates
+  // d = 32db + 8a + 4*half + 0..3.
+  const float l_tot = sum_halves(l_run);
+  if (!row_valid) return;
+  const size_t row = ((size_t)(cu0 + tok_j) * p.H + h) * p.n_splits + sp;
+  if (half == 0) {
+    p.part_ml[2 * row] = m_run;
+    p.part_ml[2 * row + 1] = l_tot;
+  }
+  float* acc = p.part_acc + row * D;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      *reinterpret_cast<f32x4*>(acc + 32 * db + 8 * a + 4 * half) =
+          f32x4{o[db][4 * a], o[db][4 * a + 1], o[db][4 * a + 2], o[db][4 * a + 3]};
+}
+
+// Merge the key splits of one (token, query head) of a verify chunk by
+// log-sum-exp, then apply the gate. One block of 128 threads (a coordinate each).
+__global__ void __launch_bounds__(128) verify_combine_kernel(VerifyCombineParams p) {
+  const int tok = blockIdx.x / p.H;
+  const int h = blockIdx.x - tok * p.H;
+  const int d = threadIdx.x;
+  const int seq = find_seq(p.cu, p.n_seqs, tok);
+  const int start = p.start_pos[seq];
+  const int len = p.cu[seq + 1] - p.cu[seq];
+  const int cseq = p.seq_idx[seq];
+  const bool cache_ok = cseq >= 0 && cseq < p.n_cache_seqs && (p.kind == 0 || ((start + 15) >> 4) <= p.max_pages);
+  const int kmin = p.kind == 0 ? max(0, start - (p.window - 1)) : 0;
+  const int j_first = cache_ok ? kmin >> 6 : max(kmin >> 6, start >> 6);
+  const int j_last = (start + len - 1) >> 6;
+  const int ns = min(p.n_splits, (j_last - j_first + p.split_tiles) / p.split_tiles);
+  const size_t row0 = ((size_t)tok * p.H + h) * p.n_splits;
+  float M = kNegInf;
+  for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, p.part_ml[2 * (row0 + sp)]);
+  float L = 0.f, A = 0.f;
+  if (M != kNegInf) {
+    for (int sp = 0; sp < ns; ++sp) {
+      const float m = p.part_ml[2 * (row0 + sp)];
+      if (m == kNegInf) continue;
+      const float sc = __builtin_amdgcn_exp2f(m - M);
+      L += sc * p.part_ml[2 * (row0 + sp) + 1];
+      A += sc * p.part_acc[(row0 + sp) * D + d];
+    }
+  }
+  const float o = L > 0.f ? A / L : 0.f;
+  const size_t idx = ((size_t)tok * p.H + h) * D + d;
+  const float bias = p.gate_bias ? p.gate_bias[h] : 0.f;
+  const float sg = __frcp_rn(1.f + __expf(-(bf16f(p.gate[idx]) + bias)));
+  bf16x2 rr;
+  rr[0] = (__bf16)(o * sg);
+  p.out[idx] = __builtin_bit_cast(uint16_t, rr[0]);
+}
+
+hipError_t launch_verify_attn(const PrefillParams& p, hipStream_t s) {
+  const long long blocks = (long long)p.G * p.n_splits * p.n_seqs;
+  const dim3 grid((unsigned)blocks), block(64 * kVerifyWaves);
+  if (p.kind == 0 && !p.kv_fp8)
+    hipLaunchKernelGGL((verify_attn_kernel<0, 0>), grid, block, 0, s, p);
+  else if (p.kind == 0)
+    hipLaunchKernelGGL((verify_attn_kernel<0, 1>), grid, block, 0, s, p);
+  else if (!p.kv_fp8)
+    hipLaunchKernelGGL((verify_attn_kernel<1, 0>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((verify_attn_kernel<1, 1>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify_combine(const VerifyCombineParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(verify_combine_kernel, dim3((unsigned)((long long)p.n_tok * p.H)), dim3(128), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {
   const long long blocks = (long long)p.G * (p.H / p.G) * p.n_seqs * p.n_qtiles;
   const dim3 grid((unsigned)blocks), local_block(64 * kPrefillWavesLocal), global_block(64 * kPrefillWavesGlobal);

@@ -159,6 +159,32 @@ beam_status beam_attn_decode(const beam_attn_config *cfg, const beam_kv_cache *c
                              int32_t max_pos, int32_t split_keys, beam_bf16 *out,
                              void *workspace, size_t ws_bytes, void *stream);
 
+/* Verify step of speculative decoding: causal attention of a few new tokens per
+ * sequence (the draft tokens plus the last accepted one) over the cached history,
+ * in one call for n_seqs sequences. The drafter proposes blocks of 8 tokens
+ * ("Beam 1.0 auf vier B300s", orcarouter.ai, the serving recipe) or up to 15
+ * that Beam checks in one pass (news.hamidun.com, the paragraph on reasoning
+ * levels and acceleration); the step is a prefill chunk of that length. Same inputs,
+ * outputs, semantics and append as beam_attn_prefill, computed the way decode
+ * is: the (token, query head) rows of one KV head share every K/V tile, and the
+ * keys are split across blocks with a log-sum-exp merge.
+ * Limits: max_chunk_len * (n_q_heads / n_kv_heads) <= 128 (21 tokens at 48/8).
+ * max_pos >= start_pos[i] + chunk length - 1 for every i (sizes the split grid;
+ * keys beyond the grid it implies are left out, without any access outside the
+ * buffers). split_keys: keys per split (multiple of 64, <= 65536), or 0 for the
+ * default (256 local, 1024 global).
+ * workspace: >= beam_verify_workspace_bytes(cfg, cache->kind, n_tok, n_seqs,
+ * max_chunk_len, max_pos, split_keys) bytes, 256-byte aligned. */
+beam_status beam_attn_verify(const beam_attn_config *cfg, const beam_kv_cache *cache,
+                             const beam_bf16 *q_raw, const beam_bf16 *k_raw,
+                             const beam_bf16 *v_raw, const beam_bf16 *q_norm_w,
+                             const beam_bf16 *k_norm_w, const beam_bf16 *gate_logits,
+                             const float *gate_bias, const int32_t *cu_seqlens,
+                             const int32_t *seq_idx, const int32_t *start_pos,
+                             int32_t n_seqs, int32_t n_tok, int32_t max_chunk_len,
+                             int32_t max_pos, int32_t split_keys, beam_bf16 *out,
+                             void *workspace, size_t ws_bytes, void *stream);
+
 /* Stage selection for the *_stages variants. Running the stages of one call
  * separately, in this order, on one stream, with the same arguments and
  * workspace, is identical to the single call (the workspace carries the state
@@ -171,12 +197,17 @@ beam_status beam_attn_decode(const beam_attn_config *cfg, const beam_kv_cache *c
  *            does not matter there). On a local cache APPEND must come after
  *            ATTENTION when the chunk has a cached prefix.
  *   decode:  PROLOGUE = query norm + RoPE/SSMax, ATTENTION = split-K partials,
- *            COMBINE = merge of the splits + gate into `out`. */
+ *            COMBINE = merge of the splits + gate into `out`.
+ *   verify:  PROLOGUE, APPEND as prefill; ATTENTION = split-key partials,
+ *            VERIFY_COMBINE = merge of the splits + gate into `out` (order:
+ *            PROLOGUE, ATTENTION, VERIFY_COMBINE, APPEND; ALL = VERIFY_ALL). */
 #define BEAM_STAGE_PROLOGUE 1u
 #define BEAM_STAGE_ATTENTION 2u
 #define BEAM_STAGE_APPEND 4u
 #define BEAM_STAGE_COMBINE 4u
 #define BEAM_STAGE_ALL 7u
+#define BEAM_STAGE_VERIFY_COMBINE 8u
+#define BEAM_STAGE_VERIFY_ALL 15u
 
 beam_status beam_attn_prefill_stages(uint32_t stages, const beam_attn_config *cfg,
                                      const beam_kv_cache *cache, const beam_bf16 *q_raw,
@@ -187,6 +218,16 @@ beam_status beam_attn_prefill_stages(uint32_t stages, const beam_attn_config *cf
                                      const int32_t *start_pos, int32_t n_seqs, int32_t n_tok,
                                      int32_t max_chunk_len, beam_bf16 *out, void *workspace,
                                      size_t ws_bytes, void *stream);
+beam_status beam_attn_verify_stages(uint32_t stages, const beam_attn_config *cfg,
+                                    const beam_kv_cache *cache, const beam_bf16 *q_raw,
+                                    const beam_bf16 *k_raw, const beam_bf16 *v_raw,
+                                    const beam_bf16 *q_norm_w, const beam_bf16 *k_norm_w,
+                                    const beam_bf16 *gate_logits, const float *gate_bias,
+                                    const int32_t *cu_seqlens, const int32_t *seq_idx,
+                                    const int32_t *start_pos, int32_t n_seqs, int32_t n_tok,
+                                    int32_t max_chunk_len, int32_t max_pos, int32_t split_keys,
+                                    beam_bf16 *out, void *workspace, size_t ws_bytes,
+                                    void *stream);
 beam_status beam_attn_decode_stages(uint32_t stages, const beam_attn_config *cfg,
                                     const beam_kv_cache *cache, const beam_bf16 *q_raw,
                                     const beam_bf16 *q_norm_w, const beam_bf16 *gate_logits,
@@ -199,6 +240,9 @@ beam_status beam_attn_decode_stages(uint32_t stages, const beam_attn_config *cfg
 size_t beam_prefill_workspace_bytes(const beam_attn_config *cfg, int32_t n_tok, int32_t n_seqs);
 size_t beam_decode_workspace_bytes(const beam_attn_config *cfg, int32_t kind, int32_t n_seqs,
                                    int32_t max_pos, int32_t split_keys);
+size_t beam_verify_workspace_bytes(const beam_attn_config *cfg, int32_t kind, int32_t n_tok,
+                                   int32_t n_seqs, int32_t max_chunk_len, int32_t max_pos,
+                                   int32_t split_keys);
 
 /* KV payload of n_global growing caches plus n_local window-sized caches, per
  * sequence ("KV memory: nine growing caches, not 52"): logical =

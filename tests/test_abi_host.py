@@ -127,3 +127,44 @@ def test_argument_checks_fail_before_launch():
     assert L.beam_kv_append(ctypes.byref(c), ctypes.byref(kc), *([None] * 5), 0, None) == 0
     assert L.beam_debug_visibility(2, 512, 0, 4, 0, 4, fake, None) == 3
     assert L.beam_status_str(5) == b"workspace too small"
+
+
+def _call_verify(cfg, cache, max_chunk=4, max_pos=100, split_keys=0, ws_bytes=1 << 30, n_tok=4, n_seqs=1):
+    L = ga.lib()
+    c = cfg.c()
+    fake = ctypes.c_void_p(0x100000)  # never dereferenced: the checks fail first
+    return L.beam_attn_verify(ctypes.byref(c), ctypes.byref(cache), fake, fake, fake, fake, fake, fake, None, fake,
+                              fake, fake, n_seqs, n_tok, max_chunk, max_pos, split_keys, fake,
+                              ctypes.c_void_p(0x1000), ws_bytes, None)
+
+
+def test_verify_workspace_and_checks():
+    cfg = ga.Config()
+    L = ga.lib()
+    # splits: global keys 0..max_pos in 64-key tiles, 16 tiles per default split
+    base = ga.prefill_workspace_bytes(cfg, 64, 8)
+    for max_pos, splits in ((0, 1), (1023, 1), (1024, 2), (131071, 128)):
+        rows = 64 * 48 * splits
+        want = base + ((rows * 8 + 255) // 256) * 256 + ((rows * 512 + 255) // 256) * 256
+        assert ga.verify_workspace_bytes(cfg, ga.GLOBAL, 64, 8, 8, max_pos) == want
+    # local: the window bounds the keys (511 + 7 positions span at most 10 tiles -> 3 splits of 4)
+    rows = 64 * 48 * 3
+    want = base + ((rows * 8 + 255) // 256) * 256 + ((rows * 512 + 255) // 256) * 256
+    assert ga.verify_workspace_bytes(cfg, ga.LOCAL, 64, 8, 8, 131071) == want
+    assert ga.verify_workspace_bytes(cfg, ga.GLOBAL, 64, 8, 8, 1000, split_keys=96) == 0
+    assert ga.verify_workspace_bytes(cfg, ga.GLOBAL, 64, 8, 8, 1000, split_keys=64) > 0
+    assert ga.verify_workspace_bytes(cfg, 2, 64, 8, 8, 1000) == 0
+    # 21 tokens x 6 heads = 126 rows fit one 128-row block; 22 do not
+    assert _call_verify(cfg, _cache(), max_chunk=22, n_tok=22) == 3
+    assert "128" in L.beam_last_error().decode()
+    assert _call_verify(cfg, _cache(), split_keys=100) == 3
+    assert _call_verify(cfg, _cache(), max_pos=2) == 3  # below max_chunk_len - 1
+    assert _call_verify(cfg, _cache(), ws_bytes=ga.prefill_workspace_bytes(cfg, 4, 1)) == 5
+    # empty work succeeds without launching
+    c, kc = cfg.c(), _cache()
+    assert L.beam_attn_verify(ctypes.byref(c), ctypes.byref(kc), *([None] * 10), 1, 0, 0, 0, 0, None, None, 0,
+                              None) == 0
+    # unknown stage bits (16 and above)
+    fake = ctypes.c_void_p(0x100000)
+    assert L.beam_attn_verify_stages(16, ctypes.byref(c), ctypes.byref(kc), *([fake] * 6), None, fake, fake, fake,
+                                     1, 4, 4, 100, 0, fake, ctypes.c_void_p(0x1000), 1 << 30, None) == 3
