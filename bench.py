@@ -11,7 +11,9 @@ layer's cache. `value` is the algorithmic attention TFLOP/s of the whole step
 Also measured in the same run (reported under "decode"): batched decode of 64
 sequences at positions uniform in [65536, 131071] over a paged bf16 cache
 (16-token pages, random page permutation), global and local layer; value in
-GB/s of KV read (4,096 B per cached key per layer).
+GB/s of KV read (4,096 B per cached key per layer). And under "verify": the
+verify step of speculative decoding on the same caches, a draft block of 8
+tokens per sequence ending at the decode position, in GB/s of cached KV read.
 
 Prints ONE JSON line on stdout. Everything else goes to stderr.
 """
@@ -45,6 +47,9 @@ _KERNEL_SOURCES = {
     "decode_split_kernel<1>": "decode.hip",
     "decode_split_kernel<0>": "decode.hip",
     "decode_fp8_kernel<1>": "decode.hip",
+    "verify_attn_kernel<1, 0>": "prefill.hip",
+    "verify_attn_kernel<0, 0>": "prefill.hip",
+    "verify_attn_kernel<1, 1>": "prefill.hip",
     "prefill_prologue_kernel<0, 0>": "prologue.hip",
     "prefill_prologue_kernel<1, 0>": "prologue.hip",
 }
@@ -196,7 +201,8 @@ def setup_decode(n_seqs=64, lo=65536, hi=131071, seed=3):
 def bench_decode(steps, warmup):
     import torch
     import global_attention_amd as ga
-    cfg, ts, gcache, lcache, fcache, d = setup_decode()
+    setup = setup_decode()
+    cfg, ts, gcache, lcache, fcache, d = setup
     n = len(ts)
     seq = _i32(list(range(n)))
     pos = _i32(ts)
@@ -231,6 +237,65 @@ def bench_decode(steps, warmup):
         res[name] = dict(bytes=nbytes, ms_per_call=el * 1e3, split_ms=split_ms,
                          gbs_call=nbytes / el / 1e9, gbs_split=nbytes / (split_ms / 1e3) / 1e9)
         log(f"[bench] decode {name}: {nbytes / 1e9:.2f} GB, call {el * 1e3:.3f} ms, split kernel {split_ms:.3f} ms")
+    res["setup"] = setup
+    return res
+
+
+def bench_verify(steps, warmup, dres, block=8, split_keys=0):
+    """Verify of `block` tokens per sequence (positions ts-block+1 .. ts) over the
+    decode caches: prologue, split attention (timed with events), combine, append."""
+    import numpy as np
+    import torch
+    import global_attention_amd as ga
+    import synth
+    cfg, ts, gcache, lcache, fcache, _ = dres["setup"]
+    n = len(ts)
+    starts = (ts - (block - 1)).astype(np.int32)
+    inp = synth.attention_inputs(cfg=3, layer=9, n_tok=n * block)
+    d = {k: _dev(v) for k, v in inp.items()}
+    cu = _i32(np.arange(n + 1) * block)
+    seq = _i32(list(range(n)))
+    st = _i32(starts)
+    max_pos = int(ts.max())
+    res = {}
+    for name, cache in (("global", gcache), ("local", lcache), ("global_fp8", fcache)):
+        out = torch.empty((n * block, H, D), dtype=torch.bfloat16, device="cuda")
+        nb = ga.verify_workspace_bytes(cfg, cache.kind, n * block, n, block, max_pos, split_keys)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        args = (cfg, cache, d["q"], d["k"], d["v"], d["q_norm_w"], d["k_norm_w"], d["gate"], cu, seq, st, block,
+                max_pos)
+        kw = dict(split_keys=split_keys, out=out, workspace=ws)
+        # global caches: the prologue also appends (one launch); local: append last
+        pro = ga.STAGE_PROLOGUE | (ga.STAGE_APPEND if cache.kind == ga.GLOBAL else 0)
+        tail = ga.STAGE_VERIFY_COMBINE | (ga.STAGE_APPEND if cache.kind == ga.LOCAL else 0)
+
+        def one(ev=None):
+            ga.verify(*args, **kw, stages=pro)
+            if ev is not None:
+                ev[0].record()
+            ga.verify(*args, **kw, stages=ga.STAGE_ATTENTION)
+            if ev is not None:
+                ev[1].record()
+            ga.verify(*args, **kw, stages=tail)
+
+        for _ in range(warmup):
+            one()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for s in range(steps):
+            one(evs[s])
+        torch.cuda.synchronize()
+        el = (time.perf_counter() - t0) / steps
+        split_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+        # cached keys each chunk reads once (the chunk's own keys come from the workspace)
+        keys = [min(int(s), W - 1) if name == "local" else int(s) for s in starts]
+        nbytes = sum(keys) * G * D * 2 * (1 if cache.dtype == ga.KV_FP8_E4M3 else 2)
+        res[name] = dict(bytes=nbytes, ms_per_call=el * 1e3, split_ms=split_ms,
+                         gbs_call=nbytes / el / 1e9, gbs_split=nbytes / (split_ms / 1e3) / 1e9,
+                         vs_decode_calls=block * dres[name]["ms_per_call"] / (el * 1e3))
+        log(f"[bench] verify {name} ({block} tokens/seq): {nbytes / 1e9:.2f} GB, call {el * 1e3:.3f} ms, "
+            f"split kernel {split_ms:.3f} ms, {res[name]['vs_decode_calls']:.2f}x {block} decode calls")
     return res
 
 
@@ -282,6 +347,7 @@ def main():
     ap.add_argument("--seq-len", type=int, default=32768)
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--verify-split-keys", type=int, default=0)
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=384)
@@ -359,6 +425,26 @@ def main():
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(f["gbs_split"] / PEAK_HBM_GBS, 4),
                          "traffic": recorded_traffic("decode_fp8_kernel<1>"),
                          "avg_launch_ms": round(f["split_ms"], 4), "bytes_per_launch": f["bytes"]},
+        }
+        v = bench_verify(args.decode_steps, 3, dres, split_keys=args.verify_split_keys)
+        vg = v["global"]
+        rec["verify"] = {
+            "workload": "verify step of an 8-token draft per sequence (positions t-7..t) on the decode caches: "
+                        "prologue, split-key attention, combine, append; global and local layer, and the "
+                        "global layer over the FP8 cache",
+            "value": round(vg["gbs_call"], 1), "unit": "GB/s",
+            "frac_of_hbm_peak": round(vg["gbs_call"] / PEAK_HBM_GBS, 4),
+            "global_bytes": vg["bytes"], "global_ms_per_call": round(vg["ms_per_call"], 4),
+            "speedup_vs_8_decode_calls": round(vg["vs_decode_calls"], 2),
+            "roofline": {"kernel": "verify_attn_kernel<1, 0>", "bound": "hbm", "achieved": round(vg["gbs_split"], 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(vg["gbs_split"] / PEAK_HBM_GBS, 4),
+                         "traffic": recorded_traffic("verify_attn_kernel<1, 0>"),
+                         "avg_launch_ms": round(vg["split_ms"], 4), "bytes_per_launch": vg["bytes"]},
+            "local": {"ms_per_call": round(v["local"]["ms_per_call"], 4),
+                      "speedup_vs_8_decode_calls": round(v["local"]["vs_decode_calls"], 2)},
+            "global_fp8": {"ms_per_call": round(v["global_fp8"]["ms_per_call"], 4),
+                           "gbs_split": round(v["global_fp8"]["gbs_split"], 1),
+                           "speedup_vs_8_decode_calls": round(v["global_fp8"]["vs_decode_calls"], 2)},
         }
     if not args.no_cpu_baseline and layers is not None:
         log(f"[bench] timing the CPU oracle on {args.cpu_rows} rows per layer")

@@ -103,7 +103,7 @@ PrefillWs prefill_ws_layout(const beam_attn_config* c, int n_tok, int n_seqs) {
   return ws;
 }
 
-int default_verify_split_keys(int kind) { return kind == BEAM_LOCAL ? 256 : 1024; }
+int default_verify_split_keys(int kind) { return kind == BEAM_LOCAL ? 256 : 2048; }
 
 // Verify (short-chunk) calls: the prefill workspace, then the split partials
 // (reference max and sum, and the unnormalised accumulator) per (token, head,
@@ -117,7 +117,7 @@ struct VerifyWs {
 bool verify_ws_layout(const beam_attn_config* c, int kind, int n_tok, int n_seqs, int max_chunk_len, int max_pos,
                       int split_keys, VerifyWs* ws) {
   if (split_keys == 0) split_keys = default_verify_split_keys(kind);
-  if (split_keys < 64 || split_keys % 64 != 0 || split_keys > 65536) return false;
+  if (split_keys < 64 || split_keys % 64 != 0 || split_keys > 64 * beam::kVerifyMaxSplitTiles) return false;
   if (n_seqs <= 0 || n_tok < 0 || max_chunk_len < 0 || max_pos < 0) return false;
   int n_tiles = (max_pos >> 6) + 1;
   if (kind == BEAM_LOCAL) {
@@ -278,7 +278,7 @@ beam_status chunk_call(bool verify, uint32_t stages, const beam_attn_config* cfg
                                     std::to_string(beam::kVerifyMaxRows));
     if (max_pos < max_chunk_len - 1) return fail(BEAM_E_RANGE, "max_pos must be >= max_chunk_len - 1");
     if (!verify_ws_layout(cfg, cache->kind, n_tok, n_seqs, max_chunk_len, max_pos, split_keys, &vws))
-      return fail(BEAM_E_RANGE, "split_keys must be 0 or a multiple of 64 in [64, 65536]");
+      return fail(BEAM_E_RANGE, "split_keys must be 0 or a multiple of 64 in [64, 8192]");
     if (ws_bytes < vws.total)
       return fail(BEAM_E_WORKSPACE, "verify workspace needs " + std::to_string(vws.total) + " bytes");
     if ((int64_t)cfg->n_kv_heads * vws.n_splits * n_seqs > 0x7fffffffLL || (int64_t)n_tok * cfg->n_q_heads > 0x7fffffffLL)

@@ -103,6 +103,7 @@ struct PrefillParams {
 // the (token, query head) rows of the chunk, 32 per wavefront.
 constexpr int kVerifyWaves = 4;
 constexpr int kVerifyMaxRows = 32 * kVerifyWaves;
+constexpr int kVerifyMaxSplitTiles = 128;  // 64-key tiles per verify split (their page ids are staged in LDS)
 
 struct VerifyCombineParams {
   const float* part_ml;

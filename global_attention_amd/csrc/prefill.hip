@@ -565,12 +565,101 @@ prefill_attn_kernel(PrefillParams p) {
 // Keys come from the cache below the chunk start and from the workspace
 // (written by the prologue) for the chunk itself, as in prefill. Each lane's
 // row has its own query position, so masks are evaluated per lane.
+//
+// The split's page ids are staged in LDS first, so the DMA address path of a
+// cached tile reads LDS instead of waiting on a block-table load.
+constexpr int kVerifyMaxPages = 4 * kVerifyMaxSplitTiles;  // 4 pages per 64-key tile
+
+// Cached K row s / V^T element (d, s) with the page id taken from the
+// LDS-staged list (pages[i] = block-table entry page0 + i) on paged caches.
+__device__ __forceinline__ const uint16_t* k_row_cached(const KeySource& ks, const int* pages, int page0, int s) {
+  if (ks.kind == 1) return ks.ck + pages[(s >> 4) - page0] * ks.page_stride + (uint32_t)((s & 15) * D);
+  return ks.ck + (uint32_t)((s % ks.window) * D);
+}
+__device__ __forceinline__ const uint16_t* v_elem_cached(const KeySource& ks, const int* pages, int page0, int d,
+                                                         int s) {
+  if (ks.kind == 1) return ks.cv + pages[(s >> 4) - page0] * ks.page_stride + (uint32_t)(d * 16 + (s & 15));
+  return ks.cv + (uint32_t)(d * ks.window + s % ks.window);
+}
+
+// DMA of a cached-prefix tile; the same chunks and LDS positions as
+// dma_tile_prefix (16 / NW instructions each for K and V per wave).
+template <int NW>
+__device__ __forceinline__ void dma_tile_cached(const KeySource& ks, const int* pages, int page0, int w, int lane,
+                                                int key0, uint16_t* sK, uint16_t* sV) {
+#pragma unroll
+  for (int i = 0; i < DmaPlan<NW>::N; ++i) {
+    const int kI = w * DmaPlan<NW>::N + i;
+    const int m = 4 * kI + (lane >> 4);
+    const int c = (lane & 15) ^ (m & 7);
+    lds_dma16(k_row_cached(ks, pages, page0, key0 + krow_key(m)) + 8 * c, sK + kI * 512);
+    const int vI = w * DmaPlan<NW>::N + i;
+    const int d = 8 * vI + (lane >> 3);
+    const int cv = (lane & 7) ^ (d & 7);
+    lds_dma16(v_elem_cached(ks, pages, page0, d, key0 + 8 * cv), sV + vI * 512);
+  }
+}
+
+// FP8 prefix tile in two phases: the codes into registers, then dequantised
+// into LDS (the chunks of fetch_prefix_fp8).
+// s_waitcnt immediate for vmcnt <= n, lgkmcnt 0, expcnt untouched (gfx9
+// fields: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]).
+constexpr int vm_lgkm_wait(int n) { return (n & 15) | (7 << 4) | (((n >> 4) & 3) << 14); }
+
+template <int NW>
+struct Fp8Regs {
+  static constexpr int R = 8 / NW;
+  u32x4 k[R], v[R];
+};
+template <int NW>
+__device__ __forceinline__ void load_prefix_fp8(const Fp8Prefix& fp, const int* pages, int page0, int tid, int key0,
+                                                Fp8Regs<NW>& r) {
+#pragma unroll
+  for (int i = 0; i < Fp8Regs<NW>::R; ++i) {
+    const int id = tid + 64 * NW * i;
+    {
+      const int m = id >> 3, c2 = id & 7;
+      const int s = key0 + krow_key(m);
+      const uint8_t* src = fp.kind == 1 ? fp.k8 + pages[(s >> 4) - page0] * fp.page_stride + (size_t)((s & 15) * D)
+                                        : fp.k8 + (size_t)((s % fp.window) * D);
+      r.k[i] = *reinterpret_cast<const u32x4*>(src + 16 * c2);
+    }
+    {
+      const int d = id >> 2, c2 = id & 3;
+      const int s = key0 + 16 * c2;
+      const uint8_t* src = fp.kind == 1 ? fp.v8 + pages[(s >> 4) - page0] * fp.page_stride + (size_t)(d * 16)
+                                        : fp.v8 + (size_t)(d * fp.window + s % fp.window);
+      r.v[i] = *reinterpret_cast<const u32x4*>(src);
+    }
+  }
+}
+template <int NW>
+__device__ __forceinline__ void store_prefix_fp8(const Fp8Prefix& fp, int tid, const Fp8Regs<NW>& r, uint16_t* sK,
+                                                 uint16_t* sV) {
+#pragma unroll
+  for (int i = 0; i < Fp8Regs<NW>::R; ++i) {
+    const int id = tid + 64 * NW * i;
+    const int m = id >> 3, ck = id & 7;
+    *reinterpret_cast<u32x4*>(sK + k_off(m, 2 * ck)) = fp8x8_dequant_bf16(r.k[i][0], r.k[i][1], fp.k_scale);
+    *reinterpret_cast<u32x4*>(sK + k_off(m, 2 * ck + 1)) = fp8x8_dequant_bf16(r.k[i][2], r.k[i][3], fp.k_scale);
+    const int d = id >> 2, cv = id & 3;
+    *reinterpret_cast<u32x4*>(sV + v_off(d, 2 * cv)) = fp8x8_dequant_bf16(r.v[i][0], r.v[i][1], fp.v_scale);
+    *reinterpret_cast<u32x4*>(sV + v_off(d, 2 * cv + 1)) = fp8x8_dequant_bf16(r.v[i][2], r.v[i][3], fp.v_scale);
+  }
+}
+
 template <int KIND, int KV_FP8>
 __global__ void __launch_bounds__(64 * kVerifyWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 verify_attn_kernel(PrefillParams p) {
   constexpr int NWAVES = kVerifyWaves;
   constexpr bool local = (KIND == 0);
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * (K_TILE + V_TILE)];
+  // One LDS object: with a second __shared__ variable the compiler tags LDS
+  // accesses with alias scopes and then makes every LDS read wait for all DMA
+  // into the same array (vmcnt(0) before each tile's MFMAs), which serialises
+  // the fetch of tile jt + 1 with the compute of tile jt.
+  constexpr int kTiles = 2 * (K_TILE + V_TILE);
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[kTiles + (KIND == 1 ? 2 * kVerifyMaxPages : 0)];
+  int* const s_pages = reinterpret_cast<int*>(smem + kTiles);
 
   const int hpg = p.H / p.G;
   int b = blockIdx.x;
@@ -632,6 +721,14 @@ verify_attn_kernel(PrefillParams p) {
     fp8.window = W;
     fp8.k_scale = p.k_scale;
     fp8.v_scale = p.v_scale;
+  }
+
+  // Page ids of the split's cached tiles (tiles j_lo .. min(j_hi, j_ws - 1);
+  // pages below (start & ~63) / 16, inside the block-table row).
+  const int page0 = 4 * j_lo;
+  if (KIND == 1 && cache_ok) {
+    const int n_pg = 4 * (min(j_hi, j_ws - 1) - j_lo + 1);
+    for (int i = tid; i < n_pg; i += 64 * NWAVES) s_pages[i] = ks.bt_row[page0 + i];
   }
 
   // This lane's row and the wave's range of query positions.
@@ -747,25 +844,65 @@ verify_attn_kernel(PrefillParams p) {
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pf[kb]), o[db], 0, 0, 0);
       }
   };
-  auto fetch = [&](int j, auto B) __attribute__((always_inline)) {
+  // DMA of tile j (workspace or bf16 cache) into buffer B.
+  auto dma = [&](int j, auto B) __attribute__((always_inline)) {
     uint16_t* sK = buf(B);
     if (j >= j_ws)
       plan.copy(ks.kw, ks.vw, ks.ws_off, j * BN, sK, sK + K_TILE);
-    else if constexpr (KV_FP8)
-      fetch_prefix_fp8<NWAVES>(fp8, tid, j * BN, sK, sK + K_TILE);
     else
-      dma_tile_prefix<NWAVES>(ks, w, lane, j * BN, sK, sK + K_TILE);
+      dma_tile_cached<NWAVES>(ks, s_pages, page0, w, lane, j * BN, sK, sK + K_TILE);
+  };
+  __builtin_amdgcn_s_waitcnt(0);  // Q' and page ids in
+  __syncthreads();
+  // Two LDS buffers: tile jt + 1 arrives while tile jt is computed. DMA tiles
+  // are sent one step ahead. FP8 prefix tiles go through registers two steps
+  // ahead (regs[b] for the tile that will use buffer b) and are converted
+  // into LDS after the MFMAs of the step before their own; such a step ends
+  // waiting for its DMA and LDS stores only, leaving the newest code loads in
+  // flight. The barrier is a bare s_barrier: the workgroup fence of
+  // __syncthreads would wait for every load still in flight. The empty asm
+  // statements keep the compiler from moving LDS accesses across it.
+  [[maybe_unused]] Fp8Regs<NWAVES> regs[2];
+  auto reg_tile = [&](int j) { return KV_FP8 && j <= j_hi && j < j_ws; };
+  auto step_end = [&](bool codes_in_flight) __attribute__((always_inline)) {
+    if (codes_in_flight)
+      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(2 * Fp8Regs<NWAVES>::R));
+    else
+      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
   auto step = [&](int jt, auto B) __attribute__((always_inline)) {
-    if (jt + 1 <= j_hi) fetch(jt + 1, std::integral_constant<int, 1 - decltype(B)::value>{});
+    constexpr int b = decltype(B)::value;
+    const int jn = jt + 1;
+    if (jn <= j_hi && !reg_tile(jn)) dma(jn, std::integral_constant<int, 1 - b>{});
+    const bool load_nn = reg_tile(jt + 2);
+    if constexpr (KV_FP8) {
+      asm volatile("" ::: "memory");  // the DMA is issued before the code loads below
+      if (load_nn) load_prefix_fp8<NWAVES>(fp8, s_pages, page0, tid, (jt + 2) * BN, regs[b]);
+    }
     tile(jt, B);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    if constexpr (KV_FP8) {
+      if (reg_tile(jn))
+        store_prefix_fp8<NWAVES>(fp8, tid, regs[1 - b], buf(std::integral_constant<int, 1 - b>{}),
+                                 buf(std::integral_constant<int, 1 - b>{}) + K_TILE);
+    }
+    step_end(load_nn);
   };
-
-  fetch(j_lo, std::integral_constant<int, 0>{});
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  if (reg_tile(j_lo)) {
+    if constexpr (KV_FP8) {
+      load_prefix_fp8<NWAVES>(fp8, s_pages, page0, tid, j_lo * BN, regs[0]);
+      store_prefix_fp8<NWAVES>(fp8, tid, regs[0], smem, smem + K_TILE);
+    }
+  } else {
+    dma(j_lo, std::integral_constant<int, 0>{});
+  }
+  if constexpr (KV_FP8) {
+    asm volatile("" ::: "memory");
+    if (reg_tile(j_lo + 1)) load_prefix_fp8<NWAVES>(fp8, s_pages, page0, tid, (j_lo + 1) * BN, regs[1]);
+  }
+  step_end(reg_tile(j_lo + 1));
   for (int jt = j_lo; jt <= j_hi; jt += 2) {
     step(jt, std::integral_constant<int, 0>{});
     if (jt + 1 > j_hi) break;
@@ -828,6 +965,7 @@ __global__ void __launch_bounds__(128) verify_combine_kernel(VerifyCombineParams
 }
 
 hipError_t launch_verify_attn(const PrefillParams& p, hipStream_t s) {
+  if (p.split_tiles * 4 > kVerifyMaxPages) return hipErrorInvalidValue;
   const long long blocks = (long long)p.G * p.n_splits * p.n_seqs;
   const dim3 grid((unsigned)blocks), block(64 * kVerifyWaves);
   if (p.kind == 0 && !p.kv_fp8)

@@ -171,8 +171,8 @@ beam_status beam_attn_decode(const beam_attn_config *cfg, const beam_kv_cache *c
  * Limits: max_chunk_len * (n_q_heads / n_kv_heads) <= 128 (21 tokens at 48/8).
  * max_pos >= start_pos[i] + chunk length - 1 for every i (sizes the split grid;
  * keys beyond the grid it implies are left out, without any access outside the
- * buffers). split_keys: keys per split (multiple of 64, <= 65536), or 0 for the
- * default (256 local, 1024 global).
+ * buffers). split_keys: keys per split (multiple of 64, <= 8192), or 0 for the
+ * default (256 local, 2048 global).
  * workspace: >= beam_verify_workspace_bytes(cfg, cache->kind, n_tok, n_seqs,
  * max_chunk_len, max_pos, split_keys) bytes, 256-byte aligned. */
 beam_status beam_attn_verify(const beam_attn_config *cfg, const beam_kv_cache *cache,

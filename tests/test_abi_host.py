@@ -141,9 +141,9 @@ def _call_verify(cfg, cache, max_chunk=4, max_pos=100, split_keys=0, ws_bytes=1 
 def test_verify_workspace_and_checks():
     cfg = ga.Config()
     L = ga.lib()
-    # splits: global keys 0..max_pos in 64-key tiles, 16 tiles per default split
+    # splits: global keys 0..max_pos in 64-key tiles, 32 tiles per default split
     base = ga.prefill_workspace_bytes(cfg, 64, 8)
-    for max_pos, splits in ((0, 1), (1023, 1), (1024, 2), (131071, 128)):
+    for max_pos, splits in ((0, 1), (2047, 1), (2048, 2), (131071, 64)):
         rows = 64 * 48 * splits
         want = base + ((rows * 8 + 255) // 256) * 256 + ((rows * 512 + 255) // 256) * 256
         assert ga.verify_workspace_bytes(cfg, ga.GLOBAL, 64, 8, 8, max_pos) == want
@@ -153,6 +153,8 @@ def test_verify_workspace_and_checks():
     assert ga.verify_workspace_bytes(cfg, ga.LOCAL, 64, 8, 8, 131071) == want
     assert ga.verify_workspace_bytes(cfg, ga.GLOBAL, 64, 8, 8, 1000, split_keys=96) == 0
     assert ga.verify_workspace_bytes(cfg, ga.GLOBAL, 64, 8, 8, 1000, split_keys=64) > 0
+    assert ga.verify_workspace_bytes(cfg, ga.GLOBAL, 64, 8, 8, 1000, split_keys=8192) > 0
+    assert ga.verify_workspace_bytes(cfg, ga.GLOBAL, 64, 8, 8, 1000, split_keys=8256) == 0
     assert ga.verify_workspace_bytes(cfg, 2, 64, 8, 8, 1000) == 0
     # 21 tokens x 6 heads = 126 rows fit one 128-row block; 22 do not
     assert _call_verify(cfg, _cache(), max_chunk=22, n_tok=22) == 3
