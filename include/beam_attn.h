@@ -173,6 +173,11 @@ beam_status beam_attn_decode(const beam_attn_config *cfg, const beam_kv_cache *c
  * keys beyond the grid it implies are left out, without any access outside the
  * buffers). split_keys: keys per split (multiple of 64, <= 8192), or 0 for the
  * default (256 local, 2048 global).
+ * Rejected draft tokens: on a GLOBAL cache the next call simply starts at the
+ * first rejected position (its slots are overwritten). A LOCAL ring keeps only
+ * the last `window` positions, so appending a rejected token would evict a key
+ * the next chunk needs: on local layers run beam_attn_verify_stages without
+ * BEAM_STAGE_APPEND and append the accepted tokens with beam_kv_append.
  * workspace: >= beam_verify_workspace_bytes(cfg, cache->kind, n_tok, n_seqs,
  * max_chunk_len, max_pos, split_keys) bytes, 256-byte aligned. */
 beam_status beam_attn_verify(const beam_attn_config *cfg, const beam_kv_cache *cache,

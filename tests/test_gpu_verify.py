@@ -213,3 +213,44 @@ def test_verify_64seq_128k_draft8_sampled():
             ref = _chunk_oracle(kind, batch[sq], s0, kh, v, pos)
             compare(outs[sq], ref, f"verify {name} seq {sq} start={s0}")
     del gcache, lcache
+
+
+@pytest.mark.parametrize("kind", [O.LOCAL, O.GLOBAL])
+def test_verify_accept_and_roll_back(kind):
+    """An 8-token draft of which 3 tokens are accepted, then a new draft from
+    the first rejected position. Global: the call appends all 8 and the next
+    chunk overwrites the rejected slots. Local: verify without the append
+    stage, then the accepted tokens go in with kv_append."""
+    hist, draft, acc = 900, 8, 3
+    x = synth.attention_inputs(22, 10 * kind, hist + draft)          # history + first draft
+    y = synth.attention_inputs(23, 10 * kind, draft)                 # second draft
+    y["q_norm_w"], y["k_norm_w"] = x["q_norm_w"], x["k_norm_w"]
+    cache, _ = _cache(kind, 22, [hist + acc + draft])
+    _prefill(cache, [_slice(x, 0, hist)], [0], [0])
+    stages = ga.STAGE_VERIFY_ALL if kind == O.GLOBAL else ga.STAGE_VERIFY_ALL & ~ga.STAGE_APPEND
+
+    def run(chunk, s0):
+        lens, cu, cat = _packed([chunk])
+        out = ga.verify(CFG, cache, cat("q"), cat("k"), cat("v"), dev_bf16(chunk["q_norm_w"]),
+                        dev_bf16(chunk["k_norm_w"]), cat("gate"), dev_i32(cu), dev_i32([0]), dev_i32([s0]), draft,
+                        s0 + draft - 1, stages=stages)
+        sync()
+        if kind == O.LOCAL:  # append the accepted tokens only
+            ga.kv_append(CFG, cache, dev_bf16(chunk["k"][:acc]), dev_bf16(chunk["v"][:acc]),
+                         dev_bf16(chunk["k_norm_w"]), dev_i32([0] * acc), dev_i32(np.arange(s0, s0 + acc)))
+            sync()
+        return host_bits(out)
+
+    say(f"[case] verify accept/roll back kind={kind}: first draft at {hist}")
+    o1 = run(_slice(x, hist, draft), hist)
+    ref1 = O.attention_layer(kind, x["q"][hist:], x["k"], x["v"], x["q_norm_w"], x["k_norm_w"], x["gate"][hist:],
+                             np.arange(hist, hist + draft), np.arange(hist + draft))
+    compare(o1, ref1, f"first draft kind={kind}")
+    s1 = hist + acc
+    say(f"[case] verify accept/roll back kind={kind}: second draft at {s1}")
+    o2 = run(y, s1)
+    k_all = np.concatenate([x["k"][:s1], y["k"]])
+    v_all = np.concatenate([x["v"][:s1], y["v"]])
+    ref2 = O.attention_layer(kind, y["q"], k_all, v_all, y["q_norm_w"], y["k_norm_w"], y["gate"],
+                             np.arange(s1, s1 + draft), np.arange(s1 + draft))
+    compare(o2, ref2, f"second draft kind={kind}")
