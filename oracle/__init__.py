@@ -5,3 +5,4 @@ baseline leg of bench.py; never by the product path.
 """
 from .beam_attention import *  # noqa: F401,F403
 from .beam_attention import Config, LOCAL, GLOBAL  # noqa: F401
+from . import router  # noqa: F401

@@ -10,6 +10,8 @@ SeedSequence([cfg, tensor_id, layer, b])))`` as float32 N(0,1) values (blocks
 are drawn in parallel threads), which are rounded to bfloat16 with
 round-to-nearest-even and kept as ``uint16`` bit patterns.
 RMSNorm weights are 1 + 0.1*N(0,1), gate logits N(0,1), gate bias absent.
+Router inputs (the MoE layers' expert selection): hidden states bf16 N(0,1),
+a float32 weight 0.02*N(0,1) and a float32 selection bias 0.05*N(0,1).
 Position/page structure (decode contexts, random page permutation, chunked
 prefill lengths) is drawn from the same kind of generator with its own id.
 """
@@ -25,6 +27,7 @@ _THREADS = max(1, min(16, os.cpu_count() or 1))
 
 # tensor ids for SeedSequence([cfg, tensor_id, layer])
 T_Q, T_K, T_V, T_GATE, T_QW, T_KW, T_POS, T_PERM, T_LEN, T_MISC = range(10)
+T_RX, T_RW, T_RB = 10, 11, 12  # router: hidden states, weight, selection bias
 
 
 def rng(cfg: int, tensor_id: int, layer: int = 0) -> np.random.Generator:
@@ -79,6 +82,29 @@ def attention_inputs(cfg: int, layer: int, n_tok: int, n_q: int = 48, n_kv: int 
         gate=normal_bf16((n_tok, n_q, d), cfg, T_GATE, layer),
         q_norm_w=normal_bf16((d,), cfg, T_QW, layer, scale=0.1, offset=1.0),
         k_norm_w=normal_bf16((d,), cfg, T_KW, layer, scale=0.1, offset=1.0),
+    )
+
+
+def normal_f32(shape, cfg: int, tensor_id: int, layer: int = 0, scale: float = 1.0) -> np.ndarray:
+    """float32 scale*N(0,1), drawn in seeded blocks of 1024 rows (kept in float32)."""
+    shape = tuple(shape)
+    out = np.empty(shape, dtype=np.float32)
+    rows = shape[0] if shape else 1
+    for b in range(max(1, -(-rows // BLOCK_ROWS))):
+        lo, hi = b * BLOCK_ROWS, min(rows, (b + 1) * BLOCK_ROWS)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg, tensor_id, layer, b])))
+        out[lo:hi] = g.standard_normal(size=(hi - lo,) + shape[1:], dtype=np.float32) * np.float32(scale)
+    return out
+
+
+def router_inputs(cfg: int, layer: int, n_tok: int, hidden: int = 5120, n_experts: int = 256):
+    """Router inputs of one MoE layer: bf16 bits of the normalised hidden states
+    x ~ N(0,1) [n_tok][hidden], a float32 weight W ~ N(0, 0.02^2) [n_experts][hidden]
+    (logits of standard deviation ~1.4) and a float32 selection bias ~ N(0, 0.05^2)."""
+    return dict(
+        x=normal_bf16((n_tok, hidden), cfg, T_RX, layer),
+        w=normal_f32((n_experts, hidden), cfg, T_RW, layer, scale=0.02),
+        bias=normal_f32((n_experts,), cfg, T_RB, layer, scale=0.05),
     )
 
 
