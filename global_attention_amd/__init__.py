@@ -33,6 +33,7 @@ EXPORTED = [
     "beam_prefill_workspace_bytes", "beam_decode_workspace_bytes", "beam_verify_workspace_bytes",
     "beam_kv_bytes", "beam_kv_page_slot", "beam_debug_visibility",
     "beam_status_str", "beam_last_error",
+    "beam_router", "beam_router_logits", "beam_router_select",
 ]
 
 
@@ -73,6 +74,25 @@ class Config:
                        self.rope_theta, self.rms_eps, self.ssmax_base, self.ssmax_exp)
 
 
+class CRouterConfig(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("n_groups", ctypes.c_int32),
+                ("topk_groups", ctypes.c_int32), ("top_k", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+@dataclass
+class RouterConfig:
+    """Group-limited sigmoid router of one MoE layer (include/beam_router.h)."""
+    hidden: int = 5120
+    n_experts: int = 256
+    n_groups: int = 8
+    topk_groups: int = 4
+    top_k: int = 8
+    scale: float = 2.5
+
+    def c(self) -> CRouterConfig:
+        return CRouterConfig(self.hidden, self.n_experts, self.n_groups, self.topk_groups, self.top_k, self.scale)
+
+
 _lib = None
 
 
@@ -102,12 +122,16 @@ def lib() -> ctypes.CDLL:
     L.beam_kv_bytes.argtypes = [I64, I32, I32, I32, I32, I32, I32, I32, P, P]
     L.beam_kv_page_slot.argtypes = [P, I32, I32, I32, I32, P, P]
     L.beam_debug_visibility.argtypes = [I32, I32, I32, I32, I32, I32, P, P]
+    L.beam_router.argtypes = [P, P, P, P, I32, P, P, P]
+    L.beam_router_logits.argtypes = [P, P, P, I32, P, P]
+    L.beam_router_select.argtypes = [P, P, P, I32, P, P, P]
     L.beam_status_str.argtypes = [I32]
     L.beam_status_str.restype = ctypes.c_char_p
     L.beam_last_error.restype = ctypes.c_char_p
     for name in ("beam_kv_append", "beam_attn_prefill", "beam_attn_decode", "beam_attn_prefill_stages",
                  "beam_attn_decode_stages", "beam_attn_verify", "beam_attn_verify_stages", "beam_kv_bytes",
-                 "beam_kv_page_slot", "beam_debug_visibility"):
+                 "beam_kv_page_slot", "beam_debug_visibility", "beam_router", "beam_router_logits",
+                 "beam_router_select"):
         getattr(L, name).restype = I32
     _lib = L
     return L
@@ -347,3 +371,60 @@ def debug_visibility(kind: int, window: int, t0: int, n_q: int, s0: int, n_k: in
     mask = torch.empty((n_q, n_k), dtype=torch.uint8, device=device)
     _check(lib().beam_debug_visibility(kind, window, t0, n_q, s0, n_k, _ptr(mask), _stream(stream)))
     return mask
+
+
+# ---------------------------------------------------------------- router
+
+def _router_outputs(rc: RouterConfig, n_tok: int, device, idx, wts):
+    import torch
+    if idx is None:
+        idx = torch.empty((n_tok, rc.top_k), dtype=torch.int32, device=device)
+    if wts is None:
+        wts = torch.empty((n_tok, rc.top_k), dtype=torch.float32, device=device)
+    _need(idx, torch.int32, (n_tok, rc.top_k), "topk_idx")
+    _need(wts, torch.float32, (n_tok, rc.top_k), "topk_w")
+    return idx, wts
+
+
+def router(rc: RouterConfig, x, w, bias=None, topk_idx=None, topk_w=None, stream=None):
+    """Expert selection of one MoE layer: returns (topk_idx int32, topk_w float32),
+    each [n_tok][top_k], best first (beam_router)."""
+    import torch
+    n_tok = x.shape[0]
+    _need(x, torch.bfloat16, (n_tok, rc.hidden), "x")
+    _need(w, torch.float32, (rc.n_experts, rc.hidden), "w")
+    if bias is not None:
+        _need(bias, torch.float32, (rc.n_experts,), "bias")
+    topk_idx, topk_w = _router_outputs(rc, n_tok, x.device, topk_idx, topk_w)
+    c = rc.c()
+    _check(lib().beam_router(ctypes.byref(c), _ptr(x), _ptr(w), _ptr(bias), n_tok, _ptr(topk_idx), _ptr(topk_w),
+                             _stream(stream)))
+    return topk_idx, topk_w
+
+
+def router_logits(rc: RouterConfig, x, w, out=None, stream=None):
+    """fp32 router logits [n_tok][n_experts] = x W^T (beam_router_logits)."""
+    import torch
+    n_tok = x.shape[0]
+    _need(x, torch.bfloat16, (n_tok, rc.hidden), "x")
+    _need(w, torch.float32, (rc.n_experts, rc.hidden), "w")
+    if out is None:
+        out = torch.empty((n_tok, rc.n_experts), dtype=torch.float32, device=x.device)
+    _need(out, torch.float32, (n_tok, rc.n_experts), "logits")
+    c = rc.c()
+    _check(lib().beam_router_logits(ctypes.byref(c), _ptr(x), _ptr(w), n_tok, _ptr(out), _stream(stream)))
+    return out
+
+
+def router_select(rc: RouterConfig, logits, bias=None, topk_idx=None, topk_w=None, stream=None):
+    """Selection from fp32 logits [n_tok][n_experts] (beam_router_select)."""
+    import torch
+    n_tok = logits.shape[0]
+    _need(logits, torch.float32, (n_tok, rc.n_experts), "logits")
+    if bias is not None:
+        _need(bias, torch.float32, (rc.n_experts,), "bias")
+    topk_idx, topk_w = _router_outputs(rc, n_tok, logits.device, topk_idx, topk_w)
+    c = rc.c()
+    _check(lib().beam_router_select(ctypes.byref(c), _ptr(logits), _ptr(bias), n_tok, _ptr(topk_idx), _ptr(topk_w),
+                                    _stream(stream)))
+    return topk_idx, topk_w

@@ -3,10 +3,12 @@
 // synchronises; every call only enqueues work on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdio>
 #include <string>
 
 #include "beam_attn.h"
+#include "beam_router.h"
 #include "beam_device.h"
 #include "beam_kernels.h"
 
@@ -584,6 +586,81 @@ beam_status beam_debug_visibility(int32_t kind, int32_t window, int32_t t0, int3
                               "visibility launch");
   if (st != BEAM_OK) return st;
   return ok();
+}
+
+// ---------------------------------------------------------------- router
+
+}  // extern "C"
+
+namespace {
+
+beam_status check_router(const beam_router_config* c, int32_t n_tok) {
+  if (!c) return fail(BEAM_E_NULL, "router config is NULL");
+  if (c->hidden <= 0 || c->hidden % beam::kRouterKChunk != 0)
+    return fail(BEAM_E_UNSUPPORTED, "router hidden width must be a positive multiple of 32");
+  if (c->n_experts != beam::kRouterExperts || c->n_groups != beam::kRouterGroups)
+    return fail(BEAM_E_UNSUPPORTED, "router supports 256 experts in 8 groups");
+  if (c->topk_groups < 1 || c->topk_groups > beam::kRouterGroups || c->top_k < 1 || c->top_k > 8)
+    return fail(BEAM_E_UNSUPPORTED, "router needs 1 <= topk_groups <= 8 and 1 <= top_k <= 8");
+  if (!std::isfinite(c->scale)) return fail(BEAM_E_RANGE, "router scale must be finite");
+  if (n_tok < 0) return fail(BEAM_E_RANGE, "n_tok must be >= 0");
+  return BEAM_OK;
+}
+
+beam::RouterParams router_params(const beam_router_config* c, int32_t n_tok) {
+  beam::RouterParams p{};
+  p.n_tok = n_tok;
+  p.hidden = c->hidden;
+  p.topk_groups = c->topk_groups;
+  p.top_k = c->top_k;
+  p.scale = c->scale;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+beam_status beam_router(const beam_router_config* cfg, const beam_bf16* x, const float* w, const float* bias,
+                        int32_t n_tok, int32_t* topk_idx, float* topk_w, void* stream) {
+  beam_status st;
+  if ((st = check_router(cfg, n_tok)) != BEAM_OK) return st;
+  if (n_tok == 0) return ok();
+  if (!x || !w || !topk_idx || !topk_w) return fail(BEAM_E_NULL, "NULL input/output pointer");
+  beam::RouterParams p = router_params(cfg, n_tok);
+  p.x = x;
+  p.w = w;
+  p.bias = bias;
+  p.idx = topk_idx;
+  p.wts = topk_w;
+  return hip_status(beam::launch_router_fused(p, (hipStream_t)stream), "router launch");
+}
+
+beam_status beam_router_logits(const beam_router_config* cfg, const beam_bf16* x, const float* w, int32_t n_tok,
+                               float* logits, void* stream) {
+  beam_status st;
+  if ((st = check_router(cfg, n_tok)) != BEAM_OK) return st;
+  if (n_tok == 0) return ok();
+  if (!x || !w || !logits) return fail(BEAM_E_NULL, "NULL input/output pointer");
+  beam::RouterParams p = router_params(cfg, n_tok);
+  p.x = x;
+  p.w = w;
+  p.logits_out = logits;
+  return hip_status(beam::launch_router_logits(p, (hipStream_t)stream), "router logits launch");
+}
+
+beam_status beam_router_select(const beam_router_config* cfg, const float* logits, const float* bias, int32_t n_tok,
+                               int32_t* topk_idx, float* topk_w, void* stream) {
+  beam_status st;
+  if ((st = check_router(cfg, n_tok)) != BEAM_OK) return st;
+  if (n_tok == 0) return ok();
+  if (!logits || !topk_idx || !topk_w) return fail(BEAM_E_NULL, "NULL input/output pointer");
+  beam::RouterParams p = router_params(cfg, n_tok);
+  p.logits_in = logits;
+  p.bias = bias;
+  p.idx = topk_idx;
+  p.wts = topk_w;
+  return hip_status(beam::launch_router_select(p, (hipStream_t)stream), "router select launch");
 }
 
 }  // extern "C"

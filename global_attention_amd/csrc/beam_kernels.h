@@ -160,4 +160,25 @@ hipError_t launch_decode_combine(const CombineParams& p, int n_seqs, hipStream_t
 hipError_t launch_verify_attn(const PrefillParams& p, hipStream_t s);
 hipError_t launch_verify_combine(const VerifyCombineParams& p, hipStream_t s);
 
+// ---- group-limited sigmoid router (MoE expert selection) ----
+constexpr int kRouterExperts = 256;
+constexpr int kRouterGroups = 8;
+constexpr int kRouterBlockTokens = 128;  // tokens per block of the logits GEMM
+constexpr int kRouterKChunk = 32;        // hidden must be a multiple
+
+struct RouterParams {
+  const uint16_t* x;       // bf16 [n_tok][hidden]
+  const float* w;          // [256][hidden]
+  const float* bias;       // [256] or nullptr (zero)
+  const float* logits_in;  // select: [n_tok][256]
+  float* logits_out;       // logits: [n_tok][256]
+  int32_t* idx;            // [n_tok][top_k]
+  float* wts;              // [n_tok][top_k]
+  int n_tok, hidden, topk_groups, top_k;
+  float scale;
+};
+hipError_t launch_router_logits(const RouterParams& p, hipStream_t s);
+hipError_t launch_router_select(const RouterParams& p, hipStream_t s);
+hipError_t launch_router_fused(const RouterParams& p, hipStream_t s);
+
 }  // namespace beam

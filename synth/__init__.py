@@ -108,6 +108,19 @@ def router_inputs(cfg: int, layer: int, n_tok: int, hidden: int = 5120, n_expert
     )
 
 
+def router_inputs_exact(cfg: int, layer: int, n_tok: int, hidden: int = 5120, n_experts: int = 256):
+    """Router inputs on a coarse grid: x integers in [-8, 8] (bf16 bits), W
+    integers in [-4, 4] times 2^-10 (float32), bias multiples of 2^-12 in
+    [-0.125, 0.125]. Every product x*W is a multiple of 2^-10 below 2^-5 in
+    magnitude, so every partial sum over up to 2^17 terms stays exact in
+    float32 in any order (logits of standard deviation ~0.9)."""
+    g = rng(cfg, T_RX, layer)
+    x = g.integers(-8, 9, size=(n_tok, hidden)).astype(np.float32)
+    w = (g.integers(-4, 5, size=(n_experts, hidden)) * 2.0 ** -10).astype(np.float32)
+    bias = (g.integers(-512, 513, size=n_experts) * 2.0 ** -12).astype(np.float32)
+    return dict(x=f32_to_bf16_bits(x), w=w, bias=bias)
+
+
 def decode_positions(cfg: int, n_seqs: int, lo: int, hi: int) -> np.ndarray:
     """Zero-based positions t of the new token, uniform integers in [lo, hi]."""
     return rng(cfg, T_POS).integers(lo, hi + 1, size=n_seqs).astype(np.int32)

@@ -170,3 +170,29 @@ def test_verify_workspace_and_checks():
     fake = ctypes.c_void_p(0x100000)
     assert L.beam_attn_verify_stages(16, ctypes.byref(c), ctypes.byref(kc), *([fake] * 6), None, fake, fake, fake,
                                      1, 4, 4, 100, 0, fake, ctypes.c_void_p(0x1000), 1 << 30, None) == 3
+
+
+def test_router_argument_checks():
+    L = ga.lib()
+    fake = ctypes.c_void_p(0x100000)
+
+    def call(rc, n_tok=4, x=fake):
+        c = rc.c()
+        return L.beam_router(ctypes.byref(c), x, fake, None, n_tok, fake, fake, None)
+
+    assert call(ga.RouterConfig(hidden=100)) == 4
+    assert call(ga.RouterConfig(hidden=0)) == 4
+    assert call(ga.RouterConfig(n_experts=128)) == 4
+    assert call(ga.RouterConfig(n_groups=4)) == 4
+    assert call(ga.RouterConfig(topk_groups=0)) == 4
+    assert call(ga.RouterConfig(topk_groups=9)) == 4
+    assert call(ga.RouterConfig(top_k=9)) == 4
+    assert call(ga.RouterConfig(scale=float("nan"))) == 3
+    assert call(ga.RouterConfig(), n_tok=-1) == 3
+    assert call(ga.RouterConfig(), x=None) == 1
+    assert call(ga.RouterConfig(), n_tok=0, x=None) == 0          # empty work, nothing launched
+    assert L.beam_router(None, fake, fake, None, 4, fake, fake, None) == 1
+    c = ga.RouterConfig().c()
+    assert L.beam_router_logits(ctypes.byref(c), fake, fake, 4, None, None) == 1
+    assert L.beam_router_select(ctypes.byref(c), None, None, 4, fake, fake, None) == 1
+    assert L.beam_router_select(ctypes.byref(c), None, None, 0, None, None, None) == 0
