@@ -14,6 +14,9 @@ sequences at positions uniform in [65536, 131071] over a paged bf16 cache
 GB/s of KV read (4,096 B per cached key per layer). And under "verify": the
 verify step of speculative decoding on the same caches, a draft block of 8
 tokens per sequence ending at the decode position, in GB/s of cached KV read.
+And under "router": the MoE router of one layer over the same 32,768 tokens
+(fp32 logits GEMM with the group-limited top-8 selection fused), in TFLOP/s
+against the fp32 MFMA peak.
 
 Prints ONE JSON line on stdout. Everything else goes to stderr.
 """
@@ -32,6 +35,7 @@ if ROOT not in sys.path:
 METRIC = "prefill attn TFLOP/s @32K; decode KV GB/s @128K ctx (% of MI355X peak)"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 bf16 flop/clk x 2.4 GHz (AMD: 2.5 PFLOP/s dense)
 PEAK_HBM_GBS = 8000.0       # HBM3E, 8 TB/s
+PEAK_FP32_MFMA_TFLOPS = 157.3  # dense fp32 matrix (v_mfma_f32_*f32), AMD's figure
 H, G, D, W = 48, 8, 128, 512
 FLOP_PER_PAIR = 4 * D * H   # QK^T and PV over all query heads of one (query, key) pair
 
@@ -50,6 +54,7 @@ _KERNEL_SOURCES = {
     "verify_attn_kernel<1, 0>": "prefill.hip",
     "verify_attn_kernel<0, 0>": "prefill.hip",
     "verify_attn_kernel<1, 1>": "prefill.hip",
+    "router_gemm_kernel<true>": "router.hip",
     "prefill_prologue_kernel<0, 0>": "prologue.hip",
     "prefill_prologue_kernel<1, 0>": "prologue.hip",
 }
@@ -299,6 +304,37 @@ def bench_verify(steps, warmup, dres, block=8, split_keys=0):
     return res
 
 
+def bench_router(T, steps, warmup):
+    """The MoE router of one layer over T tokens: fp32 logits (hidden 5120 x 256
+    experts) with the group-limited top-8 selection fused, timed with events."""
+    import torch
+    import global_attention_amd as ga
+    import synth
+    rc = ga.RouterConfig()
+    inp = synth.router_inputs(40, 0, T)
+    x = _dev(inp["x"]).view(T, rc.hidden)
+    w = torch.from_numpy(inp["w"]).cuda()
+    b = torch.from_numpy(inp["bias"]).cuda()
+    idx = torch.empty((T, rc.top_k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, rc.top_k), dtype=torch.float32, device="cuda")
+    # a call lasts ~0.7 ms: warm up and time at least 20 (the clock settles
+    # over the first few dozen calls)
+    warmup, steps = max(warmup, 20), max(steps, 20)
+    for _ in range(warmup):
+        ga.router(rc, x, w, b, topk_idx=idx, topk_w=wts)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in evs:
+        e[0].record()
+        ga.router(rc, x, w, b, topk_idx=idx, topk_w=wts)
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    flops = 2.0 * T * rc.n_experts * rc.hidden
+    log(f"[bench] router T={T}: {ms:.3f} ms, {flops / (ms / 1e3) / 1e12:.1f} TFLOP/s (fp32 MFMA)")
+    return dict(ms=ms, flops=flops)
+
+
 # --------------------------------------------------------------------------- CPU oracle
 
 def cpu_baseline(layers, T, rows):
@@ -348,6 +384,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--verify-split-keys", type=int, default=0)
+    ap.add_argument("--skip-router", action="store_true")
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=384)
@@ -445,6 +482,19 @@ def main():
             "global_fp8": {"ms_per_call": round(v["global_fp8"]["ms_per_call"], 4),
                            "gbs_split": round(v["global_fp8"]["gbs_split"], 1),
                            "speedup_vs_8_decode_calls": round(v["global_fp8"]["vs_decode_calls"], 2)},
+        }
+    if not args.skip_router:
+        rr = bench_router(T, args.steps, args.warmup)
+        tf = rr["flops"] / (rr["ms"] / 1e3) / 1e12
+        rec["router"] = {
+            "workload": f"group-limited sigmoid router of one MoE layer: {T} tokens, hidden 5120 (bf16), 256 experts "
+                        "(fp32 weight), fp32 logits, 8 groups keep 4, top-8, weights x2.5; logits fused with the "
+                        "selection",
+            "value": round(tf, 2), "unit": "TFLOP/s", "ms_per_call": round(rr["ms"], 4),
+            "roofline": {"kernel": "router_gemm_kernel<true>", "bound": "mfma", "achieved": round(tf, 2),
+                         "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_FP32_MFMA_TFLOPS, 4),
+                         "traffic": recorded_traffic("router_gemm_kernel<true>"),
+                         "avg_launch_ms": round(rr["ms"], 4), "flop_per_launch": rr["flops"]},
         }
     if not args.no_cpu_baseline and layers is not None:
         log(f"[bench] timing the CPU oracle on {args.cpu_rows} rows per layer")

@@ -165,6 +165,7 @@ constexpr int kRouterExperts = 256;
 constexpr int kRouterGroups = 8;
 constexpr int kRouterBlockTokens = 128;  // tokens per block of the logits GEMM
 constexpr int kRouterKChunk = 32;        // hidden must be a multiple
+constexpr int kRouterTopKMax = 8;        // largest supported top_k
 
 struct RouterParams {
   const uint16_t* x;       // bf16 [n_tok][hidden]

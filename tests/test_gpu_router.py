@@ -70,7 +70,7 @@ def _tie_logits(n):
 
 @pytest.mark.parametrize("groups,k", [(4, 8), (1, 8), (8, 8), (4, 1), (2, 5)])
 def test_select_bit_exact(groups, k):
-    n = 2003                                                   # not a multiple of 4 tokens per block
+    n = 2003                                                   # not a multiple of 64 tokens per block
     z = synth.normal_f32((n, 256), 30, 0, scale=1.5)
     z[:600] = _tie_logits(600)
     bias = synth.router_inputs(30, 0, 1, hidden=32)["bias"]
