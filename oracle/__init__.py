@@ -6,3 +6,4 @@ baseline leg of bench.py; never by the product path.
 from .beam_attention import *  # noqa: F401,F403
 from .beam_attention import Config, LOCAL, GLOBAL  # noqa: F401
 from . import router  # noqa: F401
+from . import projection  # noqa: F401

@@ -12,6 +12,10 @@ round-to-nearest-even and kept as ``uint16`` bit patterns.
 RMSNorm weights are 1 + 0.1*N(0,1), gate logits N(0,1), gate bias absent.
 Router inputs (the MoE layers' expert selection): hidden states bf16 N(0,1),
 a float32 weight 0.02*N(0,1) and a float32 selection bias 0.05*N(0,1).
+Projection inputs (the GEMMs around attention): the normalised sublayer input
+x bf16 N(0,1) [n_tok][hidden]; the stacked Wq/Wk/Wv/Wg rows and W_o bf16
+N(0,1)/sqrt(fan_in), so that projected values are about N(0,1) like the
+attention inputs above.
 Position/page structure (decode contexts, random page permutation, chunked
 prefill lengths) is drawn from the same kind of generator with its own id.
 """
@@ -28,6 +32,7 @@ _THREADS = max(1, min(16, os.cpu_count() or 1))
 # tensor ids for SeedSequence([cfg, tensor_id, layer])
 T_Q, T_K, T_V, T_GATE, T_QW, T_KW, T_POS, T_PERM, T_LEN, T_MISC = range(10)
 T_RX, T_RW, T_RB = 10, 11, 12  # router: hidden states, weight, selection bias
+T_PX, T_PW, T_PO = 13, 14, 15  # projections: sublayer input, stacked Wq/Wk/Wv/Wg, W_o
 
 
 def rng(cfg: int, tensor_id: int, layer: int = 0) -> np.random.Generator:
@@ -146,3 +151,19 @@ def paged_block_table(cfg: int, ctx_lens, page_size: int = 16, extra_pages: int 
 
 def chunked_lengths(cfg: int, n_seqs: int, lo: int, hi: int) -> np.ndarray:
     return rng(cfg, T_LEN).integers(lo, hi + 1, size=n_seqs).astype(np.int64)
+
+
+def projection_inputs(cfg: int, layer: int, n_tok: int, hidden: int = 5120, n_q: int = 48, n_kv: int = 8,
+                      d: int = 128, with_w_o: bool = True):
+    """bf16 bits of the sublayer input x [n_tok][hidden], the stacked
+    projection weight [(2 n_q + 2 n_kv) d][hidden] (rows of Wq, Wk, Wv, Wg in
+    this order), W_o [hidden][n_q d] and the two RMSNorm weights."""
+    out = dict(
+        x=normal_bf16((n_tok, hidden), cfg, T_PX, layer),
+        w_qkvg=normal_bf16(((2 * n_q + 2 * n_kv) * d, hidden), cfg, T_PW, layer, scale=hidden ** -0.5),
+        q_norm_w=normal_bf16((d,), cfg, T_QW, layer, scale=0.1, offset=1.0),
+        k_norm_w=normal_bf16((d,), cfg, T_KW, layer, scale=0.1, offset=1.0),
+    )
+    if with_w_o:
+        out["w_o"] = normal_bf16((hidden, n_q * d), cfg, T_PO, layer, scale=(n_q * d) ** -0.5)
+    return out
