@@ -26,6 +26,7 @@ STAGE_COMBINE = 4
 STAGE_ALL = 7
 STAGE_VERIFY_COMBINE = 8
 STAGE_VERIFY_ALL = 15
+STAGE_PROLOGUE_KV = 16
 
 EXPORTED = [
     "beam_kv_append", "beam_attn_prefill", "beam_attn_decode", "beam_attn_verify",
@@ -34,6 +35,7 @@ EXPORTED = [
     "beam_kv_bytes", "beam_kv_page_slot", "beam_debug_visibility",
     "beam_status_str", "beam_last_error",
     "beam_router", "beam_router_logits", "beam_router_select",
+    "beam_attn_project", "beam_out_project",
 ]
 
 
@@ -125,13 +127,15 @@ def lib() -> ctypes.CDLL:
     L.beam_router.argtypes = [P, P, P, P, I32, P, P, P]
     L.beam_router_logits.argtypes = [P, P, P, I32, P, P]
     L.beam_router_select.argtypes = [P, P, P, I32, P, P, P]
+    L.beam_attn_project.argtypes = [P, I32, P, I32, P, P, P, P, I32, I32, P, P, P, P, SZ, P]
+    L.beam_out_project.argtypes = [P, P, I32, I32, I32, P, P]
     L.beam_status_str.argtypes = [I32]
     L.beam_status_str.restype = ctypes.c_char_p
     L.beam_last_error.restype = ctypes.c_char_p
     for name in ("beam_kv_append", "beam_attn_prefill", "beam_attn_decode", "beam_attn_prefill_stages",
                  "beam_attn_decode_stages", "beam_attn_verify", "beam_attn_verify_stages", "beam_kv_bytes",
                  "beam_kv_page_slot", "beam_debug_visibility", "beam_router", "beam_router_logits",
-                 "beam_router_select"):
+                 "beam_router_select", "beam_attn_project", "beam_out_project"):
         getattr(L, name).restype = I32
     _lib = L
     return L
@@ -265,7 +269,7 @@ def prefill(cfg: Config, cache: KVCache, q_raw, k_raw, v_raw, q_norm_w, k_norm_w
     n_tok, n_seqs, out = _chunk_args(cfg, q_raw, k_raw, v_raw, q_norm_w, k_norm_w, gate, cu_seqlens, seq_idx,
                                      start_pos, gate_bias, out)
     nbytes = prefill_workspace_bytes(cfg, n_tok, n_seqs)
-    workspace = _workspace(nbytes, q_raw.device, workspace)
+    workspace = _workspace(nbytes, k_raw.device, workspace)
     c, kc = cfg.c(), cache.c()
     _check(lib().beam_attn_prefill_stages(
         stages, ctypes.byref(c), ctypes.byref(kc), _ptr(q_raw), _ptr(k_raw), _ptr(v_raw), _ptr(q_norm_w),
@@ -286,7 +290,7 @@ def verify(cfg: Config, cache: KVCache, q_raw, k_raw, v_raw, q_norm_w, k_norm_w,
     nbytes = verify_workspace_bytes(cfg, cache.kind, n_tok, n_seqs, max_chunk_len, max_pos, split_keys)
     if nbytes == 0:
         raise BeamError(3, "invalid verify sizes (max_chunk_len / max_pos / split_keys)")
-    workspace = _workspace(nbytes, q_raw.device, workspace)
+    workspace = _workspace(nbytes, k_raw.device, workspace)
     c, kc = cfg.c(), cache.c()
     _check(lib().beam_attn_verify_stages(
         stages, ctypes.byref(c), ctypes.byref(kc), _ptr(q_raw), _ptr(k_raw), _ptr(v_raw), _ptr(q_norm_w),
@@ -298,10 +302,11 @@ def verify(cfg: Config, cache: KVCache, q_raw, k_raw, v_raw, q_norm_w, k_norm_w,
 
 def _chunk_args(cfg, q_raw, k_raw, v_raw, q_norm_w, k_norm_w, gate, cu_seqlens, seq_idx, start_pos, gate_bias, out):
     import torch
-    n_tok = q_raw.shape[0]
+    n_tok = k_raw.shape[0]
     n_seqs = cu_seqlens.shape[0] - 1
     H, G, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
-    _need(q_raw, torch.bfloat16, (n_tok, H, d), "q_raw")
+    if q_raw is not None:
+        _need(q_raw, torch.bfloat16, (n_tok, H, d), "q_raw")
     _need(k_raw, torch.bfloat16, (n_tok, G, d), "k_raw")
     _need(v_raw, torch.bfloat16, (n_tok, G, d), "v_raw")
     _need(gate, torch.bfloat16, (n_tok, H, d), "gate")
@@ -313,7 +318,7 @@ def _chunk_args(cfg, q_raw, k_raw, v_raw, q_norm_w, k_norm_w, gate, cu_seqlens, 
     if gate_bias is not None:
         _need(gate_bias, torch.float32, (H,), "gate_bias")
     if out is None:
-        out = torch.empty((n_tok, H, d), dtype=torch.bfloat16, device=q_raw.device)
+        out = torch.empty((n_tok, H, d), dtype=torch.bfloat16, device=k_raw.device)
     _need(out, torch.bfloat16, (n_tok, H, d), "out")
     return n_tok, n_seqs, out
 
@@ -428,3 +433,50 @@ def router_select(rc: RouterConfig, logits, bias=None, topk_idx=None, topk_w=Non
     _check(lib().beam_router_select(ctypes.byref(c), _ptr(logits), _ptr(bias), n_tok, _ptr(topk_idx), _ptr(topk_w),
                                     _stream(stream)))
     return topk_idx, topk_w
+
+
+def attn_project(cfg: Config, kind: int, x, w_qkvg, q_norm_w, cu_seqlens, start_pos, workspace=None, k_raw=None,
+                 v_raw=None, gate=None, stream=None):
+    """QKV/gate projection of a prefill chunk with the query prologue fused
+    (beam_attn_project). x: bf16 [n_tok][hidden]; w_qkvg: bf16
+    [(2H + 2G) d][hidden] (Wq, Wk, Wv, Wg rows). Writes Q' into the prefill
+    workspace and returns (k_raw, v_raw, gate, workspace); run prefill(...,
+    q_raw=None, workspace=workspace, stages=STAGE_PROLOGUE_KV | ...) next."""
+    import torch
+    n_tok, hidden = x.shape
+    n_seqs = cu_seqlens.shape[0] - 1
+    H, G, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    _need(x, torch.bfloat16, (n_tok, hidden), "x")
+    _need(w_qkvg, torch.bfloat16, ((2 * H + 2 * G) * d, hidden), "w_qkvg")
+    _need(q_norm_w, torch.bfloat16, (d,), "q_norm_w")
+    _need(cu_seqlens, torch.int32, (n_seqs + 1,), "cu_seqlens")
+    _need(start_pos, torch.int32, (n_seqs,), "start_pos")
+    dev = x.device
+    k_raw = torch.empty((n_tok, G, d), dtype=torch.bfloat16, device=dev) if k_raw is None else k_raw
+    v_raw = torch.empty((n_tok, G, d), dtype=torch.bfloat16, device=dev) if v_raw is None else v_raw
+    gate = torch.empty((n_tok, H, d), dtype=torch.bfloat16, device=dev) if gate is None else gate
+    _need(k_raw, torch.bfloat16, (n_tok, G, d), "k_raw")
+    _need(v_raw, torch.bfloat16, (n_tok, G, d), "v_raw")
+    _need(gate, torch.bfloat16, (n_tok, H, d), "gate")
+    workspace = _workspace(prefill_workspace_bytes(cfg, n_tok, n_seqs), dev, workspace)
+    c = cfg.c()
+    _check(lib().beam_attn_project(ctypes.byref(c), kind, _ptr(x), hidden, _ptr(w_qkvg), _ptr(q_norm_w),
+                                   _ptr(cu_seqlens), _ptr(start_pos), n_seqs, n_tok, _ptr(k_raw), _ptr(v_raw),
+                                   _ptr(gate), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return k_raw, v_raw, gate, workspace
+
+
+def out_project(y, w_o, out=None, stream=None):
+    """out [n_tok][out_features] = y W_o^T in bf16 (beam_out_project); y may be
+    [n_tok][H][d] or [n_tok][in_features]."""
+    import torch
+    n_tok = y.shape[0]
+    y2 = y.reshape(n_tok, -1)
+    out_f, in_f = w_o.shape
+    _need(y2, torch.bfloat16, (n_tok, in_f), "y")
+    _need(w_o, torch.bfloat16, (out_f, in_f), "w_o")
+    if out is None:
+        out = torch.empty((n_tok, out_f), dtype=torch.bfloat16, device=y.device)
+    _need(out, torch.bfloat16, (n_tok, out_f), "out")
+    _check(lib().beam_out_project(_ptr(y2), _ptr(w_o), n_tok, in_f, out_f, _ptr(out), _stream(stream)))
+    return out

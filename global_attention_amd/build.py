@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbeam_attn.so")
-SOURCES = ["beam_attn.hip", "prologue.hip", "prefill.hip", "decode.hip", "router.hip"]
+SOURCES = ["beam_attn.hip", "prologue.hip", "prefill.hip", "decode.hip", "router.hip", "gemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -8,6 +8,7 @@
 #include <string>
 
 #include "beam_attn.h"
+#include "beam_proj.h"
 #include "beam_router.h"
 #include "beam_device.h"
 #include "beam_kernels.h"
@@ -259,7 +260,10 @@ beam_status chunk_call(bool verify, uint32_t stages, const beam_attn_config* cfg
                        int32_t max_pos, int32_t split_keys, beam_bf16* out, void* workspace, size_t ws_bytes,
                        void* stream) {
   beam_status st;
-  if (stages & ~(verify ? 15u : 7u)) return fail(BEAM_E_RANGE, "unknown stage bits");
+  if (stages & ~(verify ? 15u | BEAM_STAGE_PROLOGUE_KV : 7u | BEAM_STAGE_PROLOGUE_KV))
+    return fail(BEAM_E_RANGE, "unknown stage bits");
+  if ((stages & BEAM_STAGE_PROLOGUE) && (stages & BEAM_STAGE_PROLOGUE_KV))
+    return fail(BEAM_E_RANGE, "BEAM_STAGE_PROLOGUE and BEAM_STAGE_PROLOGUE_KV are exclusive");
   if ((st = check_cfg(cfg)) != BEAM_OK) return st;
   if ((st = check_cache(cache)) != BEAM_OK) return st;
   if (n_seqs <= 0) return fail(BEAM_E_RANGE, "n_seqs must be positive");
@@ -267,8 +271,8 @@ beam_status chunk_call(bool verify, uint32_t stages, const beam_attn_config* cfg
   if (n_tok == 0) return ok();
   if (max_chunk_len == 0 || max_chunk_len > n_tok)
     return fail(BEAM_E_RANGE, "max_chunk_len must be in [1, n_tok]");
-  if (!q_raw || !k_raw || !v_raw || !q_norm_w || !k_norm_w || !gate_logits || !cu_seqlens || !seq_idx ||
-      !start_pos || !out)
+  if ((!q_raw && (stages & BEAM_STAGE_PROLOGUE)) || !k_raw || !v_raw || !q_norm_w || !k_norm_w || !gate_logits ||
+      !cu_seqlens || !seq_idx || !start_pos || !out)
     return fail(BEAM_E_NULL, "NULL input/output pointer");
   if (!workspace) return fail(BEAM_E_NULL, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(BEAM_E_RANGE, "workspace must be 256-byte aligned");
@@ -315,7 +319,9 @@ beam_status chunk_call(bool verify, uint32_t stages, const beam_attn_config* cfg
   pp.ck = static_cast<uint16_t*>(cache->k);
   pp.cv = static_cast<uint16_t*>(cache->v);
   // Global layers: the append rides along with the prologue when both run.
-  pp.append = cache->kind == BEAM_GLOBAL && (stages & BEAM_STAGE_PROLOGUE) && (stages & BEAM_STAGE_APPEND);
+  const bool prologue = stages & (BEAM_STAGE_PROLOGUE | BEAM_STAGE_PROLOGUE_KV);
+  pp.append = cache->kind == BEAM_GLOBAL && prologue && (stages & BEAM_STAGE_APPEND);
+  pp.with_q = (stages & BEAM_STAGE_PROLOGUE) != 0;
   pp.kv_fp8 = cache->dtype == BEAM_KV_FP8_E4M3;
   pp.k_scale = cache->k_scale;
   pp.v_scale = cache->v_scale;
@@ -333,7 +339,7 @@ beam_status chunk_call(bool verify, uint32_t stages, const beam_attn_config* cfg
   pp.ssmax_base = cfg->ssmax_base;
   pp.ssmax_exp = cfg->ssmax_exp;
   const int n_tiles = (max_chunk_len + 63) / 64 + 1;
-  if ((stages & BEAM_STAGE_PROLOGUE) &&
+  if (prologue &&
       (st = hip_status(beam::launch_prefill_prologue(pp, n_seqs, n_tiles, s), "prologue launch")) != BEAM_OK)
     return st;
 
@@ -661,6 +667,91 @@ beam_status beam_router_select(const beam_router_config* cfg, const float* logit
   p.idx = topk_idx;
   p.wts = topk_w;
   return hip_status(beam::launch_router_select(p, (hipStream_t)stream), "router select launch");
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- projections
+
+namespace {
+
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+beam_status check_gemm_sizes(int32_t n_tok, int32_t k, int64_t n_feat, const char* what) {
+  if (n_tok < 0) return fail(BEAM_E_RANGE, "n_tok must be >= 0");
+  if (k <= 0 || k % 64 != 0 || k > 65536)
+    return fail(BEAM_E_UNSUPPORTED, std::string(what) + ": the contraction width must be a multiple of 64 in [64, 65536]");
+  if (n_feat <= 0 || n_feat % beam::kGemmTile != 0)
+    return fail(BEAM_E_UNSUPPORTED, std::string(what) + ": the output width must be a positive multiple of 256");
+  const int64_t blocks = (n_feat / beam::kGemmTile) * (((int64_t)n_tok + beam::kGemmTile - 1) / beam::kGemmTile);
+  if (blocks > 0x7fffffffLL) return fail(BEAM_E_RANGE, std::string(what) + ": grid too large");
+  return BEAM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+beam_status beam_attn_project(const beam_attn_config* cfg, int32_t kind, const beam_bf16* x, int32_t hidden,
+                              const beam_bf16* w_qkvg, const beam_bf16* q_norm_w, const int32_t* cu_seqlens,
+                              const int32_t* start_pos, int32_t n_seqs, int32_t n_tok, beam_bf16* k_raw,
+                              beam_bf16* v_raw, beam_bf16* gate_logits, void* workspace, size_t ws_bytes,
+                              void* stream) {
+  beam_status st;
+  if ((st = check_cfg(cfg)) != BEAM_OK) return st;
+  if (kind != BEAM_LOCAL && kind != BEAM_GLOBAL) return fail(BEAM_E_RANGE, "kind must be 0 or 1");
+  if (n_seqs <= 0) return fail(BEAM_E_RANGE, "n_seqs must be positive");
+  const int64_t n_feat = (int64_t)(2 * cfg->n_q_heads + 2 * cfg->n_kv_heads) * beam::D;
+  if ((st = check_gemm_sizes(n_tok, hidden, n_feat, "projection")) != BEAM_OK) return st;
+  if (n_tok == 0) return ok();
+  if (!x || !w_qkvg || !q_norm_w || !cu_seqlens || !start_pos || !k_raw || !v_raw || !gate_logits)
+    return fail(BEAM_E_NULL, "NULL input/output pointer");
+  if (!aligned16(x) || !aligned16(w_qkvg) || !aligned16(k_raw) || !aligned16(v_raw) || !aligned16(gate_logits))
+    return fail(BEAM_E_RANGE, "x, w_qkvg, k_raw, v_raw and gate_logits must be 16-byte aligned");
+  if (!workspace) return fail(BEAM_E_NULL, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(BEAM_E_RANGE, "workspace must be 256-byte aligned");
+  const PrefillWs ws = prefill_ws_layout(cfg, n_tok, n_seqs);
+  if (ws_bytes < ws.total) return fail(BEAM_E_WORKSPACE, "prefill workspace needs " + std::to_string(ws.total) + " bytes");
+  beam::GemmParams p{};
+  p.x = x;
+  p.w = w_qkvg;
+  p.n_tok = n_tok;
+  p.n_feat = (int)n_feat;
+  p.K = hidden;
+  p.q_out = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + ws.qp);
+  p.k_out = k_raw;
+  p.v_out = v_raw;
+  p.g_out = gate_logits;
+  p.q_norm_w = q_norm_w;
+  p.cu = cu_seqlens;
+  p.start_pos = start_pos;
+  p.n_seqs = n_seqs;
+  p.kind = kind;
+  p.H = cfg->n_q_heads;
+  p.G = cfg->n_kv_heads;
+  p.rope_theta = cfg->rope_theta;
+  p.rms_eps = cfg->rms_eps;
+  p.ssmax_base = cfg->ssmax_base;
+  p.ssmax_exp = cfg->ssmax_exp;
+  return hip_status(beam::launch_gemm(p, beam::kEpiQkvg, (hipStream_t)stream), "projection launch");
+}
+
+beam_status beam_out_project(const beam_bf16* y, const beam_bf16* w_o, int32_t n_tok, int32_t in_features,
+                             int32_t out_features, beam_bf16* out, void* stream) {
+  beam_status st;
+  if ((st = check_gemm_sizes(n_tok, in_features, out_features, "output projection")) != BEAM_OK) return st;
+  if (n_tok == 0) return ok();
+  if (!y || !w_o || !out) return fail(BEAM_E_NULL, "NULL input/output pointer");
+  if (!aligned16(y) || !aligned16(w_o) || !aligned16(out)) return fail(BEAM_E_RANGE, "y, w_o and out must be 16-byte aligned");
+  beam::GemmParams p{};
+  p.x = y;
+  p.w = w_o;
+  p.n_tok = n_tok;
+  p.n_feat = out_features;
+  p.K = in_features;
+  p.out = out;
+  p.ld_out = out_features;
+  return hip_status(beam::launch_gemm(p, beam::kEpiPlain, (hipStream_t)stream), "output projection launch");
 }
 
 }  // extern "C"

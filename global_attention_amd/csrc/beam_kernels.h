@@ -28,6 +28,8 @@ struct PrologueParams {
   // (the append stage, fused; new positions never share a slot with the
   // cached prefix that attention reads).
   int append;
+  // 0: K/V parts only (Q' is already in the workspace)
+  int with_q;
   int kind, H, G, P;
   float rope_theta, rms_eps, ssmax_base, ssmax_exp;
   // FP8 E4M3 cache: ck/cv hold one-byte codes at the same element offsets.
@@ -159,6 +161,32 @@ hipError_t launch_decode_split(const DecodeParams& p, int n_seqs, hipStream_t s)
 hipError_t launch_decode_combine(const CombineParams& p, int n_seqs, hipStream_t s);
 hipError_t launch_verify_attn(const PrefillParams& p, hipStream_t s);
 hipError_t launch_verify_combine(const VerifyCombineParams& p, hipStream_t s);
+
+// ---- projection GEMMs: out[t][f] = sum_k x[t][k] w[f][k] (bf16, fp32 accumulate) ----
+constexpr int kGemmTile = 256;  // n_feat must be a multiple; K a multiple of 64
+constexpr int kEpiPlain = 0;    // out[t][ld_out], columns f
+constexpr int kEpiQkvg = 1;     // Q' (fused norm + position op) / K / V / gate heads
+
+struct GemmParams {
+  const uint16_t* x;  // [n_tok][K]
+  const uint16_t* w;  // [n_feat][K]
+  int n_tok, n_feat, K;
+  // plain epilogue
+  uint16_t* out;
+  int ld_out;
+  // QKV/gate epilogue: rows of w are the H query heads, G key heads, G value
+  // heads and H gate heads (128 rows each)
+  uint16_t* q_out;  // Q' [n_tok][H][D] (base-2 softmax scale folded in)
+  uint16_t* k_out;  // raw K [n_tok][G][D]
+  uint16_t* v_out;  // raw V [n_tok][G][D]
+  uint16_t* g_out;  // raw gate logits [n_tok][H][D]
+  const uint16_t* q_norm_w;
+  const int32_t* cu;
+  const int32_t* start_pos;
+  int n_seqs, kind, H, G;
+  float rope_theta, rms_eps, ssmax_base, ssmax_exp;
+};
+hipError_t launch_gemm(const GemmParams& p, int epi, hipStream_t s);
 
 // ---- group-limited sigmoid router (MoE expert selection) ----
 constexpr int kRouterExperts = 256;

@@ -432,7 +432,7 @@ __global__ void visibility_kernel(int kind, int window, int t0, int n_q, int s0,
 namespace beam {
 
 hipError_t launch_prefill_prologue(const PrologueParams& p, int n_seqs, int n_tiles, hipStream_t s) {
-  const int parts = kPrologueFixedParts + (p.H + kQHeadsPerBlock - 1) / kQHeadsPerBlock;
+  const int parts = kPrologueFixedParts + (p.with_q ? (p.H + kQHeadsPerBlock - 1) / kQHeadsPerBlock : 0);
   if (p.G > kMaxHeadsPerGroup || p.G > 2 * kVHeadsPerBlock) return hipErrorInvalidValue;
   const dim3 grid(n_seqs, n_tiles, parts), block(256);
   if (p.kind == 0 && !p.kv_fp8)

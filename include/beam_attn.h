@@ -213,6 +213,11 @@ beam_status beam_attn_verify(const beam_attn_config *cfg, const beam_kv_cache *c
 #define BEAM_STAGE_ALL 7u
 #define BEAM_STAGE_VERIFY_COMBINE 8u
 #define BEAM_STAGE_VERIFY_ALL 15u
+/* The prologue without the queries: K_hat and V^T into the workspace (and the
+ * fused append on a global cache), with Q' already in the workspace's query
+ * region, written by beam_attn_project (beam_proj.h). q_raw may then be NULL.
+ * Takes the place of BEAM_STAGE_PROLOGUE (prefill and verify). */
+#define BEAM_STAGE_PROLOGUE_KV 16u
 
 beam_status beam_attn_prefill_stages(uint32_t stages, const beam_attn_config *cfg,
                                      const beam_kv_cache *cache, const beam_bf16 *q_raw,

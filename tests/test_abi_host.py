@@ -168,7 +168,7 @@ def test_verify_workspace_and_checks():
                               None) == 0
     # unknown stage bits (16 and above)
     fake = ctypes.c_void_p(0x100000)
-    assert L.beam_attn_verify_stages(16, ctypes.byref(c), ctypes.byref(kc), *([fake] * 6), None, fake, fake, fake,
+    assert L.beam_attn_verify_stages(32, ctypes.byref(c), ctypes.byref(kc), *([fake] * 6), None, fake, fake, fake,
                                      1, 4, 4, 100, 0, fake, ctypes.c_void_p(0x1000), 1 << 30, None) == 3
 
 
@@ -196,3 +196,56 @@ def test_router_argument_checks():
     assert L.beam_router_logits(ctypes.byref(c), fake, fake, 4, None, None) == 1
     assert L.beam_router_select(ctypes.byref(c), None, None, 4, fake, fake, None) == 1
     assert L.beam_router_select(ctypes.byref(c), None, None, 0, None, None, None) == 0
+
+
+def test_projection_argument_checks():
+    L = ga.lib()
+    fake = ctypes.c_void_p(0x100000)
+    cfg = ga.Config()
+    c = cfg.c()
+    ws_need = ga.prefill_workspace_bytes(cfg, 4, 1)
+
+    def proj(kind=ga.GLOBAL, hidden=5120, n_tok=4, x=fake, ws=ctypes.c_void_p(0x1000), ws_bytes=ws_need):
+        return L.beam_attn_project(ctypes.byref(c), kind, x, hidden, fake, fake, fake, fake, 1, n_tok, fake, fake,
+                                   fake, ws, ws_bytes, None)
+
+    assert proj(kind=2) == 3
+    assert proj(hidden=100) == 4                       # not a multiple of 64
+    assert proj(hidden=0) == 4
+    assert proj(hidden=65536 + 64) == 4
+    assert proj(n_tok=-1) == 3
+    assert proj(x=None) == 1
+    assert proj(x=ctypes.c_void_p(0x100008)) == 3      # not 16-byte aligned
+    assert proj(ws=ctypes.c_void_p(0x1010)) == 3       # not 256-byte aligned
+    assert proj(ws_bytes=ws_need - 1) == 5
+    assert proj(n_tok=0, x=None) == 0                  # empty work, nothing launched
+    assert L.beam_attn_project(None, 0, fake, 5120, fake, fake, fake, fake, 1, 4, fake, fake, fake, fake, 0,
+                               None) == 1
+
+    def outp(n_tok=4, k=6144, n_out=5120, y=fake):
+        return L.beam_out_project(y, fake, n_tok, k, n_out, fake, None)
+
+    assert outp(k=100) == 4
+    assert outp(n_out=5000) == 4                       # not a multiple of 256
+    assert outp(n_out=0) == 4
+    assert outp(y=None) == 1
+    assert outp(y=ctypes.c_void_p(0x100004)) == 3
+    assert outp(n_tok=0, y=None) == 0
+    assert outp(n_tok=1 << 30, n_out=1 << 30) == 3     # grid beyond 2^31 blocks
+
+
+def test_prologue_kv_stage_rules():
+    L = ga.lib()
+    fake = ctypes.c_void_p(0x100000)
+    c, kc = ga.Config().c(), _cache()
+
+    def call(stages, q=fake):
+        return L.beam_attn_prefill_stages(stages, ctypes.byref(c), ctypes.byref(kc), q, *([fake] * 5), None, fake,
+                                          fake, fake, 1, 4, 4, fake, ctypes.c_void_p(0x1000), 10, None)
+
+    # the two prologue forms exclude each other; checked before the workspace size
+    assert call(ga.STAGE_PROLOGUE | ga.STAGE_PROLOGUE_KV) == 3
+    # q_raw may be NULL only without the full prologue (here the small workspace is what fails next)
+    assert call(ga.STAGE_PROLOGUE_KV | ga.STAGE_ATTENTION, q=None) == 5
+    assert call(ga.STAGE_PROLOGUE | ga.STAGE_ATTENTION, q=None) == 1
+    assert call(32) == 3
