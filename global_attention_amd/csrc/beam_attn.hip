@@ -679,8 +679,8 @@ bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0;
 
 beam_status check_gemm_sizes(int32_t n_tok, int32_t k, int64_t n_feat, const char* what) {
   if (n_tok < 0) return fail(BEAM_E_RANGE, "n_tok must be >= 0");
-  if (k <= 0 || k % 64 != 0 || k > 65536)
-    return fail(BEAM_E_UNSUPPORTED, std::string(what) + ": the contraction width must be a multiple of 64 in [64, 65536]");
+  if (k <= 0 || k % 128 != 0 || k > 65536)
+    return fail(BEAM_E_UNSUPPORTED, std::string(what) + ": the contraction width must be a multiple of 128 in [128, 65536]");
   if (n_feat <= 0 || n_feat % beam::kGemmTile != 0)
     return fail(BEAM_E_UNSUPPORTED, std::string(what) + ": the output width must be a positive multiple of 256");
   const int64_t blocks = (n_feat / beam::kGemmTile) * (((int64_t)n_tok + beam::kGemmTile - 1) / beam::kGemmTile);

@@ -163,7 +163,7 @@ hipError_t launch_verify_attn(const PrefillParams& p, hipStream_t s);
 hipError_t launch_verify_combine(const VerifyCombineParams& p, hipStream_t s);
 
 // ---- projection GEMMs: out[t][f] = sum_k x[t][k] w[f][k] (bf16, fp32 accumulate) ----
-constexpr int kGemmTile = 256;  // n_feat must be a multiple; K a multiple of 64
+constexpr int kGemmTile = 256;  // n_feat must be a multiple; K a multiple of 128
 constexpr int kEpiPlain = 0;    // out[t][ld_out], columns f
 constexpr int kEpiQkvg = 1;     // Q' (fused norm + position op) / K / V / gate heads
 

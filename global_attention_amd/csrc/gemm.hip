@@ -35,19 +35,25 @@ namespace {
 
 constexpr int kTB = kGemmTile;         // features and tokens per block
 constexpr int kTK = 64;                // k per LDS stage
-constexpr int kOpTile = kTB * kTK;     // elements of one operand tile
-constexpr int kStage = 2 * kOpTile;    // W tile then X tile
+constexpr int kOpTile = kTB * kTK;     // elements of one operand tile (32 KiB)
+constexpr int kBufs = 2;               // LDS stage buffers (each a W tile and an X tile)
 constexpr int kRopePairs = D / 2;      // rotate-half pairs per head
 constexpr int kXcds = 8;               // XCDs of an MI355X (32 CUs each)
 constexpr int kPatchF = 4, kPatchT = 8;  // tiles per patch (feature x token): 32 = one per CU of an XCD
 constexpr int kGrid = kXcds * kPatchF * kPatchT;
-// LDS: two stages; after the k loop the same bytes stage the output tile
-// (4 waves x 128 x 128 bf16). The RoPE frequencies (revolutions per position,
-// float64) follow, inside the one LDS object.
-constexpr int kSmemElems = 2 * kStage + kRopePairs * 4;
+// LDS: two stage buffers (W tile, X tile) of 64 KiB. After the k loop the
+// same 128 KiB stage the output tile (4 waves x 128 x 128 bf16); the RoPE
+// frequencies (revolutions per position, float64) sit behind them.
+constexpr int kSmemElems = 2 * kBufs * kOpTile + 4 * (D / 2);
+constexpr int kFreqOff = 2 * kBufs * kOpTile;  // element offset of the RoPE table
 
 // Element offset of 16-byte chunk c (k = 8c .. 8c+7) of row r of an operand tile.
 __device__ __forceinline__ int op_off(int r, int c) { return r * kTK + ((c ^ (r & 7)) << 3); }
+
+// s_waitcnt: at most n vector-memory operations outstanding, LDS/scalar 0,
+// export count untouched (gfx9 fields vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8],
+// vmcnt[5:4] at bits 15:14).
+constexpr int vm_wait(int n) { return (n & 15) | (7 << 4) | (((n >> 4) & 3) << 14); }
 
 __device__ __forceinline__ void lds_dma16(const uint16_t* src, uint16_t* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
@@ -66,7 +72,7 @@ __device__ __forceinline__ float sum_lane_halves(float x) {
 template <int EPI>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) gemm_bf16_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[kSmemElems];
-  double* s_freq = reinterpret_cast<double*>(smem + 2 * kStage);
+  double* s_freq = reinterpret_cast<double*>(smem + kFreqOff);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -94,33 +100,43 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     if (ft >= n_ft || tt >= n_tt) continue;
     const int f0 = ft * kTB, n0 = tt * kTB;
 
-    // DMA plan: per stage each wave moves 8 KiB of W rows and 8 KiB of X rows,
-    // 1 KiB (8 rows) per instruction; lane l carries row 8i + (l >> 3), LDS
-    // chunk l & 7, i.e. source chunk (l & 7) ^ ((l >> 3) & 7).
+    // Loads per stage and wave: 8 KiB of W rows through registers and 8 KiB
+    // of X rows by LDS DMA, 1 KiB (8 rows of 128 bytes) per instruction, lane
+    // l on row 8(8w + i) + (l >> 3). The W rows are read in order (chunk
+    // l & 7) and written to their swizzled LDS chunk; the DMA lands lane l at
+    // LDS chunk l & 7, so it reads source chunk (l & 7) ^ ((l >> 3) & 7).
     const uint16_t* wsrc = p.w + (size_t)f0 * K;
     const uint16_t* xsrc = p.x + (size_t)n0 * K;
     uint32_t w_off[8], x_off[8];
+    int w_lds[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = 8 * (8 * w + i) + (lane >> 3);
       const int c = (lane & 7) ^ ((lane >> 3) & 7);
-      w_off[i] = (uint32_t)(r * K + 8 * c);
+      w_off[i] = (uint32_t)(r * K + 8 * (lane & 7));
+      w_lds[i] = op_off(r, lane & 7);
       const int rt = min(r, p.n_tok - 1 - n0);  // rows past the last token re-read it
       x_off[i] = (uint32_t)(rt * K + 8 * c);
     }
-    auto dma = [&](int k0, uint16_t* st) __attribute__((always_inline)) {
+    u32x4 wr0[8], wr1[8];  // W rows of two stages in flight
+    auto load_w = [&](int k0, u32x4(&r)[8]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        lds_dma16(wsrc + k0 + w_off[i], st + (8 * w + i) * 512);
-        lds_dma16(xsrc + k0 + x_off[i], st + kOpTile + (8 * w + i) * 512);
-      }
+      for (int i = 0; i < 8; ++i) r[i] = *reinterpret_cast<const u32x4*>(wsrc + k0 + w_off[i]);
+    };
+    auto store_w = [&](uint16_t* st, const u32x4(&r)[8]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(st + w_lds[i]) = r[i];
+    };
+    auto dma_x = [&](int k0, uint16_t* st) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) lds_dma16(xsrc + k0 + x_off[i], st + kOpTile + (8 * w + i) * 512);
     };
 
     // Fragment offsets: row 32b + (l & 31) of the wave's half, chunk 2kk + h.
     int frag[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) frag[kk] = op_off(r32, 2 * kk + h);
-    const int a_base = 128 * wm * kTK, b_base = kOpTile + 128 * wn * kTK;
+    const int a_base = 128 * wm * kTK, b_base = 128 * wn * kTK;
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -136,10 +152,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
       u32x4 a[4], b[4];
     };
     auto read_frags = [&](const uint16_t* st, int kk, Frags& f) __attribute__((always_inline)) {
+      const uint16_t* sw = st;
+      const uint16_t* sx = st + kOpTile;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) f.a[mb] = *reinterpret_cast<const u32x4*>(st + a_base + 32 * mb * kTK + frag[kk]);
+      for (int mb = 0; mb < 4; ++mb) f.a[mb] = *reinterpret_cast<const u32x4*>(sw + a_base + 32 * mb * kTK + frag[kk]);
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) f.b[nb] = *reinterpret_cast<const u32x4*>(st + b_base + 32 * nb * kTK + frag[kk]);
+      for (int nb = 0; nb < 4; ++nb) f.b[nb] = *reinterpret_cast<const u32x4*>(sx + b_base + 32 * nb * kTK + frag[kk]);
     };
     auto mfmas = [&](const Frags& f) __attribute__((always_inline)) {
 #pragma unroll
@@ -148,21 +166,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
         for (int nb = 0; nb < 4; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(f.a[mb]), as_bf16x8(f.b[nb]), acc[mb][nb], 0, 0, 0);
     };
-    // Stage s (LDS buffer cur) starts with its k-step 0 in registers. Each
-    // k-step's 16 MFMAs run with the 8 fragment reads of the next k-step
-    // interleaved with the first 8 (one read per MFMA), so at most 8 LDS
-    // reads are in flight (the LDS counter holds 15) and each has 8 MFMAs to
-    // land before the next k-step needs it. The barrier
-    // follows the stage's last LDS read: the next stage's first fragments are
-    // read during the last 16 MFMAs, and the DMA of stage s + 1 (into the
-    // other buffer, free once every wave passed the previous barrier) has the
-    // first 48 MFMAs to land.
-    const int nk = K / kTK;
-    dma(0, smem);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    Frags fa, fb;
-    read_frags(smem, 0, fa);
+    // The 16 MFMAs of one k-step with the 8 fragment reads of the next
+    // interleaved into the first 8 (one read per MFMA): at most 8 LDS reads
+    // are in flight (the LDS counter holds 15) and each has 8 MFMAs to land.
+    // In the stage's last k-step the W rows of the next stage are written to
+    // LDS between the last 8 MFMAs.
     auto step = [&](const Frags& cur_f, const uint16_t* st, int kk, Frags& nxt_f) __attribute__((always_inline)) {
       read_frags(st, kk, nxt_f);
       mfmas(cur_f);
@@ -171,22 +179,73 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // the last 8 MFMAs: the reads land meanwhile
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       __builtin_amdgcn_sched_barrier(0);
     };
-    // Every stage is the same code (no branch, so the accumulators never
-    // need copies): the last one re-loads its own chunk into the idle buffer
-    // and reads a k-step that is not used.
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = (kt & 1) * kStage, nxt = kStage - cur;
-      dma(min(kt + 1, nk - 1) * kTK, smem + nxt);
+    auto step_store = [&](const Frags& cur_f, const uint16_t* st, int kk, Frags& nxt_f, uint16_t* st_w,
+                          const u32x4(&r)[8]) __attribute__((always_inline)) {
+      read_frags(st, kk, nxt_f);
+      mfmas(cur_f);
+      store_w(st_w, r);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one LDS write
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      }
       __builtin_amdgcn_sched_barrier(0);
-      step(fa, smem + cur, 1, fb);
-      step(fb, smem + cur, 2, fa);
-      step(fa, smem + cur, 3, fb);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      step(fb, smem + nxt, 0, fa);
+    };
+
+    // Stage s lives in LDS buffer s % 2; its X rows arrive by DMA issued one
+    // stage ahead, its W rows in registers loaded two stages ahead. In stage
+    // s: DMA of X(s+1) into the other buffer (free: every wave passed the
+    // previous barrier after its last read of it), then the loads of W(s+2)
+    // (after the DMA, so the in-order counter can wait for the DMA alone);
+    // k-steps 0 .. 1 with the reads of 1 .. 2; wait for W(s+1) (16 newer
+    // operations may stay outstanding); k-step 2 with the reads of 3 and
+    // W(s+1) written into the other buffer; wait for the DMA (W(s+2) may stay
+    // outstanding) and the LDS traffic; a bare barrier (a fence would drain
+    // the loads still in flight); k-step 3 with the reads of stage s + 1's
+    // k-step 0. Stages go in pairs so the two W register sets have fixed
+    // names; every stage is the same code (the last ones re-load the final
+    // chunk and read a k-step nobody uses), so the loop has no branch and the
+    // accumulators never need copies.
+    const int nk = K / kTK;  // even (K is a multiple of 128)
+    auto kofs = [&](int kt) { return min(kt, nk - 1) * kTK; };
+    load_w(0, wr0);
+    dma_x(0, smem);
+    load_w(kofs(1), wr1);
+    __builtin_amdgcn_s_waitcnt(vm_wait(8));
+    store_w(smem, wr0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    Frags fa, fb;
+    read_frags(smem, 0, fa);
+    // (The buffers are fixed per half of the pair: with a buffer computed from
+    // kt the compiler cannot tell the DMA target from the buffer being read
+    // and waits for the DMA before every read.)
+    auto stage = [&](int kt, const uint16_t* cur, uint16_t* nxt, u32x4(&r_next)[8], u32x4(&r_load)[8])
+                     __attribute__((always_inline)) {
+      dma_x(kofs(kt + 1), nxt);
+      load_w(kofs(kt + 2), r_load);
+      __builtin_amdgcn_sched_barrier(0);
+      step(fa, cur, 1, fb);
+      step(fb, cur, 2, fa);
+      __builtin_amdgcn_s_waitcnt(vm_wait(16));
+      __builtin_amdgcn_sched_barrier(0);
+      step_store(fa, cur, 3, fb, nxt, r_next);
+      __builtin_amdgcn_s_waitcnt(vm_wait(8));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      step(fb, nxt, 0, fa);
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+      stage(kt, smem, smem + 2 * kOpTile, wr1, wr0);
+      stage(kt + 1, smem + 2 * kOpTile, smem, wr0, wr1);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();

@@ -45,7 +45,7 @@ extern "C" {
  *              [n_tok][n_q_heads][128] (the inputs of the prefill call).
  * workspace:   the prefill workspace of the chunk (>= beam_prefill_workspace_bytes,
  *              256-byte aligned); Q' is written into its query region.
- * Supported: hidden a positive multiple of 64, at most 65,536. */
+ * Supported: hidden a positive multiple of 128, at most 65,536. */
 beam_status beam_attn_project(const beam_attn_config *cfg, int32_t kind, const beam_bf16 *x,
                               int32_t hidden, const beam_bf16 *w_qkvg, const beam_bf16 *q_norm_w,
                               const int32_t *cu_seqlens, const int32_t *start_pos, int32_t n_seqs,
@@ -56,7 +56,7 @@ beam_status beam_attn_project(const beam_attn_config *cfg, int32_t kind, const b
 /* Output projection: out[t][f] = sum_k y[t][k] w_o[f][k] (bf16 in and out).
  * y: bf16 [n_tok][in_features]; w_o: bf16 [out_features][in_features];
  * out: bf16 [n_tok][out_features].
- * Supported: in_features a positive multiple of 64 (at most 65,536), out_features a
+ * Supported: in_features a positive multiple of 128 (at most 65,536), out_features a
  * positive multiple of 256. */
 beam_status beam_out_project(const beam_bf16 *y, const beam_bf16 *w_o, int32_t n_tok,
                              int32_t in_features, int32_t out_features, beam_bf16 *out,

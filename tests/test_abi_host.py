@@ -210,9 +210,10 @@ def test_projection_argument_checks():
                                    fake, ws, ws_bytes, None)
 
     assert proj(kind=2) == 3
-    assert proj(hidden=100) == 4                       # not a multiple of 64
+    assert proj(hidden=100) == 4                       # not a multiple of 128
+    assert proj(hidden=192) == 4
     assert proj(hidden=0) == 4
-    assert proj(hidden=65536 + 64) == 4
+    assert proj(hidden=65536 + 128) == 4
     assert proj(n_tok=-1) == 3
     assert proj(x=None) == 1
     assert proj(x=ctypes.c_void_p(0x100008)) == 3      # not 16-byte aligned

@@ -73,7 +73,7 @@ def _check_qprime(got_bits, want, what):
     assert np.all(err <= bound), f"{what}: {np.sum(err > bound)} elements outside the bound"
 
 
-@pytest.mark.parametrize("n_tok,k,n_out", [(300, 6144, 5120), (513, 64, 256), (1, 128, 512), (256, 192, 768)])
+@pytest.mark.parametrize("n_tok,k,n_out", [(300, 6144, 5120), (513, 128, 256), (1, 128, 512), (256, 384, 768)])
 def test_out_project_within_fp32_bound(n_tok, k, n_out):
     y = synth.normal_bf16((n_tok, k), 50, 0)
     w = synth.normal_bf16((n_out, k), 50, 1, scale=k ** -0.5)
