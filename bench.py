@@ -14,6 +14,9 @@ sequences at positions uniform in [65536, 131071] over a paged bf16 cache
 GB/s of KV read (4,096 B per cached key per layer). And under "verify": the
 verify step of speculative decoding on the same caches, a draft block of 8
 tokens per sequence ending at the decode position, in GB/s of cached KV read.
+And under "projection" / "sublayer": the QKV/gate projection (query prologue
+fused) and W_o around the same two layers, alone and end to end with the
+attention, in TFLOP/s against the bf16 MFMA peak.
 And under "router": the MoE router of one layer over the same 32,768 tokens
 (fp32 logits GEMM with the group-limited top-8 selection fused), in TFLOP/s
 against the fp32 MFMA peak.
@@ -55,6 +58,8 @@ _KERNEL_SOURCES = {
     "verify_attn_kernel<0, 0>": "prefill.hip",
     "verify_attn_kernel<1, 1>": "prefill.hip",
     "router_gemm_kernel<true>": "router.hip",
+    "gemm_bf16_kernel<1>": "gemm.hip",
+    "gemm_bf16_kernel<0>": "gemm.hip",
     "prefill_prologue_kernel<0, 0>": "prologue.hip",
     "prefill_prologue_kernel<1, 0>": "prologue.hip",
 }
@@ -335,6 +340,104 @@ def bench_router(T, steps, warmup):
     return dict(ms=ms, flops=flops)
 
 
+# --------------------------------------------------------------------------- projections
+
+HIDDEN = 5120
+N_QKVG = (2 * H + 2 * G) * D   # stacked Wq/Wk/Wv/Wg rows
+
+
+def setup_projection(T):
+    import torch
+    import synth
+    log(f"[bench] generating projection inputs T={T} hidden={HIDDEN}")
+    inp = synth.projection_inputs(41, 0, T, hidden=HIDDEN)
+    d = {k: _dev(v) for k, v in inp.items()}
+    d["x"] = d["x"].view(T, HIDDEN)
+    d["w_qkvg"] = d["w_qkvg"].view(N_QKVG, HIDDEN)
+    d["w_o"] = d["w_o"].view(HIDDEN, H * D)
+    d["k_raw"] = torch.empty((T, G, D), dtype=torch.bfloat16, device="cuda")
+    d["v_raw"] = torch.empty((T, G, D), dtype=torch.bfloat16, device="cuda")
+    d["gate"] = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+    d["out"] = torch.empty((T, HIDDEN), dtype=torch.bfloat16, device="cuda")
+    return d
+
+
+def proj_flops(T):
+    return 2.0 * T * HIDDEN * N_QKVG, 2.0 * T * (H * D) * HIDDEN
+
+
+def bench_projection(T, steps, warmup, pd, ws, meta):
+    """The QKV/gate projection with the fused query prologue (both layer kinds)
+    and W_o, each timed alone with events, at least 20 launches."""
+    import torch
+    import global_attention_amd as ga
+    cfg = ga.Config()
+    warmup, steps = max(warmup, 5), max(steps, 20)
+    calls = {
+        "qkvg_global": lambda: ga.attn_project(cfg, ga.GLOBAL, pd["x"], pd["w_qkvg"], pd["q_norm_w"], meta["cu"],
+                                               meta["start"], workspace=ws, k_raw=pd["k_raw"], v_raw=pd["v_raw"],
+                                               gate=pd["gate"]),
+        "qkvg_local": lambda: ga.attn_project(cfg, ga.LOCAL, pd["x"], pd["w_qkvg"], pd["q_norm_w"], meta["cu"],
+                                              meta["start"], workspace=ws, k_raw=pd["k_raw"], v_raw=pd["v_raw"],
+                                              gate=pd["gate"]),
+        "w_o": lambda: ga.out_project(pd["gate"].view(T, H * D), pd["w_o"], out=pd["out"]),
+    }
+    res = {}
+    for name, f in calls.items():
+        for _ in range(warmup):
+            f()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for e in evs:
+            e[0].record()
+            f()
+            e[1].record()
+        torch.cuda.synchronize()
+        res[name] = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    fq, fo = proj_flops(T)
+    log(f"[bench] projections T={T}: QKV/gate {res['qkvg_global']:.3f} ms ({fq / res['qkvg_global'] / 1e9:.1f} "
+        f"TFLOP/s), W_o {res['w_o']:.3f} ms ({fo / res['w_o'] / 1e9:.1f} TFLOP/s)")
+    return res
+
+
+def sublayer_step(cfg, layers, meta, pd, T):
+    """Both layers end to end: x -> QKV/gate projection (query prologue fused)
+    -> prefill without the query prologue -> W_o."""
+    import global_attention_amd as ga
+    for L in layers:
+        ga.attn_project(cfg, L["kind"], pd["x"], pd["w_qkvg"], pd["q_norm_w"], meta["cu"], meta["start"],
+                        workspace=L["ws"], k_raw=pd["k_raw"], v_raw=pd["v_raw"], gate=pd["gate"])
+        args = (cfg, L["cache"], None, pd["k_raw"], pd["v_raw"], pd["q_norm_w"], pd["k_norm_w"], pd["gate"],
+                meta["cu"], meta["seq"], meta["start"], T)
+        if L["kind"] == ga.GLOBAL:
+            ga.prefill(*args, out=L["out"], workspace=L["ws"],
+                       stages=ga.STAGE_PROLOGUE_KV | ga.STAGE_APPEND | ga.STAGE_ATTENTION)
+        else:
+            ga.prefill(*args, out=L["out"], workspace=L["ws"], stages=ga.STAGE_PROLOGUE_KV | ga.STAGE_ATTENTION)
+            ga.prefill(*args, out=L["out"], workspace=L["ws"], stages=ga.STAGE_APPEND)
+        ga.out_project(L["out"].view(T, H * D), pd["w_o"], out=pd["out"])
+
+
+def bench_sublayer(T, steps, warmup, layers, meta, pd):
+    import torch
+    import global_attention_amd as ga
+    cfg = ga.Config()
+    for _ in range(warmup):
+        sublayer_step(cfg, layers, meta, pd, T)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        sublayer_step(cfg, layers, meta, pd, T)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    fq, fo = proj_flops(T)
+    flops = 2 * (fq + fo) + FLOP_PER_PAIR * (pairs_global(T) + pairs_local(T))
+    log(f"[bench] sublayer pair (projections + attention) T={T}: {ms:.3f} ms, {flops / ms / 1e9:.1f} TFLOP/s")
+    return dict(ms=ms, flops=flops)
+
+
 # --------------------------------------------------------------------------- CPU oracle
 
 def cpu_baseline(layers, T, rows):
@@ -385,6 +488,7 @@ def main():
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--verify-split-keys", type=int, default=0)
     ap.add_argument("--skip-router", action="store_true")
+    ap.add_argument("--skip-projection", action="store_true")
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=384)
@@ -433,6 +537,35 @@ def main():
             "local_attn_ms": round(l_ms, 4), "local_attn_tflops": round(l_flops / (l_ms / 1e3) / 1e12, 2)}
         log(f"[bench] prefill step {r['ms_per_step']:.3f} ms -> {rec['value']} TFLOP/s; "
             f"global attn {g_ms:.3f} ms ({achieved:.1f} TFLOP/s), local attn {l_ms:.3f} ms")
+    if not args.skip_prefill and not args.skip_projection:
+        pf_layers = layers  # the prefill layers' caches and workspaces
+        meta = dict(cu=_i32([0, T]), seq=_i32([0]), start=_i32([0]))
+        pd = setup_projection(T)
+        pr = bench_projection(T, args.steps, args.warmup, pd, pf_layers[1]["ws"], meta)
+        fq, fo = proj_flops(T)
+        tq = fq / (pr["qkvg_global"] / 1e3) / 1e12
+        to = fo / (pr["w_o"] / 1e3) / 1e12
+        tot = (fq + fo) / ((pr["qkvg_global"] + pr["w_o"]) / 1e3) / 1e12
+        rec["projection"] = {
+            "workload": f"QKV/gate projection of {T} tokens (hidden 5120 -> 6144 + 1024 + 1024 + 6144, bf16, "
+                        "query RMSNorm + position op fused, Q' into the prefill workspace) and W_o (6144 -> 5120)",
+            "value": round(tot, 2), "unit": "TFLOP/s",
+            "qkvg_ms": {"global": round(pr["qkvg_global"], 4), "local": round(pr["qkvg_local"], 4)},
+            "w_o_ms": round(pr["w_o"], 4), "w_o_tflops": round(to, 2),
+            "roofline": {"kernel": "gemm_bf16_kernel<1>", "bound": "mfma", "achieved": round(tq, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tq / PEAK_BF16_TFLOPS, 4),
+                         "traffic": recorded_traffic("gemm_bf16_kernel<1>"),
+                         "avg_launch_ms": round(pr["qkvg_global"], 4), "flop_per_launch": fq},
+        }
+        sr = bench_sublayer(T, args.steps, args.warmup, pf_layers, meta, pd)
+        rec["sublayer"] = {
+            "workload": f"one local + one global attention sublayer end to end at T={T}: QKV/gate projection with "
+                        "the query prologue fused, K/V prologue + attention + append, W_o",
+            "value": round(sr["flops"] / (sr["ms"] / 1e3) / 1e12, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(sr["ms"], 4), "flop_per_step": sr["flops"],
+        }
+        del pd
+        torch.cuda.empty_cache()
     if not args.skip_decode:
         dres = bench_decode(args.decode_steps, 3)
         g = dres["global"]
