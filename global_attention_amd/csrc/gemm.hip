@@ -182,6 +182,39 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
       __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       __builtin_amdgcn_sched_barrier(0);
     };
+    // The stage's loads are spread over its first two k-steps so the memory
+    // pipeline sees a steady stream instead of a burst that stalls the MFMA
+    // issue behind it. The X DMAs set M0 and stay where the source puts them:
+    // one after each of k-step 0's first 8 MFMAs. The W loads of k-step 1 are
+    // placed by scheduling groups, one per MFMA.
+    auto step_dma = [&](const Frags& cur_f, const uint16_t* st, int kk, Frags& nxt_f, int k0x, uint16_t* stx)
+                        __attribute__((always_inline)) {
+      read_frags(st, kk, nxt_f);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur_f.a[mb]), as_bf16x8(cur_f.b[nb]),
+                                                                acc[mb][nb], 0, 0, 0);
+          const int i = 4 * mb + nb;
+          if (i < 8) lds_dma16(xsrc + k0x + x_off[i], stx + kOpTile + (8 * w + i) * 512);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto step_loads = [&](const Frags& cur_f, const uint16_t* st, int kk, Frags& nxt_f, int k0w, u32x4(&r)[8])
+                          __attribute__((always_inline)) {
+      read_frags(st, kk, nxt_f);
+      load_w(k0w, r);
+      mfmas(cur_f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one W load
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
     auto step_store = [&](const Frags& cur_f, const uint16_t* st, int kk, Frags& nxt_f, uint16_t* st_w,
                           const u32x4(&r)[8]) __attribute__((always_inline)) {
       read_frags(st, kk, nxt_f);
@@ -230,11 +263,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     // and waits for the DMA before every read.)
     auto stage = [&](int kt, const uint16_t* cur, uint16_t* nxt, u32x4(&r_next)[8], u32x4(&r_load)[8])
                      __attribute__((always_inline)) {
-      dma_x(kofs(kt + 1), nxt);
-      load_w(kofs(kt + 2), r_load);
       __builtin_amdgcn_sched_barrier(0);
-      step(fa, cur, 1, fb);
-      step(fb, cur, 2, fa);
+      step_dma(fa, cur, 1, fb, kofs(kt + 1), nxt);
+      step_loads(fb, cur, 2, fa, kofs(kt + 2), r_load);
       __builtin_amdgcn_s_waitcnt(vm_wait(16));
       __builtin_amdgcn_sched_barrier(0);
       step_store(fa, cur, 3, fb, nxt, r_next);
