@@ -184,3 +184,23 @@ def test_project_full_size_sampled():
     out = ga.out_project(y, dev_bf16(inp["w_o"]))
     sync()
     _check_product(host_bits(out[ri]), host_bits(y[ri]), inp["w_o"], "W_o full")
+
+
+def test_project_many_sequences_and_empty_chunks():
+    """Six chunks, two of them empty, at scattered start positions (the
+    epilogue finds each token's sequence and position); local layer, so every
+    query head is rotated at its own position."""
+    lens = [5, 0, 130, 1, 0, 300]
+    starts = [0, 7, 4095, 70000, 12, 1]
+    hidden, n = 256, sum(lens)
+    inp = synth.projection_inputs(54, 0, n, hidden=hidden, with_w_o=False)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    say(f"[case] attn_project many sequences lens={lens} starts={starts}")
+    k_raw, v_raw, gate, ws = ga.attn_project(CFG, A.LOCAL, dev_bf16(inp["x"]), dev_bf16(inp["w_qkvg"]),
+                                             dev_bf16(inp["q_norm_w"]), dev_i32(cu), dev_i32(starts))
+    sync()
+    q, _, _, _ = P.project_qkvg(inp["x"], inp["w_qkvg"])
+    want = P.queries_prime(A.LOCAL, q, inp["q_norm_w"], _positions(cu, starts)) * QBASE
+    _check_qprime(_queries_region(ws, n), want, "Q' many sequences")
+    rows = np.cumsum([0, H * D, G * D, G * D, H * D])
+    _check_product(host_bits(gate), inp["x"], inp["w_qkvg"][rows[3]:rows[4]], "gate many sequences")
