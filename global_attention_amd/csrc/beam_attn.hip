@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdio>
+#include <initializer_list>
 #include <string>
 
 #include "beam_attn.h"
@@ -28,6 +29,16 @@ beam_status ok() {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// The kernels move tensor rows with 8- and 16-byte vector accesses (and the
+// caches with 16-byte LDS DMA): every bf16 tensor must be 16-byte aligned
+// (NULL, for an optional argument, passes).
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+bool all_aligned16(std::initializer_list<const void*> ps) {
+  for (const void* q : ps)
+    if (!aligned16(q)) return false;
+  return true;
+}
 
 beam_status check_cfg(const beam_attn_config* c) {
   if (!c) return fail(BEAM_E_NULL, "cfg is NULL");
@@ -54,6 +65,7 @@ beam_status check_cache(const beam_kv_cache* kv) {
       !(kv->k_scale > 0.f && kv->v_scale > 0.f && kv->k_scale < 3.0e38f && kv->v_scale < 3.0e38f))
     return fail(BEAM_E_RANGE, "FP8 cache scales must be finite and positive");
   if (!kv->k || !kv->v) return fail(BEAM_E_NULL, "cache k/v is NULL");
+  if (!all_aligned16({kv->k, kv->v})) return fail(BEAM_E_RANGE, "cache k/v must be 16-byte aligned");
   if (kv->n_seqs <= 0) return fail(BEAM_E_RANGE, "cache n_seqs must be positive");
   if (kv->kind == BEAM_GLOBAL) {
     if (kv->page_size != 16) return fail(BEAM_E_UNSUPPORTED, "page_size must be 16");
@@ -218,6 +230,7 @@ beam_status beam_kv_append(const beam_attn_config* cfg, const beam_kv_cache* cac
   if (n_tok < 0) return fail(BEAM_E_RANGE, "n_tok must be >= 0");
   if (n_tok == 0) return ok();
   if (!k_raw || !v_raw || !k_norm_w || !seq_idx || !pos) return fail(BEAM_E_NULL, "NULL input pointer");
+  if (!all_aligned16({k_raw, v_raw, k_norm_w})) return fail(BEAM_E_RANGE, "k_raw, v_raw and k_norm_w must be 16-byte aligned");
   beam::AppendParams p{};
   p.k_raw = k_raw;
   p.v_raw = v_raw;
@@ -274,6 +287,8 @@ beam_status chunk_call(bool verify, uint32_t stages, const beam_attn_config* cfg
   if ((!q_raw && (stages & BEAM_STAGE_PROLOGUE)) || !k_raw || !v_raw || !q_norm_w || !k_norm_w || !gate_logits ||
       !cu_seqlens || !seq_idx || !start_pos || !out)
     return fail(BEAM_E_NULL, "NULL input/output pointer");
+  if (!all_aligned16({q_raw, k_raw, v_raw, q_norm_w, k_norm_w, gate_logits, out}))
+    return fail(BEAM_E_RANGE, "bf16 tensors (q_raw, k_raw, v_raw, norm weights, gate_logits, out) must be 16-byte aligned");
   if (!workspace) return fail(BEAM_E_NULL, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(BEAM_E_RANGE, "workspace must be 256-byte aligned");
   VerifyWs vws{};
@@ -499,6 +514,8 @@ beam_status beam_attn_decode_stages(uint32_t stages, const beam_attn_config* cfg
     return fail(BEAM_E_RANGE, "max_pos beyond block-table capacity");
   if (!q_raw || !q_norm_w || !gate_logits || !seq_idx || !pos || !out)
     return fail(BEAM_E_NULL, "NULL input/output pointer");
+  if (!all_aligned16({q_raw, q_norm_w, gate_logits, out}))
+    return fail(BEAM_E_RANGE, "bf16 tensors (q_raw, q_norm_w, gate_logits, out) must be 16-byte aligned");
   if (!workspace) return fail(BEAM_E_NULL, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(BEAM_E_RANGE, "workspace must be 256-byte aligned");
   DecodeWs ws;
@@ -674,8 +691,6 @@ beam_status beam_router_select(const beam_router_config* cfg, const float* logit
 // ---------------------------------------------------------------- projections
 
 namespace {
-
-bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
 beam_status check_gemm_sizes(int32_t n_tok, int32_t k, int64_t n_feat, const char* what) {
   if (n_tok < 0) return fail(BEAM_E_RANGE, "n_tok must be >= 0");

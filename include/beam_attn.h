@@ -29,6 +29,8 @@
  *     undefined behaviour.
  *   - Only head_dim == 128 is supported (BEAM_E_UNSUPPORTED). Inputs and
  *     outputs are bf16; the KV cache is bf16 or FP8 E4M3 (below).
+ *   - Every bf16 tensor and the cache's k/v buffers must be 16-byte aligned
+ *     (BEAM_E_RANGE otherwise); the workspaces 256-byte aligned.
  *   - Calls hold no global mutable state and may be made from several threads.
  *
  * KV cache layouts (beam_kv_cache.k / .v)

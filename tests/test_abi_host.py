@@ -250,3 +250,44 @@ def test_prologue_kv_stage_rules():
     assert call(ga.STAGE_PROLOGUE_KV | ga.STAGE_ATTENTION, q=None) == 5
     assert call(ga.STAGE_PROLOGUE | ga.STAGE_ATTENTION, q=None) == 1
     assert call(32) == 3
+
+
+def test_tensor_alignment_checks():
+    """bf16 tensors move with 8- and 16-byte vector accesses: a pointer that is
+    not 16-byte aligned is rejected (BEAM_E_RANGE) before any launch."""
+    L = ga.lib()
+    fake = ctypes.c_void_p(0x100000)
+    odd = ctypes.c_void_p(0x100008)
+    c = ga.Config().c()
+    kc = _cache()
+
+    def prefill(i):
+        t = [fake] * 6
+        t[i] = odd
+        return L.beam_attn_prefill(ctypes.byref(c), ctypes.byref(kc), *t, None, fake, fake, fake, 1, 4, 4, fake,
+                                   ctypes.c_void_p(0x1000), 1 << 30, None)
+
+    for i in range(6):  # q_raw, k_raw, v_raw, q_norm_w, k_norm_w, gate_logits
+        assert prefill(i) == 3 and "aligned" in L.beam_last_error().decode()
+    assert L.beam_attn_prefill(ctypes.byref(c), ctypes.byref(kc), *([fake] * 6), None, fake, fake, fake, 1, 4, 4,
+                               odd, ctypes.c_void_p(0x1000), 1 << 30, None) == 3  # out
+
+    def decode(i):
+        t = [fake] * 3
+        t[i] = odd
+        return L.beam_attn_decode(ctypes.byref(c), ctypes.byref(kc), *t, None, fake, fake, 1, 63, 0, fake,
+                                  ctypes.c_void_p(0x1000), 1 << 30, None)
+
+    for i in range(3):  # q_raw, q_norm_w, gate_logits
+        assert decode(i) == 3 and "aligned" in L.beam_last_error().decode()
+
+    def append(i):
+        t = [fake] * 3
+        t[i] = odd
+        return L.beam_kv_append(ctypes.byref(c), ctypes.byref(kc), *t, fake, fake, 4, None)
+
+    for i in range(3):  # k_raw, v_raw, k_norm_w
+        assert append(i) == 3 and "aligned" in L.beam_last_error().decode()
+    # the cache's own buffers
+    bad = ga.CCache(ga.GLOBAL, 0x200008, 0x300000, 16, 10, 0x400000, 4, 2)
+    assert L.beam_kv_append(ctypes.byref(c), ctypes.byref(bad), fake, fake, fake, fake, fake, 4, None) == 3
