@@ -17,12 +17,15 @@
 //
 // LDS layout. Tiles that lie inside the chunk are copied from the workspace
 // straight into LDS with global_load_lds_dwordx4 (no staging registers).
-//   K:   64 rows x 256 B. LDS row m holds key kappa(m) = m with bits 2 and 3
-//        swapped; the MFMA output row order then becomes natural key order,
-//        which is the order the PV operand needs.
+//   K:   two coordinate halves, each 64 rows x 128 B. LDS row m holds key
+//        kappa(m) = m with bits 2 and 3 swapped; the MFMA output row order
+//        then becomes natural key order, which is the order the PV operand
+//        needs.
 //   V^T: 128 rows (coordinates) x 128 B (64 keys, natural order).
-// Both XOR-swizzle their 16-byte chunks with the low 3 bits of the row, which
-// keeps the b128 operand reads free of bank conflicts without padding.
+// Both XOR-swizzle their 16-byte chunks with bits 1..3 of the row. A b128
+// read is served 16 lanes per LDS cycle, and the operand reads have those
+// lanes on 16 consecutive rows, two per 256-byte bank line: the swizzle puts
+// their chunks on 16 different bank groups, without padding.
 // Tiles of the cached prefix are also copied by DMA, each lane addressing its
 // chunk in the paged cache or ring; the prologue has already copied the cached
 // keys of the chunk's first tile into the workspace, so no tile mixes the two.
@@ -66,9 +69,17 @@ constexpr float kRescaleThreshold = 8.0f;
 
 // Key held by LDS row m of a K tile (bits 2 and 3 swapped; an involution).
 __device__ __forceinline__ int krow_key(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
-// Element offsets of 16-byte chunk c of K row m and of V^T row d.
-__device__ __forceinline__ int k_off(int m, int c) { return m * D + ((c ^ (m & 7)) << 3); }
-__device__ __forceinline__ int v_off(int d, int c) { return d * BN + ((c ^ (d & 7)) << 3); }
+// LDS tile layout. Every LDS row is 128 bytes (eight 16-byte chunks) and
+// chunk c of row r sits at position c ^ ((r >> 1) & 7): the 16 lanes that one
+// LDS cycle serves read rows r .. r+15 (two rows per 256-byte bank line), so
+// their chunks land on 16 distinct bank groups. K is stored as two halves of
+// 64 coordinates, [half][64 rows][64]; V^T as [128 rows][64 keys].
+constexpr int K_HALF = BN * 64;  // elements of one coordinate half of a K tile
+__device__ __forceinline__ int swz(int r, int c) { return (c ^ ((r >> 1) & 7)) << 3; }
+// Element offsets of 16-byte chunk c (coordinates 8c .. 8c+7) of K row m, and
+// of chunk c (keys 8c .. 8c+7) of V^T row d.
+__device__ __forceinline__ int k_off(int m, int c) { return (c >> 3) * K_HALF + m * 64 + swz(m, c & 7); }
+__device__ __forceinline__ int v_off(int d, int c) { return d * BN + swz(d, c); }
 
 // Combine a value held by lanes l and l^32 (the two key halves of a query)
 // with v_permlane32_swap, without an LDS round trip.
@@ -134,14 +145,14 @@ __device__ __forceinline__ DmaPlan<NW> make_dma_plan(int w, int lane) {
   DmaPlan<NW> pl;
 #pragma unroll
   for (int i = 0; i < DmaPlan<NW>::N; ++i) {
-    const int kI = w * DmaPlan<NW>::N + i;  // K rows 4kI .. 4kI+3
-    const int m = 4 * kI + (lane >> 4);
-    const int c = (lane & 15) ^ (m & 7);
-    pl.k_src[i] = (uint32_t)(krow_key(m) * D + 8 * c);
+    const int kI = w * DmaPlan<NW>::N + i;  // K half kI / 8, rows 8(kI % 8) .. +7
+    const int m = 8 * (kI & 7) + (lane >> 3);
+    const int c = (lane & 7) ^ ((m >> 1) & 7);
+    pl.k_src[i] = (uint32_t)(krow_key(m) * D + 64 * (kI >> 3) + 8 * c);
     pl.k_lds[i] = kI * 512;
     const int vI = w * DmaPlan<NW>::N + i;  // V^T rows 8vI .. 8vI+7
     const int d = 8 * vI + (lane >> 3);
-    const int cv = (lane & 7) ^ (d & 7);
+    const int cv = (lane & 7) ^ ((d >> 1) & 7);
     pl.v_src[i] = (uint32_t)(d * BN + 8 * cv);
     pl.v_lds[i] = vI * 512;
   }
@@ -168,13 +179,13 @@ __device__ __forceinline__ void dma_tile_prefix(const KeySource& ks, int w, int 
 #pragma unroll
   for (int i = 0; i < DmaPlan<NW>::N; ++i) {
     const int kI = w * DmaPlan<NW>::N + i;
-    const int m = 4 * kI + (lane >> 4);
-    const int c = (lane & 15) ^ (m & 7);
-    lds_dma16(k_row_src(ks, key0 + krow_key(m)) + 8 * c, sK + kI * 512);
+    const int m = 8 * (kI & 7) + (lane >> 3);
+    const int c = (lane & 7) ^ ((m >> 1) & 7);
+    lds_dma16(k_row_src(ks, key0 + krow_key(m)) + 64 * (kI >> 3) + 8 * c, sK + kI * 512);
 
     const int vI = w * DmaPlan<NW>::N + i;
     const int d = 8 * vI + (lane >> 3);
-    const int cv = (lane & 7) ^ (d & 7);
+    const int cv = (lane & 7) ^ ((d >> 1) & 7);
     lds_dma16(v_elem_src(ks, d, key0 + 8 * cv), sV + vI * 512);
   }
 }
@@ -349,8 +360,8 @@ prefill_attn_kernel(PrefillParams p) {
     for (int i = 0; i < 16; ++i) sref[nb][i] = 0.f;
   }
   // Loop-invariant LDS element offsets of this lane's operand chunks: K row n,
-  // chunk (2q + half) ^ (n & 7) for q = 0..3 (chunks 8..15 add 64 elements and
-  // M-block 1 adds 32 rows); V^T row n, chunk (2kb + half) ^ (n & 7) (row
+  // chunk 2q + half for q = 0..3 (chunks 8..15 are the second coordinate half,
+  // K_HALF further; M-block 1 adds 32 rows); V^T row n, chunk 2kb + half (row
   // block db adds 32 rows).
   int koff[4], voff[4];
 #pragma unroll
@@ -379,7 +390,7 @@ prefill_attn_kernel(PrefillParams p) {
     for (int kk = 0; kk < 8; ++kk) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(sK + koff[kk & 3] + 64 * (kk >> 2) + 32 * D * mb);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sK + koff[kk & 3] + K_HALF * (kk >> 2) + 32 * 64 * mb);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
           s[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qf[nb][kk]),
@@ -590,18 +601,19 @@ __device__ __forceinline__ void dma_tile_cached(const KeySource& ks, const int* 
 #pragma unroll
   for (int i = 0; i < DmaPlan<NW>::N; ++i) {
     const int kI = w * DmaPlan<NW>::N + i;
-    const int m = 4 * kI + (lane >> 4);
-    const int c = (lane & 15) ^ (m & 7);
-    lds_dma16(k_row_cached(ks, pages, page0, key0 + krow_key(m)) + 8 * c, sK + kI * 512);
+    const int m = 8 * (kI & 7) + (lane >> 3);
+    const int c = (lane & 7) ^ ((m >> 1) & 7);
+    lds_dma16(k_row_cached(ks, pages, page0, key0 + krow_key(m)) + 64 * (kI >> 3) + 8 * c, sK + kI * 512);
     const int vI = w * DmaPlan<NW>::N + i;
     const int d = 8 * vI + (lane >> 3);
-    const int cv = (lane & 7) ^ (d & 7);
+    const int cv = (lane & 7) ^ ((d >> 1) & 7);
     lds_dma16(v_elem_cached(ks, pages, page0, d, key0 + 8 * cv), sV + vI * 512);
   }
 }
 
 // FP8 prefix tile in two phases: the codes into registers, then dequantised
 // into LDS (the chunks of fetch_prefix_fp8).
+
 // s_waitcnt immediate for vmcnt <= n, lgkmcnt 0, expcnt untouched (gfx9
 // fields: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]).
 constexpr int vm_lgkm_wait(int n) { return (n & 15) | (7 << 4) | (((n >> 4) & 3) << 14); }
@@ -783,7 +795,7 @@ verify_attn_kernel(PrefillParams p) {
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(sK + koff[kk & 3] + 64 * (kk >> 2) + 32 * D * mb);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sK + koff[kk & 3] + K_HALF * (kk >> 2) + 32 * 64 * mb);
         s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qf[kk]), kk == 0 ? sref : s[mb], 0,
                                                         0, 0);
       }
