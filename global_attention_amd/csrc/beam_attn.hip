@@ -118,7 +118,15 @@ PrefillWs prefill_ws_layout(const beam_attn_config* c, int n_tok, int n_seqs) {
   return ws;
 }
 
-int default_verify_split_keys(int kind) { return kind == BEAM_LOCAL ? 256 : 2048; }
+// Default keys per verify split: 256 on local layers (the window spans at most
+// a few tiles). On global layers 4096 keys when that still gives at least 1024
+// blocks (two per CU slot at two blocks per CU), else 2048. Longer splits mean
+// fewer partials to merge and less per-block work.
+int default_verify_split_keys(const beam_attn_config* c, int kind, int n_seqs, int max_pos) {
+  if (kind == BEAM_LOCAL) return 256;
+  const long long blocks = (long long)n_seqs * c->n_kv_heads * (max_pos / 4096 + 1);
+  return blocks >= 1024 ? 4096 : 2048;
+}
 
 // Verify (short-chunk) calls: the prefill workspace, then the split partials
 // (reference max and sum, and the unnormalised accumulator) per (token, head,
@@ -131,7 +139,7 @@ struct VerifyWs {
 
 bool verify_ws_layout(const beam_attn_config* c, int kind, int n_tok, int n_seqs, int max_chunk_len, int max_pos,
                       int split_keys, VerifyWs* ws) {
-  if (split_keys == 0) split_keys = default_verify_split_keys(kind);
+  if (split_keys == 0) split_keys = default_verify_split_keys(c, kind, n_seqs, max_pos);
   if (split_keys < 64 || split_keys % 64 != 0 || split_keys > 64 * beam::kVerifyMaxSplitTiles) return false;
   if (n_seqs <= 0 || n_tok < 0 || max_chunk_len < 0 || max_pos < 0) return false;
   int n_tiles = (max_pos >> 6) + 1;

@@ -174,7 +174,8 @@ beam_status beam_attn_decode(const beam_attn_config *cfg, const beam_kv_cache *c
  * max_pos >= start_pos[i] + chunk length - 1 for every i (sizes the split grid;
  * keys beyond the grid it implies are left out, without any access outside the
  * buffers). split_keys: keys per split (multiple of 64, <= 8192), or 0 for the
- * default (256 local, 2048 global).
+ * default: 256 local; global 4096 if n_seqs * n_kv_heads * (max_pos / 4096 + 1)
+ * >= 1024, else 2048.
  * Rejected draft tokens: on a GLOBAL cache the next call simply starts at the
  * first rejected position (its slots are overwritten). A LOCAL ring keeps only
  * the last `window` positions, so appending a rejected token would evict a key
