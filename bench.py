@@ -14,6 +14,7 @@ sequences at positions uniform in [65536, 131071] over a paged bf16 cache
 GB/s of KV read (4,096 B per cached key per layer). And under "verify": the
 verify step of speculative decoding on the same caches, a draft block of 8
 tokens per sequence ending at the decode position, in GB/s of cached KV read.
+And under "decode_1m": one sequence at position 1,048,575 (4 GiB of cache).
 And under "projection" / "sublayer": the QKV/gate projection (query prologue
 fused) and W_o around the same two layers, alone and end to end with the
 attention, in TFLOP/s against the bf16 MFMA peak.
@@ -249,6 +250,56 @@ def bench_decode(steps, warmup):
         log(f"[bench] decode {name}: {nbytes / 1e9:.2f} GB, call {el * 1e3:.3f} ms, split kernel {split_ms:.3f} ms")
     res["setup"] = setup
     return res
+
+
+def bench_decode_1m(steps, warmup):
+    """One sequence at t = 1,048,575 on a global layer: 65,536 pages (4 GiB of
+    bf16 K+V, far beyond the 256 MB MALL) dealt by a random permutation; the
+    split-key decode with its prologue and combine, timed as in bench_decode."""
+    import torch
+    import global_attention_amd as ga
+    import synth
+    cfg = ga.Config()
+    T = 1 << 20
+    bt, n_pages = synth.paged_block_table(4, [T])
+    cache = ga.KVCache.allocate_global(cfg, n_pages, torch.from_numpy(bt))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4)
+    for t in (cache.k, cache.v):
+        for p0 in range(0, n_pages, 8192):
+            t[p0:p0 + 8192].normal_(generator=gen)
+    inp = synth.attention_inputs(cfg=4, layer=9, n_tok=1)
+    d = {k: _dev(v) for k, v in inp.items()}
+    seq, pos, max_pos = _i32([0]), _i32([T - 1]), T - 1
+    out = torch.empty((1, H, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(ga.decode_workspace_bytes(cfg, ga.GLOBAL, 1, max_pos), dtype=torch.uint8, device="cuda")
+    args = (cfg, cache, d["q"], d["q_norm_w"], d["gate"], seq, pos, max_pos)
+
+    def one(ev=None):
+        ga.decode(*args, out=out, workspace=ws, stages=ga.STAGE_PROLOGUE)
+        if ev is not None:
+            ev[0].record()
+        ga.decode(*args, out=out, workspace=ws, stages=ga.STAGE_ATTENTION)
+        if ev is not None:
+            ev[1].record()
+        ga.decode(*args, out=out, workspace=ws, stages=ga.STAGE_COMBINE)
+
+    warmup, steps = max(warmup, 5), max(steps, 50)
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        one(evs[s])
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) / steps
+    split_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    nbytes = T * G * D * 2 * 2
+    log(f"[bench] decode 1M: {nbytes / 2 ** 30:.0f} GiB, call {el * 1e3:.3f} ms, split kernel {split_ms:.3f} ms")
+    del cache
+    return dict(bytes=nbytes, ms_per_call=el * 1e3, split_ms=split_ms, gbs_call=nbytes / el / 1e9,
+                gbs_split=nbytes / (split_ms / 1e3) / 1e9)
 
 
 def bench_verify(steps, warmup, dres, block=8, split_keys=0):
@@ -615,6 +666,19 @@ def main():
             "global_fp8": {"ms_per_call": round(v["global_fp8"]["ms_per_call"], 4),
                            "gbs_split": round(v["global_fp8"]["gbs_split"], 1),
                            "speedup_vs_8_decode_calls": round(v["global_fp8"]["vs_decode_calls"], 2)},
+        }
+        del dres, v
+        torch.cuda.empty_cache()
+        m = bench_decode_1m(args.decode_steps, 5)
+        rec["decode_1m"] = {
+            "workload": "one sequence at position 1,048,575 on a global layer: 65,536 permuted 16-token pages, "
+                        "4 GiB of bf16 K+V",
+            "value": round(m["gbs_call"], 1), "unit": "GB/s",
+            "frac_of_hbm_peak": round(m["gbs_call"] / PEAK_HBM_GBS, 4),
+            "ms_per_call": round(m["ms_per_call"], 4), "bytes": m["bytes"],
+            "roofline": {"kernel": "decode_split_kernel<1>", "bound": "hbm", "achieved": round(m["gbs_split"], 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(m["gbs_split"] / PEAK_HBM_GBS, 4),
+                         "traffic": None, "avg_launch_ms": round(m["split_ms"], 4), "bytes_per_launch": m["bytes"]},
         }
     if not args.skip_router:
         rr = bench_router(T, args.steps, args.warmup)

@@ -445,10 +445,14 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(CombineParams p) {
   const int n_keys = p.kind == 0 ? min(t + 1, p.window) : t + 1;
   const int ns = (n_keys + p.split_keys - 1) / p.split_keys;
   const size_t row0 = ((size_t)seq * p.H + h) * p.n_splits;
+  // Unrolled so that a long context (hundreds of splits, few blocks) keeps
+  // eight independent loads in flight per thread.
   float M = kNegInf;
+#pragma unroll 8
   for (int s = 0; s < ns; ++s) M = fmaxf(M, p.part_ml[2 * (row0 + s)]);
   float L = 0.f, A = 0.f;
   if (M != kNegInf) {
+#pragma unroll 8
     for (int s = 0; s < ns; ++s) {
       const float sc = __builtin_amdgcn_exp2f(p.part_ml[2 * (row0 + s)] - M);
       L += sc * p.part_ml[2 * (row0 + s) + 1];

@@ -956,9 +956,11 @@ __global__ void __launch_bounds__(128) verify_combine_kernel(VerifyCombineParams
   const int ns = min(p.n_splits, (j_last - j_first + p.split_tiles) / p.split_tiles);
   const size_t row0 = ((size_t)tok * p.H + h) * p.n_splits;
   float M = kNegInf;
+#pragma unroll 8
   for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, p.part_ml[2 * (row0 + sp)]);
   float L = 0.f, A = 0.f;
   if (M != kNegInf) {
+#pragma unroll 8
     for (int sp = 0; sp < ns; ++sp) {
       const float m = p.part_ml[2 * (row0 + sp)];
       if (m == kNegInf) continue;
