@@ -539,6 +539,9 @@ def main():
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--verify-split-keys", type=int, default=0)
     ap.add_argument("--skip-router", action="store_true")
+    ap.add_argument("--skip-decode-1m", action="store_true",
+                    help="leave out the 1M-token decode (it launches decode_split_kernel<1> at another size, which "
+                         "would mix into that kernel's per-kernel profile averages)")
     ap.add_argument("--skip-projection", action="store_true")
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -669,6 +672,7 @@ def main():
         }
         del dres, v
         torch.cuda.empty_cache()
+    if not args.skip_decode and not args.skip_decode_1m:
         m = bench_decode_1m(args.decode_steps, 5)
         rec["decode_1m"] = {
             "workload": "one sequence at position 1,048,575 on a global layer: 65,536 permuted 16-token pages, "
