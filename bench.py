@@ -551,7 +551,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the attention path shards by "
-              f"KV head or sequence with no exchange, but no multi-GPU run is part of this build.",
+              f"KV head or sequence with no exchange, and no multi-GPU run is implemented.",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
