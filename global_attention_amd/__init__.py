@@ -32,7 +32,7 @@ EXPORTED = [
     "beam_kv_append", "beam_attn_prefill", "beam_attn_decode", "beam_attn_verify",
     "beam_attn_prefill_stages", "beam_attn_decode_stages", "beam_attn_verify_stages",
     "beam_prefill_workspace_bytes", "beam_decode_workspace_bytes", "beam_verify_workspace_bytes",
-    "beam_kv_bytes", "beam_kv_page_slot", "beam_debug_visibility",
+    "beam_kv_bytes", "beam_kv_page_slot", "beam_debug_visibility", "beam_debug_validate_cache",
     "beam_status_str", "beam_last_error",
     "beam_router", "beam_router_logits", "beam_router_select",
     "beam_attn_project", "beam_out_project",
@@ -124,6 +124,7 @@ def lib() -> ctypes.CDLL:
     L.beam_kv_bytes.argtypes = [I64, I32, I32, I32, I32, I32, I32, I32, P, P]
     L.beam_kv_page_slot.argtypes = [P, I32, I32, I32, I32, P, P]
     L.beam_debug_visibility.argtypes = [I32, I32, I32, I32, I32, I32, P, P]
+    L.beam_debug_validate_cache.argtypes = [P, P, P, P]
     L.beam_router.argtypes = [P, P, P, P, I32, P, P, P]
     L.beam_router_logits.argtypes = [P, P, P, I32, P, P]
     L.beam_router_select.argtypes = [P, P, P, I32, P, P, P]
@@ -134,8 +135,8 @@ def lib() -> ctypes.CDLL:
     L.beam_last_error.restype = ctypes.c_char_p
     for name in ("beam_kv_append", "beam_attn_prefill", "beam_attn_decode", "beam_attn_prefill_stages",
                  "beam_attn_decode_stages", "beam_attn_verify", "beam_attn_verify_stages", "beam_kv_bytes",
-                 "beam_kv_page_slot", "beam_debug_visibility", "beam_router", "beam_router_logits",
-                 "beam_router_select", "beam_attn_project", "beam_out_project"):
+                 "beam_kv_page_slot", "beam_debug_visibility", "beam_debug_validate_cache", "beam_router",
+                 "beam_router_logits", "beam_router_select", "beam_attn_project", "beam_out_project"):
         getattr(L, name).restype = I32
     _lib = L
     return L
@@ -376,6 +377,23 @@ def debug_visibility(kind: int, window: int, t0: int, n_q: int, s0: int, n_k: in
     mask = torch.empty((n_q, n_k), dtype=torch.uint8, device=device)
     _check(lib().beam_debug_visibility(kind, window, t0, n_q, s0, n_k, _ptr(mask), _stream(stream)))
     return mask
+
+
+def debug_validate_cache(cache: KVCache, n_tokens=None, stream=None):
+    """Per cache sequence, the number of used block-table entries that name no
+    physical page (-1: the length does not fit the row); int32 device tensor
+    [n_seqs] (beam_debug_validate_cache). n_tokens: int32 device [n_seqs] or
+    None for whole rows."""
+    import torch
+    if cache.kind != GLOBAL:
+        raise ValueError("only a paged (global) cache has a block table")
+    n = cache.block_table.shape[0]
+    if n_tokens is not None:
+        _need(n_tokens, torch.int32, (n,), "n_tokens")
+    n_bad = torch.empty((n,), dtype=torch.int32, device=cache.block_table.device)
+    kc = cache.c()
+    _check(lib().beam_debug_validate_cache(ctypes.byref(kc), _ptr(n_tokens), _ptr(n_bad), _stream(stream)))
+    return n_bad
 
 
 # ---------------------------------------------------------------- router

@@ -422,6 +422,7 @@ beam_status chunk_call(bool verify, uint32_t stages, const beam_attn_config* cfg
     cp.n_tok = n_tok;
     cp.n_splits = vws.n_splits;
     cp.split_tiles = vws.split_tiles;
+    cp.max_pos = max_pos;
     if ((stages & BEAM_STAGE_VERIFY_COMBINE) &&
         (st = hip_status(beam::launch_verify_combine(cp, s), "verify combine launch")) != BEAM_OK)
       return st;
@@ -582,6 +583,8 @@ beam_status beam_attn_decode_stages(uint32_t stages, const beam_attn_config* cfg
   cp.part_ml = ml;
   cp.part_acc = acc;
   cp.pos = pos;
+  cp.seq_idx = seq_idx;
+  cp.n_cache_seqs = cache->n_seqs;
   cp.gate = gate_logits;
   cp.gate_bias = gate_bias;
   cp.out = out;
@@ -615,6 +618,21 @@ beam_status beam_debug_visibility(int32_t kind, int32_t window, int32_t t0, int3
   if ((int64_t)n_q * n_k == 0) return ok();
   beam_status st = hip_status(beam::launch_visibility(kind, window, t0, n_q, s0, n_k, mask, (hipStream_t)stream),
                               "visibility launch");
+  if (st != BEAM_OK) return st;
+  return ok();
+}
+
+beam_status beam_debug_validate_cache(const beam_kv_cache* cache, const int32_t* n_tokens, int32_t* n_bad,
+                                      void* stream) {
+  if (!cache) return fail(BEAM_E_NULL, "cache is NULL");
+  if (cache->kind != BEAM_GLOBAL) return fail(BEAM_E_RANGE, "only a paged (GLOBAL) cache has a block table");
+  if (!cache->block_table || !n_bad) return fail(BEAM_E_NULL, "block_table or n_bad is NULL");
+  if (cache->n_seqs <= 0 || cache->max_pages_per_seq <= 0 || cache->n_pages <= 0 || cache->page_size <= 0)
+    return fail(BEAM_E_RANGE, "n_seqs, max_pages_per_seq, n_pages and page_size must be positive");
+  beam_status st = hip_status(beam::launch_validate_cache(cache->block_table, cache->max_pages_per_seq,
+                                                          cache->n_pages, cache->page_size, cache->n_seqs,
+                                                          n_tokens, n_bad, (hipStream_t)stream),
+                              "validate_cache launch");
   if (st != BEAM_OK) return st;
   return ok();
 }

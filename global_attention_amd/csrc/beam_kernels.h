@@ -119,6 +119,7 @@ struct VerifyCombineParams {
   const int32_t* bt;
   int max_pages, n_cache_seqs;
   int kind, window, H, n_seqs, n_tok, n_splits, split_tiles;
+  int max_pos;  // a sequence whose chunk ends past max_pos gets NaN rows (its keys lie beyond the split grid)
 };
 
 struct DecodeParams {
@@ -141,6 +142,8 @@ struct CombineParams {
   const float* part_ml;
   const float* part_acc;
   const int32_t* pos;
+  const int32_t* seq_idx;  // a row outside [0, n_cache_seqs) gets NaN (the split kernel read nothing for it)
+  int n_cache_seqs;
   const uint16_t* gate;
   const float* gate_bias;
   uint16_t* out;
@@ -156,6 +159,8 @@ hipError_t launch_kv_append(const AppendParams& p, hipStream_t s);
 hipError_t launch_decode_q_prologue(const DecodeQParams& p, hipStream_t s);
 hipError_t launch_visibility(int kind, int window, int t0, int n_q, int s0, int n_k, uint8_t* mask,
                              hipStream_t s);
+hipError_t launch_validate_cache(const int32_t* bt, int max_pages, int n_pages, int page_size, int n_seqs,
+                                 const int32_t* n_tokens, int32_t* n_bad, hipStream_t s);
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s);
 hipError_t launch_decode_split(const DecodeParams& p, int n_seqs, hipStream_t s);
 hipError_t launch_decode_combine(const CombineParams& p, int n_seqs, hipStream_t s);

@@ -437,9 +437,10 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(CombineParams p) {
   const int h = blockIdx.x - seq * p.H;
   const int d = threadIdx.x;
   const int t = p.pos[seq];
+  const int cseq = p.seq_idx[seq];
   const size_t idx = ((size_t)seq * p.H + h) * D + d;
-  if (t < 0 || t > p.max_pos) {
-    p.out[idx] = 0x7fc0;  // NaN: the position was outside the decode grid
+  if (t < 0 || t > p.max_pos || cseq < 0 || cseq >= p.n_cache_seqs) {
+    p.out[idx] = 0x7fc0;  // NaN: the position was outside the decode grid, or the cache row does not exist
     return;
   }
   const int n_keys = p.kind == 0 ? min(t + 1, p.window) : t + 1;

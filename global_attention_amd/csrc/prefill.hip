@@ -686,6 +686,7 @@ verify_attn_kernel(PrefillParams p) {
   const int cseq = p.seq_idx[seq];
   const int W = p.window;
   const int t_last = start + len - 1;
+  if (start < 0) return;  // the combine writes NaN for this sequence
 
   KeySource ks;
   ks.kw = p.kw + (size_t)g * p.P * D;
@@ -953,6 +954,11 @@ __global__ void __launch_bounds__(128) verify_combine_kernel(VerifyCombineParams
   const int kmin = p.kind == 0 ? max(0, start - (p.window - 1)) : 0;
   const int j_first = cache_ok ? kmin >> 6 : max(kmin >> 6, start >> 6);
   const int j_last = (start + len - 1) >> 6;
+  const size_t idx = ((size_t)tok * p.H + h) * D + d;
+  if (start < 0 || start + len - 1 > p.max_pos) {
+    p.out[idx] = 0x7fc0;  // NaN: the chunk reaches past max_pos, beyond the keys the split grid covers
+    return;
+  }
   const int ns = min(p.n_splits, (j_last - j_first + p.split_tiles) / p.split_tiles);
   const size_t row0 = ((size_t)tok * p.H + h) * p.n_splits;
   float M = kNegInf;
@@ -970,7 +976,6 @@ __global__ void __launch_bounds__(128) verify_combine_kernel(VerifyCombineParams
     }
   }
   const float o = L > 0.f ? A / L : 0.f;
-  const size_t idx = ((size_t)tok * p.H + h) * D + d;
   const float bias = p.gate_bias ? p.gate_bias[h] : 0.f;
   const float sg = __frcp_rn(1.f + __expf(-(bf16f(p.gate[idx]) + bias)));
   bf16x2 rr;

@@ -427,9 +427,49 @@ __global__ void visibility_kernel(int kind, int window, int t0, int n_q, int s0,
   mask[i] = visible(kind, window, t0 + r, s0 + c) ? 1 : 0;
 }
 
+// ----------------------------------------------------------------------------
+// Block-table check of a paged cache (debug entry point): one block per cache
+// sequence counts the entries of its used range that name no physical page.
+// Only the ids are compared; no page is read.
+// ----------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) validate_cache_kernel(const int32_t* bt, int max_pages, int n_pages,
+                                                             int page_size, const int32_t* n_tokens,
+                                                             int32_t* n_bad) {
+  const int c = blockIdx.x;
+  int used = max_pages;
+  if (n_tokens) {
+    const long long nt = n_tokens[c];
+    const long long np = (nt + page_size - 1) / page_size;
+    if (nt < 0 || np > max_pages) {
+      if (threadIdx.x == 0) n_bad[c] = -1;  // the length itself does not fit the row
+      return;
+    }
+    used = (int)np;
+  }
+  const int32_t* row = bt + (size_t)c * max_pages;
+  int cnt = 0;
+  for (int i = threadIdx.x; i < used; i += 256) {
+    const int pg = row[i];
+    cnt += (pg < 0 || pg >= n_pages) ? 1 : 0;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+  __shared__ int s_cnt[4];
+  if ((threadIdx.x & 63) == 0) s_cnt[threadIdx.x >> 6] = cnt;
+  __syncthreads();
+  if (threadIdx.x == 0) n_bad[c] = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+}
+
 }  // namespace beam
 
 namespace beam {
+
+hipError_t launch_validate_cache(const int32_t* bt, int max_pages, int n_pages, int page_size, int n_seqs,
+                                 const int32_t* n_tokens, int32_t* n_bad, hipStream_t s) {
+  hipLaunchKernelGGL(validate_cache_kernel, dim3((unsigned)n_seqs), dim3(256), 0, s, bt, max_pages, n_pages,
+                     page_size, n_tokens, n_bad);
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill_prologue(const PrologueParams& p, int n_seqs, int n_tiles, hipStream_t s) {
   const int parts = kPrologueFixedParts + (p.with_q ? (p.H + kQHeadsPerBlock - 1) / kQHeadsPerBlock : 0);

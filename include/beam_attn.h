@@ -151,7 +151,9 @@ beam_status beam_attn_prefill(const beam_attn_config *cfg, const beam_kv_cache *
  * The new token (position pos[i], cache sequence seq_idx[i]) must already have
  * been appended with beam_kv_append.
  * q_raw, gate_logits, out: bf16 [n_seqs][n_q_heads][head_dim].
- * max_pos >= every pos[i] (sizes the split grid).
+ * max_pos >= every pos[i] (sizes the split grid). A sequence whose pos[i] lies
+ * outside [0, max_pos], or whose seq_idx[i] names no cache sequence, is not read
+ * and its output rows are NaN.
  * split_keys: keys per split (multiple of 128, <= 65536), or 0 for the default.
  * workspace: >= beam_decode_workspace_bytes(cfg, kind, n_seqs, max_pos, split_keys). */
 beam_status beam_attn_decode(const beam_attn_config *cfg, const beam_kv_cache *cache,
@@ -171,9 +173,9 @@ beam_status beam_attn_decode(const beam_attn_config *cfg, const beam_kv_cache *c
  * is: the (token, query head) rows of one KV head share every K/V tile, and the
  * keys are split across blocks with a log-sum-exp merge.
  * Limits: max_chunk_len * (n_q_heads / n_kv_heads) <= 128 (21 tokens at 48/8).
- * max_pos >= start_pos[i] + chunk length - 1 for every i (sizes the split grid;
- * keys beyond the grid it implies are left out, without any access outside the
- * buffers). split_keys: keys per split (multiple of 64, <= 8192), or 0 for the
+ * max_pos >= start_pos[i] + chunk length - 1 for every i (sizes the split grid).
+ * A sequence that breaks this (or has start_pos[i] < 0) gets NaN output rows:
+ * the split grid does not cover its keys. split_keys: keys per split (multiple of 64, <= 8192), or 0 for the
  * default: 256 local; global 4096 if n_seqs * n_kv_heads * (max_pos / 4096 + 1)
  * >= 1024, else 2048.
  * Rejected draft tokens: on a GLOBAL cache the next call simply starts at the
@@ -276,6 +278,23 @@ beam_status beam_kv_page_slot(const int32_t *block_table_host, int32_t max_pages
  * mask: device uint8 [n_q][n_k]. */
 beam_status beam_debug_visibility(int32_t kind, int32_t window, int32_t t0, int32_t n_q,
                                   int32_t s0, int32_t n_k, uint8_t *mask, void *stream);
+
+/* Opt-in check of a paged (GLOBAL) cache's block table. Block-table entries are
+ * device data that the attention calls take on trust; a serving stack fills
+ * them from its page allocator (the pages' serving recipes run a paged FP8 E4M3
+ * cache with 64-token pages: "Beam 1.0 auf vier B300s", orcarouter.ai, section
+ * "Was vier B300s hinsichtlich des Speichers tatsächlich bringen").
+ * For every cache sequence c (0 <= c < cache->n_seqs):
+ *   n_bad[c] = number of entries block_table[c][i], 0 <= i < ceil(n_tokens[c] / page_size),
+ *              that are < 0 or >= cache->n_pages;
+ *            = -1 if n_tokens[c] < 0 or needs more pages than the row holds.
+ * n_tokens: device int32 [cache->n_seqs], positions held per sequence, or NULL
+ * to check whole rows. n_bad: device int32 [cache->n_seqs], written by the call.
+ * Only ids are compared: no page of k/v is read, so a bad entry is safe here.
+ * Enqueued on `stream`; read n_bad after a sync. A LOCAL cache has no block
+ * table (BEAM_E_RANGE). */
+beam_status beam_debug_validate_cache(const beam_kv_cache *cache, const int32_t *n_tokens, int32_t *n_bad,
+                                      void *stream);
 
 const char *beam_status_str(beam_status s);
 /* Message of the last failed call on this thread ("" if none). */

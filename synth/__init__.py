@@ -9,7 +9,9 @@ first (token) axis; block b is drawn by ``numpy.random.Generator(PCG64(
 SeedSequence([cfg, tensor_id, layer, b])))`` as float32 N(0,1) values (blocks
 are drawn in parallel threads), which are rounded to bfloat16 with
 round-to-nearest-even and kept as ``uint16`` bit patterns.
-RMSNorm weights are 1 + 0.1*N(0,1), gate logits N(0,1), gate bias absent.
+RMSNorm weights are 1 + 0.1*N(0,1), gate logits N(0,1), gate bias absent in
+the workload configurations; where a test exercises the per-head gate bias it
+is float32 0.5*N(0,1) per query head (``gate_bias``).
 Router inputs (the MoE layers' expert selection): hidden states bf16 N(0,1),
 a float32 weight 0.02*N(0,1) and a float32 selection bias 0.05*N(0,1).
 Projection inputs (the GEMMs around attention): the normalised sublayer input
@@ -33,6 +35,7 @@ _THREADS = max(1, min(16, os.cpu_count() or 1))
 T_Q, T_K, T_V, T_GATE, T_QW, T_KW, T_POS, T_PERM, T_LEN, T_MISC = range(10)
 T_RX, T_RW, T_RB = 10, 11, 12  # router: hidden states, weight, selection bias
 T_PX, T_PW, T_PO = 13, 14, 15  # projections: sublayer input, stacked Wq/Wk/Wv/Wg, W_o
+T_GB = 16  # per-head gate bias
 
 
 def rng(cfg: int, tensor_id: int, layer: int = 0) -> np.random.Generator:
@@ -167,3 +170,8 @@ def projection_inputs(cfg: int, layer: int, n_tok: int, hidden: int = 5120, n_q:
     if with_w_o:
         out["w_o"] = normal_bf16((hidden, n_q * d), cfg, T_PO, layer, scale=(n_q * d) ** -0.5)
     return out
+
+
+def gate_bias(cfg: int, layer: int, n_q: int = 48, scale: float = 0.5) -> np.ndarray:
+    """float32 per-query-head gate bias, scale*N(0,1) [n_q]."""
+    return normal_f32((n_q,), cfg, T_GB, layer, scale=scale)

@@ -296,3 +296,23 @@ def test_tensor_alignment_checks():
     # the cache's own buffers
     bad = ga.CCache(ga.GLOBAL, 0x200008, 0x300000, 16, 10, 0x400000, 4, 2)
     assert L.beam_kv_append(ctypes.byref(c), ctypes.byref(bad), fake, fake, fake, fake, fake, 4, None) == 3
+
+
+def test_validate_cache_argument_checks():
+    """beam_debug_validate_cache checks its host-visible arguments before any
+    launch: a local cache has no block table, NULL pointers and empty tables
+    are refused."""
+    L = ga.lib()
+    fake = ctypes.c_void_p(0x100000)
+    loc = _cache(ga.LOCAL)
+    assert L.beam_debug_validate_cache(ctypes.byref(loc), None, fake, None) == 3
+    assert "block table" in L.beam_last_error().decode()
+    assert L.beam_debug_validate_cache(None, None, fake, None) == 1
+    glb = _cache()
+    assert L.beam_debug_validate_cache(ctypes.byref(glb), None, None, None) == 1
+    glb.block_table = None
+    assert L.beam_debug_validate_cache(ctypes.byref(glb), None, fake, None) == 1
+    for field in ("n_seqs", "max_pages_per_seq", "n_pages", "page_size"):
+        c = _cache()
+        setattr(c, field, 0)
+        assert L.beam_debug_validate_cache(ctypes.byref(c), None, fake, None) == 3, field
