@@ -30,7 +30,7 @@ STAGE_PROLOGUE_KV = 16
 
 EXPORTED = [
     "beam_kv_append", "beam_attn_prefill", "beam_attn_decode", "beam_attn_verify",
-    "beam_attn_prefill_stages", "beam_attn_decode_stages", "beam_attn_verify_stages",
+    "beam_attn_prefill_stages", "beam_attn_decode_stages", "beam_attn_verify_stages", "beam_attn_decode_noalloc",
     "beam_prefill_workspace_bytes", "beam_decode_workspace_bytes", "beam_verify_workspace_bytes",
     "beam_kv_bytes", "beam_kv_page_slot", "beam_debug_visibility", "beam_debug_validate_cache",
     "beam_status_str", "beam_last_error",
@@ -113,6 +113,7 @@ def lib() -> ctypes.CDLL:
     U32 = ctypes.c_uint32
     L.beam_attn_prefill_stages.argtypes = [U32] + L.beam_attn_prefill.argtypes
     L.beam_attn_decode_stages.argtypes = [U32] + L.beam_attn_decode.argtypes
+    L.beam_attn_decode_noalloc.argtypes = [P, P, P, P, P, P, P, P, I32, I32, I32, P, P]
     L.beam_attn_verify.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, P, P, SZ, P]
     L.beam_attn_verify_stages.argtypes = [U32] + L.beam_attn_verify.argtypes
     L.beam_verify_workspace_bytes.argtypes = [P, I32, I32, I32, I32, I32, I32]
@@ -133,7 +134,8 @@ def lib() -> ctypes.CDLL:
     L.beam_status_str.argtypes = [I32]
     L.beam_status_str.restype = ctypes.c_char_p
     L.beam_last_error.restype = ctypes.c_char_p
-    for name in ("beam_kv_append", "beam_attn_prefill", "beam_attn_decode", "beam_attn_prefill_stages",
+    for name in ("beam_kv_append", "beam_attn_prefill", "beam_attn_decode", "beam_attn_decode_noalloc",
+                 "beam_attn_prefill_stages",
                  "beam_attn_decode_stages", "beam_attn_verify", "beam_attn_verify_stages", "beam_kv_bytes",
                  "beam_kv_page_slot", "beam_debug_visibility", "beam_debug_validate_cache", "beam_router",
                  "beam_router_logits", "beam_router_select", "beam_attn_project", "beam_out_project"):
@@ -350,6 +352,32 @@ def decode(cfg: Config, cache: KVCache, q_raw, q_norm_w, gate, seq_idx, pos, max
         stages, ctypes.byref(c), ctypes.byref(kc), _ptr(q_raw), _ptr(q_norm_w), _ptr(gate), _ptr(gate_bias),
         _ptr(seq_idx), _ptr(pos), n, max_pos, split_keys, _ptr(out), _ptr(workspace), workspace.numel(),
         _stream(stream)))
+    return out
+
+
+DECODE_SCRATCH_BYTES = 32 << 20  # BEAM_DECODE_SCRATCH_BYTES
+
+
+def decode_noalloc(cfg: Config, cache: KVCache, q_raw, q_norm_w, gate, seq_idx, pos, max_pos: int, out,
+                   gate_bias=None, split_keys: int = 0, stream=None):
+    """decode() through beam_attn_decode_noalloc: no workspace; the library's
+    own per-GPU scratch array holds the split partials. `out` [n_seqs][H][d]
+    (bf16) is the caller's; the call allocates nothing."""
+    import torch
+    n = q_raw.shape[0]
+    H, d = cfg.n_q_heads, cfg.head_dim
+    _need(q_raw, torch.bfloat16, (n, H, d), "q_raw")
+    _need(gate, torch.bfloat16, (n, H, d), "gate")
+    _need(q_norm_w, torch.bfloat16, (d,), "q_norm_w")
+    _need(seq_idx, torch.int32, (n,), "seq_idx")
+    _need(pos, torch.int32, (n,), "pos")
+    _need(out, torch.bfloat16, (n, H, d), "out")
+    if gate_bias is not None:
+        _need(gate_bias, torch.float32, (H,), "gate_bias")
+    c, kc = cfg.c(), cache.c()
+    _check(lib().beam_attn_decode_noalloc(
+        ctypes.byref(c), ctypes.byref(kc), _ptr(q_raw), _ptr(q_norm_w), _ptr(gate), _ptr(gate_bias),
+        _ptr(seq_idx), _ptr(pos), n, max_pos, split_keys, _ptr(out), _stream(stream)))
     return out
 
 

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdio>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 
 #include "beam_attn.h"
@@ -599,6 +600,69 @@ beam_status beam_attn_decode_stages(uint32_t stages, const beam_attn_config* cfg
       (st = hip_status(beam::launch_decode_combine(cp, n_seqs, s), "decode combine launch")) != BEAM_OK)
     return st;
   return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// Library-owned decode scratch for beam_attn_decode_noalloc: the split
+// partials and Q' of one call. A file-scope device array, so each GPU the
+// library runs on holds its own copy until the process ends. Host code never
+// uses the array's name as an address (on the host it is only a stand-in):
+// the device address is looked up once per device with hipGetSymbolAddress
+// and kept here.
+__device__ __attribute__((aligned(256))) unsigned char scratch[BEAM_DECODE_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device, with that device current).
+beam_status scratch_address(void** ptr) {
+  int dev = -1;
+  beam_status st = hip_status(hipGetDevice(&dev), "hipGetDevice");
+  if (st != BEAM_OK) return st;
+  if (dev < 0 || dev >= kMaxDevices) return fail(BEAM_E_UNSUPPORTED, "device index beyond the scratch table (64)");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    st = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (st != BEAM_OK) return st;
+    if (!p) return fail(BEAM_E_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return BEAM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+beam_status beam_attn_decode_noalloc(const beam_attn_config* cfg, const beam_kv_cache* cache, const beam_bf16* q_raw,
+                                     const beam_bf16* q_norm_w, const beam_bf16* gate_logits, const float* gate_bias,
+                                     const int32_t* seq_idx, const int32_t* pos, int32_t n_seqs, int32_t max_pos,
+                                     int32_t split_keys, beam_bf16* out, void* stream) {
+  beam_status st;
+  if ((st = check_cfg(cfg)) != BEAM_OK) return st;
+  if ((st = check_cache(cache)) != BEAM_OK) return st;
+  if (n_seqs < 0) return fail(BEAM_E_RANGE, "n_seqs must be >= 0");
+  if (n_seqs == 0) return ok();
+  if (max_pos < 0) return fail(BEAM_E_RANGE, "max_pos must be >= 0");
+  DecodeWs ws;
+  if (!decode_ws_layout(cfg, cache->kind, n_seqs, max_pos, split_keys, &ws))
+    return fail(BEAM_E_RANGE, "split_keys must be 0 or a multiple of 128 in [128, 65536]");
+  if (ws.total > (size_t)BEAM_DECODE_SCRATCH_BYTES)
+    return fail(BEAM_E_WORKSPACE, "decode needs " + std::to_string(ws.total) +
+                                      " bytes of scratch; the library's array holds " +
+                                      std::to_string((size_t)BEAM_DECODE_SCRATCH_BYTES) +
+                                      " (pass fewer sequences or a larger split_keys)");
+  void* ptr = nullptr;
+  if ((st = scratch_address(&ptr)) != BEAM_OK) return st;
+  return beam_attn_decode_stages(BEAM_STAGE_ALL, cfg, cache, q_raw, q_norm_w, gate_logits, gate_bias, seq_idx, pos,
+                                 n_seqs, max_pos, split_keys, out, ptr, (size_t)BEAM_DECODE_SCRATCH_BYTES, stream);
 }
 
 beam_status beam_attn_decode(const beam_attn_config* cfg, const beam_kv_cache* cache, const beam_bf16* q_raw,

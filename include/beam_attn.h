@@ -163,6 +163,27 @@ beam_status beam_attn_decode(const beam_attn_config *cfg, const beam_kv_cache *c
                              int32_t max_pos, int32_t split_keys, beam_bf16 *out,
                              void *workspace, size_t ws_bytes, void *stream);
 
+/* beam_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments, stages (all three) and
+ * results as beam_attn_decode. The split partials and the normalised queries
+ * live instead in a library-owned device array of BEAM_DECODE_SCRATCH_BYTES,
+ * one per GPU the library runs on, held until the process ends; its address is
+ * looked up on the first call on a device (that device current). The call
+ * allocates and frees nothing. Nothing in the array needs to start at zero:
+ * every value a call reads was written earlier in the same call.
+ * Errors: BEAM_E_WORKSPACE if beam_decode_workspace_bytes(cfg, kind, n_seqs,
+ * max_pos, split_keys) exceeds BEAM_DECODE_SCRATCH_BYTES (a larger split_keys
+ * or fewer sequences per call shrink it), plus those of beam_attn_decode.
+ * Calls that overlap on one GPU (several streams or threads) share the array
+ * and race: the caller serialises them. */
+#define BEAM_DECODE_SCRATCH_BYTES (32u << 20)
+beam_status beam_attn_decode_noalloc(const beam_attn_config *cfg, const beam_kv_cache *cache,
+                                     const beam_bf16 *q_raw, const beam_bf16 *q_norm_w,
+                                     const beam_bf16 *gate_logits, const float *gate_bias,
+                                     const int32_t *seq_idx, const int32_t *pos, int32_t n_seqs,
+                                     int32_t max_pos, int32_t split_keys, beam_bf16 *out, void *stream);
+
 /* Verify step of speculative decoding: causal attention of a few new tokens per
  * sequence (the draft tokens plus the last accepted one) over the cached history,
  * in one call for n_seqs sequences. The drafter proposes blocks of 8 tokens
