@@ -55,3 +55,52 @@ def compare(got_bits, ref, what="", max_abs=MAX_ABS, rel_l2=REL_L2):
     assert mx <= max_abs, f"{what}: max abs error {mx} > {max_abs}"
     assert rl2 <= rel_l2, f"{what}: relative L2 error {rl2} > {rel_l2}"
     return mx, rl2, worst
+
+
+class Agreement:
+    """Max-abs and relative-L2 error of one bf16 GPU output against a float64
+    reference, accumulated block by block (rows of any block size, in any
+    order, from several threads), so that a large output never has to sit in
+    host memory as float64 at once. check() applies the same bar as compare()
+    to the whole output and reports the worst head."""
+
+    def __init__(self, what: str, n_heads: int = 48):
+        import threading
+        self.what = what
+        self.lock = threading.Lock()
+        self.mx = 0.0
+        self.e2 = 0.0
+        self.r2 = 0.0
+        self.he2 = np.zeros(n_heads)
+        self.hr2 = np.zeros(n_heads)
+        self.elems = 0
+
+    def add(self, got_bits, ref, heads=None):
+        """got_bits / ref: [rows, n, d] for the query heads `heads` (an index
+        or slice into the head axis; all heads if None)."""
+        got = bf16_to_f64(got_bits)
+        ref = np.asarray(ref, dtype=np.float64)
+        assert got.shape == ref.shape, (got.shape, ref.shape)
+        assert np.all(np.isfinite(got)), f"{self.what}: non-finite output"
+        err = got - ref
+        he2 = np.sum(err * err, axis=(0, 2))
+        hr2 = np.sum(ref * ref, axis=(0, 2))
+        mx = float(np.max(np.abs(err))) if err.size else 0.0
+        hs = slice(None) if heads is None else heads
+        with self.lock:
+            self.mx = max(self.mx, mx)
+            self.he2[hs] += he2
+            self.hr2[hs] += hr2
+            self.e2 += float(he2.sum())
+            self.r2 += float(hr2.sum())
+            self.elems += got.size
+
+    def check(self, max_abs=MAX_ABS, rel_l2=REL_L2):
+        rl2 = float(np.sqrt(self.e2 / self.r2)) if self.r2 > 0 else float(np.sqrt(self.e2))
+        ok = self.hr2 > 0
+        worst = float(np.max(np.sqrt(self.he2[ok] / self.hr2[ok]))) if ok.any() else 0.0
+        say(f"[parity] {self.what}: elements={self.elems} max_abs={self.mx:.3e} rel_l2={rl2:.3e} "
+            f"worst_head_rel_l2={worst:.3e}")
+        assert self.mx <= max_abs, f"{self.what}: max abs error {self.mx} > {max_abs}"
+        assert rl2 <= rel_l2, f"{self.what}: relative L2 error {rl2} > {rel_l2}"
+        return self.mx, rl2, worst
