@@ -460,10 +460,10 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(CombineParams p) {
       A += sc * p.part_acc[(row0 + s) * D + d];
     }
   }
-  const float o = L > 0.f ? A / L * p.v_scale : 0.f;
+  const float o = L > 0.f ? A * __builtin_amdgcn_rcpf(L) * p.v_scale : 0.f;
   const float bias = p.gate_bias ? p.gate_bias[h] : 0.f;
   const float gz = bf16f(p.gate[idx]) + bias;
-  const float y = o / (1.f + __expf(-gz));
+  const float y = o * __builtin_amdgcn_rcpf(1.f + __expf(-gz));
   bf16x2 r;
   r[0] = (__bf16)y;
   p.out[idx] = __builtin_bit_cast(uint16_t, r[0]);

@@ -398,35 +398,62 @@ prefill_attn_kernel(PrefillParams p) {
       }
     }
   };
-  // Element i of block mb holds key 64j + 32mb + 16(i>>3) + 8*half + (i&7).
+  // Element i of block mb holds key 64j + 8*half + c with c = 32mb + 16(i>>3)
+  // + (i&7), a constant of the element. Per lane and tile the visible range
+  // of c is [t - (W-1) - base, t - base] (base = 64j + 8*half), so each
+  // element costs one compare against an inline constant and one select, and
+  // only the bound that cuts into the tile is tested.
   auto apply_mask = [&](int j, f32x16 (&s)[NB][2]) {
+    const int k0 = j * BN;
+    const bool diag = k0 + BN - 1 > wq_lo;
+    const bool edge = local && k0 < wq_hi - (W - 1);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int t = wq_lo + 32 * nb + n;
+      const int base = k0 + 8 * half;
+      if (diag) {
+        const int hi = t - base;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int sk = j * BN + 32 * mb + 16 * (i >> 3) + 8 * half + (i & 7);
-          if (!visible(KIND, W, t, sk)) s[nb][mb][i] = kNegInf;
-        }
+          for (int i = 0; i < 16; ++i)
+            if (32 * mb + 16 * (i >> 3) + (i & 7) > hi) s[nb][mb][i] = kNegInf;
+      }
+      if (edge) {
+        const int lo = t - (W - 1) - base;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (32 * mb + 16 * (i >> 3) + (i & 7) < lo) s[nb][mb][i] = kNegInf;
+      }
     }
   };
   // Shift of the reference this tile needs, per query: the tile max of the
   // shifted scores when it exceeds the threshold (or is the first finite
   // score of the query), else 0.
-  auto row_shift = [&](const f32x16 (&s)[NB][2], float (&delta)[NB], bool (&need)[NB]) {
-    bool grow = false;
+  auto tile_max = [&](const f32x16 (&s)[NB][2], float (&mt)[NB]) {
+    bool maybe = false;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      float mt = kNegInf;
+      float x = kNegInf;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[nb][mb][i]);
-      mt = max_halves(mt);
-      need[nb] = (m_run[nb] == kNegInf) ? (mt != kNegInf) : (mt > kRescaleThreshold);
-      delta[nb] = need[nb] ? mt : 0.f;
+        for (int i = 0; i < 16; ++i) x = fmaxf(x, s[nb][mb][i]);
+      mt[nb] = max_halves(x);
+      // a reference moves only on a query's first finite score or when the
+      // tile max passes the threshold: one cheap test per lane
+      maybe = maybe || mt[nb] > kRescaleThreshold || m_run[nb] == kNegInf;
+    }
+    return maybe;
+  };
+  auto row_shift = [&](const float (&mt)[NB], float (&delta)[NB], bool (&need)[NB]) {
+    bool grow = false;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      need[nb] = (m_run[nb] == kNegInf) ? (mt[nb] != kNegInf) : (mt[nb] > kRescaleThreshold);
+      delta[nb] = need[nb] ? mt[nb] : 0.f;
       grow = grow || need[nb];
     }
     return grow;
@@ -502,9 +529,12 @@ prefill_attn_kernel(PrefillParams p) {
     f32x16 st[NB][2];
     qk(B, st);
     if (needs_mask(j)) apply_mask(j, st);
-    float delta[NB];
-    bool need[NB];
-    if (__any(row_shift(st, delta, need))) rescale(delta, need, st);
+    float mt[NB];
+    if (__any(tile_max(st, mt))) {
+      float delta[NB];
+      bool need[NB];
+      if (__any(row_shift(mt, delta, need))) rescale(delta, need, st);
+    }
     u32x4 pf[NB][4];
     softmax(st, pf);
     pv(B, pf);
@@ -543,7 +573,7 @@ prefill_attn_kernel(PrefillParams p) {
     const int t = wq_lo + 32 * nb + n;
     const float l_tot = sum_halves(l_run[nb]);
     if (t > qlast) continue;
-    const float inv = l_tot > 0.f ? __frcp_rn(l_tot) : 0.f;
+    const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
     const size_t tok = (size_t)(cu0 + (t - start));
     const uint16_t* grow_ = p.gate + (tok * p.H + h) * D;
     uint16_t* orow = p.out + (tok * p.H + h) * D;
@@ -557,7 +587,9 @@ prefill_attn_kernel(PrefillParams p) {
         float y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float sg = __frcp_rn(1.f + __expf(-(gz[e] + bias)));
+          // v_rcp_f32 (1 ulp): a correctly rounded division here costs ~12
+          // instructions per element, and the result is rounded to bf16 next
+          const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-(gz[e] + bias)));
           y[e] = o[nb][db][4 * a + e] * inv * sg;
         }
         *reinterpret_cast<u32x2*>(orow + d0) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
@@ -975,9 +1007,9 @@ __global__ void __launch_bounds__(128) verify_combine_kernel(VerifyCombineParams
       A += sc * p.part_acc[(row0 + sp) * D + d];
     }
   }
-  const float o = L > 0.f ? A / L : 0.f;
+  const float o = L > 0.f ? A * __builtin_amdgcn_rcpf(L) : 0.f;
   const float bias = p.gate_bias ? p.gate_bias[h] : 0.f;
-  const float sg = __frcp_rn(1.f + __expf(-(bf16f(p.gate[idx]) + bias)));
+  const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-(bf16f(p.gate[idx]) + bias)));
   bf16x2 rr;
   rr[0] = (__bf16)(o * sg);
   p.out[idx] = __builtin_bit_cast(uint16_t, rr[0]);

@@ -295,7 +295,9 @@ beam_status beam_kv_page_slot(const int32_t *block_table_host, int32_t max_pages
                               int32_t *slot);
 
 /* mask[i][j] = 1 iff key position s0+j is visible to query position t0+i for the
- * layer kind, computed on the GPU by the same predicate the kernels use.
+ * layer kind, computed on the GPU by the predicate the decode and verify kernels
+ * use (the prefill kernel applies the same rule per tile as two bounds on the
+ * key's offset in the tile).
  * mask: device uint8 [n_q][n_k]. */
 beam_status beam_debug_visibility(int32_t kind, int32_t window, int32_t t0, int32_t n_q,
                                   int32_t s0, int32_t n_k, uint8_t *mask, void *stream);
