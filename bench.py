@@ -21,6 +21,12 @@ attention, in TFLOP/s against the bf16 MFMA peak.
 And under "router": the MoE router of one layer over the same 32,768 tokens
 (fp32 logits GEMM with the group-limited top-8 selection fused), in TFLOP/s
 against the fp32 MFMA peak.
+And under "schedule52": the full 52-layer attention schedule (9 global, 43
+local layers) as a chunked prefill of 8 sequences of 4K-64K tokens in
+8192-token chunks, aggregate TFLOP/s, with the oracle timed on sampled rows.
+And under "measured_ceilings": the bf16 MFMA rate on random operands and the
+streaming HBM read rate this GPU sustains (include/beam_probe.h); every
+roofline object also gives its fraction of that measured ceiling.
 
 Prints ONE JSON line on stdout. Everything else goes to stderr.
 """
@@ -53,6 +59,7 @@ _KERNEL_SOURCES = {
     "prefill_attn_kernel<1, 8, 0>": "prefill.hip",
     "prefill_attn_kernel<0, 4, 0>": "prefill.hip",
     "decode_split_kernel<1>": "decode.hip",
+    "decode_split_kernel<1> (1M)": "decode.hip",
     "decode_split_kernel<0>": "decode.hip",
     "decode_fp8_kernel<1>": "decode.hip",
     "verify_attn_kernel<1, 0>": "prefill.hip",
@@ -275,30 +282,35 @@ def bench_decode_1m(steps, warmup):
     ws = torch.empty(ga.decode_workspace_bytes(cfg, ga.GLOBAL, 1, max_pos), dtype=torch.uint8, device="cuda")
     args = (cfg, cache, d["q"], d["q_norm_w"], d["gate"], seq, pos, max_pos)
 
-    def one(ev=None):
+    def staged(ev):
         ga.decode(*args, out=out, workspace=ws, stages=ga.STAGE_PROLOGUE)
-        if ev is not None:
-            ev[0].record()
+        ev[0].record()
         ga.decode(*args, out=out, workspace=ws, stages=ga.STAGE_ATTENTION)
-        if ev is not None:
-            ev[1].record()
+        ev[1].record()
         ga.decode(*args, out=out, workspace=ws, stages=ga.STAGE_COMBINE)
 
     warmup, steps = max(warmup, 5), max(steps, 50)
     for _ in range(warmup):
-        one()
+        ga.decode(*args, out=out, workspace=ws)
     torch.cuda.synchronize()
+    # whole calls, back to back (the GPU never waits for the host): GPU time per call
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        ga.decode(*args, out=out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    call_ms = e0.elapsed_time(e1) / steps
+    # the split kernel alone, bracketed by events on the library's stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    t0 = time.perf_counter()
-    for s in range(steps):
-        one(evs[s])
+    for s_ in range(steps):
+        staged(evs[s_])
     torch.cuda.synchronize()
-    el = (time.perf_counter() - t0) / steps
     split_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
     nbytes = T * G * D * 2 * 2
-    log(f"[bench] decode 1M: {nbytes / 2 ** 30:.0f} GiB, call {el * 1e3:.3f} ms, split kernel {split_ms:.3f} ms")
+    log(f"[bench] decode 1M: {nbytes / 2 ** 30:.0f} GiB, call {call_ms:.3f} ms, split kernel {split_ms:.3f} ms")
     del cache
-    return dict(bytes=nbytes, ms_per_call=el * 1e3, split_ms=split_ms, gbs_call=nbytes / el / 1e9,
+    return dict(bytes=nbytes, ms_per_call=call_ms, split_ms=split_ms, gbs_call=nbytes / (call_ms / 1e3) / 1e9,
                 gbs_split=nbytes / (split_ms / 1e3) / 1e9)
 
 
@@ -510,10 +522,227 @@ def cpu_baseline(layers, T, rows):
         vis = (qs + 1) if L["kind"] == O.GLOBAL else np.minimum(qs + 1, W)
         flops += FLOP_PER_PAIR * int(vis.sum())
     el = time.perf_counter() - t0
+    facts = cpu_facts()
     return dict(value=flops / el / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
+                host_cpu_count=facts["cpu_count"], host_affinity=facts["affinity"], blas_threads=facts["blas_threads"],
+                workers=1,
                 sample=f"float64 NumPy oracle on the last {rows} query rows (all 48 heads) of the T=32768 "
                        f"local and global layers, full key history, incl. K normalisation; "
                        f"{flops / 1e9:.1f} GFLOP in {el:.1f} s")
+
+
+def cpu_facts():
+    """Host cores the oracle can use, and the BLAS threads it does use."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except Exception:
+        affinity = None
+    return dict(cpu_count=os.cpu_count(), affinity=affinity, blas_threads=int(blas))
+
+
+# --------------------------------------------------------------------------- ceilings
+
+def _probe_mfma(ops, n_blocks, iters, distinct, reps):
+    """Median TFLOP/s of `reps` runs of the MFMA probe, after one untimed run of the same length."""
+    import statistics
+    import torch
+    import global_attention_amd as ga
+    out = torch.empty((n_blocks * 256,), dtype=torch.float32, device="cuda")
+    ga.probe_mfma_bf16(ops[:n_blocks * 256 * 64], n_blocks, iters, distinct, out)
+    rates = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        flops = ga.probe_mfma_bf16(ops[:n_blocks * 256 * 64], n_blocks, iters, distinct, out)
+        e1.record()
+        torch.cuda.synchronize()
+        rates.append(flops / (e0.elapsed_time(e1) / 1e3) / 1e12)
+    return statistics.median(rates), e0.elapsed_time(e1)
+
+
+def measure_ceilings(reps=3, sweep=False):
+    """What this GPU sustains, measured with the library's probes
+    (include/beam_probe.h): bf16 MFMA on N(0,1) operands that change on every
+    MFMA, in a register-only loop run for about 5 ms (the chip boosts for a
+    fraction of a millisecond, then settles at its power limit); and a
+    streaming HBM read of 8 GiB (best of four grid sizes). With sweep=True
+    also the boosted short run, and operands repeated or constant."""
+    import torch
+    import global_attention_amd as ga
+    nb_max = 1024
+    rnd = torch.randn((nb_max * 256 * 128,), device="cuda").to(torch.bfloat16).view(torch.int32)
+    one = torch.ones((nb_max * 256 * 128,), device="cuda").to(torch.bfloat16).view(torch.int32)
+    # the matrix pipe's own sustained ceiling (operands that never switch), and
+    # the rate on N(0,1) operands that change on every MFMA
+    mfma, ms = _probe_mfma(one, 1024, 3000, 1, reps)
+    mfma_rnd, _ = _probe_mfma(rnd, 1024, 3000, 8, reps)
+    res = dict(mfma_bf16_tflops=round(mfma, 1), mfma_bf16_random_tflops=round(mfma_rnd, 1))
+    if sweep:
+        rows = []
+        for name, ops in (("random N(0,1)", rnd), ("constant 1.0", one)):
+            for distinct in (8, 1):
+                for nb, iters in ((512, 400), (1024, 3000)):
+                    r, t = _probe_mfma(ops, nb, iters, distinct, reps)
+                    rows.append(dict(operands=name, distinct=distinct, blocks=nb, iters=iters, ms=round(t, 3),
+                                     tflops=round(r, 1)))
+                    log(f"[bench] mfma probe {name}, {distinct} distinct, {nb} x {iters}: {t:.3f} ms, {r:.1f} TFLOP/s")
+        res["mfma_sweep"] = rows
+    del rnd, one
+    buf = torch.empty((8 << 30,), dtype=torch.uint8, device="cuda")
+    rout = torch.empty((16384 * 256,), dtype=torch.int32, device="cuda")
+    best_read, best_grid = 0.0, 0
+    for nb in (1024, 2048, 4096, 8192):
+        ga.probe_stream_read(buf, nb, rout[:nb * 256])
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            nbytes = ga.probe_stream_read(buf, nb, rout[:nb * 256])
+            e1.record()
+            torch.cuda.synchronize()
+            gbs = nbytes / (e0.elapsed_time(e1) / 1e3) / 1e9
+            if gbs > best_read:
+                best_read, best_grid = gbs, nb
+    del buf, rout
+    torch.cuda.empty_cache()
+    log(f"[bench] ceilings: bf16 MFMA sustained {mfma:.1f} TFLOP/s (constant operands), {mfma_rnd:.1f} TFLOP/s "
+        f"(N(0,1) operands changing every MFMA) in {ms:.1f} ms runs; streaming read {best_read:.1f} GB/s "
+        f"({best_grid} blocks)")
+    res.update(hbm_read_gbs=round(best_read, 1),
+               method="beam_probe_mfma_bf16: 1024 blocks x 4 waves x 3000 iterations x 16 "
+                      "v_mfma_f32_32x32x16_bf16 from registers, ~5 ms per run (past the boost), median of "
+                      f"{reps} runs after one untimed run; mfma_bf16_tflops: constant 1.0 operands (the pipe at "
+                      "the power limit with no operand switching; the bound every bf16 kernel sits under), "
+                      "mfma_bf16_random_tflops: N(0,1) operands changing on every MFMA; beam_probe_stream_read: "
+                      f"8 GiB, 16-byte non-temporal loads, best of 4 grids x {reps}")
+    return res
+
+
+# --------------------------------------------------------------------------- 52-layer schedule
+
+def bench_schedule52(reps=2, oracle_rows=32):
+    """The full 52-layer attention schedule (global at 6, 12, ..., 48, 52, local
+    elsewhere): chunked varlen prefill of 8 sequences with lengths U[4096,
+    65536] in 8192-token chunks, each layer with its own cache (paged for
+    global layers, 512-slot rings for local ones). Raw projections per
+    (sequence, layer kind) come from torch's seeded device RNG and are reused
+    by every layer of that kind; norm weights are per layer. Every chunk's
+    batch is assembled before the timed region. Returns aggregate TFLOP/s
+    over all layers and steps, and the oracle timed on sampled rows."""
+    import numpy as np
+    import torch
+    import global_attention_amd as ga
+    import oracle as O
+    import synth
+    cfg = ga.Config()
+    CH = 8192
+    lens = synth.chunked_lengths(5, 8, 4096, 65536)
+    n = len(lens)
+    kinds = O.layer_kinds(52)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    raw = {}
+    for kind in (ga.LOCAL, ga.GLOBAL):
+        for i in range(n):
+            L = int(lens[i])
+            raw[kind, i] = {key: torch.randn((L, hh, D), generator=gen, device="cuda").to(torch.bfloat16)
+                            for key, hh in (("q", H), ("k", G), ("v", G), ("gate", H))}
+    qw = [_dev(synth.normal_bf16((D,), 5, synth.T_QW, l, scale=0.1, offset=1.0)) for l in range(52)]
+    kw = [_dev(synth.normal_bf16((D,), 5, synth.T_KW, l, scale=0.1, offset=1.0)) for l in range(52)]
+
+    def fresh_caches():
+        cs = []
+        for l, kind in enumerate(kinds):
+            if kind == ga.GLOBAL:
+                bt, n_pages = synth.paged_block_table(1000 + l, lens)
+                cs.append(ga.KVCache.allocate_global(cfg, n_pages, torch.from_numpy(bt)))
+            else:
+                cs.append(ga.KVCache.allocate_local(cfg, n))
+        return cs
+
+    n_steps = int(-(-int(lens.max()) // CH))
+    steps = []
+    flops = 0
+    for st in range(n_steps):
+        s0 = st * CH
+        seqs = [i for i in range(n) if lens[i] > s0]
+        clen = [min(CH, int(lens[i]) - s0) for i in seqs]
+        cu = np.concatenate([[0], np.cumsum(clen)]).astype(np.int32)
+        batch = {kind: {key: torch.cat([raw[kind, i][key][s0:s0 + c] for i, c in zip(seqs, clen)])
+                        for key in ("q", "k", "v", "gate")} for kind in (ga.LOCAL, ga.GLOBAL)}
+        steps.append(dict(s0=s0, seqs=seqs, clen=clen, cu=cu, batch=batch, cu_d=_i32(cu), seq_d=_i32(seqs),
+                          start_d=_i32([s0] * len(seqs)), n_tok=int(cu[-1])))
+        for c in clen:
+            t = np.arange(s0, s0 + c)
+            flops += FLOP_PER_PAIR * (9 * int((t + 1).sum()) + 43 * int(np.minimum(t + 1, W).sum()))
+    max_tok = n * CH
+    ws = torch.empty(ga.prefill_workspace_bytes(cfg, max_tok, n), dtype=torch.uint8, device="cuda")
+    out = torch.empty((max_tok, H, D), dtype=torch.bfloat16, device="cuda")
+    keep = {}  # (layer, step) -> out rows of the longest sequence's last chunk
+    longest = int(np.argmax(lens))
+
+    def run(caches, record=False):
+        for si, stp in enumerate(steps):
+            for l, kind in enumerate(kinds):
+                b = stp["batch"][kind]
+                ga.prefill(cfg, caches[l], b["q"], b["k"], b["v"], qw[l], kw[l], b["gate"], stp["cu_d"],
+                           stp["seq_d"], stp["start_d"], max(stp["clen"]), out=out[:stp["n_tok"]], workspace=ws)
+                if record and si == len(steps) - 1 and l in (kinds.index(ga.LOCAL), kinds.index(ga.GLOBAL)):
+                    j = stp["seqs"].index(longest)
+                    keep[l] = out[int(stp["cu"][j]):int(stp["cu"][j + 1])].clone()
+
+    ms = []
+    for r in range(reps):
+        caches = fresh_caches()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run(caches, record=(r == reps - 1))
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+        del caches
+    best = min(ms)
+    log(f"[bench] 52-layer chunked prefill: {flops / 1e12:.1f} TFLOP in {best:.1f} ms = "
+        f"{flops / best / 1e9:.1f} TFLOP/s (runs {', '.join(f'{m:.1f}' for m in ms)} ms)")
+    # oracle on sampled rows of the longest sequence's last chunk, first local and first global layer
+    from tests.helpers import Agreement  # comparison helper only; the oracle itself is oracle/
+    stp = steps[-1]
+    c = stp["clen"][stp["seqs"].index(longest)]
+    rows = np.unique(np.linspace(0, c - 1, oracle_rows).astype(np.int64))
+    pos = stp["s0"] + rows
+    bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    ofl, oel, agree = 0, 0.0, {}
+    for l in sorted(keep):
+        kind = kinds[l]
+        rr = raw[kind, longest]
+        last = int(pos.max()) + 1
+        idx = torch.from_numpy(pos).cuda()
+        args = (kind, bits(rr["q"][idx]), bits(rr["k"][:last]), bits(rr["v"][:last]), bits(qw[l]), bits(kw[l]),
+                bits(rr["gate"][idx]), pos, np.arange(last))
+        t0 = time.perf_counter()
+        ref = O.attention_layer(*args)
+        oel += time.perf_counter() - t0
+        vis = (pos + 1) if kind == ga.GLOBAL else np.minimum(pos + 1, W)
+        ofl += FLOP_PER_PAIR * int(vis.sum())
+        a = Agreement(f"52-layer schedule layer {l + 1}, {len(rows)} rows")
+        a.add(bits(keep[l])[rows], ref)
+        import contextlib
+        with contextlib.redirect_stdout(sys.stderr):  # stdout carries only the JSON line
+            mx, rl2, _ = a.check()
+        agree[f"layer_{l + 1}"] = dict(max_abs=float(f"{mx:.3e}"), rel_l2=float(f"{rl2:.3e}"))
+    del raw, steps, out, ws
+    torch.cuda.empty_cache()
+    return dict(flops=flops, ms=best, ms_runs=[round(m, 2) for m in ms], lens=[int(x) for x in lens],
+                oracle=dict(value=ofl / oel / 1e12, unit="TFLOP/s", seconds=round(oel, 2), **cpu_facts(),
+                            sample=f"float64 oracle on {len(rows)} rows of the last chunk of the longest sequence, "
+                                   f"first local and first global layer ({ofl / 1e9:.1f} GFLOP)",
+                            parity=agree))
 
 
 def copy_calibration(nbytes=1 << 30, reps=3):
@@ -542,7 +771,15 @@ def main():
     ap.add_argument("--skip-decode-1m", action="store_true",
                     help="leave out the 1M-token decode (it launches decode_split_kernel<1> at another size, which "
                          "would mix into that kernel's per-kernel profile averages)")
+    ap.add_argument("--decode-1m-only", action="store_true",
+                    help="of the decode lines run only the 1M-token decode (for its own counter runs)")
     ap.add_argument("--skip-projection", action="store_true")
+    ap.add_argument("--skip-schedule", action="store_true", help="leave out the 52-layer chunked schedule")
+    ap.add_argument("--skip-ceilings", action="store_true", help="leave out the measured MFMA / HBM ceilings")
+    ap.add_argument("--ceilings-sweep", action="store_true",
+                    help="only the ceilings, with the MFMA probe also boosted (short) and on repeated or constant "
+                         "operands")
+    ap.add_argument("--schedule-reps", type=int, default=2)
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=384)
@@ -557,6 +794,11 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.ceilings_sweep:
+        import global_attention_amd as ga
+        ga.lib()
+        print(json.dumps({"measured_ceilings": measure_ceilings(sweep=True)}), flush=True)
+        return
 
     import torch
     import global_attention_amd as ga
@@ -570,6 +812,17 @@ def main():
                                   f"(SSMax) layer, 48 Q / 8 KV heads, d=128, bf16 N(0,1) inputs",
                       "seq_len": T, "global_batch": 1, "parallelism": "none (1 GPU)"}}
     layers = None
+    ceil = None
+    if not args.skip_ceilings:
+        ceil = measure_ceilings()
+        rec["measured_ceilings"] = ceil
+
+    def measured(_unused, value, kind):
+        if ceil is None:
+            return {}
+        peak = ceil["mfma_bf16_tflops"] if kind == "mfma" else ceil["hbm_read_gbs"]
+        return {"measured_peak": peak, "frac_of_measured_peak": round(value / peak, 4)}
+
     if not args.skip_prefill:
         r = bench_prefill(T, args.steps, args.warmup)
         layers = r["layers"]
@@ -584,11 +837,19 @@ def main():
                            "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                            "traffic": recorded_traffic("prefill_attn_kernel<1, 8, 0>"),
-                           "avg_launch_ms": round(g_ms, 4), "flop_per_launch": g_flops}
+                           "avg_launch_ms": round(g_ms, 4), "flop_per_launch": g_flops,
+                           **measured(None, achieved, "mfma")}
         l_flops = FLOP_PER_PAIR * pairs_local(T)
+        l_tf = l_flops / (l_ms / 1e3) / 1e12
         rec["prefill_layers"] = {
             "global_attn_ms": round(g_ms, 4), "global_attn_tflops": round(achieved, 2),
-            "local_attn_ms": round(l_ms, 4), "local_attn_tflops": round(l_flops / (l_ms / 1e3) / 1e12, 2)}
+            "local_attn_ms": round(l_ms, 4), "local_attn_tflops": round(l_tf, 2),
+            "local_roofline": {"kernel": "prefill_attn_kernel<0, 4, 0> (local layer)", "bound": "mfma",
+                               "achieved": round(l_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                               "frac": round(l_tf / PEAK_BF16_TFLOPS, 4),
+                               "traffic": recorded_traffic("prefill_attn_kernel<0, 4, 0>"),
+                               "avg_launch_ms": round(l_ms, 4), "flop_per_launch": l_flops,
+                               **measured(None, l_tf, "mfma")}}
         log(f"[bench] prefill step {r['ms_per_step']:.3f} ms -> {rec['value']} TFLOP/s; "
             f"global attn {g_ms:.3f} ms ({achieved:.1f} TFLOP/s), local attn {l_ms:.3f} ms")
     if not args.skip_prefill and not args.skip_projection:
@@ -620,7 +881,20 @@ def main():
         }
         del pd
         torch.cuda.empty_cache()
-    if not args.skip_decode:
+    if not args.skip_schedule:
+        sc = bench_schedule52(args.schedule_reps)
+        tf = sc["flops"] / (sc["ms"] / 1e3) / 1e12
+        rec["schedule52"] = {
+            "workload": "full 52-layer attention schedule (global at 6,12,...,48,52; 43 local, window 512): "
+                        "chunked varlen prefill of 8 sequences, lengths U[4096,65536] "
+                        f"({', '.join(str(x) for x in sc['lens'])}), 8192-token chunks, one cache per layer "
+                        "(paged for global, 512-slot rings for local)",
+            "value": round(tf, 2), "unit": "TFLOP/s", "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            **({"frac_of_measured_peak": round(tf / ceil["mfma_bf16_tflops"], 4)} if ceil else {}),
+            "ms_per_pass": round(sc["ms"], 2), "ms_runs": sc["ms_runs"], "flop_per_pass": sc["flops"],
+            "cpu_sample": sc["oracle"],
+        }
+    if not args.skip_decode and not args.decode_1m_only:
         dres = bench_decode(args.decode_steps, 3)
         g = dres["global"]
         rec["decode"] = {
@@ -632,7 +906,8 @@ def main():
             "roofline": {"kernel": "decode_split_kernel<1>", "bound": "hbm", "achieved": round(g["gbs_split"], 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(g["gbs_split"] / PEAK_HBM_GBS, 4),
                          "traffic": recorded_traffic("decode_split_kernel<1>"),
-                         "avg_launch_ms": round(g["split_ms"], 4), "bytes_per_launch": g["bytes"]},
+                         "avg_launch_ms": round(g["split_ms"], 4), "bytes_per_launch": g["bytes"],
+                         **measured(None, g["gbs_split"], "hbm")},
             "local": {"bytes": dres["local"]["bytes"], "ms_per_call": round(dres["local"]["ms_per_call"], 4),
                       "gbs_call": round(dres["local"]["gbs_call"], 1),
                       "note": "134 MB of rings can stay resident in the 256 MB MALL between calls"},
@@ -648,7 +923,8 @@ def main():
             "roofline": {"kernel": "decode_fp8_kernel<1>", "bound": "hbm", "achieved": round(f["gbs_split"], 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(f["gbs_split"] / PEAK_HBM_GBS, 4),
                          "traffic": recorded_traffic("decode_fp8_kernel<1>"),
-                         "avg_launch_ms": round(f["split_ms"], 4), "bytes_per_launch": f["bytes"]},
+                         "avg_launch_ms": round(f["split_ms"], 4), "bytes_per_launch": f["bytes"],
+                         **measured(None, f["gbs_split"], "hbm")},
         }
         v = bench_verify(args.decode_steps, 3, dres, split_keys=args.verify_split_keys)
         vg = v["global"]
@@ -663,7 +939,8 @@ def main():
             "roofline": {"kernel": "verify_attn_kernel<1, 0>", "bound": "hbm", "achieved": round(vg["gbs_split"], 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(vg["gbs_split"] / PEAK_HBM_GBS, 4),
                          "traffic": recorded_traffic("verify_attn_kernel<1, 0>"),
-                         "avg_launch_ms": round(vg["split_ms"], 4), "bytes_per_launch": vg["bytes"]},
+                         "avg_launch_ms": round(vg["split_ms"], 4), "bytes_per_launch": vg["bytes"],
+                         **measured(None, vg["gbs_split"], "hbm")},
             "local": {"ms_per_call": round(v["local"]["ms_per_call"], 4),
                       "speedup_vs_8_decode_calls": round(v["local"]["vs_decode_calls"], 2)},
             "global_fp8": {"ms_per_call": round(v["global_fp8"]["ms_per_call"], 4),
@@ -672,7 +949,7 @@ def main():
         }
         del dres, v
         torch.cuda.empty_cache()
-    if not args.skip_decode and not args.skip_decode_1m:
+    if not args.skip_decode_1m and not (args.skip_decode and not args.decode_1m_only):
         m = bench_decode_1m(args.decode_steps, 5)
         rec["decode_1m"] = {
             "workload": "one sequence at position 1,048,575 on a global layer: 65,536 permuted 16-token pages, "
@@ -682,7 +959,9 @@ def main():
             "ms_per_call": round(m["ms_per_call"], 4), "bytes": m["bytes"],
             "roofline": {"kernel": "decode_split_kernel<1>", "bound": "hbm", "achieved": round(m["gbs_split"], 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(m["gbs_split"] / PEAK_HBM_GBS, 4),
-                         "traffic": None, "avg_launch_ms": round(m["split_ms"], 4), "bytes_per_launch": m["bytes"]},
+                         "traffic": recorded_traffic("decode_split_kernel<1> (1M)"),
+                         "avg_launch_ms": round(m["split_ms"], 4), "bytes_per_launch": m["bytes"],
+                         **measured(None, m["gbs_split"], "hbm")},
         }
     if not args.skip_router:
         rr = bench_router(T, args.steps, args.warmup)
@@ -700,6 +979,9 @@ def main():
     if not args.no_cpu_baseline and layers is not None:
         log(f"[bench] timing the CPU oracle on {args.cpu_rows} rows per layer")
         rec["cpu_baseline"] = cpu_baseline(layers, T, args.cpu_rows)
+        if rec["value"]:
+            # vs_baseline stays null: the pages publish no throughput for this path
+            rec["cpu_baseline"]["gpu_over_oracle"] = round(rec["value"] / rec["cpu_baseline"]["value"], 1)
     print(json.dumps(rec), flush=True)
 
 

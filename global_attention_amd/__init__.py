@@ -36,6 +36,7 @@ EXPORTED = [
     "beam_status_str", "beam_last_error",
     "beam_router", "beam_router_logits", "beam_router_select",
     "beam_attn_project", "beam_out_project",
+    "beam_probe_mfma_bf16", "beam_probe_stream_read",
 ]
 
 
@@ -105,6 +106,10 @@ def lib() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m global_attention_amd.build`")
+    # torch first: its HIP runtime then serves the library too. Loaded the other
+    # way round, torch's libraries (which ask for the runtime by its unversioned
+    # file name) would bring a second copy of the runtime into the process.
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     L.beam_kv_append.argtypes = [P, P, P, P, P, P, P, I32, P]
@@ -131,6 +136,8 @@ def lib() -> ctypes.CDLL:
     L.beam_router_select.argtypes = [P, P, P, I32, P, P, P]
     L.beam_attn_project.argtypes = [P, I32, P, I32, P, P, P, P, I32, I32, P, P, P, P, SZ, P]
     L.beam_out_project.argtypes = [P, P, I32, I32, I32, P, P]
+    L.beam_probe_mfma_bf16.argtypes = [P, I32, I32, I32, P, P]
+    L.beam_probe_stream_read.argtypes = [P, SZ, I32, P, P]
     L.beam_status_str.argtypes = [I32]
     L.beam_status_str.restype = ctypes.c_char_p
     L.beam_last_error.restype = ctypes.c_char_p
@@ -138,7 +145,8 @@ def lib() -> ctypes.CDLL:
                  "beam_attn_prefill_stages",
                  "beam_attn_decode_stages", "beam_attn_verify", "beam_attn_verify_stages", "beam_kv_bytes",
                  "beam_kv_page_slot", "beam_debug_visibility", "beam_debug_validate_cache", "beam_router",
-                 "beam_router_logits", "beam_router_select", "beam_attn_project", "beam_out_project"):
+                 "beam_router_logits", "beam_router_select", "beam_attn_project", "beam_out_project",
+                 "beam_probe_mfma_bf16", "beam_probe_stream_read"):
         getattr(L, name).restype = I32
     _lib = L
     return L
@@ -526,3 +534,26 @@ def out_project(y, w_o, out=None, stream=None):
     _need(out, torch.bfloat16, (n_tok, out_f), "out")
     _check(lib().beam_out_project(_ptr(y2), _ptr(w_o), n_tok, in_f, out_f, _ptr(out), _stream(stream)))
     return out
+
+
+# ---------------------------------------------------------------- measurement instruments
+
+def probe_mfma_bf16(operands, n_blocks: int, iters: int, distinct: int = 8, out=None, stream=None):
+    """Register-only bf16 MFMA loop (beam_probe_mfma_bf16); operands: int32
+    device tensor [n_blocks * 256 * 64] of bf16 pairs. Returns the flops it ran."""
+    import torch
+    _need(operands, torch.int32, (n_blocks * 256 * 64,), "operands")
+    if out is None:
+        out = torch.empty((n_blocks * 256,), dtype=torch.float32, device=operands.device)
+    _check(lib().beam_probe_mfma_bf16(_ptr(operands), n_blocks, iters, distinct, _ptr(out), _stream(stream)))
+    return n_blocks * 4 * iters * 16 * 32768
+
+
+def probe_stream_read(buf, n_blocks: int, out=None, stream=None):
+    """Streaming read of a device tensor (beam_probe_stream_read); returns the bytes read."""
+    import torch
+    nbytes = buf.numel() * buf.element_size()
+    if out is None:
+        out = torch.empty((n_blocks * 256,), dtype=torch.int32, device=buf.device)
+    _check(lib().beam_probe_stream_read(_ptr(buf), nbytes, n_blocks, _ptr(out), _stream(stream)))
+    return nbytes

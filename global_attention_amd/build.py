@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbeam_attn.so")
-SOURCES = ["beam_attn.hip", "prologue.hip", "prefill.hip", "decode.hip", "router.hip", "gemm.hip"]
+SOURCES = ["beam_attn.hip", "prologue.hip", "prefill.hip", "decode.hip", "router.hip", "gemm.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -46,7 +46,7 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         obj = os.path.join(OBJDIR, src.replace(".hip", ".o"))
         objs.append(obj)
         cmds.append([HIPCC, *FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])
-    with ThreadPoolExecutor(max_workers=min(5, len(cmds))) as ex:
+    with ThreadPoolExecutor(max_workers=min(7, len(cmds))) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)

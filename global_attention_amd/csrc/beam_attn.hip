@@ -165,6 +165,12 @@ beam_status hip_status(hipError_t e, const char* what) {
 
 }  // namespace
 
+namespace beam {
+beam_status set_error(beam_status s, const char* what, hipError_t e) {
+  return fail(s, std::string(what) + (e != hipSuccess ? std::string(": ") + hipGetErrorString(e) : std::string()));
+}
+}  // namespace beam
+
 extern "C" {
 
 const char* beam_status_str(beam_status s) {

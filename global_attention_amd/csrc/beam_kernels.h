@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "beam_attn.h"
+
 namespace beam {
 
 struct PrologueParams {
@@ -151,6 +153,15 @@ struct CombineParams {
   int kind, window, H, n_splits, split_keys;
   float v_scale;  // FP8 cache: V scale applied to O (1 for bf16)
 };
+
+// Every launcher clears an error an earlier runtime call left unread on this
+// thread before it launches, so that the status it returns (hipGetLastError
+// after the launch) is about its own launch only.
+inline void clear_stale_error() { (void)hipGetLastError(); }
+
+// Records a failed call's message for beam_last_error() (host, thread-local)
+// and returns the status; for the sources other than beam_attn.hip.
+beam_status set_error(beam_status s, const char* what, hipError_t e);
 
 // Host-side launchers (each defined next to its kernel). They return the
 // launch status of the HIP runtime.

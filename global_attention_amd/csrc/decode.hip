@@ -470,6 +470,7 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(CombineParams p) {
 }
 
 hipError_t launch_decode_split(const DecodeParams& p, int n_seqs, hipStream_t s) {
+  clear_stale_error();
   const long long blocks = (long long)n_seqs * p.G * p.n_splits;
   const dim3 grid((unsigned)blocks), block(256);
   if (p.kind == 0 && !p.kv_fp8)
@@ -484,6 +485,7 @@ hipError_t launch_decode_split(const DecodeParams& p, int n_seqs, hipStream_t s)
 }
 
 hipError_t launch_decode_combine(const CombineParams& p, int n_seqs, hipStream_t s) {
+  clear_stale_error();
   hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(n_seqs * p.H)), dim3(128), 0, s, p);
   return hipGetLastError();
 }

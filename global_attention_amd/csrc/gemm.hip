@@ -384,6 +384,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 }
 
 hipError_t launch_gemm(const GemmParams& p, int epi, hipStream_t s) {
+  clear_stale_error();
   if (epi == kEpiQkvg)
     hipLaunchKernelGGL(gemm_bf16_kernel<kEpiQkvg>, dim3(kGrid), dim3(256), 0, s, p);
   else

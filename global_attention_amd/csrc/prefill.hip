@@ -1016,6 +1016,7 @@ __global__ void __launch_bounds__(128) verify_combine_kernel(VerifyCombineParams
 }
 
 hipError_t launch_verify_attn(const PrefillParams& p, hipStream_t s) {
+  clear_stale_error();
   if (p.split_tiles * 4 > kVerifyMaxPages) return hipErrorInvalidValue;
   const long long blocks = (long long)p.G * p.n_splits * p.n_seqs;
   const dim3 grid((unsigned)blocks), block(64 * kVerifyWaves);
@@ -1031,11 +1032,13 @@ hipError_t launch_verify_attn(const PrefillParams& p, hipStream_t s) {
 }
 
 hipError_t launch_verify_combine(const VerifyCombineParams& p, hipStream_t s) {
+  clear_stale_error();
   hipLaunchKernelGGL(verify_combine_kernel, dim3((unsigned)((long long)p.n_tok * p.H)), dim3(128), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {
+  clear_stale_error();
   const long long blocks = (long long)p.G * (p.H / p.G) * p.n_seqs * p.n_qtiles;
   const dim3 grid((unsigned)blocks), local_block(64 * kPrefillWavesLocal), global_block(64 * kPrefillWavesGlobal);
   if (p.kind == 0 && !p.kv_fp8)

@@ -466,12 +466,14 @@ namespace beam {
 
 hipError_t launch_validate_cache(const int32_t* bt, int max_pages, int n_pages, int page_size, int n_seqs,
                                  const int32_t* n_tokens, int32_t* n_bad, hipStream_t s) {
+  clear_stale_error();
   hipLaunchKernelGGL(validate_cache_kernel, dim3((unsigned)n_seqs), dim3(256), 0, s, bt, max_pages, n_pages,
                      page_size, n_tokens, n_bad);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_prologue(const PrologueParams& p, int n_seqs, int n_tiles, hipStream_t s) {
+  clear_stale_error();
   const int parts = kPrologueFixedParts + (p.with_q ? (p.H + kQHeadsPerBlock - 1) / kQHeadsPerBlock : 0);
   if (p.G > kMaxHeadsPerGroup || p.G > 2 * kVHeadsPerBlock) return hipErrorInvalidValue;
   const dim3 grid(n_seqs, n_tiles, parts), block(256);
@@ -487,17 +489,20 @@ hipError_t launch_prefill_prologue(const PrologueParams& p, int n_seqs, int n_ti
 }
 
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t s) {
+  clear_stale_error();
   hipLaunchKernelGGL(kv_append_kernel, dim3((p.n_tok + 15) / 16), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_q_prologue(const DecodeQParams& p, hipStream_t s) {
+  clear_stale_error();
   hipLaunchKernelGGL(decode_q_prologue_kernel, dim3((p.n_seqs * p.H + 15) / 16), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_visibility(int kind, int window, int t0, int n_q, int s0, int n_k, uint8_t* mask,
                              hipStream_t s) {
+  clear_stale_error();
   long long n = (long long)n_q * n_k;
   hipLaunchKernelGGL(visibility_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, kind,
                      window, t0, n_q, s0, n_k, mask);

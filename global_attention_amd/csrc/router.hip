@@ -339,18 +339,21 @@ __global__ void __launch_bounds__(256) router_select_kernel(RouterParams p) {
 }
 
 hipError_t launch_router_logits(const RouterParams& p, hipStream_t s) {
+  clear_stale_error();
   const unsigned blocks = (unsigned)((p.n_tok + kRouterBlockTokens - 1) / kRouterBlockTokens);
   hipLaunchKernelGGL(router_gemm_kernel<false>, dim3(blocks), dim3(512), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_router_fused(const RouterParams& p, hipStream_t s) {
+  clear_stale_error();
   const unsigned blocks = (unsigned)((p.n_tok + kRouterBlockTokens - 1) / kRouterBlockTokens);
   hipLaunchKernelGGL(router_gemm_kernel<true>, dim3(blocks), dim3(512), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_router_select(const RouterParams& p, hipStream_t s) {
+  clear_stale_error();
   hipLaunchKernelGGL(router_select_kernel, dim3((unsigned)((p.n_tok + 63) / 64)), dim3(256), 0, s, p);
   return hipGetLastError();
 }

@@ -23,7 +23,9 @@
  *     enqueued on it in order; faults surface at the caller's next sync.
  *   - Arguments are checked on the host before anything is enqueued. On error a
  *     call returns a non-zero beam_status, launches nothing, and sets a
- *     thread-local message readable with beam_last_error().
+ *     thread-local message readable with beam_last_error(). BEAM_E_HIP reports
+ *     a launch of the call itself: an error that an earlier runtime call left
+ *     unread on the thread is cleared before the call launches.
  *   - Device-resident indices (block-table entries, seq_idx, positions,
  *     cu_seqlens) are not read by the host; out-of-range values in them are
  *     undefined behaviour.
