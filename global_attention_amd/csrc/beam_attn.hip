@@ -120,13 +120,16 @@ PrefillWs prefill_ws_layout(const beam_attn_config* c, int n_tok, int n_seqs) {
 }
 
 // Default keys per verify split: 256 on local layers (the window spans at most
-// a few tiles). On global layers 4096 keys when that still gives at least 1024
-// blocks (two per CU slot at two blocks per CU), else 2048. Longer splits mean
-// fewer partials to merge and less per-block work.
+// a few tiles). On global layers the longest of 8192, 4096 keys that still
+// gives at least 1024 blocks (two per CU slot at two blocks per CU), else
+// 2048. Longer splits mean fewer partials to merge and less per-block work.
 int default_verify_split_keys(const beam_attn_config* c, int kind, int n_seqs, int max_pos) {
   if (kind == BEAM_LOCAL) return 256;
-  const long long blocks = (long long)n_seqs * c->n_kv_heads * (max_pos / 4096 + 1);
-  return blocks >= 1024 ? 4096 : 2048;
+  for (int keys = 8192; keys >= 4096; keys /= 2) {
+    const long long blocks = (long long)n_seqs * c->n_kv_heads * (max_pos / keys + 1);
+    if (blocks >= 1024) return keys;
+  }
+  return 2048;
 }
 
 // Verify (short-chunk) calls: the prefill workspace, then the split partials
@@ -408,7 +411,8 @@ beam_status chunk_call(bool verify, uint32_t stages, const beam_attn_config* cfg
     ap.split_tiles = vws.split_tiles;
     ap.n_splits = vws.n_splits;
     if ((stages & BEAM_STAGE_ATTENTION) &&
-        (st = hip_status(beam::launch_verify_attn(ap, s), "verify attention launch")) != BEAM_OK)
+        (st = hip_status(beam::launch_verify_attn(ap, max_chunk_len * (cfg->n_q_heads / cfg->n_kv_heads), s),
+                         "verify attention launch")) != BEAM_OK)
       return st;
     beam::VerifyCombineParams cp{};
     cp.part_ml = ap.part_ml;
@@ -430,6 +434,7 @@ beam_status chunk_call(bool verify, uint32_t stages, const beam_attn_config* cfg
     cp.n_splits = vws.n_splits;
     cp.split_tiles = vws.split_tiles;
     cp.max_pos = max_pos;
+    cp.v_scale = cache->dtype == BEAM_KV_FP8_E4M3 ? cache->v_scale : 1.f;
     if ((stages & BEAM_STAGE_VERIFY_COMBINE) &&
         (st = hip_status(beam::launch_verify_combine(cp, s), "verify combine launch")) != BEAM_OK)
       return st;

@@ -122,6 +122,7 @@ struct VerifyCombineParams {
   int max_pages, n_cache_seqs;
   int kind, window, H, n_seqs, n_tok, n_splits, split_tiles;
   int max_pos;  // a sequence whose chunk ends past max_pos gets NaN rows (its keys lie beyond the split grid)
+  float v_scale;  // FP8 cache: V scale applied to O (1 for bf16)
 };
 
 struct DecodeParams {
@@ -175,7 +176,7 @@ hipError_t launch_validate_cache(const int32_t* bt, int max_pages, int n_pages, 
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s);
 hipError_t launch_decode_split(const DecodeParams& p, int n_seqs, hipStream_t s);
 hipError_t launch_decode_combine(const CombineParams& p, int n_seqs, hipStream_t s);
-hipError_t launch_verify_attn(const PrefillParams& p, hipStream_t s);
+hipError_t launch_verify_attn(const PrefillParams& p, int max_rows, hipStream_t s);
 hipError_t launch_verify_combine(const VerifyCombineParams& p, hipStream_t s);
 
 // ---- projection GEMMs: out[t][f] = sum_k x[t][k] w[f][k] (bf16, fp32 accumulate) ----

@@ -190,60 +190,106 @@ __device__ __forceinline__ void dma_tile_prefix(const KeySource& ks, int w, int 
   }
 }
 
-// Prefix tile from an FP8 E4M3 cache: the DMA engine cannot convert, so each
-// thread loads 16 codes of a K row (or of a V^T row), dequantises them to bf16
-// (decode(code) * scale, one rounding) and stores the two 16-byte chunks at
-// their swizzled LDS positions. k8/v8 are the byte bases of the (sequence,
-// KV head) in the cache, at the element offsets the bf16 layout uses.
-struct Fp8Prefix {
-  const uint8_t* k8;
+// ---------------------------------------------------------------- FP8 code tiles
+// A tile of the cached prefix of an FP8 cache is moved into LDS as its raw
+// codes by the same LDS DMA as a bf16 tile (16 KiB instead of 32): the DMA
+// copies bytes and cannot convert. The MFMA operands are read as 8 codes
+// (ds_read_b64) and converted exactly to bf16 in registers (every E4M3 value
+// is a bf16 value); the attention then runs in the cache's code space (Q'
+// times k_scale, O times v_scale). Layout in the slot (bytes):
+//   K codes  [0, 8192):    row m (key kappa(m), as the bf16 tile) of 128 B,
+//                          16-byte chunk c at position c ^ ((m >> 1) & 7);
+//   V^T codes [8192, 16384): row d of 64 B (keys in order), 16-byte chunk c
+//                          (16 keys, one page) at position c ^ ((d >> 2) & 3).
+// Each swizzle spreads the 32 lanes of one b64 read over 16 positions: two
+// lanes per bank pair, the least any 128-B (64-B) row layout allows here.
+constexpr int kCodeVOff = 8192;
+
+struct CodeSource {
+  const uint8_t* k8;  // K codes of (cache row or page base, KV head g): + page * page_stride
   const uint8_t* v8;
-  const int32_t* bt_row;
-  size_t page_stride;  // bytes per page of the paged cache (all KV heads)
+  size_t page_stride;  // bytes per page of the paged cache (all KV heads); 0 on a ring
   int kind, window;
-  float k_scale, v_scale;
 };
 
-__device__ __forceinline__ u32x4 fp8x8_dequant_bf16(uint32_t w0, uint32_t w1, float scale) {
-  float a[4], b[4];
-  fp8x4_to_f32(w0, a);
-  fp8x4_to_f32(w1, b);
-  return u32x4{pack_bf16x2(a[0] * scale, a[1] * scale), pack_bf16x2(a[2] * scale, a[3] * scale),
-               pack_bf16x2(b[0] * scale, b[1] * scale), pack_bf16x2(b[2] * scale, b[3] * scale)};
+__device__ __forceinline__ CodeSource make_code_source(const PrefillParams& p, int kind, int cseq, int g) {
+  CodeSource c;
+  const size_t head = kind == 1 ? (size_t)g * 16 * D : ((size_t)cseq * p.G + g) * p.window * D;
+  c.k8 = reinterpret_cast<const uint8_t*>(p.ck) + head;
+  c.v8 = reinterpret_cast<const uint8_t*>(p.cv) + head;
+  c.page_stride = kind == 1 ? (size_t)p.G * 16 * D : 0;
+  c.kind = kind;
+  c.window = p.window;
+  return c;
 }
 
-template <int NW>
-__device__ __forceinline__ void fetch_prefix_fp8(const Fp8Prefix& fp, int tid, int key0, uint16_t* sK, uint16_t* sV) {
-  constexpr int R = 8 / NW;  // 16-byte loads per thread, for K and for V
-  u32x4 kc[R], vc[R];
+// DMA of the code tile whose first key is key0 (a multiple of 64): 8 K and 8
+// V instructions of 1 KiB, 8 / NW of each per wave. page(i) is the physical
+// page of logical page i (paged caches).
+template <int NW, typename PageOf>
+__device__ __forceinline__ void dma_code_tile(const CodeSource& c, PageOf page, int w, int lane, int key0,
+                                              uint8_t* slot) {
+  // every source address first (the page lookups together), then the DMAs
+  const uint8_t* ksrc[8 / NW];
+  const uint8_t* vsrc[8 / NW];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int id = tid + 64 * NW * r;  // 0..511
-    {
-      const int m = id >> 3, c2 = id & 7;  // LDS row m, codes 16c2 .. 16c2+15
+  for (int i = 0; i < 8 / NW; ++i) {
+    const int ins = w * (8 / NW) + i;
+    {  // K rows 8 ins .. 8 ins + 7
+      const int m = 8 * ins + (lane >> 3);
+      const int cc = (lane & 7) ^ ((m >> 1) & 7);
       const int s = key0 + krow_key(m);
-      const uint8_t* src = fp.kind == 1 ? fp.k8 + fp.bt_row[s >> 4] * fp.page_stride + (size_t)((s & 15) * D)
-                                        : fp.k8 + (size_t)((s % fp.window) * D);
-      kc[r] = *reinterpret_cast<const u32x4*>(src + 16 * c2);
+      ksrc[i] = (c.kind == 1 ? c.k8 + (size_t)page(s >> 4) * c.page_stride + (uint32_t)((s & 15) * D)
+                             : c.k8 + (uint32_t)((s % c.window) * D)) + 16 * cc;
     }
-    {
-      const int d = id >> 2, c2 = id & 3;  // V^T row d, keys 16c2 .. 16c2+15 (one page / no ring wrap)
-      const int s = key0 + 16 * c2;
-      const uint8_t* src = fp.kind == 1 ? fp.v8 + fp.bt_row[s >> 4] * fp.page_stride + (size_t)(d * 16)
-                                        : fp.v8 + (size_t)(d * fp.window + s % fp.window);
-      vc[r] = *reinterpret_cast<const u32x4*>(src);
+    {  // V^T rows 16 ins .. 16 ins + 15
+      const int d = 16 * ins + (lane >> 2);
+      const int cc = (lane & 3) ^ ((d >> 2) & 3);
+      const int s = key0 + 16 * cc;
+      vsrc[i] = c.kind == 1 ? c.v8 + (size_t)page(s >> 4) * c.page_stride + (uint32_t)(d * 16)
+                            : c.v8 + (uint32_t)(d * c.window + s % c.window);
     }
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int id = tid + 64 * NW * r;
-    const int m = id >> 3, ck = id & 7;
-    *reinterpret_cast<u32x4*>(sK + k_off(m, 2 * ck)) = fp8x8_dequant_bf16(kc[r][0], kc[r][1], fp.k_scale);
-    *reinterpret_cast<u32x4*>(sK + k_off(m, 2 * ck + 1)) = fp8x8_dequant_bf16(kc[r][2], kc[r][3], fp.k_scale);
-    const int d = id >> 2, cv = id & 3;
-    *reinterpret_cast<u32x4*>(sV + v_off(d, 2 * cv)) = fp8x8_dequant_bf16(vc[r][0], vc[r][1], fp.v_scale);
-    *reinterpret_cast<u32x4*>(sV + v_off(d, 2 * cv + 1)) = fp8x8_dequant_bf16(vc[r][2], vc[r][3], fp.v_scale);
+  for (int i = 0; i < 8 / NW; ++i) {
+    const int ins = w * (8 / NW) + i;
+    lds_dma16(reinterpret_cast<const uint16_t*>(ksrc[i]), reinterpret_cast<uint16_t*>(slot + 1024 * ins));
+    lds_dma16(reinterpret_cast<const uint16_t*>(vsrc[i]), reinterpret_cast<uint16_t*>(slot + kCodeVOff + 1024 * ins));
   }
+}
+
+// Per-lane byte offsets of the code operands: K for k-step kk (8 offsets,
+// + 4096 for M-block 1), V^T for key block kb (4 offsets, + 2048 per row block).
+struct CodeOffsets {
+  int k[8];
+  int v[4];
+};
+__device__ __forceinline__ CodeOffsets code_offsets(int n, int half) {
+  CodeOffsets co;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) co.k[kk] = n * 128 + 16 * (kk ^ ((n >> 1) & 7)) + 8 * half;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) co.v[kb] = kCodeVOff + n * 64 + 16 * (kb ^ ((n >> 2) & 3)) + 8 * half;
+  return co;
+}
+__device__ __forceinline__ u32x4 codes_to_bf16(u32x2 c) {
+  const u32x2 lo = fp8x4_to_bf16x4(c[0]), hi = fp8x4_to_bf16x4(c[1]);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+// K fragment of k-step kk, M-block mb: row n + 32 mb, codes 16 kk + 8 half + 0..7.
+__device__ __forceinline__ u32x4 code_kfrag(const uint8_t* slot, const CodeOffsets& co, int kk, int mb) {
+  return codes_to_bf16(*reinterpret_cast<const u32x2*>(slot + co.k[kk] + 4096 * mb));
+}
+// V^T fragment of key block kb, row block db: row 32 db + n, keys 16 kb + 8 half + 0..7.
+__device__ __forceinline__ u32x4 code_vfrag(const uint8_t* slot, const CodeOffsets& co, int kb, int db) {
+  return codes_to_bf16(*reinterpret_cast<const u32x2*>(slot + co.v[kb] + 2048 * db));
+}
+// Q' fragments times k_scale (one bf16 rounding), for the code space of an FP8 cache.
+__device__ __forceinline__ void scale_frags(u32x4 (&qf)[8], float k_scale) {
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qf[kk][c] = pack_bf16x2(bf16lo(qf[kk][c]) * k_scale, bf16hi(qf[kk][c]) * k_scale);
 }
 
 // ---------------------------------------------------------------- kernel
@@ -309,18 +355,8 @@ prefill_attn_kernel(PrefillParams p) {
   ks.kind = KIND;
   ks.window = W;
   const DmaPlan<NWAVES> plan = make_dma_plan<NWAVES>(w, lane);
-  Fp8Prefix fp8;
-  if constexpr (KV_FP8) {
-    const size_t head = KIND == 1 ? (size_t)g * 16 * D : ((size_t)cseq * p.G + g) * W * D;
-    fp8.k8 = reinterpret_cast<const uint8_t*>(p.ck) + head;
-    fp8.v8 = reinterpret_cast<const uint8_t*>(p.cv) + head;
-    fp8.bt_row = ks.bt_row;
-    fp8.page_stride = (size_t)p.G * 16 * D;
-    fp8.kind = KIND;
-    fp8.window = W;
-    fp8.k_scale = p.k_scale;
-    fp8.v_scale = p.v_scale;
-  }
+  CodeSource cs8;
+  if constexpr (KV_FP8) cs8 = make_code_source(p, KIND, cseq, g);
 
   // Q' fragments (B operand of S^T = K Q'^T): lane holds query n of N-block nb,
   // coordinates 16kk + 8*half + 0..7.
@@ -334,6 +370,7 @@ prefill_attn_kernel(PrefillParams p) {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
       qf[nb][kk] = valid ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk) : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (KV_FP8) scale_frags(qf[nb], p.k_scale);  // code space: q' k_scale against the codes
   }
 
   const int j_ws = start >> 6;  // first tile in the workspace; earlier tiles are wholly cached
@@ -369,6 +406,8 @@ prefill_attn_kernel(PrefillParams p) {
     koff[q] = k_off(n, 2 * q + half);
     voff[q] = v_off(n, 2 * q + half);
   }
+  [[maybe_unused]] CodeOffsets co;
+  if constexpr (KV_FP8) co = code_offsets(n, half);
 
   // ---- pieces of one 64-key tile of attention for this wave's queries ----
   // Tile jt uses LDS slot (jt - j_lo) % SLOTS; the loop is unrolled by SLOTS
@@ -384,13 +423,18 @@ prefill_attn_kernel(PrefillParams p) {
   };
   // S^T - m = K Q'^T - m: LDS rows 32mb + (lane&31) on M, queries 32nb + n on
   // N; the chain starts from sref = -m.
-  auto qk = [&](auto B, f32x16 (&s)[NB][2]) {
+  // CODES: the tile holds FP8 codes (converted after the LDS read).
+  auto qk = [&](auto B, auto CODES, f32x16 (&s)[NB][2]) {
     const uint16_t* sK = buf(B);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(sK + koff[kk & 3] + K_HALF * (kk >> 2) + 32 * 64 * mb);
+        u32x4 a;
+        if constexpr (decltype(CODES)::value)
+          a = code_kfrag(reinterpret_cast<const uint8_t*>(sK), co, kk, mb);
+        else
+          a = *reinterpret_cast<const u32x4*>(sK + koff[kk & 3] + K_HALF * (kk >> 2) + 32 * 64 * mb);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
           s[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qf[nb][kk]),
@@ -499,13 +543,17 @@ prefill_attn_kernel(PrefillParams p) {
     }
   };
   // O^T += V^T P^T: A operand = coordinates 32db + n, keys 16kb + 8*half + 0..7.
-  auto pv = [&](auto B, const u32x4 (&pf)[NB][4]) {
+  auto pv = [&](auto B, auto CODES, const u32x4 (&pf)[NB][4]) {
     const uint16_t* sV = buf(B) + K_TILE;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(sV + voff[kb] + 32 * BN * db);
+        u32x4 a;
+        if constexpr (decltype(CODES)::value)
+          a = code_vfrag(reinterpret_cast<const uint8_t*>(buf(B)), co, kb, db);
+        else
+          a = *reinterpret_cast<const u32x4*>(sV + voff[kb] + 32 * BN * db);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
           o[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pf[nb][kb]), o[nb][db], 0, 0, 0);
@@ -518,16 +566,16 @@ prefill_attn_kernel(PrefillParams p) {
     if (j >= j_ws)
       plan.copy(ks.kw, ks.vw, ks.ws_off, j * BN, sK, sK + K_TILE);
     else if constexpr (KV_FP8)
-      fetch_prefix_fp8<NWAVES>(fp8, tid, j * BN, sK, sK + K_TILE);
+      dma_code_tile<NWAVES>(cs8, [&](int pg) { return ks.bt_row[pg]; }, w, lane, j * BN,
+                            reinterpret_cast<uint8_t*>(sK));
     else
       dma_tile_prefix<NWAVES>(ks, w, lane, j * BN, sK, sK + K_TILE);
   };
 
-  // One 64-key tile of attention for this wave's queries.
-  auto compute_tile = [&](int j, auto B) __attribute__((always_inline)) {
-    if (!active(j)) return;
+  // One 64-key tile of attention for this wave's queries (CODES: an FP8 code tile).
+  auto tile = [&](int j, auto B, auto CODES) __attribute__((always_inline)) {
     f32x16 st[NB][2];
-    qk(B, st);
+    qk(B, CODES, st);
     if (needs_mask(j)) apply_mask(j, st);
     float mt[NB];
     if (__any(tile_max(st, mt))) {
@@ -537,7 +585,13 @@ prefill_attn_kernel(PrefillParams p) {
     }
     u32x4 pf[NB][4];
     softmax(st, pf);
-    pv(B, pf);
+    pv(B, CODES, pf);
+  };
+  // The main loop sees bf16 tiles only (over an FP8 cache the code tiles of
+  // the cached prefix run first, in a loop of their own).
+  auto compute_tile = [&](int j, auto B) __attribute__((always_inline)) {
+    if (!active(j)) return;
+    tile(j, B, std::false_type{});
   };
   // Stage of tiles j0 .. j0+TPS-1 in slots S0 .. S0+TPS-1: before tile j0+u
   // is computed, tile j0+TPS+u is sent to the other stage's slot (freed by the
@@ -554,12 +608,38 @@ prefill_attn_kernel(PrefillParams p) {
   };
 
   // ---- tile loop ----
+  int j_main = j_lo;
+  if constexpr (KV_FP8) {
+    // FP8 code tiles of the cached prefix (below the chunk's first tile), one
+    // per step in buffers 0 and 1; then the main loop starts afresh.
+    const int jc = min(j_hi, j_ws - 1);
+    if (j_lo <= jc) {
+      const auto CODE = std::true_type{};
+      const auto S0 = std::integral_constant<int, 0>{};
+      const auto S1 = std::integral_constant<int, 1>{};
+      fetch(j_lo, S0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      for (int jt = j_lo; jt <= jc; jt += 2) {
+        if (jt + 1 <= jc) fetch(jt + 1, S1);
+        if (active(jt)) tile(jt, S0, CODE);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (jt + 1 > jc) break;
+        if (jt + 2 <= jc) fetch(jt + 2, S0);
+        if (active(jt + 1)) tile(jt + 1, S1, CODE);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+      j_main = jc + 1;
+    }
+  }
   static_for<TPS>([&](auto U) __attribute__((always_inline)) {
-    if (j_lo + decltype(U)::value <= j_hi) fetch(j_lo + decltype(U)::value, U);
+    if (j_main + decltype(U)::value <= j_hi) fetch(j_main + decltype(U)::value, U);
   });
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int jt = j_lo; jt <= j_hi; jt += SLOTS) {
+  for (int jt = j_main; jt <= j_hi; jt += SLOTS) {
     stage(jt, std::integral_constant<int, 0>{});
     if (jt + TPS > j_hi) break;
     stage(jt + TPS, std::integral_constant<int, TPS>{});
@@ -573,7 +653,8 @@ prefill_attn_kernel(PrefillParams p) {
     const int t = wq_lo + 32 * nb + n;
     const float l_tot = sum_halves(l_run[nb]);
     if (t > qlast) continue;
-    const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
+    // 1 / l, and v_scale over an FP8 cache (code space)
+    const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) * (KV_FP8 ? p.v_scale : 1.f) : 0.f;
     const size_t tok = (size_t)(cu0 + (t - start));
     const uint16_t* grow_ = p.gate + (tok * p.H + h) * D;
     uint16_t* orow = p.out + (tok * p.H + h) * D;
@@ -630,78 +711,46 @@ __device__ __forceinline__ const uint16_t* v_elem_cached(const KeySource& ks, co
 template <int NW>
 __device__ __forceinline__ void dma_tile_cached(const KeySource& ks, const int* pages, int page0, int w, int lane,
                                                 int key0, uint16_t* sK, uint16_t* sV) {
+  // every source address first (the page lookups together), then the DMAs
+  const uint16_t* ksrc[DmaPlan<NW>::N];
+  const uint16_t* vsrc[DmaPlan<NW>::N];
 #pragma unroll
   for (int i = 0; i < DmaPlan<NW>::N; ++i) {
     const int kI = w * DmaPlan<NW>::N + i;
     const int m = 8 * (kI & 7) + (lane >> 3);
     const int c = (lane & 7) ^ ((m >> 1) & 7);
-    lds_dma16(k_row_cached(ks, pages, page0, key0 + krow_key(m)) + 64 * (kI >> 3) + 8 * c, sK + kI * 512);
+    ksrc[i] = k_row_cached(ks, pages, page0, key0 + krow_key(m)) + 64 * (kI >> 3) + 8 * c;
     const int vI = w * DmaPlan<NW>::N + i;
     const int d = 8 * vI + (lane >> 3);
     const int cv = (lane & 7) ^ ((d >> 1) & 7);
-    lds_dma16(v_elem_cached(ks, pages, page0, d, key0 + 8 * cv), sV + vI * 512);
+    vsrc[i] = v_elem_cached(ks, pages, page0, d, key0 + 8 * cv);
+  }
+#pragma unroll
+  for (int i = 0; i < DmaPlan<NW>::N; ++i) {
+    const int kI = w * DmaPlan<NW>::N + i;
+    lds_dma16(ksrc[i], sK + kI * 512);
+    lds_dma16(vsrc[i], sV + kI * 512);
   }
 }
-
-// FP8 prefix tile in two phases: the codes into registers, then dequantised
-// into LDS (the chunks of fetch_prefix_fp8).
 
 // s_waitcnt immediate for vmcnt <= n, lgkmcnt 0, expcnt untouched (gfx9
 // fields: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]).
 constexpr int vm_lgkm_wait(int n) { return (n & 15) | (7 << 4) | (((n >> 4) & 3) << 14); }
 
-template <int NW>
-struct Fp8Regs {
-  static constexpr int R = 8 / NW;
-  u32x4 k[R], v[R];
-};
-template <int NW>
-__device__ __forceinline__ void load_prefix_fp8(const Fp8Prefix& fp, const int* pages, int page0, int tid, int key0,
-                                                Fp8Regs<NW>& r) {
-#pragma unroll
-  for (int i = 0; i < Fp8Regs<NW>::R; ++i) {
-    const int id = tid + 64 * NW * i;
-    {
-      const int m = id >> 3, c2 = id & 7;
-      const int s = key0 + krow_key(m);
-      const uint8_t* src = fp.kind == 1 ? fp.k8 + pages[(s >> 4) - page0] * fp.page_stride + (size_t)((s & 15) * D)
-                                        : fp.k8 + (size_t)((s % fp.window) * D);
-      r.k[i] = *reinterpret_cast<const u32x4*>(src + 16 * c2);
-    }
-    {
-      const int d = id >> 2, c2 = id & 3;
-      const int s = key0 + 16 * c2;
-      const uint8_t* src = fp.kind == 1 ? fp.v8 + pages[(s >> 4) - page0] * fp.page_stride + (size_t)(d * 16)
-                                        : fp.v8 + (size_t)(d * fp.window + s % fp.window);
-      r.v[i] = *reinterpret_cast<const u32x4*>(src);
-    }
-  }
-}
-template <int NW>
-__device__ __forceinline__ void store_prefix_fp8(const Fp8Prefix& fp, int tid, const Fp8Regs<NW>& r, uint16_t* sK,
-                                                 uint16_t* sV) {
-#pragma unroll
-  for (int i = 0; i < Fp8Regs<NW>::R; ++i) {
-    const int id = tid + 64 * NW * i;
-    const int m = id >> 3, ck = id & 7;
-    *reinterpret_cast<u32x4*>(sK + k_off(m, 2 * ck)) = fp8x8_dequant_bf16(r.k[i][0], r.k[i][1], fp.k_scale);
-    *reinterpret_cast<u32x4*>(sK + k_off(m, 2 * ck + 1)) = fp8x8_dequant_bf16(r.k[i][2], r.k[i][3], fp.k_scale);
-    const int d = id >> 2, cv = id & 3;
-    *reinterpret_cast<u32x4*>(sV + v_off(d, 2 * cv)) = fp8x8_dequant_bf16(r.v[i][0], r.v[i][1], fp.v_scale);
-    *reinterpret_cast<u32x4*>(sV + v_off(d, 2 * cv + 1)) = fp8x8_dequant_bf16(r.v[i][2], r.v[i][3], fp.v_scale);
-  }
-}
-
-template <int KIND, int KV_FP8>
-__global__ void __launch_bounds__(64 * kVerifyWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// NWAVES = 4: two bf16 tile buffers (64 KiB), two blocks per CU. NWAVES = 2
+// (FP8 caches, chunks of at most 64 rows): one buffer (32 KiB, two 16-KiB
+// code tiles), four blocks per CU, so that every wave of the CU has rows and
+// the MFMA work of a CU spreads over all four SIMDs.
+template <int KIND, int KV_FP8, int NWAVES>
+__global__ void __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 verify_attn_kernel(PrefillParams p) {
-  constexpr int NWAVES = kVerifyWaves;
   constexpr bool local = (KIND == 0);
+  constexpr int NSLOT = NWAVES == 4 ? 2 : 1;  // bf16 tile buffers
   // One LDS object: with a second __shared__ variable the compiler tags LDS
   // accesses with alias scopes and then makes every LDS read wait for all DMA
   // into the same array (vmcnt(0) before each tile's MFMAs), which serialises
   // the fetch of tile jt + 1 with the compute of tile jt.
-  constexpr int kTiles = 2 * (K_TILE + V_TILE);
+  constexpr int kTiles = NSLOT * (K_TILE + V_TILE);
   __shared__ __attribute__((aligned(1024))) uint16_t smem[kTiles + (KIND == 1 ? 2 * kVerifyMaxPages : 0)];
   int* const s_pages = reinterpret_cast<int*>(smem + kTiles);
 
@@ -755,18 +804,8 @@ verify_attn_kernel(PrefillParams p) {
   const int n = lane & 31;
   const int half = lane >> 5;
   const DmaPlan<NWAVES> plan = make_dma_plan<NWAVES>(w, lane);
-  Fp8Prefix fp8;
-  if constexpr (KV_FP8) {
-    const size_t head = KIND == 1 ? (size_t)g * 16 * D : ((size_t)cseq * p.G + g) * W * D;
-    fp8.k8 = reinterpret_cast<const uint8_t*>(p.ck) + head;
-    fp8.v8 = reinterpret_cast<const uint8_t*>(p.cv) + head;
-    fp8.bt_row = ks.bt_row;
-    fp8.page_stride = (size_t)p.G * 16 * D;
-    fp8.kind = KIND;
-    fp8.window = W;
-    fp8.k_scale = p.k_scale;
-    fp8.v_scale = p.v_scale;
-  }
+  CodeSource cs8;
+  if constexpr (KV_FP8) cs8 = make_code_source(p, KIND, cseq, g);
 
   // Page ids of the split's cached tiles (tiles j_lo .. min(j_hi, j_ws - 1);
   // pages below (start & ~63) / 16, inside the block-table row).
@@ -794,6 +833,7 @@ verify_attn_kernel(PrefillParams p) {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
       qf[kk] = row_valid ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk) : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (KV_FP8) scale_frags(qf, p.k_scale);  // code space: q' k_scale against the codes
   }
   f32x16 o[4];
 #pragma unroll
@@ -810,6 +850,8 @@ verify_attn_kernel(PrefillParams p) {
     koff[q] = k_off(n, 2 * q + half);
     voff[q] = v_off(n, 2 * q + half);
   }
+  [[maybe_unused]] CodeOffsets co;
+  if constexpr (KV_FP8) co = code_offsets(n, half);
 
   auto buf = [&](auto B) -> uint16_t* { return smem + decltype(B)::value * (K_TILE + V_TILE); };
   auto active = [&](int j) __attribute__((always_inline)) {
@@ -820,18 +862,29 @@ verify_attn_kernel(PrefillParams p) {
     const int k0 = j * BN;
     return (k0 + BN - 1 > wq_lo) || (local && k0 < wq_hi - (W - 1));
   };
-  auto tile = [&](int j, auto B) __attribute__((always_inline)) {
-    if (!active(j)) return;
-    const uint16_t* sK = buf(B);
+  // A operand fragments of one tile: bf16 tiles (workspace, bf16 cache) or
+  // FP8 code tiles (converted exactly after the LDS read).
+  // Code tiles sit in 16 KiB sub-buffers: `sub` of them past buffer B.
+  auto kfrag = [&](auto B, auto CODES, int sub, int kk, int mb) __attribute__((always_inline)) -> u32x4 {
+    if constexpr (decltype(CODES)::value)
+      return code_kfrag(reinterpret_cast<const uint8_t*>(buf(B)) + 16384 * sub, co, kk, mb);
+    else
+      return *reinterpret_cast<const u32x4*>(buf(B) + koff[kk & 3] + K_HALF * (kk >> 2) + 32 * 64 * mb);
+  };
+  auto vfrag = [&](auto B, auto CODES, int sub, int kb, int db) __attribute__((always_inline)) -> u32x4 {
+    if constexpr (decltype(CODES)::value)
+      return code_vfrag(reinterpret_cast<const uint8_t*>(buf(B)) + 16384 * sub, co, kb, db);
+    else
+      return *reinterpret_cast<const u32x4*>(buf(B) + K_TILE + voff[kb] + 32 * BN * db);
+  };
+  auto tile = [&](int j, auto B, auto CODES, int sub = 0) __attribute__((always_inline)) {
     f32x16 s[2];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(sK + koff[kk & 3] + K_HALF * (kk >> 2) + 32 * 64 * mb);
-        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qf[kk]), kk == 0 ? sref : s[mb], 0,
-                                                        0, 0);
-      }
+      for (int mb = 0; mb < 2; ++mb)
+        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kfrag(B, CODES, sub, kk, mb)), as_bf16x8(qf[kk]),
+                                                        kk == 0 ? sref : s[mb], 0, 0, 0);
     if (needs_mask(j)) {  // element i of block mb holds key 64j + 32mb + 16(i>>3) + 8*half + (i&7)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -880,78 +933,126 @@ verify_attn_kernel(PrefillParams p) {
         l_run = sum_bf16x2(pf[kb][c], l_run);
       }
     }
-    const uint16_t* sV = buf(B) + K_TILE;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(sV + voff[kb] + 32 * BN * db);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pf[kb]), o[db], 0, 0, 0);
-      }
+      for (int db = 0; db < 4; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vfrag(B, CODES, sub, kb, db)), as_bf16x8(pf[kb]), o[db],
+                                                        0, 0, 0);
   };
-  // DMA of tile j (workspace or bf16 cache) into buffer B.
+  // DMA of tile j into buffer B: the workspace, the bf16 cache, or FP8 codes.
   auto dma = [&](int j, auto B) __attribute__((always_inline)) {
     uint16_t* sK = buf(B);
     if (j >= j_ws)
       plan.copy(ks.kw, ks.vw, ks.ws_off, j * BN, sK, sK + K_TILE);
+    else if constexpr (KV_FP8)
+      dma_code_tile<NWAVES>(cs8, [&](int pg) { return s_pages[pg - page0]; }, w, lane, j * BN,
+                            reinterpret_cast<uint8_t*>(sK));
     else
       dma_tile_cached<NWAVES>(ks, s_pages, page0, w, lane, j * BN, sK, sK + K_TILE);
   };
-  __builtin_amdgcn_s_waitcnt(0);  // Q' and page ids in
-  __syncthreads();
-  // Two LDS buffers: tile jt + 1 arrives while tile jt is computed. DMA tiles
-  // are sent one step ahead. FP8 prefix tiles go through registers two steps
-  // ahead (regs[b] for the tile that will use buffer b) and are converted
-  // into LDS after the MFMAs of the step before their own; such a step ends
-  // waiting for its DMA and LDS stores only, leaving the newest code loads in
-  // flight. The barrier is a bare s_barrier: the workgroup fence of
-  // __syncthreads would wait for every load still in flight. The empty asm
-  // statements keep the compiler from moving LDS accesses across it.
-  [[maybe_unused]] Fp8Regs<NWAVES> regs[2];
-  auto reg_tile = [&](int j) { return KV_FP8 && j <= j_hi && j < j_ws; };
-  auto step_end = [&](bool codes_in_flight) __attribute__((always_inline)) {
-    if (codes_in_flight)
-      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(2 * Fp8Regs<NWAVES>::R));
-    else
-      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
+  // Each step ends with an explicit wait for its DMA and a bare s_barrier:
+  // the workgroup fence of __syncthreads would also wait for loads the
+  // compiler cannot see as finished. The empty asm statements keep the
+  // compiler from moving LDS accesses across it.
+  auto step_end = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  auto step = [&](int jt, auto B) __attribute__((always_inline)) {
-    constexpr int b = decltype(B)::value;
-    const int jn = jt + 1;
-    if (jn <= j_hi && !reg_tile(jn)) dma(jn, std::integral_constant<int, 1 - b>{});
-    const bool load_nn = reg_tile(jt + 2);
-    if constexpr (KV_FP8) {
-      asm volatile("" ::: "memory");  // the DMA is issued before the code loads below
-      if (load_nn) load_prefix_fp8<NWAVES>(fp8, s_pages, page0, tid, (jt + 2) * BN, regs[b]);
-    }
-    tile(jt, B);
-    if constexpr (KV_FP8) {
-      if (reg_tile(jn))
-        store_prefix_fp8<NWAVES>(fp8, tid, regs[1 - b], buf(std::integral_constant<int, 1 - b>{}),
-                                 buf(std::integral_constant<int, 1 - b>{}) + K_TILE);
-    }
-    step_end(load_nn);
+  // One step: tile jt + 1 is sent to the other buffer while tile jt is
+  // computed from buffer B.
+  // The chunk's own tiles (workspace) alone, for the second loop over an FP8
+  // cache, where no cached tile follows.
+  auto dma_ws = [&](int j, auto B) __attribute__((always_inline)) {
+    uint16_t* sK = buf(B);
+    plan.copy(ks.kw, ks.vw, ks.ws_off, j * BN, sK, sK + K_TILE);
   };
-  if (reg_tile(j_lo)) {
-    if constexpr (KV_FP8) {
-      load_prefix_fp8<NWAVES>(fp8, s_pages, page0, tid, j_lo * BN, regs[0]);
-      store_prefix_fp8<NWAVES>(fp8, tid, regs[0], smem, smem + K_TILE);
+  auto step = [&](int jt, auto B, auto CODES, auto& fetch) __attribute__((always_inline)) {
+    if (jt + 1 <= j_hi) fetch(jt + 1, std::integral_constant<int, 1 - decltype(B)::value>{});
+    if (active(jt)) tile(jt, B, CODES);
+    step_end();
+  };
+  const auto S0 = std::integral_constant<int, 0>{};
+  const auto S1 = std::integral_constant<int, 1>{};
+  __builtin_amdgcn_s_waitcnt(0);  // Q' and page ids in
+  __syncthreads();
+  int jt = j_lo;
+  if constexpr (KV_FP8) {
+    // The code tiles of an FP8 cache (the cached keys below the chunk) come
+    // first, in a loop of their own: one kind of tile per loop body keeps the
+    // register allocation as tight as in a single-kind kernel. A code tile
+    // takes 16 KiB, so the two buffers hold four: the DMA runs three tiles
+    // ahead, and each step waits only for the tile the next step computes
+    // (each tile is 16 / NWAVES DMA instructions of every wave).
+    constexpr int kPerTile = 16 / NWAVES;  // DMA instructions of a wave per code tile
+    constexpr int NSUB = 2 * NSLOT;         // 16-KiB code tile buffers
+    constexpr int AHEAD = NSUB - 1;         // tiles in flight beyond the one computed
+    const int jc = min(j_hi, j_ws - 1);
+    if (j_lo <= jc) {
+      auto sub = [&](auto U) { return reinterpret_cast<uint8_t*>(smem) + 16384 * decltype(U)::value; };
+      auto dma_c = [&](int j, auto U) __attribute__((always_inline)) {
+        dma_code_tile<NWAVES>(cs8, [&](int pg) { return s_pages[pg - page0]; }, w, lane, j * BN, sub(U));
+      };
+      // wait until tile j + 1 has landed (the tiles after it may stay in flight)
+      auto wait_next = [&](int j) __attribute__((always_inline)) {
+        const int ahead = min(j + AHEAD, jc) - (j + 1);
+        if (AHEAD >= 3 && ahead >= 2)
+          __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(2 * kPerTile));
+        else if (AHEAD >= 2 && ahead >= 1)
+          __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(kPerTile));
+        else
+          __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      };
+      auto cstep = [&](int j, auto U) __attribute__((always_inline)) {
+        constexpr int u = decltype(U)::value;
+        if (j + AHEAD <= jc) dma_c(j + AHEAD, std::integral_constant<int, (u + AHEAD) % NSUB>{});
+        if (active(j)) tile(j, std::integral_constant<int, 0>{}, std::true_type{}, u);
+        wait_next(j);
+      };
+      static_for<AHEAD>([&](auto U) __attribute__((always_inline)) {
+        if (j_lo + decltype(U)::value <= jc) dma_c(j_lo + decltype(U)::value, U);
+      });
+      wait_next(j_lo - 1);
+      for (; jt <= jc; jt += NSUB) {
+        bool done = false;
+        static_for<NSUB>([&](auto U) __attribute__((always_inline)) {
+          if (!done && jt + decltype(U)::value <= jc) cstep(jt + decltype(U)::value, U);
+          else done = true;
+        });
+        if (done) break;
+      }
+      jt = jc + 1;
+    }
+  }
+  // bf16 tiles (the workspace, or a bf16 cache) in two buffers: tile jt + 1
+  // arrives while tile jt is computed.
+  const auto BF = std::false_type{};
+  auto& fetch2 = [&]() -> auto& {
+    if constexpr (KV_FP8) return dma_ws; else return dma;
+  }();
+  if constexpr (NSLOT == 2) {
+    if (jt <= j_hi) {
+      fetch2(jt, S0);
+      step_end();
+    }
+    for (; jt <= j_hi; jt += 2) {
+      step(jt, S0, BF, fetch2);
+      if (jt + 1 > j_hi) break;
+      step(jt + 1, S1, BF, fetch2);
     }
   } else {
-    dma(j_lo, std::integral_constant<int, 0>{});
-  }
-  if constexpr (KV_FP8) {
-    asm volatile("" ::: "memory");
-    if (reg_tile(j_lo + 1)) load_prefix_fp8<NWAVES>(fp8, s_pages, page0, tid, (j_lo + 1) * BN, regs[1]);
-  }
-  step_end(reg_tile(j_lo + 1));
-  for (int jt = j_lo; jt <= j_hi; jt += 2) {
-    step(jt, std::integral_constant<int, 0>{});
-    if (jt + 1 > j_hi) break;
-    step(jt + 1, std::integral_constant<int, 1>{});
+    // one buffer: fetch, compute, then free it for the next tile
+    for (; jt <= j_hi; ++jt) {
+      fetch2(jt, S0);
+      step_end();
+      if (active(jt)) tile(jt, S0, BF);
+      step_end();
+    }
   }
 
   // Partials of this split: lane holds row n's sum half and coordinates
@@ -1007,7 +1108,7 @@ __global__ void __launch_bounds__(128) verify_combine_kernel(VerifyCombineParams
       A += sc * p.part_acc[(row0 + sp) * D + d];
     }
   }
-  const float o = L > 0.f ? A * __builtin_amdgcn_rcpf(L) : 0.f;
+  const float o = L > 0.f ? A * __builtin_amdgcn_rcpf(L) * p.v_scale : 0.f;
   const float bias = p.gate_bias ? p.gate_bias[h] : 0.f;
   const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-(bf16f(p.gate[idx]) + bias)));
   bf16x2 rr;
@@ -1015,19 +1116,24 @@ __global__ void __launch_bounds__(128) verify_combine_kernel(VerifyCombineParams
   p.out[idx] = __builtin_bit_cast(uint16_t, rr[0]);
 }
 
-hipError_t launch_verify_attn(const PrefillParams& p, hipStream_t s) {
+hipError_t launch_verify_attn(const PrefillParams& p, int max_rows, hipStream_t s) {
   clear_stale_error();
   if (p.split_tiles * 4 > kVerifyMaxPages) return hipErrorInvalidValue;
   const long long blocks = (long long)p.G * p.n_splits * p.n_seqs;
-  const dim3 grid((unsigned)blocks), block(64 * kVerifyWaves);
+  const dim3 grid((unsigned)blocks), block4(64 * kVerifyWaves), block2(128);
+  const bool two = p.kv_fp8 && max_rows <= 64;  // FP8 cache, chunks of at most 64 rows: 2-wave blocks
   if (p.kind == 0 && !p.kv_fp8)
-    hipLaunchKernelGGL((verify_attn_kernel<0, 0>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((verify_attn_kernel<0, 0, 4>), grid, block4, 0, s, p);
+  else if (p.kind == 0 && two)
+    hipLaunchKernelGGL((verify_attn_kernel<0, 1, 2>), grid, block2, 0, s, p);
   else if (p.kind == 0)
-    hipLaunchKernelGGL((verify_attn_kernel<0, 1>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((verify_attn_kernel<0, 1, 4>), grid, block4, 0, s, p);
   else if (!p.kv_fp8)
-    hipLaunchKernelGGL((verify_attn_kernel<1, 0>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((verify_attn_kernel<1, 0, 4>), grid, block4, 0, s, p);
+  else if (two)
+    hipLaunchKernelGGL((verify_attn_kernel<1, 1, 2>), grid, block2, 0, s, p);
   else
-    hipLaunchKernelGGL((verify_attn_kernel<1, 1>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((verify_attn_kernel<1, 1, 4>), grid, block4, 0, s, p);
   return hipGetLastError();
 }
 

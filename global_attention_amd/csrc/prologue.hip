@@ -7,6 +7,11 @@
 // by log2(e)/sqrt(d) (and a(t+1) on global layers) so the attention kernels
 // work in base-2 logits; this is one bf16 rounding of Q, the same count as
 // rounding the normalised Q itself.
+//
+// Over an FP8 cache the attention kernels work in the cache's code space: the
+// chunk's own keys and values go into the workspace divided by k_scale and
+// v_scale (one bf16 rounding each), cached ones as their exact codes, and the
+// kernels multiply Q' by k_scale and O by v_scale.
 #include "beam_device.h"
 #include "beam_kernels.h"
 
@@ -54,13 +59,6 @@ __device__ __forceinline__ size_t cache_v_off(const PrologueParams& p, int cseq,
   *stride = p.window;
   return ((size_t)cseq * p.G + g) * D * p.window + t % p.window;
 }
-// Four FP8 codes of x / scale -> bf16 of decode(code) * scale (one rounding).
-__device__ __forceinline__ u32x2 fp8x4_dequant_bf16(uint32_t w, float scale) {
-  float f[4];
-  fp8x4_to_f32(w, f);
-  return u32x2{pack_bf16x2(f[0] * scale, f[1] * scale), pack_bf16x2(f[2] * scale, f[3] * scale)};
-}
-
 template <int KIND, int KV_FP8>
 __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p) {
   constexpr bool local = (KIND == 0);
@@ -145,10 +143,10 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
         for (int g = 0; g < kMaxHeadsPerGroup; ++g)
           if (g < p.G) {
             const size_t off = cache_k_off<KIND>(p, cseq, g, t);
-            if constexpr (KV_FP8) {
+            if constexpr (KV_FP8) {  // the codes themselves (code space, exact in bf16)
               const uint8_t* src = reinterpret_cast<const uint8_t*>(p.ck) + off;
-              clo[g] = fp8x4_dequant_bf16(*reinterpret_cast<const uint32_t*>(src + 4 * j), p.k_scale);
-              chi[g] = fp8x4_dequant_bf16(*reinterpret_cast<const uint32_t*>(src + 64 + 4 * j), p.k_scale);
+              clo[g] = fp8x4_to_bf16x4(*reinterpret_cast<const uint32_t*>(src + 4 * j));
+              chi[g] = fp8x4_to_bf16x4(*reinterpret_cast<const uint32_t*>(src + 64 + 4 * j));
             } else {
               const u32x2* src = reinterpret_cast<const u32x2*>(p.ck + off);
               clo[g] = src[j];
@@ -189,8 +187,9 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
         if (g < p.G) {
           float a[4], bq[4];
           norm_rope_f32(xlo[g], xhi[g], wk_lo, wk_hi, p.rms_eps, local, cs, sn, a, bq);
-          const u32x2 flo = u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
-          const u32x2 fhi = u32x2{pack_bf16x2(bq[0], bq[1]), pack_bf16x2(bq[2], bq[3])};
+          const float ks = KV_FP8 ? 1.f / p.k_scale : 1.f;  // code space over an FP8 cache
+          const u32x2 flo = u32x2{pack_bf16x2(a[0] * ks, a[1] * ks), pack_bf16x2(a[2] * ks, a[3] * ks)};
+          const u32x2 fhi = u32x2{pack_bf16x2(bq[0] * ks, bq[1] * ks), pack_bf16x2(bq[2] * ks, bq[3] * ks)};
           dst0[g * hstride + j] = flo;
           dst0[g * hstride + 16 + j] = fhi;
           if (append_pos(t)) {
@@ -231,11 +230,11 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
         if constexpr (KV_FP8) {
           const uint8_t* col = reinterpret_cast<const uint8_t*>(p.cv) + off;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
+          for (int q = 0; q < 4; ++q) {  // the codes themselves (code space, exact)
             float f0[4], f1[4];
             fp8x4_to_f32(col[(size_t)(8 * c + 2 * q) * stride], f0);
             fp8x4_to_f32(col[(size_t)(8 * c + 2 * q + 1) * stride], f1);
-            v[q4][q] = pack_bf16x2(f0[0] * p.v_scale, f1[0] * p.v_scale);
+            v[q4][q] = pack_bf16x2(f0[0], f1[0]);
           }
         } else {
           const uint16_t* col = p.cv + off;
@@ -264,9 +263,21 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
       const int e = tid + 256 * q4;
       const int d = e >> 3, c = e & 7;
       u32x4 o;
+      if constexpr (KV_FP8) {
+        // code space: the chunk's own values divided by v_scale; cached ones
+        // are codes already
+        const float vs = 1.f / p.v_scale;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        o[q] = (uint32_t)s_v[8 * c + 2 * q][d] | ((uint32_t)s_v[8 * c + 2 * q + 1][d] << 16);
+        for (int q = 0; q < 4; ++q) {
+          const int k0 = 8 * c + 2 * q;
+          const float s0 = tile_pos0 + k0 >= start ? vs : 1.f, s1 = tile_pos0 + k0 + 1 >= start ? vs : 1.f;
+          o[q] = pack_bf16x2(bf16f(s_v[k0][d]) * s0, bf16f(s_v[k0 + 1][d]) * s1);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          o[q] = (uint32_t)s_v[8 * c + 2 * q][d] | ((uint32_t)s_v[8 * c + 2 * q + 1][d] << 16);
+      }
       *reinterpret_cast<u32x4*>(vt + d * 64 + 8 * c) = o;
     }
     if (append) {

@@ -199,8 +199,8 @@ beam_status beam_attn_decode_noalloc(const beam_attn_config *cfg, const beam_kv_
  * max_pos >= start_pos[i] + chunk length - 1 for every i (sizes the split grid).
  * A sequence that breaks this (or has start_pos[i] < 0) gets NaN output rows:
  * the split grid does not cover its keys. split_keys: keys per split (multiple of 64, <= 8192), or 0 for the
- * default: 256 local; global 4096 if n_seqs * n_kv_heads * (max_pos / 4096 + 1)
- * >= 1024, else 2048.
+ * default: 256 local; global the longest of 8192 and 4096 keys for which
+ * n_seqs * n_kv_heads * (max_pos / keys + 1) >= 1024, else 2048.
  * Rejected draft tokens: on a GLOBAL cache the next call simply starts at the
  * first rejected position (its slots are overwritten). A LOCAL ring keeps only
  * the last `window` positions, so appending a rejected token would evict a key

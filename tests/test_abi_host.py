@@ -141,15 +141,16 @@ def _call_verify(cfg, cache, max_chunk=4, max_pos=100, split_keys=0, ws_bytes=1 
 def test_verify_workspace_and_checks():
     cfg = ga.Config()
     L = ga.lib()
-    # splits: global keys 0..max_pos in 64-key tiles; the default split is 4096 keys
-    # when 8 sequences x 8 KV heads x (max_pos // 4096 + 1) reach 1024 blocks, else 2048
+    # splits: global keys 0..max_pos in 64-key tiles; the default split is the longest
+    # of 8192 and 4096 keys for which 8 sequences x 8 KV heads x (max_pos // keys + 1)
+    # reach 1024 blocks, else 2048
     base = ga.prefill_workspace_bytes(cfg, 64, 8)
-    for max_pos, splits in ((0, 1), (2047, 1), (2048, 2), (32767, 16), (65535, 16), (65536, 17), (131071, 32)):
+    for max_pos, splits in ((0, 1), (2047, 1), (2048, 2), (32767, 16), (65535, 16), (65536, 17), (131071, 16)):
         rows = 64 * 48 * splits
         want = base + ((rows * 8 + 255) // 256) * 256 + ((rows * 512 + 255) // 256) * 256
         assert ga.verify_workspace_bytes(cfg, ga.GLOBAL, 64, 8, 8, max_pos) == want
     for max_pos in (0, 65535, 65536, 131071):
-        explicit = 4096 if 64 * (max_pos // 4096 + 1) >= 1024 else 2048
+        explicit = next((k for k in (8192, 4096) if 64 * (max_pos // k + 1) >= 1024), 2048)
         assert ga.verify_workspace_bytes(cfg, ga.GLOBAL, 64, 8, 8, max_pos) == \
             ga.verify_workspace_bytes(cfg, ga.GLOBAL, 64, 8, 8, max_pos, split_keys=explicit)
     # local: the window bounds the keys (511 + 7 positions span at most 10 tiles -> 3 splits of 4)

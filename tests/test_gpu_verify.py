@@ -215,6 +215,90 @@ def test_verify_64seq_128k_draft8_sampled():
     del gcache, lcache
 
 
+def _gather_global_codes(cache, bt_row, n_keys):
+    """Host float64 K_hat/V of one sequence's first n_keys positions from an
+    FP8 cache: the codes decoded by the oracle, times the scales: [n_keys, 8, 128]."""
+    import torch
+    n_pg = (n_keys + 15) // 16
+    idx = torch.from_numpy(np.ascontiguousarray(bt_row[:n_pg]).astype(np.int64)).cuda()
+    k = cache.k.index_select(0, idx).permute(0, 2, 1, 3).reshape(n_pg * 16, 8, 128)[:n_keys]
+    v = cache.v.index_select(0, idx).permute(0, 3, 1, 2).reshape(n_pg * 16, 8, 128)[:n_keys]
+    kc, vc = k.contiguous().cpu().numpy(), v.contiguous().cpu().numpy()
+    return O.e4m3_decode(kc) * cache.k_scale, O.e4m3_decode(vc) * cache.v_scale
+
+
+def test_verify_64seq_128k_draft8_fp8_sampled():
+    """The full-size verify step over an FP8 cache of seeded random codes
+    (inputs), 8-token drafts: the kernel with two-wave blocks (at most 64 rows
+    per chunk). Three sampled sequences against the oracle, which decodes the
+    cached codes itself."""
+    import torch
+    n, L = 64, 8
+    starts = synth.decode_positions(3, n, 65536, 131071 - L)
+    bt, n_pages = synth.paged_block_table(3, starts.astype(np.int64) + L)
+    say(f"[case] verify 64 seqs x {L} tokens over an FP8 cache: {n_pages} pages")
+    cache = ga.KVCache.allocate_global(CFG, n_pages, torch.from_numpy(bt), dtype=ga.KV_FP8_E4M3, k_scale=0.6,
+                                       v_scale=0.9)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(33)
+    for t in (cache.k, cache.v):
+        for p0 in range(0, t.shape[0], 8192):
+            blk = t[p0:p0 + 8192]
+            blk.copy_(torch.randn(blk.shape, generator=gen, device="cuda").to(torch.float8_e4m3fn).view(torch.uint8))
+    inp = synth.attention_inputs(cfg=33, layer=9, n_tok=n * L)
+    batch = [_slice(inp, L * i, L) for i in range(n)]
+    sample = (0, int(np.argmax(starts)), 41)
+    say("[case] verify 64 seqs fp8: launching")
+    outs = _verify(cache, batch, [int(s) for s in starts], list(range(n)))
+    assert all(np.all(np.isfinite(bf16_to_f64(o))) for o in outs)
+    for sq in sample:
+        s0 = int(starts[sq])
+        kh, v = _gather_global_codes(cache, bt[sq], s0)
+        ref = _chunk_oracle(O.GLOBAL, batch[sq], s0, kh, v, np.arange(s0))
+        compare(outs[sq], ref, f"verify fp8 seq {sq} start={s0}")
+    del cache
+
+
+@pytest.mark.parametrize("kind", [O.LOCAL, O.GLOBAL])
+def test_verify_fp8_short_chunks_both_block_shapes(kind):
+    """Chunks of at most 10 tokens (at most 64 rows of a KV head) over an FP8
+    cache run in two-wave blocks; the same call with max_chunk_len 11 runs in
+    four-wave blocks. Both must equal each other bit for bit (every row does the
+    same arithmetic in either shape) and match the oracle."""
+    import torch
+    fp8 = (0.6, 0.9)
+    hist = [700, 130, 64, 1]
+    steps = [[8, 1, 10, 3], [2, 10, 7, 8]]
+    total = [h + sum(st[i] for st in steps) for i, h in enumerate(hist)]
+    inps = [synth.attention_inputs(34, 10 * kind + i, m) for i, m in enumerate(total)]
+    for x in inps[1:]:
+        x["q_norm_w"], x["k_norm_w"] = inps[0]["q_norm_w"], inps[0]["k_norm_w"]
+    caches = [_cache(kind, 34, total, fp8)[0] for _ in range(2)]
+    for c in caches:
+        _prefill(c, [_slice(inps[i], 0, hist[i]) for i in range(len(hist))], [0] * len(hist), list(range(len(hist))))
+    done = list(hist)
+    for step, chunk in enumerate(steps):
+        batch = [_slice(inps[i], done[i], chunk[i]) for i in range(len(hist))]
+        max_pos = max(s + b["q"].shape[0] - 1 for s, b in zip(done, batch))
+        say(f"[case] verify fp8 kind={kind} step={step} lens={chunk}: two-wave and four-wave blocks")
+        o2 = _call(ga.verify, caches[0], batch, list(done), list(range(len(hist))), max_pos=max_pos)
+        lens, cu, cat = _packed(batch)
+        w = batch[0]
+        out = ga.verify(CFG, caches[1], cat("q"), cat("k"), cat("v"), dev_bf16(w["q_norm_w"]),
+                        dev_bf16(w["k_norm_w"]), cat("gate"), dev_i32(cu), dev_i32(list(range(len(hist)))),
+                        dev_i32(done), 11, max_pos)
+        sync()
+        o4 = host_bits(out)
+        for i, o in enumerate(o2):
+            assert np.array_equal(o, o4[cu[i]:cu[i + 1]]), f"step {step} seq {i}: block shapes differ"
+            s0, m, x = done[i], chunk[i], inps[i]
+            ref = O.attention_layer(kind, x["q"][s0:s0 + m], x["k"][:s0 + m], x["v"][:s0 + m], x["q_norm_w"],
+                                    x["k_norm_w"], x["gate"][s0:s0 + m], np.arange(s0, s0 + m), np.arange(s0 + m),
+                                    fp8_cache=(*fp8, s0))
+            compare(o, ref, f"verify fp8 kind={kind} step{step} seq{i} [{s0},{s0 + m})")
+        done = [d + c for d, c in zip(done, chunk)]
+
+
 @pytest.mark.parametrize("kind", [O.LOCAL, O.GLOBAL])
 def test_verify_accept_and_roll_back(kind):
     """An 8-token draft of which 3 tokens are accepted, then a new draft from
