@@ -431,33 +431,61 @@ __global__ void __launch_bounds__(256, 2) decode_fp8_kernel(DecodeParams p) {
 }
 
 // Log-sum-exp merge of the splits of one (sequence, query head), then the
-// per-coordinate sigmoid gate. One block of 128 threads (one per coordinate).
-__global__ void __launch_bounds__(128) decode_combine_kernel(CombineParams p) {
+// per-coordinate sigmoid gate. A block is SG groups of 128 threads (one per
+// coordinate); group sg merges splits sg, sg + SG, ... and the SG partial
+// merges are combined through LDS in group order (deterministic, no atomics).
+// Each thread keeps eight loads in flight, so a long context (hundreds of
+// splits) takes n_splits / (8 SG) memory round trips instead of n_splits / 8.
+constexpr int kCombineMaxGroups = 8;
+
+__global__ void __launch_bounds__(128 * kCombineMaxGroups) decode_combine_kernel(CombineParams p) {
   const int seq = blockIdx.x / p.H;
   const int h = blockIdx.x - seq * p.H;
-  const int d = threadIdx.x;
+  const int d = threadIdx.x & 127;
+  const int sg = threadIdx.x >> 7;
+  const int SG = blockDim.x >> 7;
   const int t = p.pos[seq];
   const int cseq = p.seq_idx[seq];
   const size_t idx = ((size_t)seq * p.H + h) * D + d;
   if (t < 0 || t > p.max_pos || cseq < 0 || cseq >= p.n_cache_seqs) {
-    p.out[idx] = 0x7fc0;  // NaN: the position was outside the decode grid, or the cache row does not exist
+    if (sg == 0) p.out[idx] = 0x7fc0;  // NaN: the position was outside the decode grid, or the cache row does not exist
     return;
   }
   const int n_keys = p.kind == 0 ? min(t + 1, p.window) : t + 1;
   const int ns = (n_keys + p.split_keys - 1) / p.split_keys;
   const size_t row0 = ((size_t)seq * p.H + h) * p.n_splits;
-  // Unrolled so that a long context (hundreds of splits, few blocks) keeps
-  // eight independent loads in flight per thread.
   float M = kNegInf;
 #pragma unroll 8
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, p.part_ml[2 * (row0 + s)]);
+  for (int s = sg; s < ns; s += SG) M = fmaxf(M, p.part_ml[2 * (row0 + s)]);
   float L = 0.f, A = 0.f;
   if (M != kNegInf) {
 #pragma unroll 8
-    for (int s = 0; s < ns; ++s) {
+    for (int s = sg; s < ns; s += SG) {
       const float sc = __builtin_amdgcn_exp2f(p.part_ml[2 * (row0 + s)] - M);
       L += sc * p.part_ml[2 * (row0 + s) + 1];
       A += sc * p.part_acc[(row0 + s) * D + d];
+    }
+  }
+  __shared__ float s_m[kCombineMaxGroups], s_l[kCombineMaxGroups], s_a[kCombineMaxGroups][D];
+  if (SG > 1) {
+    if (d == 0) {
+      s_m[sg] = M;
+      s_l[sg] = L;
+    }
+    s_a[sg][d] = A;
+    __syncthreads();
+    if (sg != 0) return;
+    M = kNegInf;
+    for (int g = 0; g < SG; ++g) M = fmaxf(M, s_m[g]);
+    L = 0.f;
+    A = 0.f;
+    if (M != kNegInf) {
+      for (int g = 0; g < SG; ++g) {
+        if (s_m[g] == kNegInf) continue;
+        const float sc = __builtin_amdgcn_exp2f(s_m[g] - M);
+        L += sc * s_l[g];
+        A += sc * s_a[g][d];
+      }
     }
   }
   const float o = L > 0.f ? A * __builtin_amdgcn_rcpf(L) * p.v_scale : 0.f;
@@ -486,7 +514,10 @@ hipError_t launch_decode_split(const DecodeParams& p, int n_seqs, hipStream_t s)
 
 hipError_t launch_decode_combine(const CombineParams& p, int n_seqs, hipStream_t s) {
   clear_stale_error();
-  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(n_seqs * p.H)), dim3(128), 0, s, p);
+  // groups of 128 threads per (sequence, head): about 32 splits per group
+  int sg = 1;
+  while (sg < kCombineMaxGroups && p.n_splits > 32 * sg) sg *= 2;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(n_seqs * p.H)), dim3(128 * sg), 0, s, p);
   return hipGetLastError();
 }
 
