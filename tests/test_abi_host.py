@@ -317,3 +317,102 @@ def test_validate_cache_argument_checks():
         c = _cache()
         setattr(c, field, 0)
         assert L.beam_debug_validate_cache(ctypes.byref(c), None, fake, None) == 3, field
+
+
+# ---- the host side under AddressSanitizer and UndefinedBehaviorSanitizer ----
+# The C ABI (beam_attn.hip) is rebuilt with the sanitizers on its host pass only
+# (its device code is not run) and linked with recording launch stubs and a
+# driver (tests/asan/); the driver prints every host-only result, the status of
+# argument-check failures and the workspace carving of valid calls.
+
+def _build_asan_driver(out_dir):
+    import subprocess
+    inc = ["-I" + os.path.join(ROOT, "include"), "-I" + os.path.join(ROOT, "global_attention_amd", "csrc"),
+           "-I" + os.path.join(ROOT, "tests", "asan")]
+    import shlex
+    san = shlex.split("-Xarch_host -fsanitize=address,undefined")  # host pass only
+    common = ["-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer"] + san + inc
+    objs = []
+    units = [(os.path.join(ROOT, "global_attention_amd", "csrc", "beam_attn.hip"),
+              ["-x", "hip", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]),
+             (os.path.join(ROOT, "tests", "asan", "launch_stubs.cpp"), []),
+             (os.path.join(ROOT, "tests", "asan", "host_abi_driver.cpp"), [])]
+    for src, extra in units:
+        obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+        subprocess.run(["hipcc"] + extra + common + ["-c", src, "-o", obj], check=True, capture_output=True)
+        objs.append(obj)
+    exe = os.path.join(out_dir, "host_abi_driver")
+    subprocess.run(["hipcc", "--hip-link", "--offload-arch=gfx950"] + san + objs + ["-o", exe, "-lpthread"],
+                   check=True, capture_output=True)
+    return exe
+
+
+# beam_status values (include/beam_attn.h)
+E_NULL, E_RANGE, E_UNSUPPORTED, E_WORKSPACE = 1, 3, 4, 5
+
+
+def test_host_side_under_address_sanitizer(tmp_path):
+    import shutil
+    import subprocess
+    if shutil.which("hipcc") is None:
+        pytest.skip("hipcc not on PATH")
+    exe = _build_asan_driver(str(tmp_path))
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0:halt_on_error=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120, cwd=str(tmp_path))
+    assert "Sanitizer" not in r.stderr and "runtime error" not in r.stderr, r.stderr[-4000:]
+    assert r.returncode == 0, r.stderr[-4000:]
+    lines = r.stdout.splitlines()
+    assert lines[-1] == "done"
+    rows = [ln.split() for ln in lines[:-1]]
+    by = {}
+    for row in rows:
+        by.setdefault(row[0], []).append(row[1:])
+
+    for n, b, st, lg, pg in by["kv_bytes"]:
+        assert int(st) == 0
+        assert (int(lg), int(pg)) == O.kv_bytes(int(n), int(b))
+    bt = (1000 - 7 * np.arange(15, dtype=np.int64)).reshape(3, 5)
+    for seq, t, st, page, slot in by["page_slot"]:
+        seq, t = int(seq), int(t)
+        if 0 <= seq < 3 and 0 <= t < 5 * 16:
+            assert int(st) == 0 and (int(page), int(slot)) == O.page_slot(bt, 16, seq, t)
+        else:
+            assert int(st) == E_RANGE
+
+    cfg = ga.Config()
+    for n_tok, n_seqs, got in by["ws_prefill"]:
+        assert int(got) == ga.prefill_workspace_bytes(cfg, int(n_tok), int(n_seqs))
+    for kind, max_pos, split, got in by["ws_decode"]:
+        assert int(got) == ga.decode_workspace_bytes(cfg, int(kind), 64, int(max_pos), int(split))
+    for kind, max_pos, got in by["ws_verify"]:
+        assert int(got) == ga.verify_workspace_bytes(cfg, int(kind), 64, 8, 8, int(max_pos))
+
+    # prefill of 1000 tokens in 3 chunks (longest 600) on a global cache: the
+    # prologue and the attention launch (the append is fused into the
+    # prologue); Q', K_hat and V^T carved without overlap inside the workspace
+    st, calls, qp, kw, vw, P, n_qtiles, _ = map(int, by["prefill_call"][0])
+    ws = ga.prefill_workspace_bytes(cfg, 1000, 3)
+    H, G, D = 48, 8, 128
+    assert st == 0 and calls == 2
+    assert qp == 0 and kw >= 1000 * H * D * 2 and vw - kw >= G * P * D * 2 and vw + G * P * D * 2 <= ws
+    assert kw % 256 == 0 and vw % 256 == 0 and P % 64 == 0 and P >= 1000
+    assert n_qtiles == -(-600 // 256)
+
+    # decode of one sequence at position 2^20 - 1, default split (2048 keys):
+    # Q' then the (max, sum) and accumulator partials of 512 splits
+    st, calls, n_splits, kpw, ml, acc = map(int, by["decode_call"][0])
+    assert st == 0 and calls == 3 and n_splits == 512
+    assert ml == H * D * 2 and acc == ml + -(-(H * n_splits * 2 * 4) // 256) * 256
+    assert acc + H * n_splits * D * 4 <= ga.decode_workspace_bytes(cfg, ga.GLOBAL, 1, 2 ** 20 - 1)
+
+    want = {"kv_bytes_null": E_NULL, "kv_bytes_neg": E_RANGE,
+            "prefill_ws_small": E_WORKSPACE, "decode_noalloc_too_big": E_WORKSPACE,
+            "append_head_dim": E_UNSUPPORTED, "append_null": E_NULL,
+            "append_page": E_UNSUPPORTED, "validate_local": E_RANGE,
+            "visibility_kind": E_RANGE, "router_experts": E_UNSUPPORTED,
+            "out_project_k": E_UNSUPPORTED}
+    got = {what: (int(st), int(msg_len)) for what, st, msg_len in by["status"]}
+    assert {k: v[0] for k, v in got.items()} == want
+    assert all(v[1] > 0 for v in got.values())
+    assert by["threads"] == [["1600"]]
