@@ -328,8 +328,10 @@ beam_status chunk_call(bool verify, uint32_t stages, const beam_attn_config* cfg
     return fail(BEAM_E_WORKSPACE, "prefill workspace needs " + std::to_string(ws.total) + " bytes");
   if (ws.P * beam::D > 0x7fffffff) return fail(BEAM_E_RANGE, "too many tokens in one call (workspace positions x 128 must stay below 2^31)");
   if (!verify) {
-    const int bq = beam::prefill_block_queries(cache->kind);
-    const int64_t blocks = (int64_t)cfg->n_q_heads * n_seqs * ((max_chunk_len + bq - 1) / bq);
+    const int hpg = cfg->n_q_heads / cfg->n_kv_heads;
+    const int bq = beam::prefill_block_queries(cache->kind, hpg);
+    const int64_t blocks = (int64_t)(cfg->n_q_heads / beam::prefill_heads_per_block(cache->kind, hpg)) * n_seqs *
+                           ((max_chunk_len + bq - 1) / bq);
     if (blocks > 0x7fffffffLL) return fail(BEAM_E_RANGE, "prefill grid too large (n_seqs x max_chunk_len)");
   }
   hipStream_t s = (hipStream_t)stream;
@@ -396,7 +398,10 @@ beam_status chunk_call(bool verify, uint32_t stages, const beam_attn_config* cfg
   ap.H = cfg->n_q_heads;
   ap.G = cfg->n_kv_heads;
   ap.n_seqs = n_seqs;
-  ap.n_qtiles = (max_chunk_len + beam::prefill_block_queries(cache->kind) - 1) / beam::prefill_block_queries(cache->kind);
+  {
+    const int bq = beam::prefill_block_queries(cache->kind, cfg->n_q_heads / cfg->n_kv_heads);
+    ap.n_qtiles = (max_chunk_len + bq - 1) / bq;
+  }
   ap.P = (int)ws.P;
   ap.kv_fp8 = cache->dtype == BEAM_KV_FP8_E4M3;
   ap.k_scale = cache->k_scale;

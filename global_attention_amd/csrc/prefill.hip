@@ -8,8 +8,10 @@
 // the parameter label"). The score matrix is never materialised (section "KV
 // memory: nine growing caches, not 52" notes flash-style kernels avoid it).
 //
-// Tiling. A block is NWAVES wavefronts x QW queries of one query head. KV tiles
-// of 64 keys are double-buffered in LDS. Each wave computes
+// Tiling. A block is NWAVES wavefronts x QW queries; on global layers all of
+// one query head, on local layers two query heads of one KV group, each with
+// 64 queries (so the four waves read the same key tiles). KV tiles of 64 keys
+// are double-buffered in LDS. Each wave computes
 // S^T = K Q'^T with v_mfma_f32_32x32x16_bf16 (keys on M, its queries on N), so
 // a lane holds one query column and the row max is an in-lane max plus one
 // v_permlane32_swap. The S accumulators are packed to bf16 and fed directly as
@@ -29,6 +31,10 @@
 // Tiles of the cached prefix are also copied by DMA, each lane addressing its
 // chunk in the paged cache or ring; the prologue has already copied the cached
 // keys of the chunk's first tile into the workspace, so no tile mixes the two.
+//
+// Epilogue. The gate logits of a local block's queries are copied into the
+// LDS slot its last tile leaves free while that tile is computed; every gate
+// value is read before the first output store.
 //
 // Softmax runs in base 2 (Q' carries log2 e / sqrt d and, on global layers,
 // a(t+1)). Each query keeps a reference m (its running max, moved only when
@@ -293,11 +299,14 @@ __device__ __forceinline__ void scale_frags(u32x4 (&qf)[8], float k_scale) {
 }
 
 // ---------------------------------------------------------------- kernel
-template <int KIND, int NWAVES, int KV_FP8>
+// HB query heads (of one KV group) per block; wave w takes head w / (NWAVES /
+// HB) and queries 32 (w % (NWAVES / HB)) .. +31 of the block's query range.
+template <int KIND, int NWAVES, int KV_FP8, int HB>
 __global__ void __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_attn_kernel(PrefillParams p) {
-  constexpr int BM = NWAVES * QW;  // queries per block
-  static_assert(16 % NWAVES == 0, "tile split");
+  constexpr int WQ = NWAVES / HB;  // waves per head
+  constexpr int BM = WQ * QW;      // queries per block
+  static_assert(16 % NWAVES == 0 && NWAVES % HB == 0, "tile split");
   constexpr int TPS = tiles_per_stage<KIND>();
   constexpr int SLOTS = 2 * TPS;  // tile slots: two stages
   __shared__ __attribute__((aligned(1024))) uint16_t smem[SLOTS * (K_TILE + V_TILE)];
@@ -306,11 +315,10 @@ prefill_attn_kernel(PrefillParams p) {
   int b = blockIdx.x;
   const int g = b % p.G;  // consecutive blocks -> consecutive XCDs -> one KV head per XCD
   b /= p.G;
-  const int hh = b % hpg;
-  b /= hpg;
+  const int hh0 = b % (hpg / HB) * HB;
+  b /= hpg / HB;
   const int seq = b % p.n_seqs;
   const int qt = p.n_qtiles - 1 - b / p.n_seqs;  // heaviest query tiles first
-  const int h = g * hpg + hh;
 
   const int cu0 = p.cu[seq];
   const int len = p.cu[seq + 1] - cu0;
@@ -325,10 +333,11 @@ prefill_attn_kernel(PrefillParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (DMA bases go to M0)
   const int n = lane & 31;
   const int half = lane >> 5;
+  const int h = g * hpg + hh0 + w / WQ;  // this wave's query head
 
   const int q0 = start + qt * BM;                   // first query position of the block
   const int qlast = min(q0 + BM, start + len) - 1;  // last valid query position
-  const int wq_lo = q0 + QW * w;
+  const int wq_lo = q0 + QW * (w % WQ);
   const int wq_hi = min(wq_lo + QW - 1, qlast);
   const bool wave_active = wq_lo <= qlast;
 
@@ -593,14 +602,36 @@ prefill_attn_kernel(PrefillParams p) {
     if (!active(j)) return;
     tile(j, B, std::false_type{});
   };
+  // Gate rows of the wave's 32 queries into LDS (local layers): 8 KiB per wave
+  // in the slot the last stage leaves free, so the epilogue's gate reads do
+  // not wait on memory. DMA instruction i moves rows 4i .. 4i+3, 16 bytes per
+  // lane; chunk c of row r lands at chunk position c ^ (r & 15), so the
+  // epilogue's reads of one chunk from 16 consecutive rows hit distinct banks.
+  // Rows past the chunk's end read the last valid row (never used).
+  auto fetch_gate = [&](auto B) __attribute__((always_inline)) {
+    uint16_t* dst = buf(B) + w * (QW * D);
+#pragma unroll
+    for (int i = 0; i < QW * D / 512; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      const int c = (lane & 15) ^ (r & 15);
+      const size_t tok = (size_t)(cu0 + (min(wq_lo + r, qlast) - start));
+      lds_dma16(p.gate + (tok * p.H + h) * D + 8 * c, dst + 512 * i);
+    }
+  };
+  static_assert(!local || (NB == 1 && NWAVES * QW * D <= K_TILE + V_TILE), "gate staging fits one slot");
   // Stage of tiles j0 .. j0+TPS-1 in slots S0 .. S0+TPS-1: before tile j0+u
   // is computed, tile j0+TPS+u is sent to the other stage's slot (freed by the
-  // previous barrier); the barrier then publishes the next stage.
+  // previous barrier); the barrier then publishes the next stage. On local
+  // layers the last stage sends the gate rows instead.
   auto stage = [&](int j0, auto S0) __attribute__((always_inline)) {
     static_for<TPS>([&](auto U) __attribute__((always_inline)) {
       constexpr int u = decltype(U)::value;
       constexpr int s0 = decltype(S0)::value;
-      if (j0 + TPS + u <= j_hi) fetch(j0 + TPS + u, std::integral_constant<int, (s0 + TPS + u) % SLOTS>{});
+      using Next = std::integral_constant<int, (s0 + TPS + u) % SLOTS>;
+      if (j0 + TPS + u <= j_hi)
+        fetch(j0 + TPS + u, Next{});
+      else if constexpr (local)
+        fetch_gate(Next{});
       if (j0 + u <= j_hi) compute_tile(j0 + u, std::integral_constant<int, s0 + u>{});
     });
     __builtin_amdgcn_s_waitcnt(0);
@@ -634,6 +665,8 @@ prefill_attn_kernel(PrefillParams p) {
       j_main = jc + 1;
     }
   }
+  // slot holding the staged gate rows: the one after the last tile's
+  const int gate_slot = (j_hi - j_main + 1) % SLOTS;
   static_for<TPS>([&](auto U) __attribute__((always_inline)) {
     if (j_main + decltype(U)::value <= j_hi) fetch(j_main + decltype(U)::value, U);
   });
@@ -646,7 +679,9 @@ prefill_attn_kernel(PrefillParams p) {
   }
 
   // Epilogue: normalise, gate, write bf16. Lane holds query n of each N-block
-  // and coordinates d = 32db + 8a + 4*half + 0..3.
+  // and coordinates d = 32db + 8a + 4*half + 0..3. Every gate value is read
+  // before the first output store (gate and output are both bf16 rows, so the
+  // compiler would otherwise keep each load behind the previous store).
   const float bias = p.gate_bias ? p.gate_bias[h] : 0.f;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -656,14 +691,28 @@ prefill_attn_kernel(PrefillParams p) {
     // 1 / l, and v_scale over an FP8 cache (code space)
     const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) * (KV_FP8 ? p.v_scale : 1.f) : 0.f;
     const size_t tok = (size_t)(cu0 + (t - start));
-    const uint16_t* grow_ = p.gate + (tok * p.H + h) * D;
     uint16_t* orow = p.out + (tok * p.H + h) * D;
+    u32x2 gvs[4][4];
+    if constexpr (local) {
+      const uint16_t* grow_ = smem + gate_slot * (K_TILE + V_TILE) + w * (QW * D) + n * D + 4 * half;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          gvs[db][a] = *reinterpret_cast<const u32x2*>(grow_ + 8 * ((4 * db + a) ^ (n & 15)));
+    } else {
+      const uint16_t* grow_ = p.gate + (tok * p.H + h) * D + 4 * half;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) gvs[db][a] = *reinterpret_cast<const u32x2*>(grow_ + 32 * db + 8 * a);
+    }
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int d0 = 32 * db + 8 * a + 4 * half;
-        const u32x2 gv = *reinterpret_cast<const u32x2*>(grow_ + d0);
+        const u32x2 gv = gvs[db][a];
         const float gz[4] = {bf16lo(gv[0]), bf16hi(gv[0]), bf16lo(gv[1]), bf16hi(gv[1])};
         float y[4];
 #pragma unroll
@@ -1145,16 +1194,22 @@ hipError_t launch_verify_combine(const VerifyCombineParams& p, hipStream_t s) {
 
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {
   clear_stale_error();
-  const long long blocks = (long long)p.G * (p.H / p.G) * p.n_seqs * p.n_qtiles;
+  const int hpg = p.H / p.G;
+  const int hb = prefill_heads_per_block(p.kind, hpg);
+  const long long blocks = (long long)p.G * (hpg / hb) * p.n_seqs * p.n_qtiles;
   const dim3 grid((unsigned)blocks), local_block(64 * kPrefillWavesLocal), global_block(64 * kPrefillWavesGlobal);
-  if (p.kind == 0 && !p.kv_fp8)
-    hipLaunchKernelGGL((prefill_attn_kernel<0, kPrefillWavesLocal, 0>), grid, local_block, 0, s, p);
+  if (p.kind == 0 && hb == 2 && !p.kv_fp8)
+    hipLaunchKernelGGL((prefill_attn_kernel<0, kPrefillWavesLocal, 0, 2>), grid, local_block, 0, s, p);
+  else if (p.kind == 0 && hb == 2)
+    hipLaunchKernelGGL((prefill_attn_kernel<0, kPrefillWavesLocal, 1, 2>), grid, local_block, 0, s, p);
+  else if (p.kind == 0 && !p.kv_fp8)
+    hipLaunchKernelGGL((prefill_attn_kernel<0, kPrefillWavesLocal, 0, 1>), grid, local_block, 0, s, p);
   else if (p.kind == 0)
-    hipLaunchKernelGGL((prefill_attn_kernel<0, kPrefillWavesLocal, 1>), grid, local_block, 0, s, p);
+    hipLaunchKernelGGL((prefill_attn_kernel<0, kPrefillWavesLocal, 1, 1>), grid, local_block, 0, s, p);
   else if (!p.kv_fp8)
-    hipLaunchKernelGGL((prefill_attn_kernel<1, kPrefillWavesGlobal, 0>), grid, global_block, 0, s, p);
+    hipLaunchKernelGGL((prefill_attn_kernel<1, kPrefillWavesGlobal, 0, 1>), grid, global_block, 0, s, p);
   else
-    hipLaunchKernelGGL((prefill_attn_kernel<1, kPrefillWavesGlobal, 1>), grid, global_block, 0, s, p);
+    hipLaunchKernelGGL((prefill_attn_kernel<1, kPrefillWavesGlobal, 1, 1>), grid, global_block, 0, s, p);
   return hipGetLastError();
 }
 

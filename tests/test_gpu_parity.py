@@ -126,14 +126,14 @@ def test_kv_append_local_ring():
 
 # ----------------------------------------------------------------- prefill
 
-def _run_prefill(kind, inp_list, starts, cache, seq_idx, max_chunk=None):
+def _run_prefill(kind, inp_list, starts, cache, seq_idx, max_chunk=None, cfg=CFG):
     """inp_list: per sequence dict of the chunk's inputs; returns out bits per seq."""
     import torch
     lens = [x["q"].shape[0] for x in inp_list]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     cat = lambda key: np.concatenate([x[key] for x in inp_list])
     w = inp_list[0]
-    out = ga.prefill(CFG, cache, dev_bf16(cat("q")), dev_bf16(cat("k")), dev_bf16(cat("v")),
+    out = ga.prefill(cfg, cache, dev_bf16(cat("q")), dev_bf16(cat("k")), dev_bf16(cat("v")),
                      dev_bf16(w["q_norm_w"]), dev_bf16(w["k_norm_w"]), dev_bf16(cat("gate")),
                      dev_i32(cu), dev_i32(seq_idx), dev_i32(starts), max_chunk or max(lens))
     sync()
@@ -213,6 +213,37 @@ def test_chunked_prefill_with_cached_prefix(kind):
                                 np.arange(s0 + n))
             compare(o, ref, f"chunk seq{sq} [{s0},{s0 + n})")
             pos_done[sq] += n
+
+
+@pytest.mark.parametrize("heads", [(8, 8), (24, 8), (16, 8), (32, 2)])
+@pytest.mark.parametrize("kind", [O.LOCAL, O.GLOBAL])
+def test_prefill_head_layouts(kind, heads):
+    """Other grouped-query layouts: one query head per KV head, an odd number
+    per KV head (local blocks then take one head), two, and sixteen; two
+    sequences in two chunks each, the second chunk unaligned over the cached
+    prefix of the first."""
+    import torch
+    nq, nkv = heads
+    cfg, ocfg = ga.Config(n_q_heads=nq, n_kv_heads=nkv), O.Config(n_q_heads=nq, n_kv_heads=nkv)
+    total = [533, 677]
+    first = [333, 77]
+    inps = [synth.attention_inputs(5, 100 * kind + 10 * nq + i, n, n_q=nq, n_kv=nkv) for i, n in enumerate(total)]
+    inps[1]["q_norm_w"], inps[1]["k_norm_w"] = inps[0]["q_norm_w"], inps[0]["k_norm_w"]
+    if kind == O.GLOBAL:
+        bt, n_pages = synth.paged_block_table(5, total)
+        cache = ga.KVCache.allocate_global(cfg, n_pages, torch.from_numpy(bt), fill=SENT)
+    else:
+        cache = ga.KVCache.allocate_local(cfg, 2, fill=SENT)
+    for step in range(2):
+        starts = [0, 0] if step == 0 else first
+        ends = first if step == 0 else total
+        batch = [{k: (v[s0:e] if v.ndim == 3 else v) for k, v in x.items()} for x, s0, e in zip(inps, starts, ends)]
+        say(f"[case] prefill heads={nq}/{nkv} kind={kind} step={step} starts={starts}")
+        outs = _run_prefill(kind, batch, starts, cache, [0, 1], cfg=cfg)
+        for sq, (x, s0, e, o) in enumerate(zip(inps, starts, ends, outs)):
+            ref = O.attention_layer(kind, x["q"][s0:e], x["k"][:e], x["v"][:e], x["q_norm_w"], x["k_norm_w"],
+                                    x["gate"][s0:e], np.arange(s0, e), np.arange(e), ocfg)
+            compare(o, ref, f"heads {nq}/{nkv} seq{sq} [{s0},{e})")
 
 
 @pytest.mark.parametrize("kind", [O.LOCAL, O.GLOBAL])
