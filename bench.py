@@ -56,15 +56,15 @@ def log(*a):
 
 _CSRC = os.path.join(ROOT, "global_attention_amd", "csrc")
 _KERNEL_SOURCES = {
-    "prefill_attn_kernel<1, 8, 0>": "prefill.hip",
-    "prefill_attn_kernel<0, 4, 0>": "prefill.hip",
+    "prefill_attn_kernel<1, 8, 0, 1>": "prefill.hip",
+    "prefill_attn_kernel<0, 4, 0, 2>": "prefill.hip",
     "decode_split_kernel<1>": "decode.hip",
     "decode_split_kernel<1> (1M)": "decode.hip",
     "decode_split_kernel<0>": "decode.hip",
     "decode_fp8_kernel<1>": "decode.hip",
-    "verify_attn_kernel<1, 0>": "prefill.hip",
-    "verify_attn_kernel<0, 0>": "prefill.hip",
-    "verify_attn_kernel<1, 1>": "prefill.hip",
+    "verify_attn_kernel<1, 0, 4>": "prefill.hip",
+    "verify_attn_kernel<0, 0, 4>": "prefill.hip",
+    "verify_attn_kernel<1, 1, 2>": "prefill.hip",
     "router_gemm_kernel<true>": "router.hip",
     "gemm_bf16_kernel<1>": "gemm.hip",
     "gemm_bf16_kernel<0>": "gemm.hip",
@@ -833,10 +833,10 @@ def main():
         l_ms = r["attn_ms"][0]
         g_flops = FLOP_PER_PAIR * pairs_global(T)
         achieved = g_flops / (g_ms / 1e3) / 1e12
-        rec["roofline"] = {"kernel": "prefill_attn_kernel<1, 8, 0> (global layer)", "bound": "mfma",
+        rec["roofline"] = {"kernel": "prefill_attn_kernel<1, 8, 0, 1> (global layer)", "bound": "mfma",
                            "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                           "traffic": recorded_traffic("prefill_attn_kernel<1, 8, 0>"),
+                           "traffic": recorded_traffic("prefill_attn_kernel<1, 8, 0, 1>"),
                            "avg_launch_ms": round(g_ms, 4), "flop_per_launch": g_flops,
                            **measured(None, achieved, "mfma")}
         l_flops = FLOP_PER_PAIR * pairs_local(T)
@@ -844,10 +844,10 @@ def main():
         rec["prefill_layers"] = {
             "global_attn_ms": round(g_ms, 4), "global_attn_tflops": round(achieved, 2),
             "local_attn_ms": round(l_ms, 4), "local_attn_tflops": round(l_tf, 2),
-            "local_roofline": {"kernel": "prefill_attn_kernel<0, 4, 0> (local layer)", "bound": "mfma",
+            "local_roofline": {"kernel": "prefill_attn_kernel<0, 4, 0, 2> (local layer)", "bound": "mfma",
                                "achieved": round(l_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                "frac": round(l_tf / PEAK_BF16_TFLOPS, 4),
-                               "traffic": recorded_traffic("prefill_attn_kernel<0, 4, 0>"),
+                               "traffic": recorded_traffic("prefill_attn_kernel<0, 4, 0, 2>"),
                                "avg_launch_ms": round(l_ms, 4), "flop_per_launch": l_flops,
                                **measured(None, l_tf, "mfma")}}
         log(f"[bench] prefill step {r['ms_per_step']:.3f} ms -> {rec['value']} TFLOP/s; "
@@ -936,9 +936,9 @@ def main():
             "frac_of_hbm_peak": round(vg["gbs_call"] / PEAK_HBM_GBS, 4),
             "global_bytes": vg["bytes"], "global_ms_per_call": round(vg["ms_per_call"], 4),
             "speedup_vs_8_decode_calls": round(vg["vs_decode_calls"], 2),
-            "roofline": {"kernel": "verify_attn_kernel<1, 0>", "bound": "hbm", "achieved": round(vg["gbs_split"], 1),
+            "roofline": {"kernel": "verify_attn_kernel<1, 0, 4>", "bound": "hbm", "achieved": round(vg["gbs_split"], 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(vg["gbs_split"] / PEAK_HBM_GBS, 4),
-                         "traffic": recorded_traffic("verify_attn_kernel<1, 0>"),
+                         "traffic": recorded_traffic("verify_attn_kernel<1, 0, 4>"),
                          "avg_launch_ms": round(vg["split_ms"], 4), "bytes_per_launch": vg["bytes"],
                          **measured(None, vg["gbs_split"], "hbm")},
             "local": {"ms_per_call": round(v["local"]["ms_per_call"], 4),

@@ -513,24 +513,33 @@ prefill_attn_kernel(PrefillParams p) {
   };
   // Move the reference up by delta: rescale O and l by 2^-delta (nothing to
   // rescale while no key was visible) and shift this tile's scores.
+  // O is still zero at a query's first visible key (alpha 1), so a block's
+  // first reference move skips the O multiply.
   auto rescale = [&](const float (&delta)[NB], const bool (&need)[NB], f32x16 (&s)[NB][2]) {
+    float alpha[NB];
+    bool scale_o = false;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const bool first = m_run[nb] == kNegInf;
-      const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(-delta[nb]);
+      alpha[nb] = first ? 1.f : __builtin_amdgcn_exp2f(-delta[nb]);
+      scale_o = scale_o || alpha[nb] != 1.f;
       if (need[nb]) m_run[nb] = (first ? 0.f : m_run[nb]) + delta[nb];
       const float r = m_run[nb] == kNegInf ? 0.f : -m_run[nb];
 #pragma unroll
       for (int i = 0; i < 16; ++i) sref[nb][i] = r;
-      l_run[nb] *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[nb][db][i] *= alpha;
+      l_run[nb] *= alpha[nb];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[nb][mb][i] -= delta[nb];
+    }
+    if (__any(scale_o)) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[nb][db][i] *= alpha[nb];
     }
   };
   // P^T operand of key block kb: elements 8(kb&1)..+7 of S block kb>>1, i.e.
@@ -682,14 +691,19 @@ prefill_attn_kernel(PrefillParams p) {
   // and coordinates d = 32db + 8a + 4*half + 0..3. Every gate value is read
   // before the first output store (gate and output are both bf16 rows, so the
   // compiler would otherwise keep each load behind the previous store).
-  const float bias = p.gate_bias ? p.gate_bias[h] : 0.f;
+  // Y = O v_scale / (l (1 + 2^z)), z = -(gate + bias) log2 e: the sigmoid and
+  // the normalisation share one reciprocal (v_rcp_f32, 1 ulp; a correctly
+  // rounded division costs ~12 instructions per element, and Y is rounded to
+  // bf16 next). v_scale applies over an FP8 cache (code space). l = 0 (no
+  // visible key, O = 0) gives Y = 0.
+  constexpr float kLog2e = 1.4426950408889634f;
+  const float zb = -(p.gate_bias ? p.gate_bias[h] : 0.f) * kLog2e;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int t = wq_lo + 32 * nb + n;
     const float l_tot = sum_halves(l_run[nb]);
     if (t > qlast) continue;
-    // 1 / l, and v_scale over an FP8 cache (code space)
-    const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) * (KV_FP8 ? p.v_scale : 1.f) : 0.f;
+    const float l_eff = l_tot > 0.f ? (KV_FP8 ? l_tot / p.v_scale : l_tot) : 1.f;
     const size_t tok = (size_t)(cu0 + (t - start));
     uint16_t* orow = p.out + (tok * p.H + h) * D;
     u32x2 gvs[4][4];
@@ -717,10 +731,8 @@ prefill_attn_kernel(PrefillParams p) {
         float y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          // v_rcp_f32 (1 ulp): a correctly rounded division here costs ~12
-          // instructions per element, and the result is rounded to bf16 next
-          const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-(gz[e] + bias)));
-          y[e] = o[nb][db][4 * a + e] * inv * sg;
+          const float ex = __builtin_amdgcn_exp2f(fmaf(gz[e], -kLog2e, zb));
+          y[e] = o[nb][db][4 * a + e] * __builtin_amdgcn_rcpf(fmaf(ex, l_eff, l_eff));
         }
         *reinterpret_cast<u32x2*>(orow + d0) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
       }
