@@ -259,7 +259,7 @@ def bench_decode(steps, warmup):
     return res
 
 
-def bench_decode_1m(steps, warmup):
+def bench_decode_1m(steps, warmup, cpu_sample=False):
     """One sequence at t = 1,048,575 on a global layer: 65,536 pages (4 GiB of
     bf16 K+V, far beyond the 256 MB MALL) dealt by a random permutation; the
     split-key decode with its prologue and combine, timed as in bench_decode."""
@@ -309,9 +309,14 @@ def bench_decode_1m(steps, warmup):
     split_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
     nbytes = T * G * D * 2 * 2
     log(f"[bench] decode 1M: {nbytes / 2 ** 30:.0f} GiB, call {call_ms:.3f} ms, split kernel {split_ms:.3f} ms")
+    res = dict(bytes=nbytes, ms_per_call=call_ms, split_ms=split_ms, gbs_call=nbytes / (call_ms / 1e3) / 1e9,
+               gbs_split=nbytes / (split_ms / 1e3) / 1e9)
+    if cpu_sample:
+        log("[bench] timing the CPU oracle on the 1M decode, KV head 0")
+        res["cpu_sample"] = cpu_decode_sample(cache, T - 1, inp, 0, [0],
+                                              "the 1M-token sequence (t = 1,048,575), KV head 0 and its 6 query heads")
     del cache
-    return dict(bytes=nbytes, ms_per_call=call_ms, split_ms=split_ms, gbs_call=nbytes / (call_ms / 1e3) / 1e9,
-                gbs_split=nbytes / (split_ms / 1e3) / 1e9)
+    return res
 
 
 def bench_verify(steps, warmup, dres, block=8, split_keys=0):
@@ -529,6 +534,47 @@ def cpu_baseline(layers, T, rows):
                 sample=f"float64 NumPy oracle on the last {rows} query rows (all 48 heads) of the T=32768 "
                        f"local and global layers, full key history, incl. K normalisation; "
                        f"{flops / 1e9:.1f} GFLOP in {el:.1f} s")
+
+
+def cpu_decode_sample(cache, t, inp, sq, heads_kv, what):
+    """Time the float64 oracle for one decode row (sequence sq at position t,
+    global layer) over its cached history, KV heads `heads_kv` and their
+    query heads: q normalisation and SSMax scale, exact softmax over all t+1
+    keys, PV, gate. The cache contents are gathered to the host first
+    (untimed); the bf16-to-float64 widening of K/V is timed, as in the prefill
+    sample. Rate: bytes of bf16 K+V the oracle processed per second."""
+    import numpy as np
+    import torch
+    import oracle as O
+    n_keys = t + 1
+    n_pg = (n_keys + 15) // 16
+    bt_row = cache.block_table[sq].cpu().numpy()
+    idx = torch.from_numpy(np.ascontiguousarray(bt_row[:n_pg]).astype(np.int64)).cuda()
+    hs = torch.tensor(heads_kv, device="cuda")
+    k = cache.k.index_select(0, idx).index_select(1, hs).permute(0, 2, 1, 3).reshape(n_pg * 16, len(heads_kv), D)
+    v = cache.v.index_select(0, idx).index_select(1, hs).permute(0, 3, 1, 2).reshape(n_pg * 16, len(heads_kv), D)
+    kb = k[:n_keys].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    vb = v[:n_keys].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    del k, v
+    hpg = H // G
+    ocfg = O.Config()
+    t0 = time.perf_counter()
+    qn = O.rms_norm(O.bf16_to_f64(inp["q"][sq])[None], O.bf16_to_f64(inp["q_norm_w"]), ocfg.rms_eps)
+    qp, _ = O.position_op(O.GLOBAL, qn, qn, np.array([t]), np.array([t]), ocfg)
+    key_pos = np.arange(n_keys)
+    for i, g in enumerate(heads_kv):
+        hq = list(range(hpg * g, hpg * g + hpg))
+        o = O.attend(O.GLOBAL, qp[:, hq], O.bf16_to_f64(kb[:, i:i + 1]), O.bf16_to_f64(vb[:, i:i + 1]),
+                     np.array([t]), key_pos, O.Config(n_q_heads=hpg, n_kv_heads=1))
+        O.output_gate(o, O.bf16_to_f64(inp["gate"][sq])[None][:, hq])
+    el = time.perf_counter() - t0
+    nbytes = n_keys * len(heads_kv) * D * 2 * 2
+    facts = cpu_facts()
+    return dict(value=round(nbytes / el / 1e9, 3), unit="GB/s", seconds=round(el, 2), kind="oracle",
+                cores=facts["blas_threads"], host_cpu_count=facts["cpu_count"], host_affinity=facts["affinity"],
+                blas_threads=facts["blas_threads"], workers=1,
+                sample=f"float64 NumPy oracle, {what}: {n_keys} keys x {len(heads_kv)} KV head(s) "
+                       f"({nbytes / 1e9:.2f} GB of bf16 K+V) in {el:.1f} s")
 
 
 def cpu_facts():
@@ -947,10 +993,21 @@ def main():
                            "gbs_split": round(v["global_fp8"]["gbs_split"], 1),
                            "speedup_vs_8_decode_calls": round(v["global_fp8"]["vs_decode_calls"], 2)},
         }
+        if not args.no_cpu_baseline:
+            import numpy as np
+            import synth
+            cfg_d, ts_d, gcache_d = dres["setup"][:3]
+            inp_d = synth.attention_inputs(cfg=3, layer=7, n_tok=len(ts_d))
+            sq = int(np.argmax(ts_d))
+            log(f"[bench] timing the CPU oracle on decode sequence {sq} (t = {int(ts_d[sq])}), all KV heads")
+            cs = cpu_decode_sample(gcache_d, int(ts_d[sq]), inp_d, sq, list(range(G)),
+                                   f"the longest of the 64 sequences (t = {int(ts_d[sq])}), all 48 query heads")
+            cs["gpu_over_oracle"] = round(g["gbs_call"] / cs["value"], 1)
+            rec["decode"]["cpu_sample"] = cs
         del dres, v
         torch.cuda.empty_cache()
     if not args.skip_decode_1m and not (args.skip_decode and not args.decode_1m_only):
-        m = bench_decode_1m(args.decode_steps, 5)
+        m = bench_decode_1m(args.decode_steps, 5, cpu_sample=not args.no_cpu_baseline)
         rec["decode_1m"] = {
             "workload": "one sequence at position 1,048,575 on a global layer: 65,536 permuted 16-token pages, "
                         "4 GiB of bf16 K+V",
@@ -963,6 +1020,9 @@ def main():
                          "avg_launch_ms": round(m["split_ms"], 4), "bytes_per_launch": m["bytes"],
                          **measured(None, m["gbs_split"], "hbm")},
         }
+        if "cpu_sample" in m:
+            m["cpu_sample"]["gpu_over_oracle"] = round(m["gbs_call"] / m["cpu_sample"]["value"], 1)
+            rec["decode_1m"]["cpu_sample"] = m["cpu_sample"]
     if not args.skip_router:
         rr = bench_router(T, args.steps, args.warmup)
         tf = rr["flops"] / (rr["ms"] / 1e3) / 1e12
