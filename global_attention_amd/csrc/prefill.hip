@@ -122,6 +122,11 @@ struct KeySource {
 __device__ __forceinline__ void lds_dma16(const uint16_t* src, uint16_t* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
+// The same with the non-temporal hint (cache policy nt): for cached K/V that
+// one block reads once (verify splits), not for tiles many blocks share.
+__device__ __forceinline__ void lds_dma16_nt(const uint16_t* src, uint16_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 2);
+}
 
 // Element offsets (relative to the tile's first key in the workspace) of the
 // chunks this lane moves with each of its DMA instructions, and the LDS
@@ -231,8 +236,8 @@ __device__ __forceinline__ CodeSource make_code_source(const PrefillParams& p, i
 
 // DMA of the code tile whose first key is key0 (a multiple of 64): 8 K and 8
 // V instructions of 1 KiB, 8 / NW of each per wave. page(i) is the physical
-// page of logical page i (paged caches).
-template <int NW, typename PageOf>
+// page of logical page i (paged caches). NT: non-temporal hint.
+template <int NW, bool NT = false, typename PageOf>
 __device__ __forceinline__ void dma_code_tile(const CodeSource& c, PageOf page, int w, int lane, int key0,
                                               uint8_t* slot) {
   // every source address first (the page lookups together), then the DMAs
@@ -259,8 +264,17 @@ __device__ __forceinline__ void dma_code_tile(const CodeSource& c, PageOf page, 
 #pragma unroll
   for (int i = 0; i < 8 / NW; ++i) {
     const int ins = w * (8 / NW) + i;
-    lds_dma16(reinterpret_cast<const uint16_t*>(ksrc[i]), reinterpret_cast<uint16_t*>(slot + 1024 * ins));
-    lds_dma16(reinterpret_cast<const uint16_t*>(vsrc[i]), reinterpret_cast<uint16_t*>(slot + kCodeVOff + 1024 * ins));
+    const uint16_t* ks = reinterpret_cast<const uint16_t*>(ksrc[i]);
+    const uint16_t* vs = reinterpret_cast<const uint16_t*>(vsrc[i]);
+    uint16_t* kd = reinterpret_cast<uint16_t*>(slot + 1024 * ins);
+    uint16_t* vd = reinterpret_cast<uint16_t*>(slot + kCodeVOff + 1024 * ins);
+    if constexpr (NT) {
+      lds_dma16_nt(ks, kd);
+      lds_dma16_nt(vs, vd);
+    } else {
+      lds_dma16(ks, kd);
+      lds_dma16(vs, vd);
+    }
   }
 }
 
@@ -767,7 +781,8 @@ __device__ __forceinline__ const uint16_t* v_elem_cached(const KeySource& ks, co
   return ks.cv + (uint32_t)(d * ks.window + s % ks.window);
 }
 
-// DMA of a cached-prefix tile; the same chunks and LDS positions as
+// DMA of a cached-prefix tile (non-temporal: a split reads its keys once);
+// the same chunks and LDS positions as
 // dma_tile_prefix (16 / NW instructions each for K and V per wave).
 template <int NW>
 __device__ __forceinline__ void dma_tile_cached(const KeySource& ks, const int* pages, int page0, int w, int lane,
@@ -789,8 +804,8 @@ __device__ __forceinline__ void dma_tile_cached(const KeySource& ks, const int* 
 #pragma unroll
   for (int i = 0; i < DmaPlan<NW>::N; ++i) {
     const int kI = w * DmaPlan<NW>::N + i;
-    lds_dma16(ksrc[i], sK + kI * 512);
-    lds_dma16(vsrc[i], sV + kI * 512);
+    lds_dma16_nt(ksrc[i], sK + kI * 512);
+    lds_dma16_nt(vsrc[i], sV + kI * 512);
   }
 }
 
@@ -1007,7 +1022,7 @@ verify_attn_kernel(PrefillParams p) {
     if (j >= j_ws)
       plan.copy(ks.kw, ks.vw, ks.ws_off, j * BN, sK, sK + K_TILE);
     else if constexpr (KV_FP8)
-      dma_code_tile<NWAVES>(cs8, [&](int pg) { return s_pages[pg - page0]; }, w, lane, j * BN,
+      dma_code_tile<NWAVES, true>(cs8, [&](int pg) { return s_pages[pg - page0]; }, w, lane, j * BN,
                             reinterpret_cast<uint8_t*>(sK));
     else
       dma_tile_cached<NWAVES>(ks, s_pages, page0, w, lane, j * BN, sK, sK + K_TILE);
@@ -1054,7 +1069,7 @@ verify_attn_kernel(PrefillParams p) {
     if (j_lo <= jc) {
       auto sub = [&](auto U) { return reinterpret_cast<uint8_t*>(smem) + 16384 * decltype(U)::value; };
       auto dma_c = [&](int j, auto U) __attribute__((always_inline)) {
-        dma_code_tile<NWAVES>(cs8, [&](int pg) { return s_pages[pg - page0]; }, w, lane, j * BN, sub(U));
+        dma_code_tile<NWAVES, true>(cs8, [&](int pg) { return s_pages[pg - page0]; }, w, lane, j * BN, sub(U));
       };
       // wait until tile j + 1 has landed (the tiles after it may stay in flight)
       auto wait_next = [&](int j) __attribute__((always_inline)) {
