@@ -134,16 +134,20 @@ __global__ void __launch_bounds__(256, 2) decode_split_kernel(DecodeParams p) {
       const int kg = kb + 16 * X;
       if (kg < k1) {
         const uint16_t* kp = kbase(kg) + nn * D + 8 * q;
-        // non-temporal: every cached byte is read once per call (measured 4-7 %
-        // faster on bf16 caches; the FP8 kernel's loads stay plain: slower there)
+        // global layers: non-temporal, every cached byte is read once per call
+        // (measured 4-7 % faster on bf16 caches; the FP8 kernel's loads stay
+        // plain: slower there). A local layer's rings (window-sized) are left
+        // to the caches.
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-          st.k[X][kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 32 * kk));
+          st.k[X][kk] = local ? *reinterpret_cast<const u32x4*>(kp + 32 * kk)
+                              : __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 32 * kk));
         int ds;
         const uint16_t* vp = vbase(kg, &ds) + 4 * q;
 #pragma unroll
         for (int db = 0; db < 8; ++db)
-          st.v[X][db] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vp + (size_t)(16 * db + nn) * ds));
+          st.v[X][db] = local ? *reinterpret_cast<const u32x2*>(vp + (size_t)(16 * db + nn) * ds)
+                              : __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vp + (size_t)(16 * db + nn) * ds));
       } else {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) st.k[X][kk] = u32x4{0u, 0u, 0u, 0u};

@@ -122,8 +122,9 @@ struct KeySource {
 __device__ __forceinline__ void lds_dma16(const uint16_t* src, uint16_t* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
-// The same with the non-temporal hint (cache policy nt): for cached K/V that
-// one block reads once (verify splits), not for tiles many blocks share.
+// The same with the non-temporal hint (cache policy nt): for a paged cache's
+// K/V that one block reads once (verify splits), not for tiles many blocks
+// share or a local layer's window-sized rings.
 __device__ __forceinline__ void lds_dma16_nt(const uint16_t* src, uint16_t* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 2);
 }
@@ -781,10 +782,10 @@ __device__ __forceinline__ const uint16_t* v_elem_cached(const KeySource& ks, co
   return ks.cv + (uint32_t)(d * ks.window + s % ks.window);
 }
 
-// DMA of a cached-prefix tile (non-temporal: a split reads its keys once);
-// the same chunks and LDS positions as
-// dma_tile_prefix (16 / NW instructions each for K and V per wave).
-template <int NW>
+// DMA of a cached-prefix tile; the same chunks and LDS positions as
+// dma_tile_prefix (16 / NW instructions each for K and V per wave). NT:
+// non-temporal hint (a verify split of a paged cache reads its keys once).
+template <int NW, bool NT>
 __device__ __forceinline__ void dma_tile_cached(const KeySource& ks, const int* pages, int page0, int w, int lane,
                                                 int key0, uint16_t* sK, uint16_t* sV) {
   // every source address first (the page lookups together), then the DMAs
@@ -804,8 +805,13 @@ __device__ __forceinline__ void dma_tile_cached(const KeySource& ks, const int* 
 #pragma unroll
   for (int i = 0; i < DmaPlan<NW>::N; ++i) {
     const int kI = w * DmaPlan<NW>::N + i;
-    lds_dma16_nt(ksrc[i], sK + kI * 512);
-    lds_dma16_nt(vsrc[i], sV + kI * 512);
+    if constexpr (NT) {
+      lds_dma16_nt(ksrc[i], sK + kI * 512);
+      lds_dma16_nt(vsrc[i], sV + kI * 512);
+    } else {
+      lds_dma16(ksrc[i], sK + kI * 512);
+      lds_dma16(vsrc[i], sV + kI * 512);
+    }
   }
 }
 
@@ -1022,10 +1028,10 @@ verify_attn_kernel(PrefillParams p) {
     if (j >= j_ws)
       plan.copy(ks.kw, ks.vw, ks.ws_off, j * BN, sK, sK + K_TILE);
     else if constexpr (KV_FP8)
-      dma_code_tile<NWAVES, true>(cs8, [&](int pg) { return s_pages[pg - page0]; }, w, lane, j * BN,
+      dma_code_tile<NWAVES, KIND == 1>(cs8, [&](int pg) { return s_pages[pg - page0]; }, w, lane, j * BN,
                             reinterpret_cast<uint8_t*>(sK));
     else
-      dma_tile_cached<NWAVES>(ks, s_pages, page0, w, lane, j * BN, sK, sK + K_TILE);
+      dma_tile_cached<NWAVES, KIND == 1>(ks, s_pages, page0, w, lane, j * BN, sK, sK + K_TILE);
   };
   // Each step ends with an explicit wait for its DMA and a bare s_barrier:
   // the workgroup fence of __syncthreads would also wait for loads the
@@ -1069,7 +1075,7 @@ verify_attn_kernel(PrefillParams p) {
     if (j_lo <= jc) {
       auto sub = [&](auto U) { return reinterpret_cast<uint8_t*>(smem) + 16384 * decltype(U)::value; };
       auto dma_c = [&](int j, auto U) __attribute__((always_inline)) {
-        dma_code_tile<NWAVES, true>(cs8, [&](int pg) { return s_pages[pg - page0]; }, w, lane, j * BN, sub(U));
+        dma_code_tile<NWAVES, KIND == 1>(cs8, [&](int pg) { return s_pages[pg - page0]; }, w, lane, j * BN, sub(U));
       };
       // wait until tile j + 1 has landed (the tiles after it may stay in flight)
       auto wait_next = [&](int j) __attribute__((always_inline)) {
