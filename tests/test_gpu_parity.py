@@ -246,6 +246,51 @@ def test_prefill_head_layouts(kind, heads):
             compare(o, ref, f"heads {nq}/{nkv} seq{sq} [{s0},{e})")
 
 
+@pytest.mark.parametrize("heads", [(8, 8), (24, 8), (16, 8), (32, 2)])
+@pytest.mark.parametrize("kind", [O.LOCAL, O.GLOBAL])
+def test_verify_and_decode_head_layouts(kind, heads):
+    """The same grouped-query layouts on the verify and decode paths: two
+    sequences with a prefilled history (900 and 300 tokens), a 5-token verify
+    chunk each, then a one-token decode (its K/V appended first)."""
+    import torch
+    nq, nkv = heads
+    cfg, ocfg = ga.Config(n_q_heads=nq, n_kv_heads=nkv), O.Config(n_q_heads=nq, n_kv_heads=nkv)
+    hist = [900, 300]
+    total = [h + 6 for h in hist]
+    inps = [synth.attention_inputs(7, 100 * kind + 10 * nq + i, n, n_q=nq, n_kv=nkv) for i, n in enumerate(total)]
+    inps[1]["q_norm_w"], inps[1]["k_norm_w"] = inps[0]["q_norm_w"], inps[0]["k_norm_w"]
+    qw, kw = inps[0]["q_norm_w"], inps[0]["k_norm_w"]
+    if kind == O.GLOBAL:
+        bt, n_pages = synth.paged_block_table(7, total)
+        cache = ga.KVCache.allocate_global(cfg, n_pages, torch.from_numpy(bt), fill=SENT)
+    else:
+        cache = ga.KVCache.allocate_local(cfg, 2, fill=SENT)
+    say(f"[case] verify/decode heads={nq}/{nkv} kind={kind}")
+    _run_prefill(kind, [{k: (v[:h] if v.ndim == 3 else v) for k, v in x.items()} for x, h in zip(inps, hist)],
+                 [0, 0], cache, [0, 1], cfg=cfg)
+    cat = lambda key, lo, hi: dev_bf16(np.concatenate([x[key][l:h] for x, l, h in zip(inps, lo, hi)]))
+    lo, hi = hist, [h + 5 for h in hist]
+    out = ga.verify(cfg, cache, cat("q", lo, hi), cat("k", lo, hi), cat("v", lo, hi), dev_bf16(qw), dev_bf16(kw),
+                    cat("gate", lo, hi), dev_i32([0, 5, 10]), dev_i32([0, 1]), dev_i32(hist), 5, max(hi) - 1)
+    sync()
+    o = host_bits(out)
+    for i, x in enumerate(inps):
+        ref = O.attention_layer(kind, x["q"][lo[i]:hi[i]], x["k"][:hi[i]], x["v"][:hi[i]], qw, kw,
+                                x["gate"][lo[i]:hi[i]], np.arange(lo[i], hi[i]), np.arange(hi[i]), ocfg)
+        compare(o[5 * i:5 * i + 5], ref, f"verify heads {nq}/{nkv} seq{i}")
+    ts = hi
+    ga.kv_append(cfg, cache, cat("k", ts, total), cat("v", ts, total), dev_bf16(kw), dev_i32([0, 1]), dev_i32(ts))
+    out = ga.decode(cfg, cache, cat("q", ts, total), dev_bf16(qw), cat("gate", ts, total), dev_i32([0, 1]),
+                    dev_i32(ts), max(ts))
+    sync()
+    o = host_bits(out)
+    for i, x in enumerate(inps):
+        t = ts[i]
+        ref = O.attention_layer(kind, x["q"][t:t + 1], x["k"][:t + 1], x["v"][:t + 1], qw, kw, x["gate"][t:t + 1],
+                                np.array([t]), np.arange(t + 1), ocfg)
+        compare(o[i:i + 1], ref, f"decode heads {nq}/{nkv} seq{i}")
+
+
 @pytest.mark.parametrize("kind", [O.LOCAL, O.GLOBAL])
 def test_prefill_stage_orders_bit_identical(kind):
     """The stage splits of a prefill call (including the global layers' fused
