@@ -109,6 +109,9 @@ struct PrefillParams {
   float* part_ml;   // [n_tok][H][n_splits][2] (reference max, sum) in base-2 logits
   float* part_acc;  // [n_tok][H][n_splits][D]
   int split_tiles, n_splits;
+  // Verify with a single split: the split kernel writes the gated output
+  // itself; a sequence whose chunk ends past max_pos gets NaN rows.
+  int max_pos;
 };
 
 // Verify attention: a block takes one (sequence, KV head, key split) and packs

@@ -849,7 +849,18 @@ verify_attn_kernel(PrefillParams p) {
   const int cseq = p.seq_idx[seq];
   const int W = p.window;
   const int t_last = start + len - 1;
-  if (start < 0) return;  // the combine writes NaN for this sequence
+  if (start < 0 || (p.n_splits == 1 && t_last > p.max_pos)) {
+    // The sequence's keys lie outside the split grid: its rows are NaN (with
+    // several splits the combine writes them).
+    if (p.n_splits == 1) {
+      const int hpg_ = p.H / p.G, g_ = blockIdx.x % p.G;
+      for (int i = threadIdx.x; i < len * hpg_ * D; i += 64 * NWAVES) {
+        const int r = i / D;
+        p.out[((size_t)(cu0 + r / hpg_) * p.H + g_ * hpg_ + r % hpg_) * D + i % D] = 0x7fc0;
+      }
+    }
+    return;
+  }
 
   KeySource ks;
   ks.kw = p.kw + (size_t)g * p.P * D;
@@ -1141,6 +1152,35 @@ verify_attn_kernel(PrefillParams p) {
   // d = 32db + 8a + 4*half + 0..3.
   const float l_tot = sum_halves(l_run);
   if (!row_valid) return;
+  if (p.n_splits == 1) {
+    // A single split needs no merge: the gated output directly, with the
+    // combine's arithmetic (so either path gives the same bits).
+    const size_t idx = ((size_t)(cu0 + tok_j) * p.H + h) * D + 4 * half;
+    const float bias = p.gate_bias ? p.gate_bias[h] : 0.f;
+    const float inv = (m_run != kNegInf && l_tot > 0.f) ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
+    const float vs = KV_FP8 ? p.v_scale : 1.f;
+    u32x2 gv[4][4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) gv[db][a] = *reinterpret_cast<const u32x2*>(p.gate + idx + 32 * db + 8 * a);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const float gz[4] = {bf16lo(gv[db][a][0]), bf16hi(gv[db][a][0]), bf16lo(gv[db][a][1]), bf16hi(gv[db][a][1])};
+        uint16_t y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ov = o[db][4 * a + e] * inv * vs;
+          const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-(gz[e] + bias)));
+          y[e] = __builtin_bit_cast(uint16_t, (__bf16)(ov * sg));
+        }
+        *reinterpret_cast<u32x2*>(p.out + idx + 32 * db + 8 * a) =
+            u32x2{(uint32_t)y[0] | ((uint32_t)y[1] << 16), (uint32_t)y[2] | ((uint32_t)y[3] << 16)};
+      }
+    return;
+  }
   const size_t row = ((size_t)(cu0 + tok_j) * p.H + h) * p.n_splits + sp;
   if (half == 0) {
     p.part_ml[2 * row] = m_run;

@@ -156,7 +156,8 @@ beam_status beam_attn_prefill(const beam_attn_config *cfg, const beam_kv_cache *
  * max_pos >= every pos[i] (sizes the split grid). A sequence whose pos[i] lies
  * outside [0, max_pos], or whose seq_idx[i] names no cache sequence, is not read
  * and its output rows are NaN.
- * split_keys: keys per split (multiple of 128, <= 65536), or 0 for the default.
+ * split_keys: keys per split (multiple of 128, <= 65536), or 0 for the default
+ * (2048 on GLOBAL layers, 128 on LOCAL layers).
  * workspace: >= beam_decode_workspace_bytes(cfg, kind, n_seqs, max_pos, split_keys). */
 beam_status beam_attn_decode(const beam_attn_config *cfg, const beam_kv_cache *cache,
                              const beam_bf16 *q_raw, const beam_bf16 *q_norm_w,
@@ -199,7 +200,9 @@ beam_status beam_attn_decode_noalloc(const beam_attn_config *cfg, const beam_kv_
  * max_pos >= start_pos[i] + chunk length - 1 for every i (sizes the split grid).
  * A sequence that breaks this (or has start_pos[i] < 0) gets NaN output rows:
  * the split grid does not cover its keys. split_keys: keys per split (multiple of 64, <= 8192), or 0 for the
- * default: 256 local; global the longest of 8192 and 4096 keys for which
+ * default: local one split over the keys a chunk can see (64 * ((window - 1 +
+ * max_chunk_len - 1) / 64 + 2) keys) when n_seqs * n_kv_heads >= 256, else 256;
+ * global the longest of 8192 and 4096 keys for which
  * n_seqs * n_kv_heads * (max_pos / keys + 1) >= 1024, else 2048.
  * Rejected draft tokens: on a GLOBAL cache the next call simply starts at the
  * first rejected position (its slots are overwritten). A LOCAL ring keeps only
@@ -233,7 +236,10 @@ beam_status beam_attn_verify(const beam_attn_config *cfg, const beam_kv_cache *c
  *            COMBINE = merge of the splits + gate into `out`.
  *   verify:  PROLOGUE, APPEND as prefill; ATTENTION = split-key partials,
  *            VERIFY_COMBINE = merge of the splits + gate into `out` (order:
- *            PROLOGUE, ATTENTION, VERIFY_COMBINE, APPEND; ALL = VERIFY_ALL). */
+ *            PROLOGUE, ATTENTION, VERIFY_COMBINE, APPEND; ALL = VERIFY_ALL).
+ *            With a single key split (beam_verify_workspace_bytes' grid; the
+ *            default on LOCAL layers) ATTENTION writes the gated `out` itself
+ *            and VERIFY_COMBINE does nothing. */
 #define BEAM_STAGE_PROLOGUE 1u
 #define BEAM_STAGE_ATTENTION 2u
 #define BEAM_STAGE_APPEND 4u

@@ -153,10 +153,16 @@ def test_verify_workspace_and_checks():
         explicit = next((k for k in (8192, 4096) if 64 * (max_pos // k + 1) >= 1024), 2048)
         assert ga.verify_workspace_bytes(cfg, ga.GLOBAL, 64, 8, 8, max_pos) == \
             ga.verify_workspace_bytes(cfg, ga.GLOBAL, 64, 8, 8, max_pos, split_keys=explicit)
-    # local: the window bounds the keys (511 + 7 positions span at most 10 tiles -> 3 splits of 4)
+    # local: the window bounds the keys (511 + 7 positions span at most 10 tiles); 8 sequences x 8 KV
+    # heads (64 blocks) -> 256-key splits, 3 of them; 32 sequences (256 blocks) -> one split of 640 keys
     rows = 64 * 48 * 3
     want = base + ((rows * 8 + 255) // 256) * 256 + ((rows * 512 + 255) // 256) * 256
     assert ga.verify_workspace_bytes(cfg, ga.LOCAL, 64, 8, 8, 131071) == want
+    base32 = ga.prefill_workspace_bytes(cfg, 256, 32)
+    rows = 256 * 48 * 1
+    want = base32 + ((rows * 8 + 255) // 256) * 256 + ((rows * 512 + 255) // 256) * 256
+    assert ga.verify_workspace_bytes(cfg, ga.LOCAL, 256, 32, 8, 131071) == want
+    assert want == ga.verify_workspace_bytes(cfg, ga.LOCAL, 256, 32, 8, 131071, split_keys=640)
     assert ga.verify_workspace_bytes(cfg, ga.GLOBAL, 64, 8, 8, 1000, split_keys=96) == 0
     assert ga.verify_workspace_bytes(cfg, ga.GLOBAL, 64, 8, 8, 1000, split_keys=64) > 0
     assert ga.verify_workspace_bytes(cfg, ga.GLOBAL, 64, 8, 8, 1000, split_keys=8192) > 0

@@ -124,9 +124,12 @@ def test_decode_nan_rows_for_missing_cache_sequence(kind):
         compare(o[i:i + 1], ref, f"decode kind={kind} row {i}")
 
 
-def test_verify_nan_rows_past_max_pos():
+@pytest.mark.parametrize("split_keys", [0, 64], ids=["one_split", "four_splits"])
+def test_verify_nan_rows_past_max_pos(split_keys):
     """Verify: a sequence whose chunk ends past max_pos gets NaN rows; the
-    other sequence of the call still matches the oracle."""
+    other sequence of the call still matches the oracle. With one key split
+    (the default here) the split kernel writes the rows itself; with 64-key
+    splits the combine does."""
     import torch
     kind = O.GLOBAL
     hist_len, chunk = [200, 300], [6, 6]
@@ -145,7 +148,7 @@ def test_verify_nan_rows_past_max_pos():
     max_pos = 205  # covers sequence 0 (ends at 205), not sequence 1 (ends at 305)
     say("[case] verify NaN rows past max_pos")
     out = ga.verify(CFG, cache, cat("q"), cat("k"), cat("v"), dev_bf16(w["q_norm_w"]), dev_bf16(w["k_norm_w"]),
-                    cat("gate"), dev_i32(cu), dev_i32([0, 1]), dev_i32(hist_len), 6, max_pos,
+                    cat("gate"), dev_i32(cu), dev_i32([0, 1]), dev_i32(hist_len), 6, max_pos, split_keys=split_keys,
                     stages=ga.STAGE_PROLOGUE | ga.STAGE_ATTENTION | ga.STAGE_VERIFY_COMBINE)
     sync()
     o = host_bits(out)
