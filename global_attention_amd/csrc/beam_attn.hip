@@ -50,7 +50,7 @@ beam_status check_cfg(const beam_attn_config* c) {
     return fail(BEAM_E_SHAPE, "n_q_heads must be a multiple of n_kv_heads");
   if (c->n_q_heads / c->n_kv_heads > 16)
     return fail(BEAM_E_UNSUPPORTED, "at most 16 query heads per KV head");
-  if (c->n_kv_heads > 8) return fail(BEAM_E_UNSUPPORTED, "at most 8 KV heads");
+  if (c->n_kv_heads > beam::kMaxKvHeads) return fail(BEAM_E_UNSUPPORTED, "at most 8 KV heads");
   if (c->window <= 0 || c->window % 64 != 0)
     return fail(BEAM_E_UNSUPPORTED, "window must be a positive multiple of 64");
   if (!(c->rms_eps >= 0.f) || !(c->ssmax_base > 0.f) || !(c->rope_theta > 0.f))

@@ -8,6 +8,10 @@
 
 namespace beam {
 
+// Largest supported number of KV heads (the append keeps one head's K/V per
+// register slot).
+constexpr int kMaxKvHeads = 8;
+
 struct PrologueParams {
   const uint16_t* q_raw;
   const uint16_t* k_raw;

@@ -355,8 +355,25 @@ __global__ void __launch_bounds__(256) kv_append_kernel(AppendParams p) {
   const u32x2* kwgt = reinterpret_cast<const u32x2*>(p.k_norm_w);
   const u32x2 w_lo = kwgt[j], w_hi = kwgt[16 + j];
 
-  for (int g = 0; g < p.G; ++g) {
-    const u32x2* src = reinterpret_cast<const u32x2*>(p.k_raw + ((size_t)tok * p.G + g) * D);
+  // Every head's K and V first, then the stores: raw K/V and the cache are all
+  // bf16 rows, so the compiler would otherwise keep each head's loads behind
+  // the previous head's stores (one memory round trip per head).
+  u32x2 kl[kMaxKvHeads], kh[kMaxKvHeads], vl[kMaxKvHeads], vh[kMaxKvHeads];
+#pragma unroll
+  for (int g = 0; g < kMaxKvHeads; ++g) {
+    if (g >= p.G) break;
+    const u32x2* ks = reinterpret_cast<const u32x2*>(p.k_raw + ((size_t)tok * p.G + g) * D);
+    const u32x2* vs = reinterpret_cast<const u32x2*>(p.v_raw + ((size_t)tok * p.G + g) * D);
+    kl[g] = ks[j];
+    kh[g] = ks[16 + j];
+    vl[g] = vs[j];       // V coordinates 4j .. 4j+3
+    vh[g] = vs[16 + j];  // 64 + 4j .. 64 + 4j+3
+  }
+  const int page = local ? 0 : p.bt[(size_t)cseq * p.max_pages + (t >> 4)];
+
+#pragma unroll
+  for (int g = 0; g < kMaxKvHeads; ++g) {
+    if (g >= p.G) break;
     size_t krow;  // element offset of the K_hat row
     size_t vcol;  // element offset of V^T element [0][slot]; coordinate d is at vcol + d * vstride
     int vstride;
@@ -367,34 +384,36 @@ __global__ void __launch_bounds__(256) kv_append_kernel(AppendParams p) {
       vcol = base * D * p.window + slot;
       vstride = p.window;
     } else {
-      int page = p.bt[(size_t)cseq * p.max_pages + (t >> 4)];
       size_t base = (size_t)page * p.G + g;
       krow = (base * 16 + (t & 15)) * D;
       vcol = base * D * 16 + (t & 15);
       vstride = 16;
     }
-    const uint16_t* vsrc = p.v_raw + ((size_t)tok * p.G + g) * D;
+    const uint16_t vlo[4] = {(uint16_t)vl[g][0], (uint16_t)(vl[g][0] >> 16), (uint16_t)vl[g][1],
+                             (uint16_t)(vl[g][1] >> 16)};
+    const uint16_t vhi[4] = {(uint16_t)vh[g][0], (uint16_t)(vh[g][0] >> 16), (uint16_t)vh[g][1],
+                             (uint16_t)(vh[g][1] >> 16)};
     if (p.kv_fp8) {
       float a[4], b[4];
-      norm_rope_f32(src[j], src[16 + j], w_lo, w_hi, p.rms_eps, local, cs, sn, a, b);
+      norm_rope_f32(kl[g], kh[g], w_lo, w_hi, p.rms_eps, local, cs, sn, a, b);
       uint8_t* k8 = reinterpret_cast<uint8_t*>(p.ck) + krow;
       *reinterpret_cast<uint32_t*>(k8 + 4 * j) = fp8x4_encode(a, p.k_scale);
       *reinterpret_cast<uint32_t*>(k8 + 64 + 4 * j) = fp8x4_encode(b, p.k_scale);
       uint8_t* v8 = reinterpret_cast<uint8_t*>(p.cv) + vcol;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        v8[(size_t)(4 * j + e) * vstride] = (uint8_t)fp8_e4m3_encode(bf16f(vsrc[4 * j + e]) / p.v_scale);
-        v8[(size_t)(64 + 4 * j + e) * vstride] = (uint8_t)fp8_e4m3_encode(bf16f(vsrc[64 + 4 * j + e]) / p.v_scale);
+        v8[(size_t)(4 * j + e) * vstride] = (uint8_t)fp8_e4m3_encode(bf16f(vlo[e]) / p.v_scale);
+        v8[(size_t)(64 + 4 * j + e) * vstride] = (uint8_t)fp8_e4m3_encode(bf16f(vhi[e]) / p.v_scale);
       }
       continue;
     }
-    HeadFrag f = norm_rope_head(src[j], src[16 + j], w_lo, w_hi, p.rms_eps, local, cs, sn, 1.0f);
+    HeadFrag f = norm_rope_head(kl[g], kh[g], w_lo, w_hi, p.rms_eps, local, cs, sn, 1.0f);
     reinterpret_cast<u32x2*>(p.ck + krow)[j] = u32x2{f.lo[0], f.lo[1]};
     reinterpret_cast<u32x2*>(p.ck + krow)[16 + j] = u32x2{f.hi[0], f.hi[1]};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      p.cv[vcol + (size_t)(4 * j + e) * vstride] = vsrc[4 * j + e];
-      p.cv[vcol + (size_t)(64 + 4 * j + e) * vstride] = vsrc[64 + 4 * j + e];
+      p.cv[vcol + (size_t)(4 * j + e) * vstride] = vlo[e];
+      p.cv[vcol + (size_t)(64 + 4 * j + e) * vstride] = vhi[e];
     }
   }
 }
