@@ -391,13 +391,13 @@ prefill_attn_kernel(PrefillParams p) {
   u32x4 qf[NB][8];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int t = wq_lo + 32 * nb + n;
-    const bool valid = t <= qlast;
+    // a query past the chunk's end loads the last valid row: its column of
+    // S, P and O only feeds its own (never written) output
+    const int t = min(wq_lo + 32 * nb + n, qlast);
     const size_t tok = (size_t)(cu0 + (t - start));
     const uint16_t* qrow = p.qp + (tok * p.H + h) * D + 8 * half;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      qf[nb][kk] = valid ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk) : u32x4{0u, 0u, 0u, 0u};
+    for (int kk = 0; kk < 8; ++kk) qf[nb][kk] = *reinterpret_cast<const u32x4*>(qrow + 16 * kk);
     if constexpr (KV_FP8) scale_frags(qf[nb], p.k_scale);  // code space: q' k_scale against the codes
   }
 
@@ -469,12 +469,24 @@ prefill_attn_kernel(PrefillParams p) {
                                                              kk == 0 ? sref[nb] : s[nb][mb], 0, 0, 0);
       }
     }
+    if constexpr (!decltype(CODES)::value) {
+      // K fragment reads run two k-steps ahead of the MFMAs that use them, so
+      // the LDS latency hides behind the matrix work (the default schedule
+      // read one k-step and waited; 1-2 % on a local layer)
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+      static_for<5>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      });
+      __builtin_amdgcn_sched_group_barrier(0x008, 6 * NB, 0);
+    }
   };
   // Element i of block mb holds key 64j + 8*half + c with c = 32mb + 16(i>>3)
   // + (i&7), a constant of the element. Per lane and tile the visible range
-  // of c is [t - (W-1) - base, t - base] (base = 64j + 8*half), so each
-  // element costs one compare against an inline constant and one select, and
-  // only the bound that cuts into the tile is tested.
+  // of c is [t - (W-1) - base, t - base] (base = 64j + 8*half): it becomes a
+  // 64-bit mask once per lane (only the bounds that cut into the tile), and
+  // each element then costs a bit-field extract and a bit-field insert (no
+  // per-element compare results held in scalar registers).
   auto apply_mask = [&](int j, f32x16 (&s)[NB][2]) {
     const int k0 = j * BN;
     const bool diag = k0 + BN - 1 > wq_lo;
@@ -483,21 +495,27 @@ prefill_attn_kernel(PrefillParams p) {
     for (int nb = 0; nb < NB; ++nb) {
       const int t = wq_lo + 32 * nb + n;
       const int base = k0 + 8 * half;
+      // visibility of key offsets c = 0..63 as a bit mask; element c keeps
+      // its score where bit c is set, else takes -inf (bit-field extract and
+      // bit-field insert: two instructions per element)
+      uint64_t vis = ~0ull;
       if (diag) {
-        const int hi = t - base;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (32 * mb + 16 * (i >> 3) + (i & 7) > hi) s[nb][mb][i] = kNegInf;
+        const int hi = t - base;  // visible: c <= hi
+        vis &= hi >= 63 ? ~0ull : hi < 0 ? 0ull : (2ull << hi) - 1;
       }
       if (edge) {
-        const int lo = t - (W - 1) - base;
+        const int lo = t - (W - 1) - base;  // visible: c >= lo
+        vis &= lo <= 0 ? ~0ull : lo >= 64 ? 0ull : ~((1ull << lo) - 1);
+      }
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb) {
+        const uint32_t word = (uint32_t)(vis >> (32 * mb));
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (32 * mb + 16 * (i >> 3) + (i & 7) < lo) s[nb][mb][i] = kNegInf;
+        for (int i = 0; i < 16; ++i) {
+          const int c = 16 * (i >> 3) + (i & 7);
+          const uint32_t m = (uint32_t)((int32_t)(word << (31 - c)) >> 31);
+          s[nb][mb][i] = __uint_as_float((__float_as_uint(s[nb][mb][i]) & m) | (0xff800000u & ~m));
+        }
       }
     }
   };
