@@ -291,6 +291,64 @@ def test_verify_and_decode_head_layouts(kind, heads):
         compare(o[i:i + 1], ref, f"decode heads {nq}/{nkv} seq{i}")
 
 
+@pytest.mark.parametrize("window", [64, 128, 1024])
+def test_local_window_sizes(window):
+    """Local layers with other windows (multiples of 64): with 64 the window
+    edge falls on the tile next to the diagonal one, with 1024 a chunk spans
+    17 tiles, and the ring holds that many slots. Two sequences: chunked
+    prefill over the cached ring (unaligned chunks), a 5-token verify step,
+    then a one-token decode (its K/V appended first)."""
+    cfg, ocfg = ga.Config(window=window), O.Config(window=window)
+    chunks = [[600, 37, 363], [511, 189]]
+    hist = [sum(c) for c in chunks]
+    total = [h + 6 for h in hist]
+    inps = [synth.attention_inputs(8, 1000 + window + i, n) for i, n in enumerate(total)]
+    inps[1]["q_norm_w"], inps[1]["k_norm_w"] = inps[0]["q_norm_w"], inps[0]["k_norm_w"]
+    qw, kw = inps[0]["q_norm_w"], inps[0]["k_norm_w"]
+    cache = ga.KVCache.allocate_local(cfg, 2, fill=SENT)
+    done = [0, 0]
+    for step in range(3):
+        batch, starts, seqs = [], [], []
+        for sq in (0, 1):
+            if step < len(chunks[sq]):
+                n, s0 = chunks[sq][step], done[sq]
+                batch.append({k: (v[s0:s0 + n] if v.ndim == 3 else v) for k, v in inps[sq].items()})
+                starts.append(s0)
+                seqs.append(sq)
+        say(f"[case] local window={window} prefill step={step} starts={starts}")
+        outs = _run_prefill(O.LOCAL, batch, starts, cache, seqs, cfg=cfg)
+        for sq, s0, o, b in zip(seqs, starts, outs, batch):
+            n = b["q"].shape[0]
+            x = inps[sq]
+            ref = O.attention_layer(O.LOCAL, x["q"][s0:s0 + n], x["k"][:s0 + n], x["v"][:s0 + n], qw, kw,
+                                    x["gate"][s0:s0 + n], np.arange(s0, s0 + n), np.arange(s0 + n), ocfg)
+            compare(o, ref, f"window {window} chunk seq{sq} [{s0},{s0 + n})")
+            done[sq] += n
+    cat = lambda key, lo, hi: dev_bf16(np.concatenate([x[key][l:h] for x, l, h in zip(inps, lo, hi)]))
+    lo, hi = hist, [h + 5 for h in hist]
+    say(f"[case] local window={window} verify")
+    out = ga.verify(cfg, cache, cat("q", lo, hi), cat("k", lo, hi), cat("v", lo, hi), dev_bf16(qw), dev_bf16(kw),
+                    cat("gate", lo, hi), dev_i32([0, 5, 10]), dev_i32([0, 1]), dev_i32(hist), 5, max(hi) - 1)
+    sync()
+    o = host_bits(out)
+    for i, x in enumerate(inps):
+        ref = O.attention_layer(O.LOCAL, x["q"][lo[i]:hi[i]], x["k"][:hi[i]], x["v"][:hi[i]], qw, kw,
+                                x["gate"][lo[i]:hi[i]], np.arange(lo[i], hi[i]), np.arange(hi[i]), ocfg)
+        compare(o[5 * i:5 * i + 5], ref, f"window {window} verify seq{i}")
+    ts = hi
+    say(f"[case] local window={window} decode")
+    ga.kv_append(cfg, cache, cat("k", ts, total), cat("v", ts, total), dev_bf16(kw), dev_i32([0, 1]), dev_i32(ts))
+    out = ga.decode(cfg, cache, cat("q", ts, total), dev_bf16(qw), cat("gate", ts, total), dev_i32([0, 1]),
+                    dev_i32(ts), max(ts))
+    sync()
+    o = host_bits(out)
+    for i, x in enumerate(inps):
+        t = ts[i]
+        ref = O.attention_layer(O.LOCAL, x["q"][t:t + 1], x["k"][:t + 1], x["v"][:t + 1], qw, kw,
+                                x["gate"][t:t + 1], np.array([t]), np.arange(t + 1), ocfg)
+        compare(o[i:i + 1], ref, f"window {window} decode seq{i}")
+
+
 @pytest.mark.parametrize("kind", [O.LOCAL, O.GLOBAL])
 def test_prefill_stage_orders_bit_identical(kind):
     """The stage splits of a prefill call (including the global layers' fused
