@@ -202,6 +202,34 @@ __device__ __forceinline__ void dma_tile_prefix(const KeySource& ks, int w, int 
   }
 }
 
+// DMA of a tile of a paged cache's prefix with the tile's four page ids
+// given (pg holds page id (lane & 3) of the tile in every lane). A K
+// instruction moves 8 rows of one page (its page id is wave-uniform); the
+// lanes of a V^T instruction span the four pages, each picks its own.
+template <int NW>
+__device__ __forceinline__ void dma_tile_paged(const KeySource& ks, int pg, int w, int lane, uint16_t* sK,
+                                               uint16_t* sV) {
+  const int p0 = __builtin_amdgcn_readlane(pg, 0), p1 = __builtin_amdgcn_readlane(pg, 1);
+  const int p2 = __builtin_amdgcn_readlane(pg, 2), p3 = __builtin_amdgcn_readlane(pg, 3);
+#pragma unroll
+  for (int i = 0; i < DmaPlan<NW>::N; ++i) {
+    const int kI = w * DmaPlan<NW>::N + i;
+    const int m = 8 * (kI & 7) + (lane >> 3);
+    const int c = (lane & 7) ^ ((m >> 1) & 7);
+    const int kp = (kI & 7) >> 1;  // page of rows 8(kI & 7) .. +7 (the row permutation stays inside a page)
+    const int kpage = kp == 0 ? p0 : kp == 1 ? p1 : kp == 2 ? p2 : p3;
+    lds_dma16(ks.ck + kpage * ks.page_stride + (uint32_t)((krow_key(m) & 15) * D + 64 * (kI >> 3) + 8 * c),
+              sK + kI * 512);
+
+    const int vI = w * DmaPlan<NW>::N + i;
+    const int d = 8 * vI + (lane >> 3);
+    const int cv = (lane & 7) ^ ((d >> 1) & 7);
+    const int vp = cv >> 1;
+    const int vpage = vp == 0 ? p0 : vp == 1 ? p1 : vp == 2 ? p2 : p3;
+    lds_dma16(ks.cv + vpage * ks.page_stride + (uint32_t)(d * 16 + 8 * (cv & 1)), sV + vI * 512);
+  }
+}
+
 // ---------------------------------------------------------------- FP8 code tiles
 // A tile of the cached prefix of an FP8 cache is moved into LDS as its raw
 // codes by the same LDS DMA as a bf16 tile (16 KiB instead of 32): the DMA
@@ -615,11 +643,22 @@ prefill_attn_kernel(PrefillParams p) {
       }
     }
   };
-  // Fetch tile j into its slot by DMA, from the workspace or the cache.
-  auto fetch = [&](int j, auto B) __attribute__((always_inline)) {
+  // Page ids of tile j of a paged prefix, one per lane: lane l holds page
+  // (l & 3) of the tile (global layers; loaded a stage ahead of the DMA).
+  auto load_pages = [&](int j) __attribute__((always_inline)) -> int {
+    if constexpr (KIND == 1) {
+      if (j < j_ws && j <= j_hi) return ks.bt_row[4 * j + (lane & 3)];
+    }
+    return 0;
+  };
+  // Fetch tile j into its slot by DMA, from the workspace or the cache (pg:
+  // the tile's page ids from load_pages, on a paged prefix).
+  auto fetch = [&](int j, auto B, int pg) __attribute__((always_inline)) {
     uint16_t* sK = buf(B);
     if (j >= j_ws)
       plan.copy(ks.kw, ks.vw, ks.ws_off, j * BN, sK, sK + K_TILE);
+    else if constexpr (KIND == 1 && !KV_FP8)
+      dma_tile_paged<NWAVES>(ks, pg, w, lane, sK, sK + K_TILE);
     else if constexpr (KV_FP8)
       dma_code_tile<NWAVES>(cs8, [&](int pg) { return ks.bt_row[pg]; }, w, lane, j * BN,
                             reinterpret_cast<uint8_t*>(sK));
@@ -669,13 +708,16 @@ prefill_attn_kernel(PrefillParams p) {
   // is computed, tile j0+TPS+u is sent to the other stage's slot (freed by the
   // previous barrier); the barrier then publishes the next stage. On local
   // layers the last stage sends the gate rows instead.
+  int pgs[TPS];  // page ids of the tiles the next stage fetches (paged prefix)
   auto stage = [&](int j0, auto S0) __attribute__((always_inline)) {
     static_for<TPS>([&](auto U) __attribute__((always_inline)) {
       constexpr int u = decltype(U)::value;
       constexpr int s0 = decltype(S0)::value;
       using Next = std::integral_constant<int, (s0 + TPS + u) % SLOTS>;
-      if (j0 + TPS + u <= j_hi)
-        fetch(j0 + TPS + u, Next{});
+      if (j0 + TPS + u <= j_hi) {
+        fetch(j0 + TPS + u, Next{}, pgs[u]);
+        pgs[u] = load_pages(j0 + 2 * TPS + u);
+      }
       else if constexpr (local)
         fetch_gate(Next{});
       if (j0 + u <= j_hi) compute_tile(j0 + u, std::integral_constant<int, s0 + u>{});
@@ -694,16 +736,16 @@ prefill_attn_kernel(PrefillParams p) {
       const auto CODE = std::true_type{};
       const auto S0 = std::integral_constant<int, 0>{};
       const auto S1 = std::integral_constant<int, 1>{};
-      fetch(j_lo, S0);
+      fetch(j_lo, S0, 0);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       for (int jt = j_lo; jt <= jc; jt += 2) {
-        if (jt + 1 <= jc) fetch(jt + 1, S1);
+        if (jt + 1 <= jc) fetch(jt + 1, S1, 0);
         if (active(jt)) tile(jt, S0, CODE);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (jt + 1 > jc) break;
-        if (jt + 2 <= jc) fetch(jt + 2, S0);
+        if (jt + 2 <= jc) fetch(jt + 2, S0, 0);
         if (active(jt + 1)) tile(jt + 1, S1, CODE);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -714,7 +756,9 @@ prefill_attn_kernel(PrefillParams p) {
   // slot holding the staged gate rows: the one after the last tile's
   const int gate_slot = (j_hi - j_main + 1) % SLOTS;
   static_for<TPS>([&](auto U) __attribute__((always_inline)) {
-    if (j_main + decltype(U)::value <= j_hi) fetch(j_main + decltype(U)::value, U);
+    constexpr int u = decltype(U)::value;
+    if (j_main + u <= j_hi) fetch(j_main + u, U, load_pages(j_main + u));
+    pgs[u] = load_pages(j_main + TPS + u);
   });
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
