@@ -33,7 +33,7 @@ EXPORTED = [
     "beam_attn_prefill_stages", "beam_attn_decode_stages", "beam_attn_verify_stages", "beam_attn_decode_noalloc",
     "beam_prefill_workspace_bytes", "beam_decode_workspace_bytes", "beam_verify_workspace_bytes",
     "beam_kv_bytes", "beam_kv_page_slot", "beam_debug_visibility", "beam_debug_validate_cache",
-    "beam_status_str", "beam_last_error",
+    "beam_kv_convert_v", "beam_status_str", "beam_last_error",
     "beam_router", "beam_router_logits", "beam_router_select",
     "beam_attn_project", "beam_out_project",
     "beam_probe_mfma_bf16", "beam_probe_stream_read",
@@ -131,6 +131,7 @@ def lib() -> ctypes.CDLL:
     L.beam_kv_page_slot.argtypes = [P, I32, I32, I32, I32, P, P]
     L.beam_debug_visibility.argtypes = [I32, I32, I32, I32, I32, I32, P, P]
     L.beam_debug_validate_cache.argtypes = [P, P, P, P]
+    L.beam_kv_convert_v.argtypes = [P, P, P, I32, P]
     L.beam_router.argtypes = [P, P, P, P, I32, P, P, P]
     L.beam_router_logits.argtypes = [P, P, P, I32, P, P]
     L.beam_router_select.argtypes = [P, P, P, I32, P, P, P]
@@ -144,7 +145,8 @@ def lib() -> ctypes.CDLL:
     for name in ("beam_kv_append", "beam_attn_prefill", "beam_attn_decode", "beam_attn_decode_noalloc",
                  "beam_attn_prefill_stages",
                  "beam_attn_decode_stages", "beam_attn_verify", "beam_attn_verify_stages", "beam_kv_bytes",
-                 "beam_kv_page_slot", "beam_debug_visibility", "beam_debug_validate_cache", "beam_router",
+                 "beam_kv_page_slot", "beam_debug_visibility", "beam_debug_validate_cache", "beam_kv_convert_v",
+                 "beam_router",
                  "beam_router_logits", "beam_router_select", "beam_attn_project", "beam_out_project",
                  "beam_probe_mfma_bf16", "beam_probe_stream_read"):
         getattr(L, name).restype = I32
@@ -430,6 +432,22 @@ def debug_validate_cache(cache: KVCache, n_tokens=None, stream=None):
     kc = cache.c()
     _check(lib().beam_debug_validate_cache(ctypes.byref(kc), _ptr(n_tokens), _ptr(n_bad), _stream(stream)))
     return n_bad
+
+
+def kv_convert_v(cfg: Config, cache: KVCache, v_token_major, to_cache: bool, stream=None):
+    """V of the cache between the token-major layout ([n_pages][n_kv][16][d]
+    global, [n_seqs][n_kv][window][d] local, as K) and the cache's own
+    coordinate-major layout (beam_kv_convert_v). to_cache: v_token_major ->
+    cache.v, else cache.v -> v_token_major. v_token_major: device tensor of the
+    cache's element type (bfloat16, or uint8 FP8 codes) and that shape."""
+    import torch
+    rows = cache.page_size if cache.kind == GLOBAL else cfg.window
+    shape = (cache.v.shape[0], cfg.n_kv_heads, rows, cfg.head_dim)
+    _need(v_token_major, torch.bfloat16 if cache.dtype == KV_BF16 else torch.uint8, shape, "v_token_major")
+    kc = cache.c()
+    _check(lib().beam_kv_convert_v(ctypes.byref(cfg.c()), ctypes.byref(kc), _ptr(v_token_major),
+                                   1 if to_cache else 0, _stream(stream)))
+    return v_token_major
 
 
 # ---------------------------------------------------------------- router

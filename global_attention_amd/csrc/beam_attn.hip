@@ -15,6 +15,7 @@
 #include "beam_router.h"
 #include "beam_device.h"
 #include "beam_kernels.h"
+#include "kv_layout.h"
 
 namespace {
 
@@ -728,6 +729,31 @@ beam_status beam_debug_validate_cache(const beam_kv_cache* cache, const int32_t*
                                                           cache->n_pages, cache->page_size, cache->n_seqs,
                                                           n_tokens, n_bad, (hipStream_t)stream),
                               "validate_cache launch");
+  if (st != BEAM_OK) return st;
+  return ok();
+}
+
+beam_status beam_kv_convert_v(const beam_attn_config* cfg, const beam_kv_cache* cache, void* v_token_major,
+                              int32_t to_cache, void* stream) {
+  if (beam_status st = check_cfg(cfg); st != BEAM_OK) return st;
+  if (beam_status st = check_cache(cache); st != BEAM_OK) return st;
+  if (!v_token_major) return fail(BEAM_E_NULL, "v_token_major is NULL");
+  if (!aligned16(v_token_major)) return fail(BEAM_E_RANGE, "v_token_major must be 16-byte aligned");
+  const bool global = cache->kind == BEAM_GLOBAL;
+  if (global && cache->n_pages <= 0) return fail(BEAM_E_RANGE, "n_pages must be positive");
+  const long long n_blocks = (long long)(global ? cache->n_pages : cache->n_seqs) * cfg->n_kv_heads;
+  const int rows = global ? cache->page_size : cfg->window;
+  const int esz = cache->dtype == BEAM_KV_FP8_E4M3 ? 1 : 2;
+  const unsigned long long bytes = (unsigned long long)n_blocks * rows * beam::D * esz;
+  if (n_blocks * (rows / beam::kVTransposeRows) > 0x7fffffffLL)
+    return fail(BEAM_E_RANGE, "cache too large for one conversion call");
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(v_token_major), b0 = reinterpret_cast<uintptr_t>(cache->v);
+  if (a0 < b0 + bytes && b0 < a0 + bytes) return fail(BEAM_E_RANGE, "v_token_major overlaps cache->v");
+  const void* src = to_cache ? v_token_major : cache->v;
+  void* dst = to_cache ? cache->v : v_token_major;
+  beam_status st = hip_status(beam::launch_kv_v_transpose(src, dst, n_blocks, rows, esz, to_cache ? 1 : 0,
+                                                          (hipStream_t)stream),
+                              "kv_convert_v launch");
   if (st != BEAM_OK) return st;
   return ok();
 }

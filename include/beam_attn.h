@@ -46,6 +46,8 @@
  *     v: bf16 [n_seqs][n_kv_heads][head_dim][window]
  *     position t lives in slot t % window.
  *   The cache stores K_hat (normalised; rotated on local layers) and raw V.
+ *   V kept token-major like K (another engine's layout) converts to and from
+ *   this layout with beam_kv_convert_v.
  *
  * FP8 KV cache (dtype BEAM_KV_FP8_E4M3; one byte per element, same layouts)
  *   The pages' serving recipes keep the cache in FP8 E4M3 (18 KiB per token
@@ -326,6 +328,29 @@ beam_status beam_debug_visibility(int32_t kind, int32_t window, int32_t t0, int3
  * table (BEAM_E_RANGE). */
 beam_status beam_debug_validate_cache(const beam_kv_cache *cache, const int32_t *n_tokens, int32_t *n_bad,
                                       void *stream);
+
+/* V of a layer's cache between the token-major layout, in which K is stored
+ * too, and the layout the attention calls read (coordinate-major within each
+ * page or ring, "KV cache layouts" above). The cache holds V of every position
+ * of the nine global layers and a window of positions on the local layers
+ * ("Beam 1.0: Local RoPE, Global NoPE and Scalable Softmax", section "KV
+ * memory: nine growing caches, not 52"); a caller that filled V token-major
+ * (page_size x head_dim rows per page and KV head, as another engine's paged
+ * cache keeps it) converts it here before any attention call, or reads the
+ * cache back that way.
+ *   token-major V: GLOBAL [n_pages][n_kv_heads][page_size][head_dim],
+ *                  LOCAL  [n_seqs][n_kv_heads][window][head_dim]
+ *                  (page_size 16; the element type of cache->dtype, bf16 or FP8 E4M3 codes)
+ * to_cache != 0: reads v_token_major, writes all of cache->v (every page, or
+ *                every ring of cache->n_seqs).
+ * to_cache == 0: reads cache->v, writes v_token_major.
+ * The bytes are moved unchanged (no scaling or rounding). v_token_major:
+ * device, caller-owned, the size of cache->v, 16-byte aligned
+ * (BEAM_E_RANGE), not overlapping cache->v (BEAM_E_RANGE: there is no
+ * in-place form). Enqueued on `stream`; nothing is allocated. K needs no
+ * conversion. */
+beam_status beam_kv_convert_v(const beam_attn_config *cfg, const beam_kv_cache *cache, void *v_token_major,
+                              int32_t to_cache, void *stream);
 
 const char *beam_status_str(beam_status s);
 /* Message of the last failed call on this thread ("" if none). */

@@ -147,6 +147,30 @@ int main() {
     status_line("router_experts", beam_router(&rc, nullptr, nullptr, nullptr, 4, nullptr, nullptr, nullptr));
     status_line("out_project_k", beam_out_project(nullptr, nullptr, 4, 100, 256, nullptr, nullptr));
   }
+  // V layout conversion: argument checks, then the blocks of a paged and a
+  // local cache (bf16 and FP8)
+  {
+    beam_kv_cache kv = global_cache(100, 8, 2);
+    status_line("convert_v_null", beam_kv_convert_v(&c, &kv, nullptr, 1, nullptr));
+    status_line("convert_v_align", beam_kv_convert_v(&c, &kv, fake(0x70000008), 1, nullptr));
+    status_line("convert_v_overlap", beam_kv_convert_v(&c, &kv, fake(0x20000000 + 100 * 8 * 16 * 128 * 2 - 16), 1,
+                                                       nullptr));
+    stub::last = stub::Record();
+    beam_status s = beam_kv_convert_v(&c, &kv, fake(0x20000000 + 100 * 8 * 16 * 128 * 2), 1, nullptr);
+    std::printf("convert_v_call %d %d %d %d %d\n", BEAM_GLOBAL, (int)s, stub::last.calls, stub::last.grid_a,
+                stub::last.grid_b);
+    beam_kv_cache loc{};
+    loc.kind = BEAM_LOCAL;
+    loc.k = fake(0x10000000);
+    loc.v = fake(0x20000000);
+    loc.n_seqs = 3;
+    loc.dtype = BEAM_KV_FP8_E4M3;
+    loc.k_scale = loc.v_scale = 1.f;
+    stub::last = stub::Record();
+    s = beam_kv_convert_v(&c, &loc, fake(0x70000000), 0, nullptr);
+    std::printf("convert_v_call %d %d %d %d %d\n", BEAM_LOCAL, (int)s, stub::last.calls, stub::last.grid_a,
+                stub::last.grid_b);
+  }
   // the thread-local message, from several threads at once
   {
     std::vector<std::thread> th;

@@ -36,6 +36,12 @@ hipError_t launch_validate_cache(const int32_t*, int, int, int, int, const int32
   ++stub::last.calls;
   return hipSuccess;
 }
+hipError_t launch_kv_v_transpose(const void*, void*, long long n_blocks, int rows, int, int, hipStream_t) {
+  ++stub::last.calls;
+  stub::last.grid_a = (int)n_blocks;
+  stub::last.grid_b = rows;
+  return hipSuccess;
+}
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t) {
   ++stub::last.calls;
   stub::last.prefill = p;

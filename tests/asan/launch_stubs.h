@@ -3,6 +3,7 @@
 #pragma once
 
 #include "beam_kernels.h"
+#include "kv_layout.h"
 
 namespace stub {
 struct Record {

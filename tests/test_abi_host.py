@@ -417,8 +417,14 @@ def test_host_side_under_address_sanitizer(tmp_path):
             "append_head_dim": E_UNSUPPORTED, "append_null": E_NULL,
             "append_page": E_UNSUPPORTED, "validate_local": E_RANGE,
             "visibility_kind": E_RANGE, "router_experts": E_UNSUPPORTED,
-            "out_project_k": E_UNSUPPORTED}
+            "out_project_k": E_UNSUPPORTED, "convert_v_null": E_NULL, "convert_v_align": E_RANGE,
+            "convert_v_overlap": E_RANGE}
     got = {what: (int(st), int(msg_len)) for what, st, msg_len in by["status"]}
     assert {k: v[0] for k, v in got.items()} == want
     assert all(v[1] > 0 for v in got.values())
+    # V layout conversion: one launch over every (page, KV head) block of 16
+    # rows, or every (ring, KV head) block of window rows
+    conv = {int(r[0]): tuple(map(int, r[1:])) for r in by["convert_v_call"]}
+    assert conv[ga.GLOBAL] == (0, 1, 100 * 8, 16)
+    assert conv[ga.LOCAL] == (0, 1, 3 * 8, 512)
     assert by["threads"] == [["1600"]]
