@@ -113,6 +113,10 @@ def _dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
 
 
+def _r4(x):
+    return None if x is None else round(x, 4)
+
+
 def _i32(x):
     import numpy as np
     import torch
@@ -216,6 +220,49 @@ def setup_decode(n_seqs=64, lo=65536, hi=131071, seed=3):
     return cfg, ts, gcache, lcache, fcache, d
 
 
+def graph_ms_per_call(call, out, calls=20, reps=5):
+    """Device time of one whole library call without the host's launch cost:
+    `calls` back-to-back calls captured in one HIP graph (torch.cuda.CUDAGraph;
+    the library enqueues kernels only, no memset or copy), replayed `reps`
+    times with eager work and a synchronisation between replays. Every
+    replay's output must equal the eager call's bit for bit, else None."""
+    import numpy as np
+    import torch
+    try:
+        call()
+        torch.cuda.synchronize()
+        want = out.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                call()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(calls):
+                call()
+        ts = []
+        for _ in range(reps):
+            out.zero_()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            if not torch.equal(out.view(torch.int16), want.view(torch.int16)):
+                log("[bench] graph replay differs from the eager call; device time not reported")
+                return None
+            ts.append(e0.elapsed_time(e1) / calls)
+        del g
+        return float(np.median(ts))
+    except Exception as e:  # capture unsupported here: report no figure
+        log(f"[bench] graph timing unavailable: {e}")
+        return None
+
+
 def bench_decode(steps, warmup):
     import torch
     import global_attention_amd as ga
@@ -252,9 +299,11 @@ def bench_decode(steps, warmup):
         split_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
         keys = [min(int(t) + 1, W) if name == "local" else int(t) + 1 for t in ts]
         nbytes = sum(keys) * G * D * 2 * (1 if cache.dtype == ga.KV_FP8_E4M3 else 2)
-        res[name] = dict(bytes=nbytes, ms_per_call=el * 1e3, split_ms=split_ms,
+        dev_ms = graph_ms_per_call(lambda: ga.decode(*args, out=out, workspace=ws), out)
+        res[name] = dict(bytes=nbytes, ms_per_call=el * 1e3, split_ms=split_ms, device_ms=dev_ms,
                          gbs_call=nbytes / el / 1e9, gbs_split=nbytes / (split_ms / 1e3) / 1e9)
-        log(f"[bench] decode {name}: {nbytes / 1e9:.2f} GB, call {el * 1e3:.3f} ms, split kernel {split_ms:.3f} ms")
+        log(f"[bench] decode {name}: {nbytes / 1e9:.2f} GB, call {el * 1e3:.3f} ms, split kernel {split_ms:.3f} ms, "
+            f"device time per call {dev_ms} ms")
     res["setup"] = setup
     return res
 
@@ -369,7 +418,8 @@ def bench_verify(steps, warmup, dres, block=8, split_keys=0):
         # cached keys each chunk reads once (the chunk's own keys come from the workspace)
         keys = [min(int(s), W - 1) if name == "local" else int(s) for s in starts]
         nbytes = sum(keys) * G * D * 2 * (1 if cache.dtype == ga.KV_FP8_E4M3 else 2)
-        res[name] = dict(bytes=nbytes, ms_per_call=el * 1e3, split_ms=split_ms,
+        dev_ms = graph_ms_per_call(lambda: ga.verify(*args, **kw), out)
+        res[name] = dict(bytes=nbytes, ms_per_call=el * 1e3, split_ms=split_ms, device_ms=dev_ms,
                          gbs_call=nbytes / el / 1e9, gbs_split=nbytes / (split_ms / 1e3) / 1e9,
                          vs_decode_calls=block * dres[name]["ms_per_call"] / (el * 1e3))
         log(f"[bench] verify {name} ({block} tokens/seq): {nbytes / 1e9:.2f} GB, call {el * 1e3:.3f} ms, "
@@ -954,9 +1004,14 @@ def main():
                          "traffic": recorded_traffic("decode_split_kernel<1>"),
                          "avg_launch_ms": round(g["split_ms"], 4), "bytes_per_launch": g["bytes"],
                          **measured(None, g["gbs_split"], "hbm")},
+            "global_device_ms_per_call": _r4(g["device_ms"]),
             "local": {"bytes": dres["local"]["bytes"], "ms_per_call": round(dres["local"]["ms_per_call"], 4),
+                      "device_ms_per_call": _r4(dres["local"]["device_ms"]),
                       "gbs_call": round(dres["local"]["gbs_call"], 1),
                       "note": "134 MB of rings can stay resident in the 256 MB MALL between calls"},
+            "device_ms_note": "device_ms_per_call: 20 whole calls (prologue, split kernel, combine) captured in "
+                              "one HIP graph and replayed, so no host launch cost; ms_per_call: the calls "
+                              "launched from Python one by one",
         }
         f = dres["global_fp8"]
         rec["decode_fp8"] = {
@@ -966,6 +1021,7 @@ def main():
             "frac_of_hbm_peak": round(f["gbs_call"] / PEAK_HBM_GBS, 4),
             "global_bytes": f["bytes"], "global_ms_per_call": round(f["ms_per_call"], 4),
             "speedup_vs_bf16_call": round(g["ms_per_call"] / f["ms_per_call"], 3),
+            "global_device_ms_per_call": _r4(f["device_ms"]),
             "roofline": {"kernel": "decode_fp8_kernel<1>", "bound": "hbm", "achieved": round(f["gbs_split"], 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(f["gbs_split"] / PEAK_HBM_GBS, 4),
                          "traffic": recorded_traffic("decode_fp8_kernel<1>"),
@@ -982,14 +1038,17 @@ def main():
             "frac_of_hbm_peak": round(vg["gbs_call"] / PEAK_HBM_GBS, 4),
             "global_bytes": vg["bytes"], "global_ms_per_call": round(vg["ms_per_call"], 4),
             "speedup_vs_8_decode_calls": round(vg["vs_decode_calls"], 2),
+            "global_device_ms_per_call": _r4(vg["device_ms"]),
             "roofline": {"kernel": "verify_attn_kernel<1, 0, 4>", "bound": "hbm", "achieved": round(vg["gbs_split"], 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(vg["gbs_split"] / PEAK_HBM_GBS, 4),
                          "traffic": recorded_traffic("verify_attn_kernel<1, 0, 4>"),
                          "avg_launch_ms": round(vg["split_ms"], 4), "bytes_per_launch": vg["bytes"],
                          **measured(None, vg["gbs_split"], "hbm")},
             "local": {"ms_per_call": round(v["local"]["ms_per_call"], 4),
+                      "device_ms_per_call": _r4(v["local"]["device_ms"]),
                       "speedup_vs_8_decode_calls": round(v["local"]["vs_decode_calls"], 2)},
             "global_fp8": {"ms_per_call": round(v["global_fp8"]["ms_per_call"], 4),
+                           "device_ms_per_call": _r4(v["global_fp8"]["device_ms"]),
                            "gbs_split": round(v["global_fp8"]["gbs_split"], 1),
                            "speedup_vs_8_decode_calls": round(v["global_fp8"]["vs_decode_calls"], 2)},
         }
