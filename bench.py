@@ -24,9 +24,10 @@ against the fp32 MFMA peak.
 And under "schedule52": the full 52-layer attention schedule (9 global, 43
 local layers) as a chunked prefill of 8 sequences of 4K-64K tokens in
 8192-token chunks, aggregate TFLOP/s, with the oracle timed on sampled rows.
-And under "measured_ceilings": the bf16 MFMA rate on random operands and the
-streaming HBM read rate this GPU sustains (include/beam_probe.h); every
-roofline object also gives its fraction of that measured ceiling.
+And under "measured_ceilings": the bf16 MFMA rates this GPU sustains on
+constant and random operands with the 32x32x16 and the 16x16x32 instruction,
+and its streaming HBM read rate (include/beam_probe.h); every roofline object
+also gives its fraction of the highest measured MFMA rate or of the read rate.
 
 Prints ONE JSON line on stdout. Everything else goes to stderr.
 """
@@ -643,18 +644,20 @@ def cpu_facts():
 
 # --------------------------------------------------------------------------- ceilings
 
-def _probe_mfma(ops, n_blocks, iters, distinct, reps):
-    """Median TFLOP/s of `reps` runs of the MFMA probe, after one untimed run of the same length."""
+def _probe_mfma(ops, n_blocks, iters, distinct, reps, shape=32):
+    """Median TFLOP/s of `reps` runs of the MFMA probe (shape 32: the 32x32x16
+    loop, 16: the 16x16x32 loop), after one untimed run of the same length."""
     import statistics
     import torch
     import global_attention_amd as ga
+    probe = ga.probe_mfma_bf16 if shape == 32 else ga.probe_mfma16_bf16
     out = torch.empty((n_blocks * 256,), dtype=torch.float32, device="cuda")
-    ga.probe_mfma_bf16(ops[:n_blocks * 256 * 64], n_blocks, iters, distinct, out)
+    probe(ops[:n_blocks * 256 * 64], n_blocks, iters, distinct, out)
     rates = []
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        flops = ga.probe_mfma_bf16(ops[:n_blocks * 256 * 64], n_blocks, iters, distinct, out)
+        flops = probe(ops[:n_blocks * 256 * 64], n_blocks, iters, distinct, out)
         e1.record()
         torch.cuda.synchronize()
         rates.append(flops / (e0.elapsed_time(e1) / 1e3) / 1e12)
@@ -677,16 +680,24 @@ def measure_ceilings(reps=3, sweep=False):
     # the rate on N(0,1) operands that change on every MFMA
     mfma, ms = _probe_mfma(one, 1024, 3000, 1, reps)
     mfma_rnd, _ = _probe_mfma(rnd, 1024, 3000, 8, reps)
-    res = dict(mfma_bf16_tflops=round(mfma, 1), mfma_bf16_random_tflops=round(mfma_rnd, 1))
+    # the same loop with the 16x16x32 instruction, which the chip sustains at a
+    # higher rate under the same power limit
+    mfma16, _ = _probe_mfma(one, 1024, 3000, 1, reps, shape=16)
+    mfma16_rnd, _ = _probe_mfma(rnd, 1024, 3000, 8, reps, shape=16)
+    res = dict(mfma_bf16_tflops=round(mfma, 1), mfma_bf16_random_tflops=round(mfma_rnd, 1),
+               mfma_bf16_16x16_tflops=round(mfma16, 1), mfma_bf16_16x16_random_tflops=round(mfma16_rnd, 1),
+               mfma_measured_peak_tflops=round(max(mfma, mfma_rnd, mfma16, mfma16_rnd), 1))
     if sweep:
         rows = []
-        for name, ops in (("random N(0,1)", rnd), ("constant 1.0", one)):
-            for distinct in (8, 1):
-                for nb, iters in ((512, 400), (1024, 3000)):
-                    r, t = _probe_mfma(ops, nb, iters, distinct, reps)
-                    rows.append(dict(operands=name, distinct=distinct, blocks=nb, iters=iters, ms=round(t, 3),
-                                     tflops=round(r, 1)))
-                    log(f"[bench] mfma probe {name}, {distinct} distinct, {nb} x {iters}: {t:.3f} ms, {r:.1f} TFLOP/s")
+        for shape in (32, 16):
+            for name, ops in (("random N(0,1)", rnd), ("constant 1.0", one)):
+                for distinct in (8, 1):
+                    for nb, iters in ((512, 400), (1024, 3000)):
+                        r, t = _probe_mfma(ops, nb, iters, distinct, reps, shape=shape)
+                        rows.append(dict(mfma=f"{shape}x{shape}", operands=name, distinct=distinct, blocks=nb,
+                                         iters=iters, ms=round(t, 3), tflops=round(r, 1)))
+                        log(f"[bench] mfma probe {shape}x{shape} {name}, {distinct} distinct, {nb} x {iters}: "
+                            f"{t:.3f} ms, {r:.1f} TFLOP/s")
         res["mfma_sweep"] = rows
     del rnd, one
     buf = torch.empty((8 << 30,), dtype=torch.uint8, device="cuda")
@@ -706,15 +717,17 @@ def measure_ceilings(reps=3, sweep=False):
                 best_read, best_grid = gbs, nb
     del buf, rout
     torch.cuda.empty_cache()
-    log(f"[bench] ceilings: bf16 MFMA sustained {mfma:.1f} TFLOP/s (constant operands), {mfma_rnd:.1f} TFLOP/s "
-        f"(N(0,1) operands changing every MFMA) in {ms:.1f} ms runs; streaming read {best_read:.1f} GB/s "
-        f"({best_grid} blocks)")
+    log(f"[bench] ceilings: bf16 MFMA sustained, 32x32x16: {mfma:.1f} TFLOP/s (constant operands), {mfma_rnd:.1f} "
+        f"TFLOP/s (N(0,1) operands changing every MFMA); 16x16x32: {mfma16:.1f} / {mfma16_rnd:.1f} TFLOP/s; "
+        f"{ms:.1f} ms runs; streaming read {best_read:.1f} GB/s ({best_grid} blocks)")
     res.update(hbm_read_gbs=round(best_read, 1),
                method="beam_probe_mfma_bf16: 1024 blocks x 4 waves x 3000 iterations x 16 "
                       "v_mfma_f32_32x32x16_bf16 from registers, ~5 ms per run (past the boost), median of "
-                      f"{reps} runs after one untimed run; mfma_bf16_tflops: constant 1.0 operands (the pipe at "
-                      "the power limit with no operand switching; the bound every bf16 kernel sits under), "
-                      "mfma_bf16_random_tflops: N(0,1) operands changing on every MFMA; beam_probe_stream_read: "
+                      f"{reps} runs after one untimed run; mfma_bf16_tflops: constant 1.0 operands (no operand "
+                      "switching), mfma_bf16_random_tflops: N(0,1) operands changing on every MFMA; "
+                      "beam_probe_mfma16_bf16: the same work as 32 v_mfma_f32_16x16x32_bf16 per iteration "
+                      "(mfma_bf16_16x16_*); mfma_measured_peak_tflops: the highest of the four, the ceiling "
+                      "frac_of_measured_peak divides by; beam_probe_stream_read: "
                       f"8 GiB, 16-byte non-temporal loads, best of 4 grids x {reps}")
     return res
 
@@ -916,7 +929,7 @@ def main():
     def measured(_unused, value, kind):
         if ceil is None:
             return {}
-        peak = ceil["mfma_bf16_tflops"] if kind == "mfma" else ceil["hbm_read_gbs"]
+        peak = ceil["mfma_measured_peak_tflops"] if kind == "mfma" else ceil["hbm_read_gbs"]
         return {"measured_peak": peak, "frac_of_measured_peak": round(value / peak, 4)}
 
     if not args.skip_prefill:
@@ -986,7 +999,7 @@ def main():
                         f"({', '.join(str(x) for x in sc['lens'])}), 8192-token chunks, one cache per layer "
                         "(paged for global, 512-slot rings for local)",
             "value": round(tf, 2), "unit": "TFLOP/s", "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-            **({"frac_of_measured_peak": round(tf / ceil["mfma_bf16_tflops"], 4)} if ceil else {}),
+            **({"frac_of_measured_peak": round(tf / ceil["mfma_measured_peak_tflops"], 4)} if ceil else {}),
             "ms_per_pass": round(sc["ms"], 2), "ms_runs": sc["ms_runs"], "flop_per_pass": sc["flops"],
             "cpu_sample": sc["oracle"],
         }

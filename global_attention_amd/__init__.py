@@ -36,7 +36,7 @@ EXPORTED = [
     "beam_kv_convert_v", "beam_status_str", "beam_last_error",
     "beam_router", "beam_router_logits", "beam_router_select",
     "beam_attn_project", "beam_out_project",
-    "beam_probe_mfma_bf16", "beam_probe_stream_read",
+    "beam_probe_mfma_bf16", "beam_probe_mfma16_bf16", "beam_probe_stream_read",
 ]
 
 
@@ -138,6 +138,7 @@ def lib() -> ctypes.CDLL:
     L.beam_attn_project.argtypes = [P, I32, P, I32, P, P, P, P, I32, I32, P, P, P, P, SZ, P]
     L.beam_out_project.argtypes = [P, P, I32, I32, I32, P, P]
     L.beam_probe_mfma_bf16.argtypes = [P, I32, I32, I32, P, P]
+    L.beam_probe_mfma16_bf16.argtypes = [P, I32, I32, I32, P, P]
     L.beam_probe_stream_read.argtypes = [P, SZ, I32, P, P]
     L.beam_status_str.argtypes = [I32]
     L.beam_status_str.restype = ctypes.c_char_p
@@ -148,7 +149,7 @@ def lib() -> ctypes.CDLL:
                  "beam_kv_page_slot", "beam_debug_visibility", "beam_debug_validate_cache", "beam_kv_convert_v",
                  "beam_router",
                  "beam_router_logits", "beam_router_select", "beam_attn_project", "beam_out_project",
-                 "beam_probe_mfma_bf16", "beam_probe_stream_read"):
+                 "beam_probe_mfma_bf16", "beam_probe_mfma16_bf16", "beam_probe_stream_read"):
         getattr(L, name).restype = I32
     _lib = L
     return L
@@ -565,6 +566,17 @@ def probe_mfma_bf16(operands, n_blocks: int, iters: int, distinct: int = 8, out=
         out = torch.empty((n_blocks * 256,), dtype=torch.float32, device=operands.device)
     _check(lib().beam_probe_mfma_bf16(_ptr(operands), n_blocks, iters, distinct, _ptr(out), _stream(stream)))
     return n_blocks * 4 * iters * 16 * 32768
+
+
+def probe_mfma16_bf16(operands, n_blocks: int, iters: int, distinct: int = 8, out=None, stream=None):
+    """The same loop with the 16x16x32 bf16 MFMA (beam_probe_mfma16_bf16); the
+    same work, returned as flops."""
+    import torch
+    _need(operands, torch.int32, (n_blocks * 256 * 64,), "operands")
+    if out is None:
+        out = torch.empty((n_blocks * 256,), dtype=torch.float32, device=operands.device)
+    _check(lib().beam_probe_mfma16_bf16(_ptr(operands), n_blocks, iters, distinct, _ptr(out), _stream(stream)))
+    return n_blocks * 4 * iters * 32 * 16384
 
 
 def probe_stream_read(buf, n_blocks: int, out=None, stream=None):

@@ -38,6 +38,35 @@ __global__ void __launch_bounds__(256) probe_mfma_kernel(const uint32_t* operand
   out[th] = s;
 }
 
+// The same work with v_mfma_f32_16x16x32_bf16: 32 MFMAs of half the flops per
+// iteration over 8 accumulators (each MFMA still reads a fresh A and B).
+__global__ void __launch_bounds__(256) probe_mfma16_kernel(const uint32_t* operands, int iters, int distinct,
+                                                           float* out) {
+  const size_t th = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const u32x4* src = reinterpret_cast<const u32x4*>(operands + th * 64);
+  u32x4 a[8], b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = src[i % distinct];
+    b[i] = src[8 + i % distinct];
+  }
+  f32x4 acc[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      acc[i & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[i & 7]), as_bf16x8(b[(3 * i + (i >> 3)) & 7]),
+                                                           acc[i & 7], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s += acc[r][i];
+  out[th] = s;
+}
+
 __global__ void __launch_bounds__(256) probe_read_kernel(const u32x4* buf, size_t n16, uint32_t* out) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -77,6 +106,19 @@ beam_status beam_probe_mfma_bf16(const uint32_t* operands, int32_t n_blocks, int
   hipLaunchKernelGGL(beam::probe_mfma_kernel, dim3((unsigned)n_blocks), dim3(256), 0, (hipStream_t)stream, operands,
                      iters, distinct, out);
   return probe_launch(hipGetLastError(), "probe_mfma launch");
+}
+
+beam_status beam_probe_mfma16_bf16(const uint32_t* operands, int32_t n_blocks, int32_t iters, int32_t distinct,
+                                   float* out, void* stream) {
+  beam::clear_stale_error();
+  if (!operands || !out) return beam::set_error(BEAM_E_NULL, "operands or out is NULL", hipSuccess);
+  if (n_blocks <= 0 || iters <= 0 || distinct < 1 || distinct > 8)
+    return beam::set_error(BEAM_E_RANGE, "n_blocks, iters > 0 and 1 <= distinct <= 8 required", hipSuccess);
+  if (reinterpret_cast<uintptr_t>(operands) % 16 != 0)
+    return beam::set_error(BEAM_E_RANGE, "operands must be 16-byte aligned", hipSuccess);
+  hipLaunchKernelGGL(beam::probe_mfma16_kernel, dim3((unsigned)n_blocks), dim3(256), 0, (hipStream_t)stream,
+                     operands, iters, distinct, out);
+  return probe_launch(hipGetLastError(), "probe_mfma16 launch");
 }
 
 beam_status beam_probe_stream_read(const void* buf, size_t bytes, int32_t n_blocks, uint32_t* out, void* stream) {

@@ -5,7 +5,9 @@
  * can be reported as a fraction of a measured ceiling beside the fraction of
  * the published peak (dense bf16 MFMA 2.5 PFLOP/s, HBM3E 8 TB/s):
  *   - the bf16 matrix-core rate on operands with random mantissas (the chip
- *     runs slower on random data than on constant data: it is power-limited);
+ *     runs slower on random data than on constant data: it is power-limited),
+ *     for the two bf16 MFMA shapes (the 16x16x32 instruction sustains about
+ *     half as much again as 32x32x16 on the same loop);
  *   - the HBM read rate of a plain streaming read.
  * Neither is part of the attention path. Conventions as in beam_attn.h:
  * device pointers, work enqueued on `stream`, arguments checked on the host
@@ -36,6 +38,12 @@ extern "C" {
  * several milliseconds. */
 beam_status beam_probe_mfma_bf16(const uint32_t *operands, int32_t n_blocks, int32_t iters, int32_t distinct,
                                  float *out, void *stream);
+
+/* The same loop with v_mfma_f32_16x16x32_bf16: 32 MFMAs per iteration over 8
+ * accumulators, the same operands and the same work (n_blocks * 4 waves *
+ * iters * 32 MFMAs * 16384 flop = the figure above). */
+beam_status beam_probe_mfma16_bf16(const uint32_t *operands, int32_t n_blocks, int32_t iters, int32_t distinct,
+                                   float *out, void *stream);
 
 /* Streaming read of `bytes` (a multiple of 16, 16-byte aligned) with 16-byte
  * non-temporal loads, grid-stride over n_blocks blocks of 256 threads, eight
