@@ -98,20 +98,23 @@ __device__ __forceinline__ float ssmax_scale(int t, float base, float expo) {
 }
 
 // RoPE inverse frequency theta^(-2i/128) of pair i (float64).
-__device__ __forceinline__ double rope_inv_freq(int i, float theta) {
-  return pow((double)theta, -2.0 * (double)i / (double)D);
+// RoPE frequency of pair i in revolutions per position: theta^(-2i/d) / (2 pi).
+__device__ __forceinline__ double rope_rev_per_pos(int i, float theta) {
+  return pow((double)theta, -2.0 * (double)i / (double)D) * 0.15915494309189533577;
 }
-// cos/sin of t * w: the angle is formed and reduced to [-pi, pi] in float64,
-// then its cosine and sine are taken in float32 (error ~1e-7, far below the
-// bf16 rounding of the rotated vectors).
-__device__ __forceinline__ void rope_cs_w(int t, double w, float* c, float* s) {
-  const double ang = (double)t * w;
-  const double two_pi = 6.283185307179586476925;
-  const float r = (float)(ang - two_pi * rint(ang / two_pi));
-  sincosf(r, s, c);
+// cos/sin of the angle of position t: formed in revolutions in float64 and
+// reduced to [-1/2, 1/2], then v_cos_f32 / v_sin_f32 (which take revolutions)
+// in float32. Their error (~1e-6) is far below the bf16 rounding of the
+// rotated vectors; a float32 product t * r would carry up to 0.01 revolutions
+// of error at t = 10^6.
+__device__ __forceinline__ void rope_cs_rev(int t, double r, float* c, float* s) {
+  const double rev = (double)t * r;
+  const float fr = (float)(rev - rint(rev));
+  *c = __builtin_amdgcn_cosf(fr);
+  *s = __builtin_amdgcn_sinf(fr);
 }
 __device__ __forceinline__ void rope_cs(int t, int i, float theta, float* c, float* s) {
-  rope_cs_w(t, rope_inv_freq(i, theta), c, s);
+  rope_cs_rev(t, rope_rev_per_pos(i, theta), c, s);
 }
 
 // Sum over the 16 lanes of an aligned 16-lane group.

@@ -60,7 +60,7 @@ __device__ __forceinline__ size_t cache_v_off(const PrologueParams& p, int cseq,
   return ((size_t)cseq * p.G + g) * D * p.window + t % p.window;
 }
 template <int KIND, int KV_FP8>
-__global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) prefill_prologue_kernel(PrologueParams p) {
   constexpr bool local = (KIND == 0);
   const int seq = blockIdx.x;
   const int part = blockIdx.z;
@@ -76,11 +76,16 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
   const int grp = tid >> 4;  // 16 groups of 16 lanes
   const int j = tid & 15;    // lane within group: coords [4j,4j+4) and [64+4j, 64+4j+4)
 
-  // Inverse RoPE frequencies of this lane's pairs 4j..4j+3.
-  double inv_freq[4];
+  // RoPE frequencies of this lane's pairs 4j..4j+3, in revolutions per
+  // position: the block's 64 values are formed once (one float64 pow per
+  // thread of the first wave) and shared through LDS.
+  double rev_freq[4];
   if (local && part != 1 && part != 2) {
+    __shared__ double s_rev[D / 2];
+    if (tid < D / 2) s_rev[tid] = rope_rev_per_pos(tid, p.rope_theta);
+    __syncthreads();
 #pragma unroll
-    for (int e = 0; e < 4; ++e) inv_freq[e] = rope_inv_freq(4 * j + e, p.rope_theta);
+    for (int e = 0; e < 4; ++e) rev_freq[e] = s_rev[4 * j + e];
   }
 
   if (part >= kPrologueFixedParts) {
@@ -106,7 +111,7 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
       float cs[4], sn[4];
       if (local) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rope_cs_w(t, inv_freq[e], &cs[e], &sn[e]);
+        for (int e = 0; e < 4; ++e) rope_cs_rev(t, rev_freq[e], &cs[e], &sn[e]);
       }
       const float scale = local ? qbase : qbase * ssmax_scale(t, p.ssmax_base, p.ssmax_exp);
       u32x2* dst = reinterpret_cast<u32x2*>(p.qp + (tok * p.H + h_lo) * D);
@@ -180,7 +185,7 @@ __global__ void __launch_bounds__(256) prefill_prologue_kernel(PrologueParams p)
       float cs[4], sn[4];
       if (local) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rope_cs_w(t, inv_freq[e], &cs[e], &sn[e]);
+        for (int e = 0; e < 4; ++e) rope_cs_rev(t, rev_freq[e], &cs[e], &sn[e]);
       }
 #pragma unroll
       for (int g = 0; g < kMaxHeadsPerGroup; ++g)
