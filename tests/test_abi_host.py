@@ -87,6 +87,7 @@ def _cache(kind=ga.GLOBAL, page_size=16):
 
 def test_argument_checks_fail_before_launch():
     L = ga.lib()
+    assert _call_prefill(ga.Config(), _cache(), n_tok=0, max_chunk=0) == 0  # empty work, nothing launched
     assert _call_prefill(ga.Config(head_dim=64), _cache()) == 4
     assert _call_prefill(ga.Config(n_q_heads=47), _cache()) == 2
     assert _call_prefill(ga.Config(n_q_heads=48, n_kv_heads=2), _cache()) == 4   # 24 heads per KV head

@@ -187,6 +187,33 @@ def test_prefill_varlen_ragged(kind):
 
 
 @pytest.mark.parametrize("kind", [O.LOCAL, O.GLOBAL])
+def test_prefill_batch_with_empty_sequences(kind):
+    """Zero-length sequences inside and at the end of a varlen batch: the
+    others match the oracle, and the empty ones' cache stays untouched."""
+    import torch
+    lens = [5, 0, 200, 0]
+    inps = [_inputs(11, 10 * kind + i, max(n, 1)) for i, n in enumerate(lens)]
+    inps = [{k: (v[:n] if v.ndim == 3 else v) for k, v in x.items()} for x, n in zip(inps, lens)]
+    for x in inps[1:]:
+        x["q_norm_w"], x["k_norm_w"] = inps[0]["q_norm_w"], inps[0]["k_norm_w"]
+    cache, bt = _cache_for(kind, 11, lens)
+    say(f"[case] prefill with empty sequences kind={kind} lens={lens}")
+    outs = _run_prefill(kind, inps, [0] * len(lens), cache, list(range(len(lens))), max_chunk=max(lens))
+    for i, (x, o) in enumerate(zip(inps, outs)):
+        assert o.shape[0] == lens[i]
+        if lens[i]:
+            pos = np.arange(lens[i])
+            compare(o, _oracle_layer(kind, x, slice(None), slice(None), pos, pos), f"seq{i} len={lens[i]}")
+    k = host_bits(cache.k)
+    if kind == O.GLOBAL:
+        used = set(int(p) for row in bt for p in row if p >= 0)
+        unused = [p for p in range(k.shape[0]) if p not in used]
+        assert unused and np.all(k[unused] == SENT)
+    else:
+        assert np.all(k[1] == SENT) and np.all(k[3] == SENT)
+
+
+@pytest.mark.parametrize("kind", [O.LOCAL, O.GLOBAL])
 def test_chunked_prefill_with_cached_prefix(kind):
     """Unaligned chunks of two interleaved sequences; each chunk attends to the
     cached prefix written by earlier chunks."""
