@@ -12,17 +12,23 @@
 // one query head, on local layers two query heads of one KV group, each with
 // 64 queries (so the four waves read the same key tiles). KV tiles of 64 keys
 // are double-buffered in LDS. Each wave computes
-// S^T = K Q'^T with v_mfma_f32_32x32x16_bf16 (keys on M, its queries on N), so
-// a lane holds one query column and the row max is an in-lane max plus one
-// v_permlane32_swap. The S accumulators are packed to bf16 and fed directly as
-// the B operand of O^T += V^T P^T.
+// S^T = K Q'^T with v_mfma_f32_16x16x32_bf16 (key blocks of 16 on M, two
+// 16-query column blocks on N): a lane holds one query of each column block,
+// a query's 64 keys of a tile are spread over the four 16-lane groups, and
+// the row max is an in-lane max plus two lane swaps (v_permlane16_swap, then
+// v_permlane32_swap). The S accumulators are packed to bf16 and fed directly
+// as the B operand of O^T += V^T P^T. Under the chip's power limit the
+// 16x16x32 form holds a higher clock than 32x32x16 for the same multiply-adds
+// (2-3 % faster on a 32K-token global layer). The verify kernel keeps
+// 32x32x16: its rows are (token, head) pairs, 32 per wave.
 //
 // LDS layout. Tiles that lie inside the chunk are copied from the workspace
 // straight into LDS with global_load_lds_dwordx4 (no staging registers).
 //   K:   two coordinate halves, each 64 rows x 128 B. LDS row m holds key
-//        kappa(m) = m with bits 2 and 3 swapped; the MFMA output row order
-//        then becomes natural key order, which is the order the PV operand
-//        needs.
+//        kappa(m), a permutation that turns the MFMA output row order into
+//        the key order the PV operand needs: in the prefill kernel row
+//        16b + 4g + i holds key 32(b >> 1) + 8g + 4(b & 1) + i (krow_key16),
+//        in the verify kernel m with bits 2 and 3 swapped (krow_key).
 //   V^T: 128 rows (coordinates) x 128 B (64 keys, natural order).
 // Both XOR-swizzle their 16-byte chunks with bits 1..3 of the row. A b128
 // read is served 16 lanes per LDS cycle, and the operand reads have those
@@ -50,8 +56,9 @@
 
 namespace beam {
 
-constexpr int QW = 32;                   // queries per wave (one 32-wide MFMA N-block)
-constexpr int NB = QW / 32;
+constexpr int QW = 32;                   // queries per wave
+constexpr int NB = QW / 32;              // 32-query column blocks (verify's 32x32x16 layout)
+constexpr int QB = QW / 16;              // 16-query column blocks (prefill's 16x16x32 layout)
 constexpr int BN = 64;                   // keys per tile
 constexpr int K_TILE = BN * D;           // bf16 elements
 constexpr int V_TILE = D * BN;
@@ -73,8 +80,17 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 constexpr float kRescaleThreshold = 8.0f;
 
-// Key held by LDS row m of a K tile (bits 2 and 3 swapped; an involution).
+// Key held by LDS row m of a K tile for the 32x32x16 operand layout (bits 2
+// and 3 swapped; an involution): the verify kernel.
 __device__ __forceinline__ int krow_key(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+// Key held by LDS row m of a K tile for the 16x16x32 layout of the prefill
+// kernel: row 16b + 4g + i (key block b = m >> 4, lane group g) holds key
+// 32(b >> 1) + 8g + 4(b & 1) + i, so lane group g's four S rows of key blocks
+// 2c and 2c+1 are keys 32c + 8g + 0..7 in order, the B operand of PV. The 8
+// rows of one DMA instruction (8a .. 8a+7) stay inside one 16-key page.
+__device__ __forceinline__ int krow_key16(int m) { return (m & 0x23) | ((m & 0x0c) << 1) | ((m & 0x10) >> 2); }
+template <bool P16>
+__device__ __forceinline__ int krow(int m) { return P16 ? krow_key16(m) : krow_key(m); }
 // LDS tile layout. Every LDS row is 128 bytes (eight 16-byte chunks) and
 // chunk c of row r sits at position c ^ ((r >> 1) & 7): the 16 lanes that one
 // LDS cycle serves read rows r .. r+15 (two rows per 256-byte bank line), so
@@ -96,6 +112,16 @@ __device__ __forceinline__ float max_halves(float x) {
 __device__ __forceinline__ float sum_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Combine a value over the four lane groups l, l^16, l^32, l^48 (the 16x16
+// layout spreads a query's keys over them): v_permlane16_swap, then 32.
+__device__ __forceinline__ float max_groups(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max_halves(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float sum_groups(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return sum_halves(__uint_as_float(r[0]) + __uint_as_float(r[1]));
 }
 
 // Where the keys of one (sequence, KV head) live: keys from start & ~63 on
@@ -152,7 +178,7 @@ struct DmaPlan {
   }
 };
 
-template <int NW>
+template <int NW, bool P16 = false>
 __device__ __forceinline__ DmaPlan<NW> make_dma_plan(int w, int lane) {
   DmaPlan<NW> pl;
 #pragma unroll
@@ -160,7 +186,7 @@ __device__ __forceinline__ DmaPlan<NW> make_dma_plan(int w, int lane) {
     const int kI = w * DmaPlan<NW>::N + i;  // K half kI / 8, rows 8(kI % 8) .. +7
     const int m = 8 * (kI & 7) + (lane >> 3);
     const int c = (lane & 7) ^ ((m >> 1) & 7);
-    pl.k_src[i] = (uint32_t)(krow_key(m) * D + 64 * (kI >> 3) + 8 * c);
+    pl.k_src[i] = (uint32_t)(krow<P16>(m) * D + 64 * (kI >> 3) + 8 * c);
     pl.k_lds[i] = kI * 512;
     const int vI = w * DmaPlan<NW>::N + i;  // V^T rows 8vI .. 8vI+7
     const int d = 8 * vI + (lane >> 3);
@@ -185,7 +211,7 @@ __device__ __forceinline__ const uint16_t* v_elem_src(const KeySource& ks, int d
 // DMA of a tile of the cached prefix (all keys below start & ~63): every lane
 // computes the address of its 16-byte chunk from the key's page or ring slot.
 // Requires a valid cache row.
-template <int NW>
+template <int NW, bool P16 = false>
 __device__ __forceinline__ void dma_tile_prefix(const KeySource& ks, int w, int lane, int key0, uint16_t* sK,
                                                 uint16_t* sV) {
 #pragma unroll
@@ -193,7 +219,7 @@ __device__ __forceinline__ void dma_tile_prefix(const KeySource& ks, int w, int 
     const int kI = w * DmaPlan<NW>::N + i;
     const int m = 8 * (kI & 7) + (lane >> 3);
     const int c = (lane & 7) ^ ((m >> 1) & 7);
-    lds_dma16(k_row_src(ks, key0 + krow_key(m)) + 64 * (kI >> 3) + 8 * c, sK + kI * 512);
+    lds_dma16(k_row_src(ks, key0 + krow<P16>(m)) + 64 * (kI >> 3) + 8 * c, sK + kI * 512);
 
     const int vI = w * DmaPlan<NW>::N + i;
     const int d = 8 * vI + (lane >> 3);
@@ -206,7 +232,7 @@ __device__ __forceinline__ void dma_tile_prefix(const KeySource& ks, int w, int 
 // given (pg holds page id (lane & 3) of the tile in every lane). A K
 // instruction moves 8 rows of one page (its page id is wave-uniform); the
 // lanes of a V^T instruction span the four pages, each picks its own.
-template <int NW>
+template <int NW, bool P16 = false>
 __device__ __forceinline__ void dma_tile_paged(const KeySource& ks, int pg, int w, int lane, uint16_t* sK,
                                                uint16_t* sV) {
   const int p0 = __builtin_amdgcn_readlane(pg, 0), p1 = __builtin_amdgcn_readlane(pg, 1);
@@ -216,9 +242,9 @@ __device__ __forceinline__ void dma_tile_paged(const KeySource& ks, int pg, int 
     const int kI = w * DmaPlan<NW>::N + i;
     const int m = 8 * (kI & 7) + (lane >> 3);
     const int c = (lane & 7) ^ ((m >> 1) & 7);
-    const int kp = (kI & 7) >> 1;  // page of rows 8(kI & 7) .. +7 (the row permutation stays inside a page)
+    const int kp = krow<P16>(8 * (kI & 7)) >> 4;  // page of rows 8(kI & 7) .. +7 (one page, wave-uniform)
     const int kpage = kp == 0 ? p0 : kp == 1 ? p1 : kp == 2 ? p2 : p3;
-    lds_dma16(ks.ck + kpage * ks.page_stride + (uint32_t)((krow_key(m) & 15) * D + 64 * (kI >> 3) + 8 * c),
+    lds_dma16(ks.ck + kpage * ks.page_stride + (uint32_t)((krow<P16>(m) & 15) * D + 64 * (kI >> 3) + 8 * c),
               sK + kI * 512);
 
     const int vI = w * DmaPlan<NW>::N + i;
@@ -266,7 +292,7 @@ __device__ __forceinline__ CodeSource make_code_source(const PrefillParams& p, i
 // DMA of the code tile whose first key is key0 (a multiple of 64): 8 K and 8
 // V instructions of 1 KiB, 8 / NW of each per wave. page(i) is the physical
 // page of logical page i (paged caches). NT: non-temporal hint.
-template <int NW, bool NT = false, typename PageOf>
+template <int NW, bool NT = false, bool P16 = false, typename PageOf>
 __device__ __forceinline__ void dma_code_tile(const CodeSource& c, PageOf page, int w, int lane, int key0,
                                               uint8_t* slot) {
   // every source address first (the page lookups together), then the DMAs
@@ -278,7 +304,7 @@ __device__ __forceinline__ void dma_code_tile(const CodeSource& c, PageOf page, 
     {  // K rows 8 ins .. 8 ins + 7
       const int m = 8 * ins + (lane >> 3);
       const int cc = (lane & 7) ^ ((m >> 1) & 7);
-      const int s = key0 + krow_key(m);
+      const int s = key0 + krow<P16>(m);
       ksrc[i] = (c.kind == 1 ? c.k8 + (size_t)page(s >> 4) * c.page_stride + (uint32_t)((s & 15) * D)
                              : c.k8 + (uint32_t)((s % c.window) * D)) + 16 * cc;
     }
@@ -333,10 +359,35 @@ __device__ __forceinline__ u32x4 code_kfrag(const uint8_t* slot, const CodeOffse
 __device__ __forceinline__ u32x4 code_vfrag(const uint8_t* slot, const CodeOffsets& co, int kb, int db) {
   return codes_to_bf16(*reinterpret_cast<const u32x2*>(slot + co.v[kb] + 2048 * db));
 }
-// Q' fragments times k_scale (one bf16 rounding), for the code space of an FP8 cache.
-__device__ __forceinline__ void scale_frags(u32x4 (&qf)[8], float k_scale) {
+// The same for the 16x16x32 layout of the prefill kernel: K for d-step kk
+// (4 offsets, + 2048 per key block of 16 rows), V^T for key chunk c2 (2
+// offsets, + 1024 per row block of 16).
+struct CodeOffsets16 {
+  int k[4];
+  int v[2];
+};
+__device__ __forceinline__ CodeOffsets16 code_offsets16(int c16, int lg) {
+  CodeOffsets16 co;
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
+  for (int kk = 0; kk < 4; ++kk) co.k[kk] = c16 * 128 + 16 * ((2 * kk + (lg >> 1)) ^ ((c16 >> 1) & 7)) + 8 * (lg & 1);
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2)
+    co.v[c2] = kCodeVOff + c16 * 64 + 16 * ((2 * c2 + (lg >> 1)) ^ ((c16 >> 2) & 3)) + 8 * (lg & 1);
+  return co;
+}
+// K fragment of d-step kk, key block kb: row 16kb + c16, codes 32kk + 8lg + 0..7.
+__device__ __forceinline__ u32x4 code_kfrag16(const uint8_t* slot, const CodeOffsets16& co, int kk, int kb) {
+  return codes_to_bf16(*reinterpret_cast<const u32x2*>(slot + co.k[kk] + 2048 * kb));
+}
+// V^T fragment of key chunk c2, row block db: row 16db + c16, keys 32c2 + 8lg + 0..7.
+__device__ __forceinline__ u32x4 code_vfrag16(const uint8_t* slot, const CodeOffsets16& co, int c2, int db) {
+  return codes_to_bf16(*reinterpret_cast<const u32x2*>(slot + co.v[c2] + 1024 * db));
+}
+// Q' fragments times k_scale (one bf16 rounding), for the code space of an FP8 cache.
+template <int NF>
+__device__ __forceinline__ void scale_frags(u32x4 (&qf)[NF], float k_scale) {
+#pragma unroll
+  for (int kk = 0; kk < NF; ++kk)
 #pragma unroll
     for (int c = 0; c < 4; ++c) qf[kk][c] = pack_bf16x2(bf16lo(qf[kk][c]) * k_scale, bf16hi(qf[kk][c]) * k_scale);
 }
@@ -378,8 +429,8 @@ prefill_attn_kernel(PrefillParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (DMA bases go to M0)
-  const int n = lane & 31;
-  const int half = lane >> 5;
+  const int c16 = lane & 15;  // row of the MFMA A operand, column of B and of C
+  const int lg = lane >> 4;   // lane group: k-slice 8lg of A and B, C rows 4lg .. 4lg+3
   const int h = g * hpg + hh0 + w / WQ;  // this wave's query head
 
   const int q0 = start + qt * BM;                   // first query position of the block
@@ -410,23 +461,23 @@ prefill_attn_kernel(PrefillParams p) {
   ks.P = p.P;
   ks.kind = KIND;
   ks.window = W;
-  const DmaPlan<NWAVES> plan = make_dma_plan<NWAVES>(w, lane);
+  const DmaPlan<NWAVES> plan = make_dma_plan<NWAVES, true>(w, lane);
   CodeSource cs8;
   if constexpr (KV_FP8) cs8 = make_code_source(p, KIND, cseq, g);
 
-  // Q' fragments (B operand of S^T = K Q'^T): lane holds query n of N-block nb,
-  // coordinates 16kk + 8*half + 0..7.
-  u32x4 qf[NB][8];
+  // Q' fragments (B operand of S^T = K Q'^T): lane holds query c16 of column
+  // block qb, coordinates 32kk + 8lg + 0..7.
+  u32x4 qf[QB][4];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
+  for (int qb = 0; qb < QB; ++qb) {
     // a query past the chunk's end loads the last valid row: its column of
     // S, P and O only feeds its own (never written) output
-    const int t = min(wq_lo + 32 * nb + n, qlast);
+    const int t = min(wq_lo + 16 * qb + c16, qlast);
     const size_t tok = (size_t)(cu0 + (t - start));
-    const uint16_t* qrow = p.qp + (tok * p.H + h) * D + 8 * half;
+    const uint16_t* qrow = p.qp + (tok * p.H + h) * D + 8 * lg;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qf[nb][kk] = *reinterpret_cast<const u32x4*>(qrow + 16 * kk);
-    if constexpr (KV_FP8) scale_frags(qf[nb], p.k_scale);  // code space: q' k_scale against the codes
+    for (int kk = 0; kk < 4; ++kk) qf[qb][kk] = *reinterpret_cast<const u32x4*>(qrow + 32 * kk);
+    if constexpr (KV_FP8) scale_frags(qf[qb], p.k_scale);  // code space: q' k_scale against the codes
   }
 
   const int j_ws = start >> 6;  // first tile in the workspace; earlier tiles are wholly cached
@@ -434,36 +485,32 @@ prefill_attn_kernel(PrefillParams p) {
   const int j_lo = cache_ok ? kmin >> 6 : max(kmin >> 6, j_ws);
   const int j_hi = qlast >> 6;
 
-  f32x16 o[NB][4];
+  f32x4 o[QB][8];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[nb][db][i] = 0.f;
+    for (int db = 0; db < 8; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   // m_run: reference of the query (kNegInf until a key is visible); sref holds
   // -m_run (0 while m_run is kNegInf) splatted, the accumulator input of S.
-  float m_run[NB], l_run[NB];
-  f32x16 sref[NB];
+  float m_run[QB], l_run[QB];
+  f32x4 sref[QB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    m_run[nb] = kNegInf;
-    l_run[nb] = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sref[nb][i] = 0.f;
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = kNegInf;
+    l_run[qb] = 0.f;
+    sref[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // Loop-invariant LDS element offsets of this lane's operand chunks: K row n,
-  // chunk 2q + half for q = 0..3 (chunks 8..15 are the second coordinate half,
-  // K_HALF further; M-block 1 adds 32 rows); V^T row n, chunk 2kb + half (row
-  // block db adds 32 rows).
-  int koff[4], voff[4];
+  // Loop-invariant LDS element offsets of this lane's operand chunks: K row
+  // c16, chunk 4kk + lg (chunks 8..15 are the second coordinate half; key
+  // block kb adds 16 rows); V^T row c16, chunk 4c2 + lg (row block db adds 16
+  // rows).
+  int koff[4], voff[2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    koff[q] = k_off(n, 2 * q + half);
-    voff[q] = v_off(n, 2 * q + half);
-  }
-  [[maybe_unused]] CodeOffsets co;
-  if constexpr (KV_FP8) co = code_offsets(n, half);
+  for (int kk = 0; kk < 4; ++kk) koff[kk] = k_off(c16, 4 * kk + lg);
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) voff[c2] = v_off(c16, 4 * c2 + lg);
+  [[maybe_unused]] CodeOffsets16 co;
+  if constexpr (KV_FP8) co = code_offsets16(c16, lg);
 
   // ---- pieces of one 64-key tile of attention for this wave's queries ----
   // Tile jt uses LDS slot (jt - j_lo) % SLOTS; the loop is unrolled by SLOTS
@@ -477,102 +524,100 @@ prefill_attn_kernel(PrefillParams p) {
     const int k0 = j * BN;
     return (k0 + BN - 1 > wq_lo) || (local && k0 < wq_hi - (W - 1));
   };
-  // S^T - m = K Q'^T - m: LDS rows 32mb + (lane&31) on M, queries 32nb + n on
-  // N; the chain starts from sref = -m.
+  // S^T - m = K Q'^T - m with v_mfma_f32_16x16x32_bf16: LDS rows 16kb + c16
+  // on M (key block kb), queries 16qb + c16 on N; the chain starts from
+  // sref = -m. Element i of block (qb, kb) holds key 32(kb >> 1) + 8lg +
+  // 4(kb & 1) + i of the tile (the K row permutation).
   // CODES: the tile holds FP8 codes (converted after the LDS read).
-  auto qk = [&](auto B, auto CODES, f32x16 (&s)[NB][2]) {
+  auto qk = [&](auto B, auto CODES, f32x4 (&s)[QB][4]) {
     const uint16_t* sK = buf(B);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
+    for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int kb = 0; kb < 4; ++kb) {
         u32x4 a;
         if constexpr (decltype(CODES)::value)
-          a = code_kfrag(reinterpret_cast<const uint8_t*>(sK), co, kk, mb);
+          a = code_kfrag16(reinterpret_cast<const uint8_t*>(sK), co, kk, kb);
         else
-          a = *reinterpret_cast<const u32x4*>(sK + koff[kk & 3] + K_HALF * (kk >> 2) + 32 * 64 * mb);
+          a = *reinterpret_cast<const u32x4*>(sK + koff[kk] + 1024 * kb);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          s[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qf[nb][kk]),
-                                                             kk == 0 ? sref[nb] : s[nb][mb], 0, 0, 0);
+        for (int qb = 0; qb < QB; ++qb)
+          s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qf[qb][kk]),
+                                                             kk == 0 ? sref[qb] : s[qb][kb], 0, 0, 0);
       }
     }
     if constexpr (!decltype(CODES)::value) {
       // K fragment reads run two k-steps ahead of the MFMAs that use them, so
-      // the LDS latency hides behind the matrix work (the default schedule
-      // read one k-step and waited; 1-2 % on a local layer)
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-      static_for<5>([&](auto) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NB, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      // the LDS latency hides behind the matrix work
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      static_for<2>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * QB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
       });
-      __builtin_amdgcn_sched_group_barrier(0x008, 6 * NB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8 * QB, 0);
     }
   };
-  // Element i of block mb holds key 64j + 8*half + c with c = 32mb + 16(i>>3)
-  // + (i&7), a constant of the element. Per lane and tile the visible range
-  // of c is [t - (W-1) - base, t - base] (base = 64j + 8*half): it becomes a
-  // 64-bit mask once per lane (only the bounds that cut into the tile), and
-  // each element then costs a bit-field extract and a bit-field insert (no
-  // per-element compare results held in scalar registers).
-  auto apply_mask = [&](int j, f32x16 (&s)[NB][2]) {
+  // Per lane and query the visible key offsets c of the tile (relative to its
+  // first key k0) are [t - (W-1) - k0, t - k0]: a 64-bit mask once per lane
+  // and column block (only the bounds that cut into the tile), shifted by the
+  // lane group's 8lg; each element then costs a bit-field extract and a
+  // bit-field insert.
+  auto apply_mask = [&](int j, f32x4 (&s)[QB][4]) {
     const int k0 = j * BN;
     const bool diag = k0 + BN - 1 > wq_lo;
     const bool edge = local && k0 < wq_hi - (W - 1);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int t = wq_lo + 32 * nb + n;
-      const int base = k0 + 8 * half;
-      // visibility of key offsets c = 0..63 as a bit mask; element c keeps
-      // its score where bit c is set, else takes -inf (bit-field extract and
-      // bit-field insert: two instructions per element)
+    for (int qb = 0; qb < QB; ++qb) {
+      const int t = wq_lo + 16 * qb + c16;
       uint64_t vis = ~0ull;
       if (diag) {
-        const int hi = t - base;  // visible: c <= hi
+        const int hi = t - k0;  // visible: c <= hi
         vis &= hi >= 63 ? ~0ull : hi < 0 ? 0ull : (2ull << hi) - 1;
       }
       if (edge) {
-        const int lo = t - (W - 1) - base;  // visible: c >= lo
+        const int lo = t - (W - 1) - k0;  // visible: c >= lo
         vis &= lo <= 0 ? ~0ull : lo >= 64 ? 0ull : ~((1ull << lo) - 1);
       }
+      const uint64_t vs = vis >> (8 * lg);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const uint32_t word = (uint32_t)(vis >> (32 * mb));
+      for (int kb = 0; kb < 4; ++kb) {
+        const uint32_t word = (uint32_t)(vs >> (32 * (kb >> 1)));
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int c = 16 * (i >> 3) + (i & 7);
+        for (int i = 0; i < 4; ++i) {
+          const int c = 4 * (kb & 1) + i;
           const uint32_t m = (uint32_t)((int32_t)(word << (31 - c)) >> 31);
-          s[nb][mb][i] = __uint_as_float((__float_as_uint(s[nb][mb][i]) & m) | (0xff800000u & ~m));
+          s[qb][kb][i] = __uint_as_float((__float_as_uint(s[qb][kb][i]) & m) | (0xff800000u & ~m));
         }
       }
     }
   };
   // Shift of the reference this tile needs, per query: the tile max of the
   // shifted scores when it exceeds the threshold (or is the first finite
-  // score of the query), else 0.
-  auto tile_max = [&](const f32x16 (&s)[NB][2], float (&mt)[NB]) {
+  // score of the query), else 0. A query's 64 keys sit in its four lane
+  // groups (16 each).
+  auto tile_max = [&](const f32x4 (&s)[QB][4], float (&mt)[QB]) {
     bool maybe = false;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
+    for (int qb = 0; qb < QB; ++qb) {
       float x = kNegInf;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x = fmaxf(x, s[nb][mb][i]);
-      mt[nb] = max_halves(x);
+        for (int i = 0; i < 4; ++i) x = fmaxf(x, s[qb][kb][i]);
+      mt[qb] = max_groups(x);
       // a reference moves only on a query's first finite score or when the
       // tile max passes the threshold: one cheap test per lane
-      maybe = maybe || mt[nb] > kRescaleThreshold || m_run[nb] == kNegInf;
+      maybe = maybe || mt[qb] > kRescaleThreshold || m_run[qb] == kNegInf;
     }
     return maybe;
   };
-  auto row_shift = [&](const float (&mt)[NB], float (&delta)[NB], bool (&need)[NB]) {
+  auto row_shift = [&](const float (&mt)[QB], float (&delta)[QB], bool (&need)[QB]) {
     bool grow = false;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      need[nb] = (m_run[nb] == kNegInf) ? (mt[nb] != kNegInf) : (mt[nb] > kRescaleThreshold);
-      delta[nb] = need[nb] ? mt[nb] : 0.f;
-      grow = grow || need[nb];
+    for (int qb = 0; qb < QB; ++qb) {
+      need[qb] = (m_run[qb] == kNegInf) ? (mt[qb] != kNegInf) : (mt[qb] > kRescaleThreshold);
+      delta[qb] = need[qb] ? mt[qb] : 0.f;
+      grow = grow || need[qb];
     }
     return grow;
   };
@@ -580,66 +625,68 @@ prefill_attn_kernel(PrefillParams p) {
   // rescale while no key was visible) and shift this tile's scores.
   // O is still zero at a query's first visible key (alpha 1), so a block's
   // first reference move skips the O multiply.
-  auto rescale = [&](const float (&delta)[NB], const bool (&need)[NB], f32x16 (&s)[NB][2]) {
-    float alpha[NB];
+  auto rescale = [&](const float (&delta)[QB], const bool (&need)[QB], f32x4 (&s)[QB][4]) {
+    float alpha[QB];
     bool scale_o = false;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const bool first = m_run[nb] == kNegInf;
-      alpha[nb] = first ? 1.f : __builtin_amdgcn_exp2f(-delta[nb]);
-      scale_o = scale_o || alpha[nb] != 1.f;
-      if (need[nb]) m_run[nb] = (first ? 0.f : m_run[nb]) + delta[nb];
-      const float r = m_run[nb] == kNegInf ? 0.f : -m_run[nb];
+    for (int qb = 0; qb < QB; ++qb) {
+      const bool first = m_run[qb] == kNegInf;
+      alpha[qb] = first ? 1.f : __builtin_amdgcn_exp2f(-delta[qb]);
+      scale_o = scale_o || alpha[qb] != 1.f;
+      if (need[qb]) m_run[qb] = (first ? 0.f : m_run[qb]) + delta[qb];
+      const float r = m_run[qb] == kNegInf ? 0.f : -m_run[qb];
+      sref[qb] = f32x4{r, r, r, r};
+      l_run[qb] *= alpha[qb];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sref[nb][i] = r;
-      l_run[nb] *= alpha[nb];
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[nb][mb][i] -= delta[nb];
+        for (int i = 0; i < 4; ++i) s[qb][kb][i] -= delta[qb];
     }
     if (__any(scale_o)) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < 8; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) o[nb][db][i] *= alpha[nb];
+          for (int i = 0; i < 4; ++i) o[qb][db][i] *= alpha[qb];
     }
   };
-  // P^T operand of key block kb: elements 8(kb&1)..+7 of S block kb>>1, i.e.
-  // keys 16kb + 8*half + 0..7 in order.
-  auto softmax = [&](const f32x16 (&s)[NB][2], u32x4 (&pf)[NB][4]) {
+  // P^T operand of key chunk c2 (keys 32c2 .. 32c2+31): lane group lg holds
+  // keys 32c2 + 8lg + 0..7 in order, elements 0..3 of S blocks 2c2 and 2c2+1.
+  auto softmax = [&](const f32x4 (&s)[QB][4], u32x4 (&pf)[QB][2]) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
+    for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int c2 = 0; c2 < 2; ++c2) {
         float e[8];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) e[jj] = __builtin_amdgcn_exp2f(s[nb][kb >> 1][8 * (kb & 1) + jj]);
+        for (int i = 0; i < 4; ++i) {
+          e[i] = __builtin_amdgcn_exp2f(s[qb][2 * c2][i]);
+          e[4 + i] = __builtin_amdgcn_exp2f(s[qb][2 * c2 + 1][i]);
+        }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          pf[nb][kb][c] = pack_bf16x2(e[2 * c], e[2 * c + 1]);
-          l_run[nb] = sum_bf16x2(pf[nb][kb][c], l_run[nb]);
+          pf[qb][c2][c] = pack_bf16x2(e[2 * c], e[2 * c + 1]);
+          l_run[qb] = sum_bf16x2(pf[qb][c2][c], l_run[qb]);
         }
       }
     }
   };
-  // O^T += V^T P^T: A operand = coordinates 32db + n, keys 16kb + 8*half + 0..7.
-  auto pv = [&](auto B, auto CODES, const u32x4 (&pf)[NB][4]) {
+  // O^T += V^T P^T: A operand = coordinates 16db + c16, keys 32c2 + 8lg + 0..7.
+  auto pv = [&](auto B, auto CODES, const u32x4 (&pf)[QB][2]) {
     const uint16_t* sV = buf(B) + K_TILE;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int c2 = 0; c2 < 2; ++c2) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
+      for (int db = 0; db < 8; ++db) {
         u32x4 a;
         if constexpr (decltype(CODES)::value)
-          a = code_vfrag(reinterpret_cast<const uint8_t*>(buf(B)), co, kb, db);
+          a = code_vfrag16(reinterpret_cast<const uint8_t*>(buf(B)), co, c2, db);
         else
-          a = *reinterpret_cast<const u32x4*>(sV + voff[kb] + 32 * BN * db);
+          a = *reinterpret_cast<const u32x4*>(sV + voff[c2] + 1024 * db);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          o[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pf[nb][kb]), o[nb][db], 0, 0, 0);
+        for (int qb = 0; qb < QB; ++qb)
+          o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(pf[qb][c2]), o[qb][db], 0, 0, 0);
       }
     }
   };
@@ -658,26 +705,26 @@ prefill_attn_kernel(PrefillParams p) {
     if (j >= j_ws)
       plan.copy(ks.kw, ks.vw, ks.ws_off, j * BN, sK, sK + K_TILE);
     else if constexpr (KIND == 1 && !KV_FP8)
-      dma_tile_paged<NWAVES>(ks, pg, w, lane, sK, sK + K_TILE);
+      dma_tile_paged<NWAVES, true>(ks, pg, w, lane, sK, sK + K_TILE);
     else if constexpr (KV_FP8)
-      dma_code_tile<NWAVES>(cs8, [&](int pg) { return ks.bt_row[pg]; }, w, lane, j * BN,
-                            reinterpret_cast<uint8_t*>(sK));
+      dma_code_tile<NWAVES, false, true>(cs8, [&](int pg) { return ks.bt_row[pg]; }, w, lane, j * BN,
+                                         reinterpret_cast<uint8_t*>(sK));
     else
-      dma_tile_prefix<NWAVES>(ks, w, lane, j * BN, sK, sK + K_TILE);
+      dma_tile_prefix<NWAVES, true>(ks, w, lane, j * BN, sK, sK + K_TILE);
   };
 
   // One 64-key tile of attention for this wave's queries (CODES: an FP8 code tile).
   auto tile = [&](int j, auto B, auto CODES) __attribute__((always_inline)) {
-    f32x16 st[NB][2];
+    f32x4 st[QB][4];
     qk(B, CODES, st);
     if (needs_mask(j)) apply_mask(j, st);
-    float mt[NB];
+    float mt[QB];
     if (__any(tile_max(st, mt))) {
-      float delta[NB];
-      bool need[NB];
+      float delta[QB];
+      bool need[QB];
       if (__any(row_shift(mt, delta, need))) rescale(delta, need, st);
     }
-    u32x4 pf[NB][4];
+    u32x4 pf[QB][2];
     softmax(st, pf);
     pv(B, CODES, pf);
   };
@@ -703,7 +750,7 @@ prefill_attn_kernel(PrefillParams p) {
       lds_dma16(p.gate + (tok * p.H + h) * D + 8 * c, dst + 512 * i);
     }
   };
-  static_assert(!local || (NB == 1 && NWAVES * QW * D <= K_TILE + V_TILE), "gate staging fits one slot");
+  static_assert(!local || (QW == 32 && NWAVES * QW * D <= K_TILE + V_TILE), "gate staging fits one slot");
   // Stage of tiles j0 .. j0+TPS-1 in slots S0 .. S0+TPS-1: before tile j0+u
   // is computed, tile j0+TPS+u is sent to the other stage's slot (freed by the
   // previous barrier); the barrier then publishes the next stage. On local
@@ -768,10 +815,11 @@ prefill_attn_kernel(PrefillParams p) {
     stage(jt + TPS, std::integral_constant<int, TPS>{});
   }
 
-  // Epilogue: normalise, gate, write bf16. Lane holds query n of each N-block
-  // and coordinates d = 32db + 8a + 4*half + 0..3. Every gate value is read
-  // before the first output store (gate and output are both bf16 rows, so the
-  // compiler would otherwise keep each load behind the previous store).
+  // Epilogue: normalise, gate, write bf16. Lane holds query c16 of each
+  // column block and coordinates d = 16db + 4lg + 0..3; its l is the sum over
+  // the four lane groups. Every gate value is read before the first output
+  // store (gate and output are both bf16 rows, so the compiler would
+  // otherwise keep each load behind the previous store).
   // Y = O v_scale / (l (1 + 2^z)), z = -(gate + bias) log2 e: the sigmoid and
   // the normalisation share one reciprocal (v_rcp_f32, 1 ulp; a correctly
   // rounded division costs ~12 instructions per element, and Y is rounded to
@@ -780,43 +828,37 @@ prefill_attn_kernel(PrefillParams p) {
   constexpr float kLog2e = 1.4426950408889634f;
   const float zb = -(p.gate_bias ? p.gate_bias[h] : 0.f) * kLog2e;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int t = wq_lo + 32 * nb + n;
-    const float l_tot = sum_halves(l_run[nb]);
+  for (int qb = 0; qb < QB; ++qb) {
+    const int t = wq_lo + 16 * qb + c16;
+    const float l_tot = sum_groups(l_run[qb]);
     if (t > qlast) continue;
     const float l_eff = l_tot > 0.f ? (KV_FP8 ? l_tot / p.v_scale : l_tot) : 1.f;
     const size_t tok = (size_t)(cu0 + (t - start));
-    uint16_t* orow = p.out + (tok * p.H + h) * D;
-    u32x2 gvs[4][4];
+    uint16_t* orow = p.out + (tok * p.H + h) * D + 4 * lg;
+    u32x2 gvs[8];
     if constexpr (local) {
-      const uint16_t* grow_ = smem + gate_slot * (K_TILE + V_TILE) + w * (QW * D) + n * D + 4 * half;
+      // staged row r = 16qb + c16: chunk 2db + (lg >> 1) at position chunk ^ (r & 15)
+      const int r = 16 * qb + c16;
+      const uint16_t* grow_ = smem + gate_slot * (K_TILE + V_TILE) + w * (QW * D) + r * D + 4 * (lg & 1);
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-          gvs[db][a] = *reinterpret_cast<const u32x2*>(grow_ + 8 * ((4 * db + a) ^ (n & 15)));
+      for (int db = 0; db < 8; ++db)
+        gvs[db] = *reinterpret_cast<const u32x2*>(grow_ + 8 * ((2 * db + (lg >> 1)) ^ (r & 15)));
     } else {
-      const uint16_t* grow_ = p.gate + (tok * p.H + h) * D + 4 * half;
+      const uint16_t* grow_ = p.gate + (tok * p.H + h) * D + 4 * lg;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) gvs[db][a] = *reinterpret_cast<const u32x2*>(grow_ + 32 * db + 8 * a);
+      for (int db = 0; db < 8; ++db) gvs[db] = *reinterpret_cast<const u32x2*>(grow_ + 16 * db);
     }
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < 8; ++db) {
+      const u32x2 gv = gvs[db];
+      const float gz[4] = {bf16lo(gv[0]), bf16hi(gv[0]), bf16lo(gv[1]), bf16hi(gv[1])};
+      float y[4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int d0 = 32 * db + 8 * a + 4 * half;
-        const u32x2 gv = gvs[db][a];
-        const float gz[4] = {bf16lo(gv[0]), bf16hi(gv[0]), bf16lo(gv[1]), bf16hi(gv[1])};
-        float y[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float ex = __builtin_amdgcn_exp2f(fmaf(gz[e], -kLog2e, zb));
-          y[e] = o[nb][db][4 * a + e] * __builtin_amdgcn_rcpf(fmaf(ex, l_eff, l_eff));
-        }
-        *reinterpret_cast<u32x2*>(orow + d0) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+      for (int e = 0; e < 4; ++e) {
+        const float ex = __builtin_amdgcn_exp2f(fmaf(gz[e], -kLog2e, zb));
+        y[e] = o[qb][db][e] * __builtin_amdgcn_rcpf(fmaf(ex, l_eff, l_eff));
       }
+      *reinterpret_cast<u32x2*>(orow + 16 * db) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
     }
   }
 }
