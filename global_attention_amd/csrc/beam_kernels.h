@@ -74,19 +74,23 @@ struct DecodeQParams {
   float k_scale;  // FP8 cache: K scale folded into Q' (1 for bf16)
 };
 
-// Prefill attention tiling: 32 queries per wavefront; 8 wavefronts per block
-// on global layers (one block per CU), 4 on local layers (two blocks per CU:
-// a window-limited tile range favours smaller, independent blocks). A local
-// block takes two query heads of one KV group (when the group's head count is
-// even) and 64 queries: its four waves then need the same key tiles (nine per
-// 64 aligned queries), so none idles at a barrier while the others compute.
+// Prefill attention tiling: 48 queries per wavefront and 8 wavefronts per
+// block on global layers (384 queries of one head, one block per CU); 32
+// queries per wavefront and 4 wavefronts per block on local layers (two
+// blocks per CU: a window-limited tile range favours smaller, independent
+// blocks). A local block takes two query heads of one KV group (when the
+// group's head count is even) and 64 queries: its four waves then need the
+// same key tiles (nine per 64 aligned queries), so none idles at a barrier
+// while the others compute.
 constexpr int kPrefillWavesGlobal = 8;
 constexpr int kPrefillWavesLocal = 4;
+constexpr int prefill_wave_queries(int kind) { return kind == 0 ? 32 : 48; }
 constexpr int prefill_heads_per_block(int kind, int heads_per_group) {
   return kind == 0 && heads_per_group % 2 == 0 ? 2 : 1;
 }
 constexpr int prefill_block_queries(int kind, int heads_per_group) {
-  return 32 * (kind == 0 ? kPrefillWavesLocal : kPrefillWavesGlobal) / prefill_heads_per_block(kind, heads_per_group);
+  return prefill_wave_queries(kind) * (kind == 0 ? kPrefillWavesLocal : kPrefillWavesGlobal) /
+         prefill_heads_per_block(kind, heads_per_group);
 }
 
 struct PrefillParams {

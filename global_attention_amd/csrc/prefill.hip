@@ -8,12 +8,12 @@
 // the parameter label"). The score matrix is never materialised (section "KV
 // memory: nine growing caches, not 52" notes flash-style kernels avoid it).
 //
-// Tiling. A block is NWAVES wavefronts x QW queries; on global layers all of
-// one query head, on local layers two query heads of one KV group, each with
-// 64 queries (so the four waves read the same key tiles). KV tiles of 64 keys
-// are double-buffered in LDS. Each wave computes
-// S^T = K Q'^T with v_mfma_f32_16x16x32_bf16 (key blocks of 16 on M, two
-// 16-query column blocks on N): a lane holds one query of each column block,
+// Tiling. A block is NWAVES wavefronts x QW queries; on global layers 8 x 48
+// queries of one query head, on local layers 4 x 32: two query heads of one
+// KV group, each with 64 queries (so the four waves read the same key tiles).
+// KV tiles of 64 keys are double-buffered in LDS. Each wave computes
+// S^T = K Q'^T with v_mfma_f32_16x16x32_bf16 (key blocks of 16 on M, three
+// or two 16-query column blocks on N): a lane holds one query of each column block,
 // a query's 64 keys of a tile are spread over the four 16-lane groups, and
 // the row max is an in-lane max plus two lane swaps (v_permlane16_swap, then
 // v_permlane32_swap). The S accumulators are packed to bf16 and fed directly
@@ -56,9 +56,7 @@
 
 namespace beam {
 
-constexpr int QW = 32;                   // queries per wave
-constexpr int NB = QW / 32;              // 32-query column blocks (verify's 32x32x16 layout)
-constexpr int QB = QW / 16;              // 16-query column blocks (prefill's 16x16x32 layout)
+constexpr int VQW = 32;                  // (token, head) rows per verify wave (one 32x32x16 N-block)
 constexpr int BN = 64;                   // keys per tile
 constexpr int K_TILE = BN * D;           // bf16 elements
 constexpr int V_TILE = D * BN;
@@ -394,10 +392,14 @@ __device__ __forceinline__ void scale_frags(u32x4 (&qf)[NF], float k_scale) {
 
 // ---------------------------------------------------------------- kernel
 // HB query heads (of one KV group) per block; wave w takes head w / (NWAVES /
-// HB) and queries 32 (w % (NWAVES / HB)) .. +31 of the block's query range.
+// HB) and queries QW (w % (NWAVES / HB)) .. +QW-1 of the block's query range.
 template <int KIND, int NWAVES, int KV_FP8, int HB>
 __global__ void __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_attn_kernel(PrefillParams p) {
+  // Queries per wave: three 16-query column blocks on global layers (each K
+  // and V^T operand read from LDS feeds three MFMAs), two on local layers.
+  constexpr int QW = prefill_wave_queries(KIND);
+  constexpr int QB = QW / 16;
   constexpr int WQ = NWAVES / HB;  // waves per head
   constexpr int BM = WQ * QW;      // queries per block
   static_assert(16 % NWAVES == 0 && NWAVES % HB == 0, "tile split");
@@ -1018,15 +1020,15 @@ verify_attn_kernel(PrefillParams p) {
 
   // This lane's row and the wave's range of query positions.
   const int n_rows = len * hpg;
-  const int r = QW * w + n;
+  const int r = VQW * w + n;
   const bool row_valid = r < n_rows;
   const int tok_j = row_valid ? r / hpg : 0;
   const int h = g * hpg + (row_valid ? r - tok_j * hpg : 0);
   const int t_row = start + tok_j;
-  const int r_lo = QW * w;
+  const int r_lo = VQW * w;
   const bool wave_active = r_lo < n_rows;
   const int wq_lo = start + r_lo / hpg;
-  const int wq_hi = start + (min(r_lo + QW, n_rows) - 1) / hpg;
+  const int wq_hi = start + (min(r_lo + VQW, n_rows) - 1) / hpg;
 
   u32x4 qf[8];
   {

@@ -1,7 +1,8 @@
 """GPU parity at the full benchmark sizes against the float64 oracle:
 every output element of the T=32768 local prefill (the oracle takes each
-512-query block with the keys of its window), three rows of every 256-query
-block of the T=32768 global prefill (its first, its last and a seeded one),
+512-query block with the keys of its window), the first and last row of every
+384-query block of the T=32768 global prefill and a seeded row of every
+48-query wave,
 all 64 sequences x 48 heads of the 64-sequence decode at 64K-128K context
 (global and local), all 8 KV heads of the 1,048,576-token decode, and a
 constructed needle at p = 1,048,576 whose probability has a closed form (the
@@ -107,16 +108,19 @@ def test_prefill_32k_local_full():
 
 
 def test_prefill_32k_global_every_block():
-    """The global-layer output on three rows of every 256-query block (its
-    first, its last, and one seeded row in between), all 48 heads, each over
-    its full causal history."""
+    """The global-layer output on the first and last row of every 384-query
+    block of the global kernel (8 waves x 48 queries; the last block holds
+    128) and on one seeded row inside every 48-query wave, all 48 heads, each
+    over its full causal history."""
     kind = O.GLOBAL
     inp, o, T = _prefill_32k(kind)
     g = np.random.default_rng(21)
-    starts = np.arange(0, T, 256)
-    rows = np.unique(np.concatenate([starts, starts + 255, starts + g.integers(1, 255, len(starts))]))
-    assert len(rows) == 3 * len(starts)
-    acc = Agreement(f"prefill 32K kind={kind} ({len(rows)} rows: 3 per 256-query block)")
+    blocks = np.arange(0, T, 384)
+    waves = np.arange(0, T, 48)
+    rows = np.unique(np.concatenate([blocks, np.minimum(blocks + 383, T - 1),
+                                     np.minimum(waves + g.integers(1, 47, len(waves)), T - 1)]))
+    assert len(rows) >= 2 * len(blocks) + len(waves) - 2
+    acc = Agreement(f"prefill 32K kind={kind} ({len(rows)} rows: the ends of each 384-query block, one per 48-query wave)")
 
     def chunk(job):
         rs, g = job
