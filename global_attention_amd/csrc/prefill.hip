@@ -506,9 +506,9 @@ prefill_attn_kernel(PrefillParams p) {
   // c16, chunk 4kk + lg (chunks 8..15 are the second coordinate half; key
   // block kb adds 16 rows); V^T row c16, chunk 4c2 + lg (row block db adds 16
   // rows).
-  int koff[4], voff[2];
+  int koff[2], voff[2];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) koff[kk] = k_off(c16, 4 * kk + lg);
+  for (int kk = 0; kk < 2; ++kk) koff[kk] = k_off(c16, 4 * kk + lg);  // d-steps 2, 3: + K_HALF
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2) voff[c2] = v_off(c16, 4 * c2 + lg);
   [[maybe_unused]] CodeOffsets16 co;
@@ -541,7 +541,7 @@ prefill_attn_kernel(PrefillParams p) {
         if constexpr (decltype(CODES)::value)
           a = code_kfrag16(reinterpret_cast<const uint8_t*>(sK), co, kk, kb);
         else
-          a = *reinterpret_cast<const u32x4*>(sK + koff[kk] + 1024 * kb);
+          a = *reinterpret_cast<const u32x4*>(sK + koff[kk & 1] + K_HALF * (kk >> 1) + 1024 * kb);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qf[qb][kk]),
