@@ -13,7 +13,8 @@
 // KV group, each with 64 queries (so the four waves read the same key tiles).
 // KV tiles of 64 keys are double-buffered in LDS. Each wave computes
 // S^T = K Q'^T with v_mfma_f32_16x16x32_bf16 (key blocks of 16 on M, three
-// or two 16-query column blocks on N): a lane holds one query of each column block,
+// or two 16-query column blocks on N, so each K or V^T operand read from LDS
+// feeds three or two MFMAs): a lane holds one query of each column block,
 // a query's 64 keys of a tile are spread over the four 16-lane groups, and
 // the row max is an in-lane max plus two lane swaps (v_permlane16_swap, then
 // v_permlane32_swap). The S accumulators are packed to bf16 and fed directly
