@@ -104,9 +104,17 @@ __device__ __forceinline__ int v_off(int d, int c) { return d * BN + swz(d, c); 
 
 // Combine a value held by lanes l and l^32 (the two key halves of a query)
 // with v_permlane32_swap, without an LDS round trip.
+// max(a, b) as one v_max_f32. The scores are never NaN; fmaxf would first
+// quiet each operand that came out of a lane swap (which the compiler cannot
+// prove canonical), an extra v_max_f32 per operand.
+__device__ __forceinline__ float max2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float max_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -116,7 +124,7 @@ __device__ __forceinline__ float sum_halves(float x) {
 // layout spreads a query's keys over them): v_permlane16_swap, then 32.
 __device__ __forceinline__ float max_groups(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return max_halves(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+  return max_halves(max2(__uint_as_float(r[0]), __uint_as_float(r[1])));
 }
 __device__ __forceinline__ float sum_groups(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
