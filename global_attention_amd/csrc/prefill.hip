@@ -1316,6 +1316,321 @@ verify_attn_kernel(PrefillParams p) {
 
 // Merge the key splits of one (token, query head) of a verify chunk by
 // log-sum-exp, then apply the gate. One block of 128 threads (a coordinate each).
+// Verify over an FP8 cache for chunks of at most 48 (token, query head) rows
+// of a KV head (an 8-token draft at 6 query heads per KV head): one wave holds
+// all rows as three 16-row column blocks of v_mfma_f32_16x16x32_bf16, so every
+// code tile is converted to bf16 once per block (not once per wave) and no
+// MFMA is spent on padding rows. Tiles, key order (krow_key16), masks and the
+// softmax are those of the prefill kernel; rows are (token, head) pairs as in
+// verify_attn_kernel, whose partials and single-split epilogue this kernel
+// writes in the same format. NSUB 16-KiB code buffers: the DMA runs NSUB - 1
+// tiles ahead; two of them hold the bf16 workspace tiles afterwards.
+template <int KIND, int NSUB>
+__global__ void __launch_bounds__(64) verify48_fp8_kernel(PrefillParams p) {
+  constexpr bool local = (KIND == 0);
+  constexpr int QB = 3;
+  static_assert(NSUB >= 2, "the workspace tile needs two code buffers");
+  constexpr int kCodeBytes = NSUB * 16384;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[kCodeBytes / 2 + (KIND == 1 ? 2 * kVerifyMaxPages : 0)];
+  int* const s_pages = reinterpret_cast<int*>(smem + kCodeBytes / 2);
+  uint8_t* const codes = reinterpret_cast<uint8_t*>(smem);
+
+  const int hpg = p.H / p.G;
+  int b = blockIdx.x;
+  const int g = b % p.G;
+  b /= p.G;
+  const int sp = b % p.n_splits;
+  const int seq = b / p.n_splits;
+  const int cu0 = p.cu[seq];
+  const int len = p.cu[seq + 1] - cu0;
+  if (len <= 0) return;
+  const int start = p.start_pos[seq];
+  const int cseq = p.seq_idx[seq];
+  const int W = p.window;
+  const int t_last = start + len - 1;
+  const int lane = threadIdx.x;
+  if (start < 0 || (p.n_splits == 1 && t_last > p.max_pos)) {
+    if (p.n_splits == 1)  // NaN rows (with several splits the combine writes them)
+      for (int i = lane; i < len * hpg * D; i += 64) {
+        const int r = i / D;
+        p.out[((size_t)(cu0 + r / hpg) * p.H + g * hpg + r % hpg) * D + i % D] = 0x7fc0;
+      }
+    return;
+  }
+
+  KeySource ks;
+  ks.kw = p.kw + (size_t)g * p.P * D;
+  ks.vw = p.vw + (size_t)g * D * p.P;
+  ks.ck = p.ck;
+  ks.cv = p.cv;
+  ks.page_stride = 0;
+  ks.bt_row = KIND == 1 ? p.bt + (size_t)cseq * p.max_pages : nullptr;
+  const bool cache_ok = cseq >= 0 && cseq < p.n_cache_seqs && (KIND == 0 || ((start + 15) >> 4) <= p.max_pages);
+  ks.ws_off = ws_region_base(cu0, seq) - (start & ~63);
+  ks.P = p.P;
+  ks.kind = KIND;
+  ks.window = W;
+  const int j_ws = start >> 6;
+  const int kmin = local ? max(0, start - (W - 1)) : 0;
+  const int j_first = cache_ok ? kmin >> 6 : max(kmin >> 6, j_ws);
+  const int j_last = t_last >> 6;
+  const int j_lo = j_first + sp * p.split_tiles;
+  if (j_lo > j_last) return;  // past this sequence's keys; the combine skips the split
+  const int j_hi = min(j_last, j_lo + p.split_tiles - 1);
+
+  const int c16 = lane & 15, lg = lane >> 4;
+  const DmaPlan<1> plan = make_dma_plan<1, true>(0, lane);
+  const CodeSource cs8 = make_code_source(p, KIND, cseq, g);
+  const int page0 = 4 * j_lo;
+  if (KIND == 1 && cache_ok) {
+    const int n_pg = 4 * (min(j_hi, j_ws - 1) - j_lo + 1);
+    for (int i = lane; i < n_pg; i += 64) s_pages[i] = ks.bt_row[page0 + i];
+  }
+
+  // Row 16qb + c16 of column block qb: token r / hpg, head r % hpg.
+  const int n_rows = len * hpg;
+  bool rv[QB];
+  int rtok[QB], rh[QB], t_row[QB];
+  u32x4 qf[QB][4];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int r = 16 * qb + c16;
+    rv[qb] = r < n_rows;
+    rtok[qb] = rv[qb] ? r / hpg : 0;
+    rh[qb] = g * hpg + (rv[qb] ? r - rtok[qb] * hpg : 0);
+    t_row[qb] = start + rtok[qb];
+    const uint16_t* qrow = p.qp + ((size_t)(cu0 + rtok[qb]) * p.H + rh[qb]) * D + 8 * lg;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qf[qb][kk] = rv[qb] ? *reinterpret_cast<const u32x4*>(qrow + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
+    scale_frags(qf[qb], p.k_scale);  // code space: q' k_scale against the codes
+  }
+  const int wq_lo = start, wq_hi = t_last;
+
+  f32x4 o[QB][8];
+  float m_run[QB], l_run[QB];
+  f32x4 sref[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[qb] = kNegInf;
+    l_run[qb] = 0.f;
+    sref[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  int koff[2], voff[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) koff[kk] = k_off(c16, 4 * kk + lg);
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) voff[c2] = v_off(c16, 4 * c2 + lg);
+  const CodeOffsets16 co = code_offsets16(c16, lg);
+
+  auto active = [&](int j) __attribute__((always_inline)) {
+    const int k0 = j * BN;
+    return k0 <= wq_hi && !(local && k0 + BN - 1 < wq_lo - (W - 1));
+  };
+  auto needs_mask = [&](int j) __attribute__((always_inline)) {
+    const int k0 = j * BN;
+    return (k0 + BN - 1 > wq_lo) || (local && k0 < wq_hi - (W - 1));
+  };
+  // One 64-key tile: a code tile at `slot` (CODES) or the bf16 tile at smem.
+  auto tile = [&](int j, auto CODES, const uint8_t* slot) __attribute__((always_inline)) {
+    constexpr bool C = decltype(CODES)::value;
+    const uint16_t* sK = smem;
+    const uint16_t* sV = smem + K_TILE;
+    f32x4 st[QB][4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        u32x4 a;
+        if constexpr (C)
+          a = code_kfrag16(slot, co, kk, kb);
+        else
+          a = *reinterpret_cast<const u32x4*>(sK + koff[kk & 1] + K_HALF * (kk >> 1) + 1024 * kb);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          st[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qf[qb][kk]),
+                                                              kk == 0 ? sref[qb] : st[qb][kb], 0, 0, 0);
+      }
+    if (needs_mask(j)) {  // element i of block (qb, kb): key 32(kb >> 1) + 8lg + 4(kb & 1) + i of the tile
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int sk = j * BN + 32 * (kb >> 1) + 8 * lg + 4 * (kb & 1) + i;
+            if (!visible(KIND, W, t_row[qb], sk)) st[qb][kb][i] = kNegInf;
+          }
+    }
+    // Reference shift per row, as in the prefill kernel.
+    bool need[QB];
+    bool any_need = false;
+    float mt[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float x = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x = fmaxf(x, st[qb][kb][i]);
+      mt[qb] = max_groups(x);
+      need[qb] = (m_run[qb] == kNegInf) ? (mt[qb] != kNegInf) : (mt[qb] > kRescaleThreshold);
+      any_need = any_need || need[qb];
+    }
+    if (__any(any_need)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float delta = need[qb] ? mt[qb] : 0.f;
+        const bool first = m_run[qb] == kNegInf;
+        const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(-delta);
+        if (need[qb]) m_run[qb] = (first ? 0.f : m_run[qb]) + delta;
+        const float rr = m_run[qb] == kNegInf ? 0.f : -m_run[qb];
+        sref[qb] = f32x4{rr, rr, rr, rr};
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[qb][db][i] *= alpha;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) st[qb][kb][i] -= delta;
+      }
+    }
+    // P^T of key chunk c2: lane group lg holds keys 32c2 + 8lg + 0..7.
+    u32x4 pf[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        float e[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          e[i] = __builtin_amdgcn_exp2f(st[qb][2 * c2][i]);
+          e[4 + i] = __builtin_amdgcn_exp2f(st[qb][2 * c2 + 1][i]);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          pf[qb][c2][c] = pack_bf16x2(e[2 * c], e[2 * c + 1]);
+          l_run[qb] = sum_bf16x2(pf[qb][c2][c], l_run[qb]);
+        }
+      }
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        u32x4 a;
+        if constexpr (C)
+          a = code_vfrag16(slot, co, c2, db);
+        else
+          a = *reinterpret_cast<const u32x4*>(sV + voff[c2] + 1024 * db);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(pf[qb][c2]), o[qb][db], 0, 0, 0);
+      }
+  };
+  // wait until at most VM vector memory operations are in flight, then a bare s_barrier
+  auto barrier = [&](auto VM) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(decltype(VM)::value));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  __builtin_amdgcn_s_waitcnt(0);  // Q' and page ids in
+  __syncthreads();
+
+  int jt = j_lo;
+  // Code tiles of the cached keys below the chunk: NSUB buffers, the DMA
+  // NSUB - 1 tiles ahead; each step waits only for the tile the next step
+  // computes (a code tile is 16 DMA instructions of the wave).
+  constexpr int AHEAD = NSUB - 1;
+  constexpr int kPerTile = 16;
+  const int jc = min(j_hi, j_ws - 1);
+  if (j_lo <= jc) {
+    auto page_of = [&](int pg) { return s_pages[pg - page0]; };
+    auto dma_c = [&](int j, int u) __attribute__((always_inline)) {
+      dma_code_tile<1, KIND == 1, true>(cs8, page_of, 0, lane, j * BN, codes + 16384 * u);
+    };
+    auto wait_next = [&](int j) __attribute__((always_inline)) {
+      const int ahead = min(j + AHEAD, jc) - (j + 1);  // tiles in flight beyond tile j + 1
+      if (AHEAD >= 3 && ahead >= 2)
+        barrier(std::integral_constant<int, 2 * kPerTile>{});
+      else if (AHEAD >= 2 && ahead >= 1)
+        barrier(std::integral_constant<int, kPerTile>{});
+      else
+        barrier(std::integral_constant<int, 0>{});
+    };
+#pragma unroll
+    for (int u = 0; u < AHEAD; ++u)
+      if (j_lo + u <= jc) dma_c(j_lo + u, u);
+    wait_next(j_lo - 1);
+    for (; jt <= jc; jt += NSUB) {
+      bool done = false;
+      static_for<NSUB>([&](auto U) __attribute__((always_inline)) {
+        constexpr int u = decltype(U)::value;
+        const int j = jt + u;
+        if (done || j > jc) {
+          done = true;
+          return;
+        }
+        if (j + AHEAD <= jc) dma_c(j + AHEAD, (u + AHEAD) % NSUB);
+        if (active(j)) tile(j, std::true_type{}, codes + 16384 * u);
+        wait_next(j);
+      });
+      if (done) break;
+    }
+    jt = jc + 1;
+  }
+  // The chunk's own tiles (bf16, from the workspace) in the first two buffers.
+  for (; jt <= j_hi; ++jt) {
+    plan.copy(ks.kw, ks.vw, ks.ws_off, jt * BN, smem, smem + K_TILE);
+    barrier(std::integral_constant<int, 0>{});
+    if (active(jt)) tile(jt, std::false_type{}, codes);
+    barrier(std::integral_constant<int, 0>{});
+  }
+
+  // Partials of this split (or, with a single split, the gated output with the
+  // combine's arithmetic): lane holds row 16qb + c16, coordinates 16db + 4lg + 0..3.
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = sum_groups(l_run[qb]);
+    if (!rv[qb]) continue;
+    const int h = rh[qb];
+    if (p.n_splits == 1) {
+      const size_t idx = ((size_t)(cu0 + rtok[qb]) * p.H + h) * D + 4 * lg;
+      const float bias = p.gate_bias ? p.gate_bias[h] : 0.f;
+      const float inv = (m_run[qb] != kNegInf && l_tot > 0.f) ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
+      u32x2 gv[8];
+#pragma unroll
+      for (int db = 0; db < 8; ++db) gv[db] = *reinterpret_cast<const u32x2*>(p.gate + idx + 16 * db);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const float gz[4] = {bf16lo(gv[db][0]), bf16hi(gv[db][0]), bf16lo(gv[db][1]), bf16hi(gv[db][1])};
+        uint16_t y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ov = o[qb][db][e] * inv * p.v_scale;
+          const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-(gz[e] + bias)));
+          y[e] = __builtin_bit_cast(uint16_t, (__bf16)(ov * sg));
+        }
+        *reinterpret_cast<u32x2*>(p.out + idx + 16 * db) =
+            u32x2{(uint32_t)y[0] | ((uint32_t)y[1] << 16), (uint32_t)y[2] | ((uint32_t)y[3] << 16)};
+      }
+      continue;
+    }
+    const size_t row = ((size_t)(cu0 + rtok[qb]) * p.H + h) * p.n_splits + sp;
+    if (lg == 0) {
+      p.part_ml[2 * row] = m_run[qb];
+      p.part_ml[2 * row + 1] = l_tot;
+    }
+    float* acc = p.part_acc + row * D + 4 * lg;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(acc + 16 * db) = o[qb][db];
+  }
+}
+
 __global__ void __launch_bounds__(128) verify_combine_kernel(VerifyCombineParams p) {
   const int tok = blockIdx.x / p.H;
   const int h = blockIdx.x - tok * p.H;
@@ -1357,13 +1672,22 @@ __global__ void __launch_bounds__(128) verify_combine_kernel(VerifyCombineParams
   p.out[idx] = __builtin_bit_cast(uint16_t, rr[0]);
 }
 
+// Code buffers of verify48_fp8_kernel (16 KiB each; 2 KiB of page ids on top).
+constexpr int kVerify48Bufs = 2;
+
 hipError_t launch_verify_attn(const PrefillParams& p, int max_rows, hipStream_t s) {
   clear_stale_error();
   if (p.split_tiles * 4 > kVerifyMaxPages) return hipErrorInvalidValue;
   const long long blocks = (long long)p.G * p.n_splits * p.n_seqs;
   const dim3 grid((unsigned)blocks), block4(64 * kVerifyWaves), block2(128);
   const bool two = p.kv_fp8 && max_rows <= 64;  // FP8 cache, chunks of at most 64 rows: 2-wave blocks
-  if (p.kind == 0 && !p.kv_fp8)
+  const bool one = p.kv_fp8 && max_rows <= 48;  // at most 48 rows: one wave holds them all
+  const dim3 block1(64);
+  if (p.kind == 0 && one)
+    hipLaunchKernelGGL((verify48_fp8_kernel<0, kVerify48Bufs>), grid, block1, 0, s, p);
+  else if (p.kind == 1 && one)
+    hipLaunchKernelGGL((verify48_fp8_kernel<1, kVerify48Bufs>), grid, block1, 0, s, p);
+  else if (p.kind == 0 && !p.kv_fp8)
     hipLaunchKernelGGL((verify_attn_kernel<0, 0, 4>), grid, block4, 0, s, p);
   else if (p.kind == 0 && two)
     hipLaunchKernelGGL((verify_attn_kernel<0, 1, 2>), grid, block2, 0, s, p);

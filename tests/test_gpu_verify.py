@@ -229,9 +229,9 @@ def _gather_global_codes(cache, bt_row, n_keys):
 
 def test_verify_64seq_128k_draft8_fp8_sampled():
     """The full-size verify step over an FP8 cache of seeded random codes
-    (inputs), 8-token drafts: the kernel with two-wave blocks (at most 64 rows
-    per chunk). Three sampled sequences against the oracle, which decodes the
-    cached codes itself."""
+    (inputs), 8-token drafts: the one-wave kernel that holds all 48 (token,
+    head) rows of a chunk. Three sampled sequences against the oracle, which
+    decodes the cached codes itself."""
     import torch
     n, L = 64, 8
     starts = synth.decode_positions(3, n, 65536, 131071 - L)
@@ -296,6 +296,53 @@ def test_verify_fp8_short_chunks_both_block_shapes(kind):
                                     x["k_norm_w"], x["gate"][s0:s0 + m], np.arange(s0, s0 + m), np.arange(s0 + m),
                                     fp8_cache=(*fp8, s0))
             compare(o, ref, f"verify fp8 kind={kind} step{step} seq{i} [{s0},{s0 + m})")
+        done = [d + c for d, c in zip(done, chunk)]
+
+
+@pytest.mark.parametrize("kind", [O.LOCAL, O.GLOBAL])
+def test_verify_fp8_48_row_kernel(kind):
+    """Chunks of at most 8 tokens (48 rows of a KV head) over an FP8 cache run
+    in the one-wave kernel (three 16-row column blocks of 16x16x32 MFMA); the
+    same call with max_chunk_len 9 runs in the two-wave 32x32x16 kernel. Both
+    are compared with the oracle and with each other (the MFMA shapes sum in
+    different orders, so not bit for bit). Histories of 700, 130, 60 (the
+    8-token chunk crosses a 64-key tile), 1 and 0 tokens; one step with
+    64-key splits (one tile per split, partials and combine), one with the
+    default split."""
+    fp8 = (0.6, 0.9)
+    hist = [700, 130, 60, 1, 0]
+    steps = [[8, 1, 8, 3, 5], [2, 8, 7, 8, 1]]
+    total = [h + sum(st[i] for st in steps) for i, h in enumerate(hist)]
+    inps = [synth.attention_inputs(36, 10 * kind + i, m) for i, m in enumerate(total)]
+    for x in inps[1:]:
+        x["q_norm_w"], x["k_norm_w"] = inps[0]["q_norm_w"], inps[0]["k_norm_w"]
+    caches = [_cache(kind, 36, total, fp8)[0] for _ in range(2)]
+    hs = [i for i, h in enumerate(hist) if h > 0]
+    for c in caches:
+        _prefill(c, [_slice(inps[i], 0, hist[i]) for i in hs], [0] * len(hs), hs)
+    done = list(hist)
+    for step, chunk in enumerate(steps):
+        batch = [_slice(inps[i], done[i], chunk[i]) for i in range(len(hist))]
+        max_pos = max(s + b["q"].shape[0] - 1 for s, b in zip(done, batch))
+        sk = 64 if step == 0 else 0
+        say(f"[case] verify fp8 kind={kind} step={step} lens={chunk} split={sk}: 48-row and two-wave kernels")
+        o1 = _call(ga.verify, caches[0], batch, list(done), list(range(len(hist))), max_pos=max_pos, split_keys=sk)
+        lens, cu, cat = _packed(batch)
+        w = batch[0]
+        out = ga.verify(CFG, caches[1], cat("q"), cat("k"), cat("v"), dev_bf16(w["q_norm_w"]),
+                        dev_bf16(w["k_norm_w"]), cat("gate"), dev_i32(cu), dev_i32(list(range(len(hist)))),
+                        dev_i32(done), 9, max_pos, split_keys=sk)
+        sync()
+        o2 = host_bits(out)
+        for i, o in enumerate(o1):
+            s0, m, x = done[i], chunk[i], inps[i]
+            ref = O.attention_layer(kind, x["q"][s0:s0 + m], x["k"][:s0 + m], x["v"][:s0 + m], x["q_norm_w"],
+                                    x["k_norm_w"], x["gate"][s0:s0 + m], np.arange(s0, s0 + m), np.arange(s0 + m),
+                                    fp8_cache=(*fp8, s0))
+            compare(o, ref, f"verify fp8 48-row kind={kind} step{step} seq{i} [{s0},{s0 + m})")
+            compare(o2[cu[i]:cu[i + 1]], ref, f"verify fp8 two-wave kind={kind} step{step} seq{i}")
+            a, b = bf16_to_f64(o), bf16_to_f64(o2[cu[i]:cu[i + 1]])
+            assert np.max(np.abs(a - b)) <= 2e-2, f"step {step} seq {i}: the two kernels differ"
         done = [d + c for d, c in zip(done, chunk)]
 
 
