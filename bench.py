@@ -65,7 +65,7 @@ _KERNEL_SOURCES = {
     "decode_fp8_kernel<1>": "decode.hip",
     "verify_attn_kernel<1, 0, 4>": "prefill.hip",
     "verify_attn_kernel<0, 0, 4>": "prefill.hip",
-    "verify_attn_kernel<1, 1, 2>": "prefill.hip",
+    "verify48_fp8_kernel<1, 2>": "prefill.hip",
     "router_gemm_kernel<true>": "router.hip",
     "gemm_bf16_kernel<1>": "gemm.hip",
     "gemm_bf16_kernel<0>": "gemm.hip",
@@ -1063,7 +1063,15 @@ def main():
             "global_fp8": {"ms_per_call": round(v["global_fp8"]["ms_per_call"], 4),
                            "device_ms_per_call": _r4(v["global_fp8"]["device_ms"]),
                            "gbs_split": round(v["global_fp8"]["gbs_split"], 1),
-                           "speedup_vs_8_decode_calls": round(v["global_fp8"]["vs_decode_calls"], 2)},
+                           "speedup_vs_8_decode_calls": round(v["global_fp8"]["vs_decode_calls"], 2),
+                           "roofline": {"kernel": "verify48_fp8_kernel<1, 2>", "bound": "hbm",
+                                        "achieved": round(v["global_fp8"]["gbs_split"], 1), "peak": PEAK_HBM_GBS,
+                                        "unit": "GB/s",
+                                        "frac": round(v["global_fp8"]["gbs_split"] / PEAK_HBM_GBS, 4),
+                                        "traffic": recorded_traffic("verify48_fp8_kernel<1, 2>"),
+                                        "avg_launch_ms": round(v["global_fp8"]["split_ms"], 4),
+                                        "bytes_per_launch": v["global_fp8"]["bytes"],
+                                        **measured(None, v["global_fp8"]["gbs_split"], "hbm")}},
         }
         if not args.no_cpu_baseline:
             import numpy as np
