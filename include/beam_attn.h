@@ -159,7 +159,8 @@ beam_status beam_attn_prefill(const beam_attn_config *cfg, const beam_kv_cache *
  * outside [0, max_pos], or whose seq_idx[i] names no cache sequence, is not read
  * and its output rows are NaN.
  * split_keys: keys per split (multiple of 128, <= 65536), or 0 for the default
- * (2048 on GLOBAL layers, 128 on LOCAL layers).
+ * (128 on LOCAL layers; on GLOBAL layers 4096 when n_seqs * n_kv_heads *
+ * ((max_pos + 1 + 4095) / 4096) >= 1024, else 2048).
  * workspace: >= beam_decode_workspace_bytes(cfg, kind, n_seqs, max_pos, split_keys). */
 beam_status beam_attn_decode(const beam_attn_config *cfg, const beam_kv_cache *cache,
                              const beam_bf16 *q_raw, const beam_bf16 *q_norm_w,

@@ -406,10 +406,11 @@ def test_host_side_under_address_sanitizer(tmp_path):
     assert kw % 256 == 0 and vw % 256 == 0 and P % 64 == 0 and P >= 1000
     assert n_qtiles == -(-600 // 384)  # 384-query blocks on global layers (8 waves x 48 queries)
 
-    # decode of one sequence at position 2^20 - 1, default split (2048 keys):
-    # Q' then the (max, sum) and accumulator partials of 512 splits
+    # decode of one sequence at position 2^20 - 1, default split (4096 keys:
+    # 8 KV heads x 256 splits reach 1024 blocks): Q' then the (max, sum) and
+    # accumulator partials of 256 splits
     st, calls, n_splits, kpw, ml, acc = map(int, by["decode_call"][0])
-    assert st == 0 and calls == 3 and n_splits == 512
+    assert st == 0 and calls == 3 and n_splits == 256 and kpw == 1024
     assert ml == H * D * 2 and acc == ml + -(-(H * n_splits * 2 * 4) // 256) * 256
     assert acc + H * n_splits * D * 4 <= ga.decode_workspace_bytes(cfg, ga.GLOBAL, 1, 2 ** 20 - 1)
 
